@@ -1,0 +1,174 @@
+"""Seeded synthetic inputs for the MoE layer: activations, router, bias and
+GGUF-blocked expert weights.
+
+Input generation only.  It contains none of the layer's arithmetic: no dequant,
+no routing, no FFN.  The quantizers below *produce* Q8_0 / Q4_0 blocks from fp32
+samples (the way a checkpoint converter would); the layer only ever *reads*
+blocks.  Both the GPU path and the CPU oracle are fed from here.
+
+Everything is plain torch so the same code runs on the CPU (small shapes) or on
+the GPU (the multi-GB layers, where a CPU generator would take minutes).  A
+(config, tensor, expert) triple names an independent torch generator, so each
+tensor and each expert can be regenerated alone.  The CPU and GPU generators
+draw different streams for the same seed: a test uses one device for one layer.
+
+Block byte layout (GGUF, little-endian, no padding):
+  Q8_0: [fp16 d][32 x int8 q]            34 bytes, value = d*q
+  Q4_0: [fp16 d][16 bytes of nibbles]    18 bytes, value = d*(q-8);
+        byte i holds element i in its low nibble and element i+16 in its high
+        nibble.
+"""
+
+import math
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from .configs import BF16, F32, Q4_0, Q8_0, BLOCK_BYTES, LayerConfig
+
+BASE_SEED = 20261202
+
+# tensor ids (part of every seed)
+T_X, T_ROUTER, T_GATE, T_UP, T_DOWN, T_SGATE, T_SUP, T_SDOWN = range(8)
+
+
+def seed_of(cid: int, tid: int, eid: int) -> int:
+    """A 63-bit seed for tensor `tid`, expert (or batch) `eid` of workload `cid`."""
+    h = BASE_SEED
+    for v in (cid, tid, eid):
+        h = (h * 6364136223846793005 + 1442695040888963407 + v) & ((1 << 64) - 1)
+        h ^= h >> 29
+    return h & ((1 << 63) - 1)
+
+
+def normal(shape, std, seed, device="cpu"):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std
+
+
+def _round_half_away(v):
+    return torch.sign(v) * torch.floor(torch.abs(v) + 0.5)
+
+
+def quantize_q8_0(w: torch.Tensor) -> torch.Tensor:
+    """fp32 [..., n] -> uint8 [..., n/32*34].  d = amax/127 (fp32), codes
+    round-half-away(x/d) clamped to +-127, d stored as fp16 (round to nearest
+    even).  An all-zero block gets d = 0 and zero codes."""
+    *lead, n = w.shape
+    assert n % 32 == 0
+    b = w.reshape(*lead, n // 32, 32)
+    amax = b.abs().amax(dim=-1, keepdim=True)
+    d = amax / 127.0
+    inv = torch.where(d > 0, 1.0 / torch.where(d > 0, d, torch.ones_like(d)),
+                      torch.zeros_like(d))
+    q = _round_half_away(b * inv).clamp(-127, 127).to(torch.int8)
+    d16 = d.to(torch.float16).view(torch.int16).view(torch.uint8)  # [..., nb, 2]
+    out = torch.cat([d16.reshape(*lead, n // 32, 2), q.view(torch.uint8)], dim=-1)
+    return out.reshape(*lead, n // 32 * 34).contiguous()
+
+
+def quantize_q4_0(w: torch.Tensor) -> torch.Tensor:
+    """fp32 [..., n] -> uint8 [..., n/32*18].  m = the element of largest
+    magnitude (first on ties, sign kept), d = m / -8, codes
+    min(15, floor(x/d + 8.5)), d stored as fp16.  d is negative whenever m > 0.
+    An all-zero block gets d = 0 and codes 8."""
+    *lead, n = w.shape
+    assert n % 32 == 0
+    b = w.reshape(*lead, n // 32, 32)
+    idx = b.abs().argmax(dim=-1, keepdim=True)
+    m = torch.gather(b, -1, idx)
+    d = m / -8.0
+    nz = d != 0
+    inv = torch.where(nz, 1.0 / torch.where(nz, d, torch.ones_like(d)),
+                      torch.zeros_like(d))
+    q = torch.floor(b * inv + 8.5).clamp(0, 15).to(torch.uint8)
+    packed = q[..., :16] | (q[..., 16:] << 4)
+    d16 = d.to(torch.float16).view(torch.int16).view(torch.uint8)
+    out = torch.cat([d16.reshape(*lead, n // 32, 2), packed], dim=-1)
+    return out.reshape(*lead, n // 32 * 18).contiguous()
+
+
+QUANTIZERS = {Q8_0: quantize_q8_0, Q4_0: quantize_q4_0}
+
+
+def quantized_normal(rows, cols, std, qtype, seed, device):
+    return QUANTIZERS[qtype](normal((rows, cols), std, seed, device))
+
+
+def to_act_dtype(t: torch.Tensor, dtype: str) -> torch.Tensor:
+    if dtype == F32:
+        return t.contiguous()
+    if dtype == BF16:
+        return t.to(torch.bfloat16).contiguous()   # round to nearest even
+    raise ValueError(dtype)
+
+
+@dataclass
+class Layer:
+    cfg: LayerConfig
+    router: torch.Tensor            # [E][H] f32|bf16
+    bias: Optional[torch.Tensor]    # [E] f32 or None
+    w_gate: torch.Tensor            # uint8 [E][F][H/32*Bq]
+    w_up: torch.Tensor              # uint8 [E][F][H/32*Bq]
+    w_down: torch.Tensor            # uint8 [E][H][F/32*Bq]
+    s_gate: Optional[torch.Tensor] = None   # uint8 [Fs][H/32*Bs]
+    s_up: Optional[torch.Tensor] = None
+    s_down: Optional[torch.Tensor] = None   # uint8 [H][Fs/32*Bs]
+
+    def to(self, device):
+        f = lambda t: None if t is None else t.to(device)
+        return Layer(self.cfg, f(self.router), f(self.bias), f(self.w_gate),
+                     f(self.w_up), f(self.w_down), f(self.s_gate), f(self.s_up),
+                     f(self.s_down))
+
+
+def zipf_bias(n_experts: int, s: float) -> torch.Tensor:
+    """b_e = -s*ln(e+1): expert 0 hottest."""
+    return torch.tensor([-s * math.log(e + 1) for e in range(n_experts)],
+                        dtype=torch.float32)
+
+
+def make_layer(cfg: LayerConfig, device="cpu", qtype: Optional[str] = None) -> Layer:
+    """All weights of one layer.  `qtype` overrides the routed-expert format
+    (the sweep runs the same fp32 samples through both quantizers)."""
+    H, E, F = cfg.hidden, cfg.n_experts, cfg.ffn
+    q = qtype or cfg.expert_q
+    c = cfg.cid
+    router = to_act_dtype(normal((E, H), cfg.router_std, seed_of(c, T_ROUTER, 0), device),
+                          cfg.router_dtype)
+    bias = zipf_bias(E, cfg.zipf).to(device) if cfg.zipf else None
+    bq = BLOCK_BYTES[q]
+    wg = torch.empty((E, F, H // 32 * bq), dtype=torch.uint8, device=device)
+    wu = torch.empty_like(wg)
+    wd = torch.empty((E, H, F // 32 * bq), dtype=torch.uint8, device=device)
+    for e in range(E):
+        wg[e] = quantized_normal(F, H, cfg.w_std, q, seed_of(c, T_GATE, e), device)
+        wu[e] = quantized_normal(F, H, cfg.w_std, q, seed_of(c, T_UP, e), device)
+        wd[e] = quantized_normal(H, F, cfg.w_std, q, seed_of(c, T_DOWN, e), device)
+    layer = Layer(cfg, router, bias, wg, wu, wd)
+    if cfg.shared_ffn:
+        Fs, qs = cfg.shared_ffn, cfg.shared_q
+        layer.s_gate = quantized_normal(Fs, H, cfg.w_std, qs, seed_of(c, T_SGATE, 0), device)
+        layer.s_up = quantized_normal(Fs, H, cfg.w_std, qs, seed_of(c, T_SUP, 0), device)
+        layer.s_down = quantized_normal(H, Fs, cfg.w_std, qs, seed_of(c, T_SDOWN, 0), device)
+    return layer
+
+
+def make_x(cfg: LayerConfig, T: int, device="cpu", variant: int = 0) -> torch.Tensor:
+    """[T][H] activations, N(0,1) rounded to the activation dtype."""
+    return to_act_dtype(normal((T, cfg.hidden), 1.0,
+                               seed_of(cfg.cid, T_X, T + 100003 * variant), device),
+                        cfg.act_dtype)
+
+
+def as_numpy_bits(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:
+    """Host copy with bf16 exposed as its uint16 bit pattern (numpy has no bf16)."""
+    if t is None:
+        return None
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()

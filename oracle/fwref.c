@@ -1,0 +1,308 @@
+/*
+ * fwref.c -- CPU oracle for the routed mixture-of-experts FFN layer run on GGUF
+ * Q8_0 / Q4_0 expert weights.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  The GPU library shares no
+ * code, header, table or helper with it, and the GPU path never calls it.
+ *
+ * It is the plain definition of what the layer computes, written for a reader
+ * to check by eye: straight loops, no blocking, no fusion, no reordering.
+ * Dequantised weights are exact in fp32 (an fp16 scale times a code of at most
+ * 8 significant bits fits in 24 bits); every sum is accumulated in fp64 in
+ * ascending index order and rounded to fp32 only where the layer's interface
+ * hands a value over (logits, gate weights, output).
+ *
+ * What is computed, and where the pages describe it:
+ *  - the layer itself: "sparse MoE execution" with grouped routed-expert
+ *    kernels per format (Flyweight 0.2.0 wheel METADATA, "Features" and
+ *    "Quantization"; Flyweight 0.5.1, "Models and formats");
+ *  - Q8_0 and Q4_0 as expert formats (Flyweight 0.5.1, "Models and formats";
+ *    Gemma 4's routed experts must be Q4_0, Flyweight 0.2.0 "Current
+ *    limitations"); the byte layout is GGUF's, which the pages do not print;
+ *  - SwiGLU expert FFNs (vOOM, module layout: layer_runner's block math);
+ *  - top-k routing with k a tunable (vOOM notes: the request-local top-2
+ *    expert schedule) and DeepSeek-shaped sigmoid routing with an always-on
+ *    shared expert (Flyweight 0.2.0, served-families table, K2-Horizon);
+ *  - a fixed-order, deterministic expert combine (vOOM notes: the rejected
+ *    gathered/fused expert prototype that changed the token stream).
+ * Where the pages are silent the plainest reading is taken: selection on the
+ * (biased) logits, descending, ties to the lower expert index, slot order =
+ * selection order; renormalisation divides each selected score by the sum of
+ * the selected scores; the shared expert is added with weight 1.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { REF_F32 = 0, REF_BF16 = 1 };
+enum { REF_Q8_0 = 0, REF_Q4_0 = 1 };
+enum { REF_SOFTMAX = 0, REF_SIGMOID = 1 };
+
+/* IEEE 754 binary16 -> value: 1 sign bit, 5 exponent bits (bias 15), 10
+ * fraction bits; exponent 0 is the subnormal range m * 2^-24. */
+float fwref_half_to_float(uint16_t h)
+{
+    int sign = h >> 15, ex = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)m, -24);
+    else if (ex == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), ex - 25);
+    return (float)(sign ? -v : v);
+}
+
+/* bfloat16 is the top half of a binary32. */
+float fwref_bf16_to_float(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static int block_bytes(int qtype) { return qtype == REF_Q8_0 ? 34 : 18; }
+
+/* Dequantise one row of n elements (n a multiple of 32).
+ * Q8_0 block: [fp16 d][32 int8 q], value_i = d * q_i.
+ * Q4_0 block: [fp16 d][16 bytes], byte i = q_i | q_{i+16} << 4,
+ *             value_i = d * (q_i - 8). */
+void fwref_dequant_row(int qtype, const uint8_t *row, int n, float *out)
+{
+    for (int b = 0; b < n / 32; ++b) {
+        const uint8_t *blk = row + (size_t)b * block_bytes(qtype);
+        float d = fwref_half_to_float((uint16_t)(blk[0] | blk[1] << 8));
+        if (qtype == REF_Q8_0) {
+            for (int i = 0; i < 32; ++i)
+                out[32 * b + i] = d * (float)(int8_t)blk[2 + i];
+        } else {
+            for (int i = 0; i < 16; ++i) {
+                out[32 * b + i] = d * (float)((blk[2 + i] & 15) - 8);
+                out[32 * b + i + 16] = d * (float)((blk[2 + i] >> 4) - 8);
+            }
+        }
+    }
+}
+
+static float act_value(int dtype, const void *base, size_t i)
+{
+    if (dtype == REF_F32)
+        return ((const float *)base)[i];
+    return fwref_bf16_to_float(((const uint16_t *)base)[i]);
+}
+
+/* Router: logits, scoring, top-k selection and renormalised gate weights.
+ *   l[t][e] = fp32( sum_h x[t][h] * W_r[e][h] + b_e )
+ *   ids[t][0..k-1]: experts in descending order of l, ties to the lower index
+ *   softmax: p_e = exp(l_e - max l) / sum_e' exp(l_e' - max l)   (all E)
+ *   sigmoid: p_e = 1 / (1 + exp(-l_e))
+ *   w[t][j] = p_{ids[t][j]} / sum_{i<k} p_{ids[t][i]}
+ * If logits_in is given it replaces the first line (it already holds the bias).
+ * Returns 0, or -1 on a bad argument. */
+int fwref_route(int T, int H, int E, int k, int act_dtype, int router_dtype, int score,
+                const void *x, const void *router_w, const float *bias,
+                const float *logits_in, float *logits, int32_t *ids, float *w)
+{
+    if (T < 0 || H <= 0 || E <= 0 || k < 1 || k > E)
+        return -1;
+    for (int t = 0; t < T; ++t) {
+        float *l = logits + (size_t)t * E;
+        for (int e = 0; e < E; ++e) {
+            if (logits_in) {
+                l[e] = logits_in[(size_t)t * E + e];
+                continue;
+            }
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h)
+                acc += (double)act_value(act_dtype, x, (size_t)t * H + h) *
+                       (double)act_value(router_dtype, router_w, (size_t)e * H + h);
+            if (bias)
+                acc += (double)bias[e];
+            l[e] = (float)acc;
+        }
+        /* k rounds of "largest remaining logit"; scanning e upwards with a
+         * strict comparison keeps the lower index on a tie. */
+        char *taken = calloc((size_t)E, 1);
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e)
+                if (!taken[e] && (best < 0 || l[e] > l[best]))
+                    best = e;
+            taken[best] = 1;
+            ids[(size_t)t * k + j] = best;
+        }
+        free(taken);
+
+        double *p = malloc(sizeof(double) * (size_t)E);
+        if (score == REF_SOFTMAX) {
+            double mx = l[0];
+            for (int e = 1; e < E; ++e)
+                if (l[e] > mx)
+                    mx = l[e];
+            double z = 0.0;
+            for (int e = 0; e < E; ++e)
+                z += exp((double)l[e] - mx);
+            for (int e = 0; e < E; ++e)
+                p[e] = exp((double)l[e] - mx) / z;
+        } else {
+            for (int e = 0; e < E; ++e)
+                p[e] = 1.0 / (1.0 + exp(-(double)l[e]));
+        }
+        double sel = 0.0;
+        for (int j = 0; j < k; ++j)
+            sel += p[ids[(size_t)t * k + j]];
+        for (int j = 0; j < k; ++j)
+            w[(size_t)t * k + j] = (float)(p[ids[(size_t)t * k + j]] / sel);
+        free(p);
+    }
+    return 0;
+}
+
+/* Token -> expert permutation, as a counting sort of the T*k (token, slot)
+ * pairs by expert, stable in pair order q = t*k + j:
+ *   offsets[e] = number of pairs routed to experts below e   (offsets[E] = T*k)
+ *   sorted[offsets[e] ..]  = the pairs routed to e, in ascending q
+ *   inv[q] = position of pair q in sorted
+ * Returns 0, or -1 if an id lies outside [0, E). */
+int fwref_permute(int T, int E, int k, const int32_t *ids, int32_t *offsets,
+                  int32_t *sorted, int32_t *inv)
+{
+    long P = (long)T * k;
+    int32_t *cursor = calloc((size_t)E + 1, sizeof(int32_t));
+    for (long q = 0; q < P; ++q) {
+        if (ids[q] < 0 || ids[q] >= E) {
+            free(cursor);
+            return -1;
+        }
+        cursor[ids[q]]++;
+    }
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e)
+        offsets[e + 1] = offsets[e] + cursor[e];
+    for (int e = 0; e < E; ++e)
+        cursor[e] = offsets[e];
+    for (long q = 0; q < P; ++q) {
+        int e = ids[q];
+        sorted[cursor[e]] = (int32_t)q;
+        inv[q] = cursor[e];
+        cursor[e]++;
+    }
+    free(cursor);
+    return 0;
+}
+
+/* One SwiGLU expert on one token:
+ *   g_f = sum_h Wg[f][h] x_h,  u_f = sum_h Wu[f][h] x_h
+ *   a_f = g_f * sigmoid(g_f) * u_f          (SiLU(gate) * up)
+ *   y_o = sum_f Wd[o][f] a_f
+ * Wg, Wu: F rows of H elements; Wd: H rows of F elements; blocked along the
+ * row (the reduction dimension). */
+static void expert_ffn(int qtype, int F, int H, const uint8_t *wg, const uint8_t *wu,
+                       const uint8_t *wd, const float *x, double *y, float *row,
+                       double *a)
+{
+    size_t rb_h = (size_t)H / 32 * block_bytes(qtype);
+    size_t rb_f = (size_t)F / 32 * block_bytes(qtype);
+    for (int f = 0; f < F; ++f) {
+        double g = 0.0, u = 0.0;
+        fwref_dequant_row(qtype, wg + f * rb_h, H, row);
+        for (int h = 0; h < H; ++h)
+            g += (double)row[h] * (double)x[h];
+        fwref_dequant_row(qtype, wu + f * rb_h, H, row);
+        for (int h = 0; h < H; ++h)
+            u += (double)row[h] * (double)x[h];
+        a[f] = g / (1.0 + exp(-g)) * u;
+    }
+    for (int o = 0; o < H; ++o) {
+        double acc = 0.0;
+        fwref_dequant_row(qtype, wd + o * rb_f, F, row);
+        for (int f = 0; f < F; ++f)
+            acc += (double)row[f] * a[f];
+        y[o] = acc;
+    }
+}
+
+/* The layer's output for T tokens:
+ *   out[t] = fp32( sum_{j<k} w[t][j] * FFN_{ids[t][j]}(x_t)  +  FFN_shared(x_t) )
+ * with the slot sum in order j = 0..k-1 and the shared expert (Fs > 0) last.
+ * Expert e's tensors start at e * F * (H/32) blocks (gate, up) and
+ * e * H * (F/32) blocks (down).  Tokens are independent, so they are spread over
+ * n_threads OpenMP threads (0: the runtime's default).
+ * Returns 0, or -1 on a bad argument or id. */
+int fwref_forward(int T, int H, int E, int k, int F, int qtype, int Fs, int qtype_s,
+                  int act_dtype, const void *x, const uint8_t *wg, const uint8_t *wu,
+                  const uint8_t *wd, const uint8_t *sg, const uint8_t *su,
+                  const uint8_t *sd, const int32_t *ids, const float *w, float *out,
+                  int n_threads)
+{
+    if (T < 0 || H <= 0 || H % 32 || F <= 0 || F % 32 || k < 1 || k > E || Fs < 0 ||
+        Fs % 32)
+        return -1;
+    for (long q = 0; q < (long)T * k; ++q)
+        if (ids[q] < 0 || ids[q] >= E)
+            return -1;
+    size_t expert_gu = (size_t)F * (H / 32) * block_bytes(qtype);
+    size_t expert_d = (size_t)H * (F / 32) * block_bytes(qtype);
+    int maxf = F > Fs ? F : Fs;
+    int maxr = H > maxf ? H : maxf;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#pragma omp parallel
+#endif
+    {
+        float *xf = malloc(sizeof(float) * (size_t)H);
+        float *row = malloc(sizeof(float) * (size_t)maxr);
+        double *a = malloc(sizeof(double) * (size_t)maxf);
+        double *y = malloc(sizeof(double) * (size_t)H);
+        double *acc = malloc(sizeof(double) * (size_t)H);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int t = 0; t < T; ++t) {
+            for (int h = 0; h < H; ++h) {
+                xf[h] = act_value(act_dtype, x, (size_t)t * H + h);
+                acc[h] = 0.0;
+            }
+            for (int j = 0; j < k; ++j) {
+                int e = ids[(size_t)t * k + j];
+                expert_ffn(qtype, F, H, wg + e * expert_gu, wu + e * expert_gu,
+                           wd + e * expert_d, xf, y, row, a);
+                for (int h = 0; h < H; ++h)
+                    acc[h] += (double)w[(size_t)t * k + j] * y[h];
+            }
+            if (Fs > 0) {
+                expert_ffn(qtype_s, Fs, H, sg, su, sd, xf, y, row, a);
+                for (int h = 0; h < H; ++h)
+                    acc[h] += y[h];
+            }
+            for (int h = 0; h < H; ++h)
+                out[(size_t)t * H + h] = (float)acc[h];
+        }
+        free(xf);
+        free(row);
+        free(a);
+        free(y);
+        free(acc);
+    }
+    return 0;
+}
+
+/* Threads an OpenMP region would use with n_threads (0: default). */
+int fwref_threads(int n_threads)
+{
+#ifdef _OPENMP
+    if (n_threads > 0)
+        return n_threads;
+    return omp_get_max_threads();
+#else
+    (void)n_threads;
+    return 1;
+#endif
+}
