@@ -1,0 +1,200 @@
+/*
+ * fwmoe.h -- C ABI of the MI355X (gfx950) routed mixture-of-experts FFN layer
+ * run directly on GGUF block-quantised expert weights.
+ *
+ * The layer is the "sparse MoE execution" with grouped routed-expert GPU
+ * kernels per weight format that Flyweight describes (Flyweight 0.2.0 wheel
+ * METADATA, "Features" and "Quantization"; Flyweight 0.5.1, "Models and
+ * formats", which lists Q4_0 and Q8_0 among the formats with grouped
+ * routed-expert GPU kernels).  Its steps:
+ *
+ *   fw_moe_route    router logits, softmax or sigmoid scores, top-k selection,
+ *                   renormalised gate weights;
+ *   fw_moe_permute  token -> expert grouping (expert-sorted pair lists);
+ *   fw_moe_forward  per expert: block dequant fused into the gate/up
+ *                   projections, SiLU(gate)*up, dequant-fused down projection;
+ *                   then the per-token weighted combine (+ shared expert).
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument is a DEVICE pointer owned by the caller, except
+ *    `desc` (host) and the host out-argument of fw_moe_read_status.  The
+ *    library allocates nothing, keeps no pointer after returning, and never
+ *    waits on the host: work is enqueued on `stream` (a hipStream_t; NULL is
+ *    the null stream) and the caller keeps every buffer alive until the stream
+ *    has passed it.  No entry point other than fw_moe_read_status synchronises,
+ *    so route -> permute -> forward can be captured in one hipGraph.  (The
+ *    pages' runtime keeps host synchronisation points inside dynamic MoE
+ *    routing -- Flyweight 0.2.0, "Current limitations" -- this ABI has none.)
+ *  - Row-major everywhere.  Device pointers must be 16-byte aligned and the
+ *    workspace 256-byte aligned.
+ *  - Arguments are validated before anything is enqueued: a negative return
+ *    means nothing was launched.  Unsupported requests are refused with
+ *    FW_EUNSUPPORTED, never served by a slower fallback (the pages' own rule of
+ *    refusing rather than silently not engaging, Flyweight 0.2.0
+ *    "Quantization").
+ *  - Data-dependent errors found on the device (an expert id outside [0, E), an
+ *    offset or pair index out of range) never fault: the offending pair is
+ *    skipped and a sticky bit is OR-ed into the status word at the start of the
+ *    workspace.  fw_moe_read_status reads it; fw_moe_clear_status resets it.
+ *  - Results are deterministic: repeated calls on the same inputs are bitwise
+ *    identical (no floating-point atomics; fixed summation orders).
+ *
+ * GGUF block layouts (the pages name the formats but print no byte layout; the
+ * layout is GGUF's, little-endian, no padding):
+ *   Q8_0: [fp16 d][32 x int8 q]                 34 bytes, value = d * q
+ *   Q4_0: [fp16 d][16 bytes]                    18 bytes, value = d * (q - 8),
+ *         byte i holds element i (low nibble) and element i+16 (high nibble).
+ * Expert tensors are blocked along the reduction dimension of each projection:
+ *   w_gate, w_up : [E][F][H/32 blocks]   row f of expert e reads x (length H)
+ *   w_down       : [E][H][F/32 blocks]   row o of expert e reads the F-vector
+ * and the shared expert's tensors are the same without the leading [E].
+ */
+#ifndef FWMOE_H
+#define FWMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum {
+    FW_OK = 0,
+    FW_EINVAL = -1,        /* bad size, null pointer or out-of-range enum   */
+    FW_EUNSUPPORTED = -2,  /* a combination this library does not serve     */
+    FW_EWORKSPACE = -3,    /* workspace missing or smaller than required    */
+    FW_EALIGN = -4,        /* a pointer is not 16-byte (workspace: 256) aligned */
+    FW_EHIP = -5           /* the HIP runtime reported an error on launch   */
+};
+
+/* Device status bits (sticky, in the workspace's status word). */
+enum {
+    FW_STATUS_BAD_EXPERT_ID = 1, /* fw_moe_permute met an id outside [0, E)      */
+    FW_STATUS_BAD_OFFSETS = 2,   /* fw_moe_forward met non-monotone / out-of-range
+                                    expert_offsets (clamped)                     */
+    FW_STATUS_BAD_PAIR = 4       /* fw_moe_forward met a sorted_pairs / inv_pos
+                                    entry out of range (skipped)                 */
+};
+
+enum { FW_F32 = 0, FW_BF16 = 1 };                 /* activation / router dtype */
+enum { FW_Q8_0 = 0, FW_Q4_0 = 1 };                /* expert weight format      */
+enum { FW_SOFTMAX_RENORM = 0, FW_SIGMOID_RENORM = 1 };
+enum { FW_PATH_AUTO = 0, FW_PATH_GEMV = 1, FW_PATH_GEMM = 2 };
+
+/* Shape and formats of one MoE layer.  All fields are int32. */
+typedef struct {
+    int32_t hidden;       /* H: multiple of 256, 256..16384                        */
+    int32_t n_experts;    /* E: 1..512                                             */
+    int32_t top_k;        /* k: 1..min(E, 16)                                      */
+    int32_t ffn;          /* F: routed expert inner size, multiple of 256, <= 16384 */
+    int32_t shared_ffn;   /* Fs: 0 = no shared expert, else multiple of 256        */
+    int32_t act_dtype;    /* FW_F32 | FW_BF16: x                                   */
+    int32_t router_dtype; /* FW_F32 | FW_BF16: router weights; must equal act_dtype */
+    int32_t expert_q;     /* FW_Q8_0 | FW_Q4_0: routed experts                     */
+    int32_t shared_q;     /* FW_Q8_0 | FW_Q4_0: shared expert (ignored if Fs = 0)  */
+    int32_t score;        /* FW_SOFTMAX_RENORM | FW_SIGMOID_RENORM                 */
+    int32_t path;         /* FW_PATH_*: forward kernel family (AUTO picks by T)    */
+} fw_moe_desc;
+
+/* Library version string. */
+const char *fw_moe_version(void);
+
+/* Check a descriptor; FW_OK or the reason it is refused. */
+int fw_moe_validate(const fw_moe_desc *desc);
+
+/* Bytes of workspace fw_moe_permute / fw_moe_forward need for up to max_T
+ * tokens; 0 if the descriptor is invalid or max_T < 0.  The same workspace may
+ * serve both calls (and any T <= max_T). */
+size_t fw_moe_workspace_size(const fw_moe_desc *desc, int32_t max_T);
+
+/* Router: logits, scores, top-k, renormalised gate weights.
+ * (Flyweight 0.2.0, served-families table: "DeepSeek-shaped MoE" -> sigmoid
+ * scores; vOOM notes: top-k as a per-request tunable; the pages give no
+ * formula -- the plainest reading is used:)
+ *   logits[t][e] = sum_h x[t][h] * router_w[e][h] + logit_bias[e]   (fp32 sum)
+ *   ids[t][j]    = the j-th largest logit of token t, ties to the lower index
+ *   softmax: w[t][j] = exp(l_j - l_max) / sum_{i<k} exp(l_i - l_max)
+ *            (equal to a softmax over all E renormalised to the selected k)
+ *   sigmoid: w[t][j] = s_j / sum_{i<k} s_i,  s = 1 / (1 + exp(-l))
+ * x          [T][H]  act_dtype             (unused if logits_in != NULL)
+ * router_w   [E][H]  router_dtype          (unused if logits_in != NULL)
+ * logit_bias [E]     fp32 or NULL          (unused if logits_in != NULL)
+ * logits_in  [T][E]  fp32 or NULL: if set, selection and weights are computed
+ *                    from these logits (which already include any bias)
+ * logits     [T][E]  fp32 out; required when logits_in is NULL, else may be
+ *                    NULL (nothing written)
+ * topk_ids   [T][k]  int32 out;  topk_w [T][k] fp32 out.
+ * Logits must be finite; ids stay in [0, E) whatever the logits. */
+int fw_moe_route(const fw_moe_desc *desc, int32_t T, const void *x, const void *router_w,
+                 const float *logit_bias, const float *logits_in, float *logits,
+                 int32_t *topk_ids, float *topk_w, void *stream);
+
+/* Token -> expert grouping (the grouped routed-expert kernels' row lists;
+ * Flyweight 0.2.0 "Quantization" and "Current limitations").  A stable counting
+ * sort of the P = T*k (token, slot) pairs q = t*k + j by expert:
+ *   expert_offsets [E+1] int32 out: pairs routed to experts below e;
+ *                  expert_offsets[E] = number of valid pairs (P if all ids valid)
+ *   sorted_pairs   [P]   int32 out: pair ids, expert-major, ascending q within
+ *                  an expert; entries past expert_offsets[E] are -1
+ *   inv_pos        [P]   int32 out: sorted_pairs[inv_pos[q]] == q; -1 for a pair
+ *                  whose id is out of range (and FW_STATUS_BAD_EXPERT_ID is set)
+ * topk_ids [T][k] int32 in.  The workspace holds the status word only.
+ * Bit-exact and unique for valid ids. */
+int fw_moe_permute(const fw_moe_desc *desc, int32_t T, const int32_t *topk_ids,
+                   int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *inv_pos,
+                   void *workspace, size_t ws_bytes, void *stream);
+
+/* Expert FFNs and combine:
+ *   for every pair q = (t, j) routed to expert e:
+ *     a = SiLU(W_gate[e] x_t) * (W_up[e] x_t),   y_q = W_down[e] a
+ *   out[t] = sum_{j<k} topk_w[t][j] * y_{(t,j)}  (slot order)  + shared(x_t)
+ * SwiGLU experts: vOOM module layout (the shared block math); the fused
+ * gate/up pass that shares each activation load: Flyweight 0.2.0 "Current
+ * limitations"; the fixed-order, deterministic combine: vOOM notes (a fused
+ * expert path that changed the token stream was rejected).
+ * x        [T][H]  act_dtype
+ * w_gate, w_up [E][F][H/32] blocks of expert_q;  w_down [E][H][F/32] blocks
+ * ws_gate, ws_up [Fs][H/32], ws_down [H][Fs/32] blocks of shared_q, or NULL
+ *          when shared_ffn == 0 (all three required when shared_ffn > 0)
+ * topk_w   [T][k] fp32;  expert_offsets, sorted_pairs, inv_pos as produced by
+ *          fw_moe_permute (validated on the device: see FW_STATUS_*)
+ * out      [T][H] fp32 out (fully overwritten)
+ * workspace / ws_bytes: at least fw_moe_workspace_size(desc, T) bytes.
+ * Numerics: weights are decoded exactly; the GEMV family (small T) multiplies
+ * and sums in fp32; the GEMM family (large T) contracts on fp16 MFMA with fp32
+ * accumulation (activations and dequantised weights rounded to fp16). */
+int fw_moe_forward(const fw_moe_desc *desc, int32_t T, const void *x, const void *w_gate,
+                   const void *w_up, const void *w_down, const void *ws_gate,
+                   const void *ws_up, const void *ws_down, const float *topk_w,
+                   const int32_t *expert_offsets, const int32_t *sorted_pairs,
+                   const int32_t *inv_pos, float *out, void *workspace, size_t ws_bytes,
+                   void *stream);
+
+/* The forward kernel family AUTO picks for T tokens (FW_PATH_GEMV or
+ * FW_PATH_GEMM), or a negative error for an invalid descriptor. */
+int fw_moe_forward_path(const fw_moe_desc *desc, int32_t T);
+
+/* Reset the workspace's status word (a fill kernel on `stream`). */
+int fw_moe_clear_status(void *workspace, void *stream);
+
+/* Blocking: wait for the device and copy the status word to *host_status.
+ * For tests and harnesses, not for the hot path. */
+int fw_moe_read_status(const void *workspace, int32_t *host_status);
+
+/* Human-readable text of a return code. */
+const char *fw_moe_status_string(int status);
+
+/* Benchmark instrumentation.  When `events` is non-NULL it must point to
+ * FW_N_STAGE_EVENTS hipEvent_t handles; every later fw_moe_forward records
+ * events[0] before its first kernel and events[s+1] after stage s, s in
+ * {0: prepare, 1: gate/up projection, 2: down projection, 3: combine}, on its
+ * stream.  NULL turns recording off.  Process-wide and not thread-safe. */
+enum { FW_N_STAGE_EVENTS = 5 };
+int fw_moe_set_stage_events(void *const *events);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FWMOE_H */

@@ -97,6 +97,61 @@ static float act_value(int dtype, const void *base, size_t i)
     return fwref_bf16_to_float(((const uint16_t *)base)[i]);
 }
 
+/* The router's work for token t (formulas at fwref_route). */
+static void route_token(int H, int E, int k, int act_dtype, int router_dtype, int score,
+                        const void *x, const void *router_w, const float *bias,
+                        const float *logits_in, int t, float *logits, int32_t *ids, float *w)
+{
+    float *l = logits + (size_t)t * E;
+    for (int e = 0; e < E; ++e) {
+        if (logits_in) {
+            l[e] = logits_in[(size_t)t * E + e];
+            continue;
+        }
+        double acc = 0.0;
+        for (int h = 0; h < H; ++h)
+            acc += (double)act_value(act_dtype, x, (size_t)t * H + h) *
+                   (double)act_value(router_dtype, router_w, (size_t)e * H + h);
+        if (bias)
+            acc += (double)bias[e];
+        l[e] = (float)acc;
+    }
+    /* k rounds of "largest remaining logit"; scanning e upwards with a
+     * strict comparison keeps the lower index on a tie. */
+    char *taken = calloc((size_t)E, 1);
+    for (int j = 0; j < k; ++j) {
+        int best = -1;
+        for (int e = 0; e < E; ++e)
+            if (!taken[e] && (best < 0 || l[e] > l[best]))
+                best = e;
+        taken[best] = 1;
+        ids[(size_t)t * k + j] = best;
+    }
+    free(taken);
+
+    double *p = malloc(sizeof(double) * (size_t)E);
+    if (score == REF_SOFTMAX) {
+        double mx = l[0];
+        for (int e = 1; e < E; ++e)
+            if (l[e] > mx)
+                mx = l[e];
+        double z = 0.0;
+        for (int e = 0; e < E; ++e)
+            z += exp((double)l[e] - mx);
+        for (int e = 0; e < E; ++e)
+            p[e] = exp((double)l[e] - mx) / z;
+    } else {
+        for (int e = 0; e < E; ++e)
+            p[e] = 1.0 / (1.0 + exp(-(double)l[e]));
+    }
+    double sel = 0.0;
+    for (int j = 0; j < k; ++j)
+        sel += p[ids[(size_t)t * k + j]];
+    for (int j = 0; j < k; ++j)
+        w[(size_t)t * k + j] = (float)(p[ids[(size_t)t * k + j]] / sel);
+    free(p);
+}
+
 /* Router: logits, scoring, top-k selection and renormalised gate weights.
  *   l[t][e] = fp32( sum_h x[t][h] * W_r[e][h] + b_e )
  *   ids[t][0..k-1]: experts in descending order of l, ties to the lower index
@@ -104,6 +159,7 @@ static float act_value(int dtype, const void *base, size_t i)
  *   sigmoid: p_e = 1 / (1 + exp(-l_e))
  *   w[t][j] = p_{ids[t][j]} / sum_{i<k} p_{ids[t][i]}
  * If logits_in is given it replaces the first line (it already holds the bias).
+ * Tokens are independent and spread over OpenMP threads.
  * Returns 0, or -1 on a bad argument. */
 int fwref_route(int T, int H, int E, int k, int act_dtype, int router_dtype, int score,
                 const void *x, const void *router_w, const float *bias,
@@ -111,56 +167,12 @@ int fwref_route(int T, int H, int E, int k, int act_dtype, int router_dtype, int
 {
     if (T < 0 || H <= 0 || E <= 0 || k < 1 || k > E)
         return -1;
-    for (int t = 0; t < T; ++t) {
-        float *l = logits + (size_t)t * E;
-        for (int e = 0; e < E; ++e) {
-            if (logits_in) {
-                l[e] = logits_in[(size_t)t * E + e];
-                continue;
-            }
-            double acc = 0.0;
-            for (int h = 0; h < H; ++h)
-                acc += (double)act_value(act_dtype, x, (size_t)t * H + h) *
-                       (double)act_value(router_dtype, router_w, (size_t)e * H + h);
-            if (bias)
-                acc += (double)bias[e];
-            l[e] = (float)acc;
-        }
-        /* k rounds of "largest remaining logit"; scanning e upwards with a
-         * strict comparison keeps the lower index on a tie. */
-        char *taken = calloc((size_t)E, 1);
-        for (int j = 0; j < k; ++j) {
-            int best = -1;
-            for (int e = 0; e < E; ++e)
-                if (!taken[e] && (best < 0 || l[e] > l[best]))
-                    best = e;
-            taken[best] = 1;
-            ids[(size_t)t * k + j] = best;
-        }
-        free(taken);
-
-        double *p = malloc(sizeof(double) * (size_t)E);
-        if (score == REF_SOFTMAX) {
-            double mx = l[0];
-            for (int e = 1; e < E; ++e)
-                if (l[e] > mx)
-                    mx = l[e];
-            double z = 0.0;
-            for (int e = 0; e < E; ++e)
-                z += exp((double)l[e] - mx);
-            for (int e = 0; e < E; ++e)
-                p[e] = exp((double)l[e] - mx) / z;
-        } else {
-            for (int e = 0; e < E; ++e)
-                p[e] = 1.0 / (1.0 + exp(-(double)l[e]));
-        }
-        double sel = 0.0;
-        for (int j = 0; j < k; ++j)
-            sel += p[ids[(size_t)t * k + j]];
-        for (int j = 0; j < k; ++j)
-            w[(size_t)t * k + j] = (float)(p[ids[(size_t)t * k + j]] / sel);
-        free(p);
-    }
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 4)
+#endif
+    for (int t = 0; t < T; ++t)
+        route_token(H, E, k, act_dtype, router_dtype, score, x, router_w, bias, logits_in, t,
+                    logits, ids, w);
     return 0;
 }
 

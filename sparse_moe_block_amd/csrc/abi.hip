@@ -1,0 +1,235 @@
+// The C ABI (declared in include/fwmoe.h): argument validation, workspace
+// layout, kernel-family choice and the launch sequence of each entry point.
+// Everything here runs on the host and enqueues asynchronously; nothing is
+// allocated and nothing waits, except fw_moe_read_status.
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace fw {
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const fw_moe_desc &d, int T) {
+    WsLayout L{};
+    const size_t H = d.hidden, F = d.ffn, Fs = d.shared_ffn, E = d.n_experts;
+    const size_t P = (size_t)T * d.top_k;
+    size_t off = sizeof(WsHeader);
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align256(off + bytes);
+        return at;
+    };
+    L.max_tiles = (int)((P + kGemmBM - 1) / kGemmBM + E);
+    L.active = take((E + 1) * sizeof(int4));
+    L.tiles = take((size_t)L.max_tiles * sizeof(int4));
+    L.xs = take((size_t)T * (H / 32) * 4);
+    L.x32 = take((size_t)T * H * 4);
+    L.x16 = take((size_t)T * H * 2);
+    L.h = take((P * F + (size_t)T * Fs) * 4);
+    L.hs = take((P * (F / 32) + (size_t)T * (Fs / 32)) * 4);
+    L.y = take((P + (Fs ? (size_t)T : 0)) * H * 4);
+    L.total = off;
+    return L;
+}
+
+}  // namespace fw
+
+using namespace fw;
+
+namespace {
+
+hipEvent_t g_events[FW_N_STAGE_EVENTS];
+bool g_events_on = false;
+
+bool al16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+bool al256(const void *p) { return ((uintptr_t)p & 255) == 0; }
+
+int check_desc(const fw_moe_desc *d) {
+    if (!d) return FW_EINVAL;
+    if (d->hidden < 256 || d->hidden > 16384 || d->hidden % 256) return FW_EINVAL;
+    if (d->n_experts < 1 || d->n_experts > kMaxExperts) return FW_EINVAL;
+    if (d->top_k < 1 || d->top_k > std::min(d->n_experts, kMaxTopK)) return FW_EINVAL;
+    if (d->ffn < 256 || d->ffn > 16384 || d->ffn % 256) return FW_EINVAL;
+    if (d->shared_ffn < 0 || d->shared_ffn > 16384 || d->shared_ffn % 256) return FW_EINVAL;
+    if (d->act_dtype != FW_F32 && d->act_dtype != FW_BF16) return FW_EINVAL;
+    if (d->router_dtype != FW_F32 && d->router_dtype != FW_BF16) return FW_EINVAL;
+    if (d->expert_q != FW_Q8_0 && d->expert_q != FW_Q4_0) return FW_EINVAL;
+    if (d->shared_q != FW_Q8_0 && d->shared_q != FW_Q4_0) return FW_EINVAL;
+    if (d->score != FW_SOFTMAX_RENORM && d->score != FW_SIGMOID_RENORM) return FW_EINVAL;
+    if (d->path < FW_PATH_AUTO || d->path > FW_PATH_GEMM) return FW_EINVAL;
+    if (d->router_dtype != d->act_dtype) return FW_EUNSUPPORTED;
+    return FW_OK;
+}
+
+int check_T(const fw_moe_desc *d, int32_t T) {
+    if (T < 0 || T > (1 << 20) || (int64_t)T * d->top_k > (1 << 24)) return FW_EINVAL;
+    return FW_OK;
+}
+
+int resolve_path(const fw_moe_desc *d, int32_t T) {
+    if (d->path != FW_PATH_AUTO) return d->path;
+    (void)T;
+    return FW_PATH_GEMV;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FW_OK : FW_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *fw_moe_version(void) { return "fwmoe 0.1.0 gfx950"; }
+
+int fw_moe_validate(const fw_moe_desc *desc) { return check_desc(desc); }
+
+size_t fw_moe_workspace_size(const fw_moe_desc *desc, int32_t max_T) {
+    if (check_desc(desc) != FW_OK || check_T(desc, max_T) != FW_OK) return 0;
+    return ws_layout(*desc, max_T).total;
+}
+
+int fw_moe_forward_path(const fw_moe_desc *desc, int32_t T) {
+    int rc = check_desc(desc);
+    if (rc != FW_OK) return rc;
+    if ((rc = check_T(desc, T)) != FW_OK) return rc;
+    return resolve_path(desc, T);
+}
+
+int fw_moe_route(const fw_moe_desc *desc, int32_t T, const void *x, const void *router_w,
+                 const float *logit_bias, const float *logits_in, float *logits,
+                 int32_t *topk_ids, float *topk_w, void *stream) {
+    int rc = check_desc(desc);
+    if (rc != FW_OK) return rc;
+    if ((rc = check_T(desc, T)) != FW_OK) return rc;
+    if (T == 0) return FW_OK;
+    if (!topk_ids || !topk_w) return FW_EINVAL;
+    if (!al16(topk_ids) || !al16(topk_w)) return FW_EALIGN;
+    const float *scores = logits_in;
+    if (!logits_in) {
+        if (!x || !router_w || !logits) return FW_EINVAL;
+        if (!al16(x) || !al16(router_w) || !al16(logits) || (logit_bias && !al16(logit_bias)))
+            return FW_EALIGN;
+        scores = logits;
+    } else if (!al16(logits_in)) {
+        return FW_EALIGN;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (!logits_in) {
+        rc = hip_status(launch_logits(*desc, T, x, router_w, logit_bias, logits, s));
+        if (rc != FW_OK) return rc;
+    }
+    return hip_status(launch_topk(*desc, T, scores, topk_ids, topk_w, s));
+}
+
+int fw_moe_permute(const fw_moe_desc *desc, int32_t T, const int32_t *topk_ids,
+                   int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *inv_pos,
+                   void *workspace, size_t ws_bytes, void *stream) {
+    int rc = check_desc(desc);
+    if (rc != FW_OK) return rc;
+    if ((rc = check_T(desc, T)) != FW_OK) return rc;
+    if (!expert_offsets || !workspace) return FW_EINVAL;
+    if (T > 0 && (!topk_ids || !sorted_pairs || !inv_pos)) return FW_EINVAL;
+    if (!al16(expert_offsets) || !al256(workspace) || (T > 0 && (!al16(topk_ids) ||
+        !al16(sorted_pairs) || !al16(inv_pos))))
+        return FW_EALIGN;
+    if (ws_bytes < sizeof(WsHeader)) return FW_EWORKSPACE;
+    return hip_status(launch_permute(*desc, T, topk_ids, expert_offsets, sorted_pairs, inv_pos,
+                                     (WsHeader *)workspace, (hipStream_t)stream));
+}
+
+int fw_moe_forward(const fw_moe_desc *desc, int32_t T, const void *x, const void *w_gate,
+                   const void *w_up, const void *w_down, const void *ws_gate,
+                   const void *ws_up, const void *ws_down, const float *topk_w,
+                   const int32_t *expert_offsets, const int32_t *sorted_pairs,
+                   const int32_t *inv_pos, float *out, void *workspace, size_t ws_bytes,
+                   void *stream) {
+    int rc = check_desc(desc);
+    if (rc != FW_OK) return rc;
+    if ((rc = check_T(desc, T)) != FW_OK) return rc;
+    if (T == 0) return FW_OK;
+    const bool shared = desc->shared_ffn > 0;
+    if (!x || !w_gate || !w_up || !w_down || !topk_w || !expert_offsets || !sorted_pairs ||
+        !inv_pos || !out || !workspace)
+        return FW_EINVAL;
+    if (shared && (!ws_gate || !ws_up || !ws_down)) return FW_EINVAL;
+    const void *ptrs[] = {x, w_gate, w_up, w_down, topk_w, expert_offsets, sorted_pairs,
+                          inv_pos, out};
+    for (const void *p : ptrs)
+        if (!al16(p)) return FW_EALIGN;
+    if (shared && (!al16(ws_gate) || !al16(ws_up) || !al16(ws_down))) return FW_EALIGN;
+    if (!al256(workspace)) return FW_EALIGN;
+    FwdArgs a;
+    a.d = *desc;
+    a.T = T;
+    a.P = T * desc->top_k;
+    a.path = resolve_path(desc, T);
+    if (a.path == FW_PATH_GEMM) return FW_EUNSUPPORTED;
+    a.L = ws_layout(*desc, T);
+    if (ws_bytes < a.L.total) return FW_EWORKSPACE;
+    a.x = x;
+    a.wg = (const uint8_t *)w_gate;
+    a.wu = (const uint8_t *)w_up;
+    a.wd = (const uint8_t *)w_down;
+    a.sg = shared ? (const uint8_t *)ws_gate : nullptr;
+    a.su = shared ? (const uint8_t *)ws_up : nullptr;
+    a.sd = shared ? (const uint8_t *)ws_down : nullptr;
+    a.topk_w = topk_w;
+    a.offsets = expert_offsets;
+    a.sorted = sorted_pairs;
+    a.inv = inv_pos;
+    a.out = out;
+    a.ws = (char *)workspace;
+    hipStream_t s = (hipStream_t)stream;
+    const bool ev = g_events_on;
+    if (ev) hipEventRecord(g_events[0], s);
+    if ((rc = hip_status(launch_prepare(a, s))) != FW_OK) return rc;
+    if (ev) hipEventRecord(g_events[1], s);
+    if ((rc = hip_status(launch_gemv_gate_up(a, s))) != FW_OK) return rc;
+    if (ev) hipEventRecord(g_events[2], s);
+    if ((rc = hip_status(launch_gemv_down(a, s))) != FW_OK) return rc;
+    if (ev) hipEventRecord(g_events[3], s);
+    if ((rc = hip_status(launch_combine(a, s))) != FW_OK) return rc;
+    if (ev) hipEventRecord(g_events[4], s);
+    return FW_OK;
+}
+
+int fw_moe_clear_status(void *workspace, void *stream) {
+    if (!workspace) return FW_EINVAL;
+    if (!al256(workspace)) return FW_EALIGN;
+    return hip_status(launch_clear_status((WsHeader *)workspace, (hipStream_t)stream));
+}
+
+int fw_moe_read_status(const void *workspace, int32_t *host_status) {
+    if (!workspace || !host_status) return FW_EINVAL;
+    if (hipDeviceSynchronize() != hipSuccess) return FW_EHIP;
+    return hip_status(hipMemcpy(host_status, workspace, sizeof(int32_t), hipMemcpyDeviceToHost));
+}
+
+const char *fw_moe_status_string(int status) {
+    switch (status) {
+        case FW_OK: return "ok";
+        case FW_EINVAL: return "invalid argument";
+        case FW_EUNSUPPORTED: return "unsupported combination";
+        case FW_EWORKSPACE: return "workspace missing or too small";
+        case FW_EALIGN: return "misaligned pointer";
+        case FW_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int fw_moe_set_stage_events(void *const *events) {
+    if (!events) {
+        g_events_on = false;
+        return FW_OK;
+    }
+    for (int i = 0; i < FW_N_STAGE_EVENTS; ++i) {
+        if (!events[i]) return FW_EINVAL;
+        g_events[i] = (hipEvent_t)events[i];
+    }
+    g_events_on = true;
+    return FW_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,171 @@
+// Forward, stages 0 and 3: the per-call schedule / activation staging, and the
+// deterministic per-token weighted combine.
+#include "common.h"
+
+namespace fw {
+namespace {
+
+constexpr int kPrepThreads = 256;
+
+// Block 0 turns expert_offsets into the list of active experts
+// (expert, first row, rows) and the grouped-GEMM tile list, clamping anything
+// out of range (FW_STATUS_BAD_OFFSETS).  Blocks 1..T stage one token row each:
+// the GEMV family needs x in fp32 plus its 32-element block sums, the GEMM
+// family x in fp16.
+__global__ __launch_bounds__(kPrepThreads) void prepare_kernel(
+    const int32_t *__restrict__ offsets, int E, int P, const void *__restrict__ x, int act_bf16,
+    int H, int T, int gemm, int max_tiles, int4 *__restrict__ active, int4 *__restrict__ tiles,
+    float *__restrict__ xs, float *__restrict__ x32, _Float16 *__restrict__ x16,
+    WsHeader *__restrict__ hdr) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    if (blockIdx.x == 0) {
+        __shared__ int wsum_a[kPrepThreads / kWave], wsum_t[kPrepThreads / kWave];
+        // each thread owns experts 2*tid and 2*tid+1
+        int beg[2], cnt[2], na = 0, nt = 0;
+        bool bad = false;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = 2 * tid + i;
+            beg[i] = cnt[i] = 0;
+            if (e < E) {
+                int b = offsets[e], n = offsets[e + 1];
+                if (e == 0 && b != 0) bad = true;
+                if (b < 0 || b > P || n < b || n > P) bad = true;
+                b = min(max(b, 0), P);
+                n = min(max(n, b), P);
+                beg[i] = b;
+                cnt[i] = n - b;
+                na += cnt[i] > 0;
+                nt += (cnt[i] + kGemmBM - 1) / kGemmBM;
+            }
+        }
+        if (bad) atomicOr(&hdr->status, FW_STATUS_BAD_OFFSETS);
+        int ia = na, it = nt;   // inclusive scans
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int oa = __shfl_up(ia, off), ot = __shfl_up(it, off);
+            if (lane >= off) {
+                ia += oa;
+                it += ot;
+            }
+        }
+        if (lane == kWave - 1) {
+            wsum_a[wave] = ia;
+            wsum_t[wave] = it;
+        }
+        __syncthreads();
+        int ba = 0, bt = 0;
+        for (int w = 0; w < wave; ++w) {
+            ba += wsum_a[w];
+            bt += wsum_t[w];
+        }
+        int pa = ba + ia - na, pt = bt + it - nt;   // exclusive positions
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (cnt[i] > 0) {
+                active[pa++] = int4{2 * tid + i, beg[i], cnt[i], 0};
+                if (gemm)   // bounded: overlapping (invalid) offsets can claim more
+                    for (int m = 0; m < cnt[i] && pt < max_tiles; m += kGemmBM)
+                        tiles[pt++] = int4{2 * tid + i, beg[i] + m, min(kGemmBM, cnt[i] - m), 0};
+            }
+        }
+        if (tid == kPrepThreads - 1) {
+            hdr->n_active = ba + ia;
+            hdr->n_tiles = min(bt + it, max_tiles);
+        }
+        return;
+    }
+    const int t = blockIdx.x - 1;
+    if (t >= T) return;
+    // 8 elements per thread per step; 4 consecutive threads cover one 32-block
+    for (int h0 = tid * 8; h0 < H; h0 += kPrepThreads * 8) {
+        float v[8];
+        if (act_bf16) {
+            const uint4 raw = *(const uint4 *)((const uint16_t *)x + (size_t)t * H + h0);
+            const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = __uint_as_float(wd[i] << 16);
+                v[2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
+            }
+        } else {
+            const float4 a = *(const float4 *)((const float *)x + (size_t)t * H + h0);
+            const float4 b = *(const float4 *)((const float *)x + (size_t)t * H + h0 + 4);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        }
+        if (gemm) {
+            typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+            h8 o;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = (_Float16)v[i];
+            *(h8 *)(x16 + (size_t)t * H + h0) = o;
+        } else {
+            *(float4 *)(x32 + (size_t)t * H + h0) = float4{v[0], v[1], v[2], v[3]};
+            *(float4 *)(x32 + (size_t)t * H + h0 + 4) = float4{v[4], v[5], v[6], v[7]};
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s += v[i];
+            s += __shfl_xor(s, 1);
+            s += __shfl_xor(s, 2);
+            if ((tid & 3) == 0) xs[(size_t)t * (H / 32) + h0 / 32] = s;
+        }
+    }
+}
+
+// out[t][o] = sum_{j<k} w[t][j] * y[inv[t*k+j]][o]  (slot order)  + y_shared[t][o]
+__global__ __launch_bounds__(256) void combine_kernel(
+    const float *__restrict__ y, const float *__restrict__ ysh, const float *__restrict__ w,
+    const int32_t *__restrict__ inv, float *__restrict__ out, int H, int k, int P,
+    WsHeader *__restrict__ hdr) {
+    const int t = blockIdx.y;
+    const int o = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (o >= H) return;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    bool bad = false;
+    for (int j = 0; j < k; ++j) {
+        const int p = inv[(size_t)t * k + j];
+        const float wj = w[(size_t)t * k + j];
+        if ((unsigned)p >= (unsigned)P) {
+            bad = true;
+            continue;
+        }
+        const float4 v = *(const float4 *)(y + (size_t)p * H + o);
+        acc.x = fmaf(wj, v.x, acc.x);
+        acc.y = fmaf(wj, v.y, acc.y);
+        acc.z = fmaf(wj, v.z, acc.z);
+        acc.w = fmaf(wj, v.w, acc.w);
+    }
+    if (ysh) {
+        const float4 v = *(const float4 *)(ysh + (size_t)t * H + o);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    *(float4 *)(out + (size_t)t * H + o) = acc;
+    if (bad) atomicOr(&hdr->status, FW_STATUS_BAD_PAIR);
+}
+
+}  // namespace
+
+hipError_t launch_prepare(const FwdArgs &a, hipStream_t s) {
+    const bool gemm = a.path == FW_PATH_GEMM;
+    prepare_kernel<<<1 + a.T, kPrepThreads, 0, s>>>(
+        a.offsets, a.d.n_experts, a.P, a.x, a.d.act_dtype == FW_BF16, a.d.hidden, a.T, gemm,
+        a.L.max_tiles, (int4 *)(a.ws + a.L.active), (int4 *)(a.ws + a.L.tiles), (float *)(a.ws + a.L.xs),
+        (float *)(a.ws + a.L.x32), (_Float16 *)(a.ws + a.L.x16), (WsHeader *)a.ws);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const FwdArgs &a, hipStream_t s) {
+    const int H = a.d.hidden;
+    const float *y = (const float *)(a.ws + a.L.y);
+    const float *ysh = a.d.shared_ffn ? y + (size_t)a.P * H : nullptr;
+    dim3 grid((H / 4 + 255) / 256, a.T);
+    combine_kernel<<<grid, 256, 0, s>>>(y, ysh, a.topk_w, a.inv, a.out, H, a.d.top_k, a.P,
+                                        (WsHeader *)a.ws);
+    return hipGetLastError();
+}
+
+}  // namespace fw

@@ -1,0 +1,124 @@
+"""GPU parity of the three C-ABI calls against the CPU oracle, on the seeded
+workloads (all five, at their full sizes; large batches compare sampled
+tokens, which the oracle computes one by one)."""
+
+import numpy as np
+import pytest
+import torch
+
+import moegen
+from sparse_moe_block_amd import fwmoe as fw
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+C = moegen
+SWEEP_Z = C.SWEEP_Q8.with_(zipf=1.3)
+# (config, T): every batch size each workload names; the sweep at a spread of T
+CASES = [(C.TINY, 4), (C.QWEN3_DECODE, 1), (C.QWEN3_DECODE, 4), (C.QWEN3_DECODE, 16),
+         (C.QWEN3_PREFILL, 2048), (C.DEEPSEEK, 1), (C.DEEPSEEK, 32), (C.DEEPSEEK, 4096),
+         (C.SWEEP_Q8, 1), (C.SWEEP_Q8, 64), (C.SWEEP_Q8, 1024), (SWEEP_Z, 8192)]
+IDS = [f"c{c.cid}{'z' if c.zipf and c.cid == 4 else ''}-T{T}" for c, T in CASES]
+
+
+def _x(cfg, T):
+    x = moegen.make_x(cfg, T, device=G.DEV)
+    return x, moegen.as_numpy_bits(x)
+
+
+@pytest.mark.parametrize("cfg,T", CASES, ids=IDS)
+def test_route(ref, cfg, T):
+    print(f"route {cfg.name} T={T}", flush=True)
+    dl = G.layer(cfg)
+    desc = G.desc_of(cfg)
+    x, xh = _x(cfg, T)
+    logits, ids, w = G.route(desc, cfg, dl, x)
+    rl, rids, rw = G.oracle_route(ref, cfg, dl, xh)
+    gl = logits.cpu().numpy()
+    assert np.abs(gl - rl).max() <= G.LOGIT_MAX_ABS
+    # near ties: the oracle's logits are fed in for those tokens, then ids must
+    # agree exactly everywhere
+    near = G.small_gaps(rl, cfg.top_k)
+    lin = gl.copy()
+    lin[near] = rl[near]
+    lin_d = torch.from_numpy(lin).to(G.DEV)
+    _, ids2, w2 = G.route(desc, cfg, dl, x, logits_in=lin_d)
+    assert np.array_equal(ids2.cpu().numpy(), rids)
+    _, rids2, rw2 = G.oracle_route(ref, cfg, dl, xh, logits_in=lin)
+    assert np.array_equal(rids2, rids)
+    assert np.abs(w2.cpu().numpy() - rw2).max() <= G.W_MAX_ABS
+    s = w2.double().sum(dim=1).cpu().numpy()
+    assert np.abs(s - 1).max() <= 1e-5
+    # tokens without near ties were routed identically from the GPU's own logits
+    assert np.array_equal(ids.cpu().numpy()[~near], rids[~near])
+
+
+@pytest.mark.parametrize("cfg,T", CASES, ids=IDS)
+def test_permute(ref, cfg, T):
+    print(f"permute {cfg.name} T={T}", flush=True)
+    dl = G.layer(cfg)
+    desc = G.desc_of(cfg)
+    x, xh = _x(cfg, T)
+    _, rids, _ = G.oracle_route(ref, cfg, dl, xh)
+    ws = G.workspace(desc, T)
+    off, sp, inv = G.permute(desc, cfg, torch.from_numpy(rids).to(G.DEV), ws)
+    roff, rsp, rinv = ref.permute(rids, cfg.n_experts)
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert np.array_equal(sp.cpu().numpy(), rsp)
+    assert np.array_equal(inv.cpu().numpy(), rinv)
+    assert fw.fw_moe_read_status(ws) == 0
+
+
+@pytest.mark.parametrize("path", ["gemv"])
+@pytest.mark.parametrize("cfg,T", CASES, ids=IDS)
+def test_forward(ref, cfg, T, path):
+    """Oracle routing in, GPU permutation + expert FFNs + combine out."""
+    print(f"forward {cfg.name} T={T} {path}", flush=True)
+    dl = G.layer(cfg)
+    desc = G.desc_of(cfg, path=path)
+    x, xh = _x(cfg, T)
+    _, rids, rw = G.oracle_route(ref, cfg, dl, xh)
+    ws = G.workspace(desc, T)
+    ids_d = torch.from_numpy(rids).to(G.DEV)
+    w_d = torch.from_numpy(rw).to(G.DEV)
+    off, sp, inv = G.permute(desc, cfg, ids_d, ws)
+    out = G.forward(desc, cfg, dl, x, w_d, off, sp, inv, ws).cpu().numpy()
+    assert fw.fw_moe_read_status(ws) == 0
+    tok = G.sample_tokens(T, 48)
+    want = G.oracle_forward(ref, cfg, dl, np.ascontiguousarray(xh[tok]), rids[tok], rw[tok])
+    G.check_out(out[tok], want)
+
+
+@pytest.mark.parametrize("cfg,T", [(C.QWEN3_DECODE, 16), (C.DEEPSEEK, 32), (C.TINY, 4)],
+                         ids=["c1-T16", "c3-T32", "c0-T4"])
+def test_end_to_end(ref, cfg, T):
+    """route -> permute -> forward on the GPU against the oracle's route +
+    forward (near-tie tokens take the oracle's logits)."""
+    dl = G.layer(cfg)
+    desc = G.desc_of(cfg)
+    x, xh = _x(cfg, T)
+    logits, _, _ = G.route(desc, cfg, dl, x)
+    rl, rids, rw = G.oracle_route(ref, cfg, dl, xh)
+    near = G.small_gaps(rl, cfg.top_k)
+    lin = logits.cpu().numpy()
+    lin[near] = rl[near]
+    _, ids, w = G.route(desc, cfg, dl, x, logits_in=torch.from_numpy(lin).to(G.DEV))
+    ws = G.workspace(desc, T)
+    off, sp, inv = G.permute(desc, cfg, ids, ws)
+    out = G.forward(desc, cfg, dl, x, w, off, sp, inv, ws).cpu().numpy()
+    want = G.oracle_forward(ref, cfg, dl, xh, rids, rw)
+    G.check_out(out, want)
+
+
+def test_repeat_is_bitwise_identical():
+    cfg, T = C.DEEPSEEK, 32
+    dl = G.layer(cfg)
+    desc = G.desc_of(cfg)
+    x, _ = _x(cfg, T)
+    outs = []
+    for _ in range(3):
+        _, ids, w = G.route(desc, cfg, dl, x)
+        ws = G.workspace(desc, T)
+        off, sp, inv = G.permute(desc, cfg, ids, ws)
+        outs.append(G.forward(desc, cfg, dl, x, w, off, sp, inv, ws).cpu())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
