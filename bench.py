@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (the "
+                         "reference kernel that scales hardware byte counters)")
     return ap.parse_args()
 
 
@@ -91,6 +94,13 @@ def main():
         fw.fw_moe_forward(desc, T, x, Li.w_gate, Li.w_up, Li.w_down, Li.s_gate, Li.s_up,
                           Li.s_down, w, off, sp, inv, out, ws, stream=stream)
 
+    if a.copy_mib:
+        src = torch.empty(a.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()

@@ -25,11 +25,8 @@ WsLayout ws_layout(const fw_moe_desc &d, int T) {
     L.max_tiles = (int)((P + kGemmBM - 1) / kGemmBM + E);
     L.active = take((E + 1) * sizeof(int4));
     L.tiles = take((size_t)L.max_tiles * sizeof(int4));
-    L.xs = take((size_t)T * (H / 32) * 4);
-    L.x32 = take((size_t)T * H * 4);
     L.x16 = take((size_t)T * H * 2);
-    L.h = take((P * F + (size_t)T * Fs) * 4);
-    L.hs = take((P * (F / 32) + (size_t)T * (Fs / 32)) * 4);
+    L.h = take((P * F + (size_t)T * Fs) * 2);
     L.y = take((P + (Fs ? (size_t)T : 0)) * H * 4);
     L.total = off;
     return L;

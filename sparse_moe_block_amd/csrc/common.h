@@ -14,7 +14,7 @@ constexpr int kWave = 64;
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 16;
 constexpr int kUnit = 256;        // elements per 16-byte-aligned run of 8 blocks
-constexpr int kGemvTokens = 8;    // tokens a GEMV lane accumulates at once
+constexpr int kGemvTokens = 4;    // tokens a GEMV lane accumulates at once
 constexpr int kGemmBM = 128;      // token rows per grouped-GEMM tile
 constexpr int kGemvMaxT = 64;     // AUTO: GEMV family up to this many tokens
 
@@ -29,14 +29,11 @@ static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 
 // Byte offsets of the per-call scratch areas inside the workspace.
 struct WsLayout {
-    size_t active;   // int32 [E + 1]                 active expert list
-    size_t tiles;    // int32 [2 * max_tiles]         (expert, first row) per GEMM tile
-    size_t xs;       // f32  [T][H/32]                block sums of x (GEMV)
-    size_t x32;      // f32  [T][H]                   x in fp32 (GEMV)
-    size_t x16;      // f16  [T][H]                   x in fp16 (GEMM)
-    size_t h;        // f32  [P][F] then [T][Fs]       SiLU(g)*u (f16 in the GEMM family)
-    size_t hs;       // f32  [P][F/32] then [T][Fs/32] block sums of h (GEMV)
-    size_t y;        // f32  [P][H] then [T][H]        per-pair expert outputs
+    size_t active;   // int4 [E + 1]              (expert, first row, rows) per active expert
+    size_t tiles;    // int4 [max_tiles]          (expert, first row, rows) per GEMM tile
+    size_t x16;      // f16  [T][H]               x (pair order for the GEMV family)
+    size_t h;        // f16  [P][F] then [T][Fs]  SiLU(g)*u (pair order for the GEMV family)
+    size_t y;        // f32  [P][H] then [T][H]   per-pair expert outputs
     size_t total;
     int max_tiles;
 };
@@ -52,11 +49,9 @@ WsLayout ws_layout(const fw_moe_desc &d, int T);
 template <int Q> struct QT;
 template <> struct QT<FW_Q4_0> {
     static constexpr int kBlockBytes = 18, kUnitBytes = 144, kUnitX4 = 9;
-    static constexpr float kOffset = 8.0f;      // codes are decoded as q, value = d*(q-8)
 };
 template <> struct QT<FW_Q8_0> {
     static constexpr int kBlockBytes = 34, kUnitBytes = 272, kUnitX4 = 17;
-    static constexpr float kOffset = 128.0f;    // codes are decoded as q+128, value = d*q
 };
 
 // Uniform read of data no kernel writes while the reader runs (schedules,
@@ -76,14 +71,6 @@ __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 }
 
-// v_and_b32 the optimiser cannot narrow: keeps the four masked nibbles in byte
-// lanes so that each converts with one v_cvt_f32_ubyte{0,1,2,3}.
-__device__ __forceinline__ uint32_t and_opaque(uint32_t v, uint32_t m) {
-    uint32_t r;
-    asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(v), "s"(m));
-    return r;
-}
-
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
     _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)bits16);
     return (float)h;
@@ -93,52 +80,108 @@ __device__ __forceinline__ uint32_t funnel16(uint32_t lo, uint32_t hi) {
     return __builtin_amdgcn_alignbyte(hi, lo, 2);   // bytes 2..5 of hi:lo
 }
 
-// Decode block B of a unit held as dwords w[]: the fp32 scale and the 32 codes
-// as floats *offset by QT<Q>::kOffset* (Q4_0: q in 0..15; Q8_0: q+128 in
-// 1..255), so that value_i = d * (c_i - kOffset).
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+
+// The code dwords of block B of a unit held as dwords w[] (4 for Q4_0, 8 for
+// Q8_0, realigned), and its fp16 scale as fp32.
 template <int Q, int B>
-__device__ __forceinline__ void decode_block(const uint32_t *w, float &d, float c[32]) {
+__device__ __forceinline__ float block_codes(const uint32_t *w, uint32_t *q) {
     if constexpr (Q == FW_Q4_0) {
-        constexpr int base = (B / 2) * 9;  // dword index of the even block of the pair
-        uint32_t q[4];
+        constexpr int base = (B / 2) * 9;   // dword index of the even block of the pair
         if constexpr (B % 2 == 0) {
-            d = half_bits_to_float(w[base] & 0xFFFFu);
 #pragma unroll
             for (int i = 0; i < 4; ++i) q[i] = funnel16(w[base + i], w[base + i + 1]);
+            return half_bits_to_float(w[base] & 0xFFFFu);
         } else {
-            d = half_bits_to_float(w[base + 4] >> 16);
 #pragma unroll
             for (int i = 0; i < 4; ++i) q[i] = w[base + 5 + i];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = and_opaque(q[i], 0x0F0F0F0Fu);
-            const uint32_t hi = and_opaque(q[i] >> 4, 0x0F0F0F0Fu);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                c[4 * i + j] = (float)((lo >> (8 * j)) & 0xFFu);
-                c[16 + 4 * i + j] = (float)((hi >> (8 * j)) & 0xFFu);
-            }
+            return half_bits_to_float(w[base + 4] >> 16);
         }
     } else {
         constexpr int base = (B / 2) * 17;
-        uint32_t q[8];
         if constexpr (B % 2 == 0) {
-            d = half_bits_to_float(w[base] & 0xFFFFu);
 #pragma unroll
             for (int i = 0; i < 8; ++i) q[i] = funnel16(w[base + i], w[base + i + 1]);
+            return half_bits_to_float(w[base] & 0xFFFFu);
         } else {
-            d = half_bits_to_float(w[base + 8] >> 16);
 #pragma unroll
             for (int i = 0; i < 8; ++i) q[i] = w[base + 9 + i];
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t u = q[i] ^ 0x80808080u;   // signed byte q -> unsigned q + 128
-#pragma unroll
-            for (int j = 0; j < 4; ++j) c[4 * i + j] = (float)((u >> (8 * j)) & 0xFFu);
+            return half_bits_to_float(w[base + 8] >> 16);
         }
     }
+}
+
+// Pair order.  The 32 elements of a block are consumed as 16 fp16 pairs; pair
+// 4m+j (m = 0..3) holds elements
+//   j = 0: (4m, 4m+2)          j = 1: (16+4m, 16+4m+2)
+//   j = 2: (4m+1, 4m+3)        j = 3: (16+4m+1, 16+4m+3)
+// On the weight side pairs j = 1, 3 carry 16 * value, on the activation side
+// value / 16 (exact scalings), so every pair product is unchanged.  This order
+// lets a Q4_0 code dword become four pairs with one mask each: the low nibbles
+// of bytes 0 and 2 sit at bits 0 and 16, their high nibbles at bits 4 and 20.
+__device__ __forceinline__ int pair_pos(int i) {   // element i -> half index in its block
+    const int hi = i >> 4, m = (i & 15) >> 2, j = i & 3;
+    return 2 * (4 * m + (j & 1) * 2 + hi) + (j >> 1);
+}
+
+// Block B of a unit as 16 exact fp16 pairs (in pair order) times its scale d:
+// value of element i = d * (pair value), pairs j = 1, 3 scaled by 16.
+//  Q4_0: (c & 0x000F000F) | 0x6400_6400 is the pair 1024 + q; minus 1032 gives
+//        q - 8.  The high nibbles masked in place give 1024 + 16q; minus 1152
+//        gives 16(q - 8).
+//  Q8_0: c ^ 0x80808080 turns signed codes into q + 128; v_perm places two of
+//        them under a 0x64 exponent byte: 1024 + 128 + q; minus 1152 gives q,
+//        and for j = 1, 3 a fused 16x - 18432 gives 16q.  All exact in fp16.
+// (c & m) | k in one v_and_or_b32.  gfx950's VOP3 encoding takes no literal
+// constants, so the mask travels in an SGPR and the exponent bits in a VGPR
+// set up once; left to itself the compiler splits the expression into a
+// v_and and a v_or with literals.
+__device__ __forceinline__ uint32_t and_or(uint32_t c, uint32_t m, uint32_t k) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(c), "s"(m), "v"(k));
+    return r;
+}
+
+template <int Q, int B>
+__device__ __forceinline__ float decode_pairs(const uint32_t *w, h2 *p, uint32_t magic) {
+    const h2 k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const h2 k1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
+    if constexpr (Q == FW_Q4_0) {
+        uint32_t q[4];
+        const float d = block_codes<Q, B>(w, q);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t c = q[m], c8 = q[m] >> 8;
+            p[4 * m + 0] = as_h2(and_or(c, 0x000F000Fu, magic)) - k1032;
+            p[4 * m + 1] = as_h2(and_or(c, 0x00F000F0u, magic)) - k1152;
+            p[4 * m + 2] = as_h2(and_or(c8, 0x000F000Fu, magic)) - k1032;
+            p[4 * m + 3] = as_h2(and_or(c8, 0x00F000F0u, magic)) - k1152;
+        }
+        return d;
+    } else {
+        uint32_t q[8];
+        const float d = block_codes<Q, B>(w, q);
+        const h2 k16 = {(_Float16)16.0f, (_Float16)16.0f};
+        const h2 k18432 = {(_Float16)18432.0f, (_Float16)18432.0f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t lo = q[m] ^ 0x80808080u, hi = q[4 + m] ^ 0x80808080u;
+            // byte selectors: 0..3 pick from the second operand, 4..7 from the first
+            p[4 * m + 0] = as_h2(__builtin_amdgcn_perm(magic, lo, 0x04020400u)) - k1152;
+            p[4 * m + 1] = as_h2(__builtin_amdgcn_perm(magic, hi, 0x04020400u)) * k16 - k18432;
+            p[4 * m + 2] = as_h2(__builtin_amdgcn_perm(magic, lo, 0x04030401u)) - k1152;
+            p[4 * m + 3] = as_h2(__builtin_amdgcn_perm(magic, hi, 0x04030401u)) * k16 - k18432;
+        }
+        return d;
+    }
+}
+
+// The exponent bits decode_pairs ORs in: 0x6400 per half (fp16 1024).
+// For Q8_0 the same register serves as the 0x64 byte source of v_perm.
+template <int Q> __device__ __forceinline__ uint32_t pair_magic() {
+    return Q == FW_Q4_0 ? 0x64006400u : 0x64646464u;
 }
 
 // ---------------------------------------------------------------------------

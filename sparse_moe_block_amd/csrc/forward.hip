@@ -9,14 +9,13 @@ constexpr int kPrepThreads = 256;
 
 // Block 0 turns expert_offsets into the list of active experts
 // (expert, first row, rows) and the grouped-GEMM tile list, clamping anything
-// out of range (FW_STATUS_BAD_OFFSETS).  Blocks 1..T stage one token row each:
-// the GEMV family needs x in fp32 plus its 32-element block sums, the GEMM
-// family x in fp16.
+// out of range (FW_STATUS_BAD_OFFSETS).  Blocks 1..T stage one token row each
+// in fp16 (bf16 values are exact in fp16): for the GEMV family in pair order
+// (see decode_pairs), for the GEMM family in natural order.
 __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(
     const int32_t *__restrict__ offsets, int E, int P, const void *__restrict__ x, int act_bf16,
     int H, int T, int gemm, int max_tiles, int4 *__restrict__ active, int4 *__restrict__ tiles,
-    float *__restrict__ xs, float *__restrict__ x32, _Float16 *__restrict__ x16,
-    WsHeader *__restrict__ hdr) {
+    _Float16 *__restrict__ x16, WsHeader *__restrict__ hdr) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     if (blockIdx.x == 0) {
         __shared__ int wsum_a[kPrepThreads / kWave], wsum_t[kPrepThreads / kWave];
@@ -77,39 +76,49 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(
     }
     const int t = blockIdx.x - 1;
     if (t >= T) return;
-    // 8 elements per thread per step; 4 consecutive threads cover one 32-block
-    for (int h0 = tid * 8; h0 < H; h0 += kPrepThreads * 8) {
-        float v[8];
+    // one 32-element block per thread
+    for (int b = tid; b < H / 32; b += kPrepThreads) {
+        float v[32];
         if (act_bf16) {
-            const uint4 raw = *(const uint4 *)((const uint16_t *)x + (size_t)t * H + h0);
-            const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+            const uint4 *src = (const uint4 *)((const uint16_t *)x + (size_t)t * H + 32 * b);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[2 * i] = __uint_as_float(wd[i] << 16);
-                v[2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
+            for (int q = 0; q < 4; ++q) {
+                const uint4 raw = src[q];
+                const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[8 * q + 2 * i] = __uint_as_float(wd[i] << 16);
+                    v[8 * q + 2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
+                }
             }
         } else {
-            const float4 a = *(const float4 *)((const float *)x + (size_t)t * H + h0);
-            const float4 b = *(const float4 *)((const float *)x + (size_t)t * H + h0 + 4);
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+            const float4 *src = (const float4 *)((const float *)x + (size_t)t * H + 32 * b);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float4 f = src[q];
+                v[4 * q] = f.x;
+                v[4 * q + 1] = f.y;
+                v[4 * q + 2] = f.z;
+                v[4 * q + 3] = f.w;
+            }
         }
+        uint32_t o[16];
         if (gemm) {
-            typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-            h8 o;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = (_Float16)v[i];
-            *(h8 *)(x16 + (size_t)t * H + h0) = o;
+            for (int i = 0; i < 16; ++i)
+                o[i] = __builtin_bit_cast(uint32_t, h2{(_Float16)v[2 * i], (_Float16)v[2 * i + 1]});
         } else {
-            *(float4 *)(x32 + (size_t)t * H + h0) = float4{v[0], v[1], v[2], v[3]};
-            *(float4 *)(x32 + (size_t)t * H + h0 + 4) = float4{v[4], v[5], v[6], v[7]};
-            float s = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) s += v[i];
-            s += __shfl_xor(s, 1);
-            s += __shfl_xor(s, 2);
-            if ((tid & 3) == 0) xs[(size_t)t * (H / 32) + h0 / 32] = s;
+            for (int pi = 0; pi < 16; ++pi) {
+                const int m = pi >> 2, j = pi & 3;
+                const int e0 = (j & 1 ? 16 : 0) + 4 * m + (j >> 1);
+                const float sc = (j & 1) ? 0.0625f : 1.0f;
+                o[pi] = __builtin_bit_cast(uint32_t, h2{(_Float16)(v[e0] * sc), (_Float16)(v[e0 + 2] * sc)});
+            }
         }
+        uint4 *dst = (uint4 *)(x16 + (size_t)t * H + 32 * b);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[q] = uint4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
     }
 }
 
@@ -153,8 +162,8 @@ hipError_t launch_prepare(const FwdArgs &a, hipStream_t s) {
     const bool gemm = a.path == FW_PATH_GEMM;
     prepare_kernel<<<1 + a.T, kPrepThreads, 0, s>>>(
         a.offsets, a.d.n_experts, a.P, a.x, a.d.act_dtype == FW_BF16, a.d.hidden, a.T, gemm,
-        a.L.max_tiles, (int4 *)(a.ws + a.L.active), (int4 *)(a.ws + a.L.tiles), (float *)(a.ws + a.L.xs),
-        (float *)(a.ws + a.L.x32), (_Float16 *)(a.ws + a.L.x16), (WsHeader *)a.ws);
+        a.L.max_tiles, (int4 *)(a.ws + a.L.active), (int4 *)(a.ws + a.L.tiles),
+        (_Float16 *)(a.ws + a.L.x16), (WsHeader *)a.ws);
     return hipGetLastError();
 }
 
