@@ -130,20 +130,36 @@ __device__ __forceinline__ void stream_units(uint4 *buf, const uint8_t *ta, cons
                                              cu32 *const *in, float (*acc)[NT]) {
     constexpr int X4 = QT<Q>::kUnitX4;
     uint32_t w[4 * X4];
+    // cur accumulates the batch being consumed; with two matrices the two
+    // accumulator sets swap after every batch (gate, up, gate, ...), which keeps
+    // a single dot_unit in the loop body
+    float cur[NTK], oth[NTK];
+#pragma unroll
+    for (int n = 0; n < NTK; ++n) cur[n] = oth[n] = 0.f;
+    const int nb = NV * (U / S);
     stage_unit<Q>(buf, ta, rowbytes, wave, lane);
-    for (int u = wave; u < U; u += S) {
-        const bool more = u + S < U;
+    for (int i = 0; i < nb; ++i) {
+        const int u = wave + (i / NV) * S;
         read_unit<Q>(buf, lane, w);
-        if (NV == 2) {
-            stage_unit<Q>(buf, tb, rowbytes, u, lane);
-            dot_unit<Q, NTK>(w, u, in, acc[0]);
-            read_unit<Q>(buf, lane, w);
-            if (more) stage_unit<Q>(buf, ta, rowbytes, u + S, lane);
-            dot_unit<Q, NTK>(w, u, in, acc[NV - 1]);
-        } else {
-            if (more) stage_unit<Q>(buf, ta, rowbytes, u + S, lane);
-            dot_unit<Q, NTK>(w, u, in, acc[0]);
+        if (i + 1 < nb) {
+            const int un = wave + ((i + 1) / NV) * S;
+            stage_unit<Q>(buf, (NV == 2 && ((i + 1) & 1)) ? tb : ta, rowbytes, un, lane);
         }
+        dot_unit<Q, NTK>(w, u, in, cur);
+        if (NV == 2) {
+#pragma unroll
+            for (int n = 0; n < NTK; ++n) {
+                const float t = cur[n];
+                cur[n] = oth[n];
+                oth[n] = t;
+            }
+        }
+    }
+    // nb is even for two matrices: cur holds gate, oth holds up
+#pragma unroll
+    for (int n = 0; n < NTK; ++n) {
+        acc[0][n] = cur[n];
+        if (NV == 2) acc[NV - 1][n] = oth[n];
     }
 }
 
