@@ -36,6 +36,8 @@ WORKLOADS = {
     "decode1": (moegen.QWEN3_DECODE, 1, 16),
     "deepseek1": (moegen.DEEPSEEK, 1, 2),
     "deepseek32": (moegen.DEEPSEEK, 32, 2),
+    "prefill2048": (moegen.QWEN3_PREFILL, 2048, 4),
+    "deepseek4096": (moegen.DEEPSEEK, 4096, 1),
 }
 
 
@@ -127,20 +129,35 @@ def main():
     stage_ms = np.array([[e[s].elapsed_time(e[s + 1]) for s in range(4)] for e in evs])
     stage_avg = stage_ms.mean(axis=0)
 
-    # dominant kernel: the gate/up projection (2/3 of the expert bytes)
-    bq = moegen.BLOCK_BYTES[cfg.expert_q]
-    gu_bytes = n_active * 2 * cfg.ffn * (H // 32) * bq       # active experts' gate+up
-    gu_bytes += T * H * 2 + P * cfg.ffn * 4                   # x in (bf16), a out (fp32)
-    if cfg.shared_ffn:
-        gu_bytes += 2 * cfg.shared_ffn * (H // 32) * moegen.BLOCK_BYTES[cfg.shared_q]
-        gu_bytes += T * cfg.shared_ffn * 4
+    # dominant kernel: the gate/up projection (2/3 of the expert bytes and flops)
+    path = fw.fw_moe_forward_path(desc, T)
     gu_ms = float(stage_avg[1])
-    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    bq = moegen.BLOCK_BYTES[cfg.expert_q]
+    if path == fw.FW_PATH_GEMV:
+        # bytes: the active experts' gate and up rows, x in (bf16), a out
+        gu_alg = n_active * 2 * cfg.ffn * (H // 32) * bq + T * H * 2 + P * cfg.ffn * 2
+        if cfg.shared_ffn:
+            gu_alg += 2 * cfg.shared_ffn * (H // 32) * moegen.BLOCK_BYTES[cfg.shared_q]
+            gu_alg += T * cfg.shared_ffn * 2
+        achieved = gu_alg / (gu_ms * 1e-3) / 1e9
+        roof = {"kernel": "gemv_kernel<gate/up>", "bound": "hbm", "achieved": achieved,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                "traffic": None, "algorithmic_bytes": gu_alg}
+    else:
+        # flops: 2 projections x 2 flops x P x H x F (+ the shared expert on T rows)
+        gu_alg = 4 * P * H * cfg.ffn + 4 * T * H * cfg.shared_ffn
+        achieved = gu_alg / (gu_ms * 1e-3) / 1e12
+        roof = {"kernel": "gemm_kernel<gate/up>", "bound": "mfma", "achieved": achieved,
+                "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_FP16_PEAK_TFLOPS, "traffic": None,
+                "algorithmic_flops": gu_alg}
     layer_bytes = (n_active * cfg.expert_bytes + cfg.shared_bytes + cfg.router_bytes +
                    cfg.act_bytes(T) + T * H * 4)
+    layer_flops = 6 * P * H * cfg.ffn + 6 * T * H * cfg.shared_ffn + 2 * T * H * E
 
     line = {
-        "metric": "MoE-layer tokens/s (decode; HBM-bound)",
+        "metric": "MoE-layer tokens/s (" + ("decode; HBM-bound" if path == fw.FW_PATH_GEMV
+                                             else "prefill; MFMA-bound") + ")",
         "value": T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -155,13 +172,12 @@ def main():
         "config": {"workload": f"{cfg.name}, T={T}", "hidden": H, "experts": E, "top_k": k,
                    "ffn": cfg.ffn, "expert_format": cfg.expert_q, "shared_ffn": cfg.shared_ffn,
                    "tokens": T, "active_experts": n_active, "weight_copies": copies,
-                   "path": fw.fw_moe_forward_path(desc, T)},
+                   "path": "gemv" if path == fw.FW_PATH_GEMV else "gemm"},
         "layer_GBps": layer_bytes / (ms * 1e-3) / 1e9,
+        "layer_TFLOPs": layer_flops / (ms * 1e-3) / 1e12,
         "stage_us": {n: round(float(v) * 1e3, 2) for n, v in
                      zip(["prepare", "gate_up", "down", "combine"], stage_avg)},
-        "roofline": {"kernel": "gemv_gate_up_kernel", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes": gu_bytes},
+        "roofline": roof,
     }
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, L, x, T, a.cpu_seconds)

@@ -68,8 +68,7 @@ int check_T(const fw_moe_desc *d, int32_t T) {
 
 int resolve_path(const fw_moe_desc *d, int32_t T) {
     if (d->path != FW_PATH_AUTO) return d->path;
-    (void)T;
-    return FW_PATH_GEMV;
+    return T <= kGemvMaxT ? FW_PATH_GEMV : FW_PATH_GEMM;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FW_OK : FW_EHIP; }
@@ -162,7 +161,6 @@ int fw_moe_forward(const fw_moe_desc *desc, int32_t T, const void *x, const void
     a.T = T;
     a.P = T * desc->top_k;
     a.path = resolve_path(desc, T);
-    if (a.path == FW_PATH_GEMM) return FW_EUNSUPPORTED;
     a.L = ws_layout(*desc, T);
     if (ws_bytes < a.L.total) return FW_EWORKSPACE;
     a.x = x;
@@ -183,9 +181,12 @@ int fw_moe_forward(const fw_moe_desc *desc, int32_t T, const void *x, const void
     if (ev) hipEventRecord(g_events[0], s);
     if ((rc = hip_status(launch_prepare(a, s))) != FW_OK) return rc;
     if (ev) hipEventRecord(g_events[1], s);
-    if ((rc = hip_status(launch_gemv_gate_up(a, s))) != FW_OK) return rc;
+    const bool gemm = a.path == FW_PATH_GEMM;
+    rc = hip_status(gemm ? launch_gemm_gate_up(a, s) : launch_gemv_gate_up(a, s));
+    if (rc != FW_OK) return rc;
     if (ev) hipEventRecord(g_events[2], s);
-    if ((rc = hip_status(launch_gemv_down(a, s))) != FW_OK) return rc;
+    rc = hip_status(gemm ? launch_gemm_down(a, s) : launch_gemv_down(a, s));
+    if (rc != FW_OK) return rc;
     if (ev) hipEventRecord(g_events[3], s);
     if ((rc = hip_status(launch_combine(a, s))) != FW_OK) return rc;
     if (ev) hipEventRecord(g_events[4], s);

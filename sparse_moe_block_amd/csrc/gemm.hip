@@ -1,0 +1,355 @@
+// Forward, GEMM family (prefill-sized batches): grouped, dequant-fused expert
+// GEMMs on MFMA.  Batched expert work is a dense contraction (the pages' runtime
+// runs prefill experts through "the dense batch kernels" and block-table MMQ
+// GEMMs -- Flyweight 0.2.0 "Features" and "Runtime controls"), so it runs on
+// the matrix cores:
+//
+//  - a tile is up to 128 rows of one expert's segment of the sorted pair list
+//    (tokens gathered through sorted_pairs) times 128 weight rows; the tile list
+//    is built on the device (prepare kernel), so no host synchronisation;
+//  - K advances 64 elements (two GGUF blocks) per step: the activation rows
+//    (fp16) and the weight rows dequantised to fp16 (exact codes times the fp16
+//    scale, one rounding) are staged in double-buffered, padded LDS;
+//  - v_mfma_f32_16x16x32_f16 with fp32 accumulation; four wavefronts in 2x2,
+//    each owning 64 x 64 of the tile (4 x 4 MFMA tiles);
+//  - gate/up: the 128 weight rows are 64 gate rows and the same 64 up rows,
+//    arranged so a lane holds gate and up of the same (token, feature) and
+//    forms SiLU(g)*u in registers; outputs leave through LDS as whole rows;
+//  - consecutive workgroups of one XCD take the column tiles of one row tile,
+//    so its gathered activation rows stay in that XCD's L2.
+//
+// fp16 rather than bf16 operands: bf16 (8-bit significand) roundings of the
+// dequantised weights cost ~3e-3 relative error on a layer output, above the
+// layer's tolerance; fp16 costs ~2.4e-4 at the same MFMA rate on gfx950.
+#include <math.h>
+
+#include "common.h"
+
+namespace fw {
+namespace {
+
+constexpr int BM = kGemmBM;   // 128 token rows
+constexpr int BN = 128;       // weight rows
+constexpr int BK = 64;        // K per step (two blocks)
+constexpr int LDK = BK + 8;   // padded LDS row (halfs): 144-byte stride
+constexpr int kThreads = 256;
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+struct Smem {
+    _Float16 a[2][BM * LDK];
+    _Float16 b[2][BN * LDK];
+};
+
+// Raw bytes of block kb of a weight row: the block pair starting at block
+// 2*(kb/2) is 4-byte aligned; block kb occupies dwords [R*s, R*s + R) of the
+// pair's window with R = 5 (Q4_0) or 9 (Q8_0), s = kb & 1.
+template <int Q> struct Raw {
+    uint32_t w[Q == FW_Q4_0 ? 5 : 9];
+};
+
+template <int Q>
+__device__ __forceinline__ void fetch_block(const uint8_t *row, int kb, Raw<Q> &r) {
+    constexpr int R = Q == FW_Q4_0 ? 5 : 9, PB = Q == FW_Q4_0 ? 36 : 68;
+    const uint32_t *p = (const uint32_t *)(row + (size_t)(kb >> 1) * PB) + (R - 1) * (kb & 1);
+#pragma unroll
+    for (int i = 0; i < R; ++i) r.w[i] = p[i];
+}
+
+// The 32 values d * code of the fetched block as fp16 (one rounding each),
+// packed two per dword in element order.
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, h2{(_Float16)a, (_Float16)b});
+}
+
+template <int Q>
+__device__ __forceinline__ void dequant_block(const Raw<Q> &r, int s, uint32_t *dst) {
+    if constexpr (Q == FW_Q4_0) {
+        uint32_t q[4];
+        float d;
+        if (s == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) q[i] = funnel16(r.w[i], r.w[i + 1]);
+            d = half_bits_to_float(r.w[0] & 0xFFFFu);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) q[i] = r.w[i + 1];
+            d = half_bits_to_float(r.w[0] >> 16);
+        }
+        // element 4i+j is the low nibble of byte j of q[i], element 16+4i+j its high nibble
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t c = q[i];
+            auto lo = [&](int j) { return d * (float)((int)((c >> (8 * j)) & 15) - 8); };
+            auto hi = [&](int j) { return d * (float)((int)((c >> (8 * j + 4)) & 15) - 8); };
+            dst[2 * i] = pack2(lo(0), lo(1));
+            dst[2 * i + 1] = pack2(lo(2), lo(3));
+            dst[8 + 2 * i] = pack2(hi(0), hi(1));
+            dst[8 + 2 * i + 1] = pack2(hi(2), hi(3));
+        }
+    } else {
+        uint32_t q[8];
+        float d;
+        if (s == 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = funnel16(r.w[i], r.w[i + 1]);
+            d = half_bits_to_float(r.w[0] & 0xFFFFu);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = r.w[i + 1];
+            d = half_bits_to_float(r.w[0] >> 16);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t c = q[i];
+            auto v = [&](int j) { return d * (float)(int)(int8_t)((c >> (8 * j)) & 0xFF); };
+            dst[2 * i] = pack2(v(0), v(1));
+            dst[2 * i + 1] = pack2(v(2), v(3));
+        }
+    }
+}
+
+// One (row tile, column tile) of one expert (or of the shared expert).
+//  GU:  A = x rows gathered through sorted_pairs (routed) or token rows
+//       (shared); weight rows = 64 gate + 64 up features; writes
+//       a = SiLU(g) * u (fp16) for 64 features;
+//  !GU: A = rows of a (fp16); weight rows = 128 outputs; writes y (fp32).
+template <int Q, bool GU>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(
+    const uint8_t *__restrict__ wa, const uint8_t *__restrict__ wb,
+    const int4 *__restrict__ tiles, WsHeader *__restrict__ hdr,
+    const int32_t *__restrict__ sorted, const _Float16 *__restrict__ ain,
+    _Float16 *__restrict__ hout, float *__restrict__ yout, int K, int N, int k, int P,
+    int col_tiles, int n_row_tiles_max, int shared, int shared_rows) {
+    __shared__ Smem sm;
+    // XCD-aware order: the workgroups one XCD runs (every 8th block) take a
+    // contiguous range of (row tile, column tile) pairs, column tiles fastest.
+    const int nblk = gridDim.x, per_xcd = nblk / 8;
+    const int lin = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    const int rt = lin / col_tiles, ct = lin % col_tiles;
+    if (rt >= n_row_tiles_max) return;
+    int expert = 0, rb = 0, rows = 0;
+    if (shared) {
+        rb = rt * BM;
+        rows = min(BM, shared_rows - rb);
+        if (rows <= 0) return;
+    } else {
+        if (rt >= ld_const(&hdr->n_tiles)) return;
+        const int4 tl = ld_const(tiles + rt);   // (expert, first row, rows)
+        expert = tl.x;
+        rb = tl.y;
+        rows = tl.z;
+    }
+    const size_t rowbytes = (size_t)(K / 32) * QT<Q>::kBlockBytes;
+    const size_t esz = (size_t)N * rowbytes;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = wave_id();
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // ---- per-thread load roles (fixed over the K loop) ----
+    // A: thread -> tile row tid/2, 32 of the 64 K-step halfs
+    const int arow = tid >> 1, ahalf = tid & 1;
+    int src_row;
+    {
+        const int r = rb + min(arow, rows - 1);
+        src_row = r;
+        if (GU && !shared) {
+            const int q = ld_const(sorted + r);
+            if ((unsigned)q >= (unsigned)P) {
+                if (arow < rows) atomicOr(&hdr->status, FW_STATUS_BAD_PAIR);
+                src_row = 0;
+            } else {
+                src_row = q / k;
+            }
+        }
+    }
+    const _Float16 *asrc = ain + (size_t)src_row * K + ahalf * 32;
+    // B: thread -> weight row tid/2 of the tile, block (tid&1) of the step
+    const int brow = tid >> 1, bblk = tid & 1;
+    const uint8_t *bsrc;
+    if (GU) {
+        // tile rows: wn*64 + [0,32) gate features, wn*64 + [32,64) up features,
+        // features ct*64 + wn*32 + [0,32)
+        const int grp = brow >> 6, within = brow & 63;
+        const int f = ct * 64 + grp * 32 + (within & 31);
+        const uint8_t *base = (within < 32) ? wa : wb;
+        bsrc = base + (size_t)expert * esz + (size_t)f * rowbytes;
+    } else {
+        bsrc = wa + (size_t)expert * esz + (size_t)(ct * BN + brow) * rowbytes;
+    }
+
+    // staging: fetch (global -> registers) before the step's MFMAs, commit
+    // (dequantise, registers -> LDS) after them
+    uint4 a0, a1, a2, a3;
+    Raw<Q> braw;
+#define FW_FETCH(step)                                                    \
+    do {                                                                  \
+        const uint4 *ap = (const uint4 *)(asrc + (step) * BK);            \
+        a0 = ap[0];                                                       \
+        a1 = ap[1];                                                       \
+        a2 = ap[2];                                                       \
+        a3 = ap[3];                                                       \
+        fetch_block<Q>(bsrc, 2 * (step) + bblk, braw);                    \
+    } while (0)
+#define FW_COMMIT(buf)                                                                   \
+    do {                                                                                 \
+        uint4 *ad = (uint4 *)&sm.a[buf][arow * LDK + ahalf * 32];                        \
+        ad[0] = a0;                                                                      \
+        ad[1] = a1;                                                                      \
+        ad[2] = a2;                                                                      \
+        ad[3] = a3;                                                                      \
+        uint32_t t[16];                                                                  \
+        dequant_block<Q>(braw, bblk, t);                                                 \
+        uint4 *bd = (uint4 *)&sm.b[buf][brow * LDK + bblk * 32];                         \
+        bd[0] = uint4{t[0], t[1], t[2], t[3]};                                           \
+        bd[1] = uint4{t[4], t[5], t[6], t[7]};                                           \
+        bd[2] = uint4{t[8], t[9], t[10], t[11]};                                         \
+        bd[3] = uint4{t[12], t[13], t[14], t[15]};                                       \
+    } while (0)
+
+    f4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+    const int steps = K / BK;
+    FW_FETCH(0);
+    FW_COMMIT(0);
+    __syncthreads();
+    const int fr = lane & 15, fk = (lane >> 4) * 8;   // fragment row / k offset
+    for (int st = 0; st < steps; ++st) {
+        const int cur = st & 1;
+        const bool more = st + 1 < steps;
+        if (more) FW_FETCH(st + 1);
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 32) {
+            h8 af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                af[i] = *(const h8 *)&sm.a[cur][(wm * 64 + i * 16 + fr) * LDK + kk + fk];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bf[j] = *(const h8 *)&sm.b[cur][(wn * 64 + j * 16 + fr) * LDK + kk + fk];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+        if (more) FW_COMMIT(cur ^ 1);
+        __syncthreads();
+    }
+
+#undef FW_FETCH
+#undef FW_COMMIT
+
+    // ---- epilogue through LDS (the staging buffers are free now) ----
+    // acc[i][j][r]: tile row wm*64 + i*16 + 4*(lane/16) + r, column wn*64 + j*16 + lane%16
+    if (GU) {
+        // a(row, feature) with feature index wn*32 + j*16 + lane%16, j = 0,1
+        _Float16 *o = (_Float16 *)&sm;   // [BM][64] fp16
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float g = acc[i][j][r], u = acc[i][j + 2][r];
+                    const int row = wm * 64 + i * 16 + 4 * (lane >> 4) + r;
+                    const int col = wn * 32 + j * 16 + (lane & 15);
+                    o[row * 64 + col] = (_Float16)(g / (1.0f + expf(-g)) * u);
+                }
+        __syncthreads();
+        // 128 rows x 128 bytes: thread -> (row tid/2, 64 bytes)
+        const int row = tid >> 1, part = tid & 1;
+        if (row < rows) {
+            const uint4 *s = (const uint4 *)&o[row * 64 + part * 32];
+            uint4 *d = (uint4 *)(hout + (size_t)(rb + row) * N + ct * 64 + part * 32);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d[i] = s[i];
+        }
+    } else {
+        // fp32 [BM][BN] = 64 KB: two passes of 64 rows
+        float *o = (float *)&sm;   // [64][BN]
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            if (wm == half) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int row = i * 16 + 4 * (lane >> 4) + r;
+                            const int col = wn * 64 + j * 16 + (lane & 15);
+                            o[row * BN + col] = acc[i][j][r];
+                        }
+            }
+            __syncthreads();
+            // 64 rows x 512 bytes: thread -> (row tid/4, 128 bytes)
+            const int row = tid >> 2, part = tid & 3;
+            const int grow = half * 64 + row;
+            if (grow < rows) {
+                const uint4 *s = (const uint4 *)&o[row * BN + part * 32];
+                uint4 *d = (uint4 *)(yout + (size_t)(rb + grow) * N + ct * BN + part * 32);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) d[i] = s[i];
+            }
+            __syncthreads();
+        }
+    }
+}
+
+template <int Q, bool GU>
+void launch(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Float16 *ain,
+            _Float16 *hout, float *yout, int K, int N, int shared, hipStream_t s) {
+    const int col_tiles = GU ? N / 64 : N / BN;
+    const int row_tiles = shared ? (a.T + BM - 1) / BM : a.L.max_tiles;
+    int nblk = row_tiles * col_tiles;
+    nblk = (nblk + 7) / 8 * 8;   // the XCD mapping wants a multiple of 8
+    gemm_kernel<Q, GU><<<nblk, kThreads, 0, s>>>(
+        wa, wb, (const int4 *)(a.ws + a.L.tiles), (WsHeader *)a.ws, a.sorted, ain, hout, yout,
+        K, N, a.d.top_k, a.P, col_tiles, row_tiles, shared, shared ? a.T : 0);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_gate_up(const FwdArgs &a, hipStream_t s) {
+    const fw_moe_desc &d = a.d;
+    const _Float16 *x = (const _Float16 *)(a.ws + a.L.x16);
+    _Float16 *h = (_Float16 *)(a.ws + a.L.h);
+    if (d.expert_q == FW_Q4_0)
+        launch<FW_Q4_0, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, 0, s);
+    else
+        launch<FW_Q8_0, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, 0, s);
+    if (d.shared_ffn > 0) {
+        _Float16 *hsh = h + (size_t)a.P * d.ffn;
+        if (d.shared_q == FW_Q4_0)
+            launch<FW_Q4_0, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, 1, s);
+        else
+            launch<FW_Q8_0, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, 1, s);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_down(const FwdArgs &a, hipStream_t s) {
+    const fw_moe_desc &d = a.d;
+    const _Float16 *h = (const _Float16 *)(a.ws + a.L.h);
+    float *y = (float *)(a.ws + a.L.y);
+    if (d.expert_q == FW_Q4_0)
+        launch<FW_Q4_0, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, 0, s);
+    else
+        launch<FW_Q8_0, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, 0, s);
+    if (d.shared_ffn > 0) {
+        const _Float16 *hsh = h + (size_t)a.P * d.ffn;
+        float *ysh = y + (size_t)a.P * d.hidden;
+        if (d.shared_q == FW_Q4_0)
+            launch<FW_Q4_0, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, 1, s);
+        else
+            launch<FW_Q8_0, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, 1, s);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fw
