@@ -162,9 +162,13 @@ int fw_moe_permute(const fw_moe_desc *desc, int32_t T, const int32_t *topk_ids,
  *          fw_moe_permute (validated on the device: see FW_STATUS_*)
  * out      [T][H] fp32 out (fully overwritten)
  * workspace / ws_bytes: at least fw_moe_workspace_size(desc, T) bytes.
- * Numerics: weights are decoded exactly; the GEMV family (small T) multiplies
- * and sums in fp32; the GEMM family (large T) contracts on fp16 MFMA with fp32
- * accumulation (activations and dequantised weights rounded to fp16). */
+ * Numerics: both families round the activations x and the SwiGLU output h to
+ * fp16 and accumulate in fp32.  The GEMV family (small T) multiplies the exact
+ * weight codes (fp16 holds every Q8_0/Q4_0 code) by fp16 activations in fp32
+ * dot products and applies each block's scale in fp32; the GEMM family (large
+ * T) contracts on fp16 MFMA with weights dequantised to fp16 (code times scale,
+ * one rounding).  Either way a layer output stays within 2e-3 max-abs and 1e-3
+ * relative L2 of an fp64 evaluation of the same layer. */
 int fw_moe_forward(const fw_moe_desc *desc, int32_t T, const void *x, const void *w_gate,
                    const void *w_up, const void *w_down, const void *ws_gate,
                    const void *ws_up, const void *ws_down, const float *topk_w,

@@ -31,8 +31,8 @@ static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 struct WsLayout {
     size_t active;   // int4 [E + 1]              (expert, first row, rows) per active expert
     size_t tiles;    // int4 [max_tiles]          (expert, first row, rows) per GEMM tile
-    size_t x16;      // f16  [T][H]               x (pair order for the GEMV family)
-    size_t h;        // f16  [P][F] then [T][Fs]  SiLU(g)*u (pair order for the GEMV family)
+    size_t x16;      // f16  [T][H]               x in pair order
+    size_t h;        // f16  [P][F] then [T][Fs]  SiLU(g)*u in pair order
     size_t y;        // f32  [P][H] then [T][H]   per-pair expert outputs
     size_t total;
     int max_tiles;
@@ -144,13 +144,13 @@ __device__ __forceinline__ uint32_t and_or(uint32_t c, uint32_t m, uint32_t k) {
     return r;
 }
 
-template <int Q, int B>
-__device__ __forceinline__ float decode_pairs(const uint32_t *w, h2 *p, uint32_t magic) {
+// The 16 exact fp16 pairs of one block from its realigned code dwords q[]
+// (4 for Q4_0, 8 for Q8_0), in pair order.
+template <int Q>
+__device__ __forceinline__ void codes_to_pairs(const uint32_t *q, h2 *p, uint32_t magic) {
     const h2 k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
     const h2 k1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
     if constexpr (Q == FW_Q4_0) {
-        uint32_t q[4];
-        const float d = block_codes<Q, B>(w, q);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const uint32_t c = q[m], c8 = q[m] >> 8;
@@ -159,10 +159,7 @@ __device__ __forceinline__ float decode_pairs(const uint32_t *w, h2 *p, uint32_t
             p[4 * m + 2] = as_h2(and_or(c8, 0x000F000Fu, magic)) - k1032;
             p[4 * m + 3] = as_h2(and_or(c8, 0x00F000F0u, magic)) - k1152;
         }
-        return d;
     } else {
-        uint32_t q[8];
-        const float d = block_codes<Q, B>(w, q);
         const h2 k16 = {(_Float16)16.0f, (_Float16)16.0f};
         const h2 k18432 = {(_Float16)18432.0f, (_Float16)18432.0f};
 #pragma unroll
@@ -174,8 +171,15 @@ __device__ __forceinline__ float decode_pairs(const uint32_t *w, h2 *p, uint32_t
             p[4 * m + 2] = as_h2(__builtin_amdgcn_perm(magic, lo, 0x04030401u)) - k1152;
             p[4 * m + 3] = as_h2(__builtin_amdgcn_perm(magic, hi, 0x04030401u)) * k16 - k18432;
         }
-        return d;
     }
+}
+
+template <int Q, int B>
+__device__ __forceinline__ float decode_pairs(const uint32_t *w, h2 *p, uint32_t magic) {
+    uint32_t q[Q == FW_Q4_0 ? 4 : 8];
+    const float d = block_codes<Q, B>(w, q);
+    codes_to_pairs<Q>(q, p, magic);
+    return d;
 }
 
 // The exponent bits decode_pairs ORs in: 0x6400 per half (fp16 1024).

@@ -10,8 +10,8 @@ constexpr int kPrepThreads = 256;
 // Block 0 turns expert_offsets into the list of active experts
 // (expert, first row, rows) and the grouped-GEMM tile list, clamping anything
 // out of range (FW_STATUS_BAD_OFFSETS).  Blocks 1..T stage one token row each
-// in fp16 (bf16 values are exact in fp16): for the GEMV family in pair order
-// (see decode_pairs), for the GEMM family in natural order.
+// in fp16 (bf16 values are exact in fp16), in the pair order both kernel
+// families consume (see decode_pairs).
 __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(
     const int32_t *__restrict__ offsets, int E, int P, const void *__restrict__ x, int act_bf16,
     int H, int T, int gemm, int max_tiles, int4 *__restrict__ active, int4 *__restrict__ tiles,
@@ -103,18 +103,12 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(
             }
         }
         uint32_t o[16];
-        if (gemm) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                o[i] = __builtin_bit_cast(uint32_t, h2{(_Float16)v[2 * i], (_Float16)v[2 * i + 1]});
-        } else {
-#pragma unroll
-            for (int pi = 0; pi < 16; ++pi) {
-                const int m = pi >> 2, j = pi & 3;
-                const int e0 = (j & 1 ? 16 : 0) + 4 * m + (j >> 1);
-                const float sc = (j & 1) ? 0.0625f : 1.0f;
-                o[pi] = __builtin_bit_cast(uint32_t, h2{(_Float16)(v[e0] * sc), (_Float16)(v[e0 + 2] * sc)});
-            }
+        for (int pi = 0; pi < 16; ++pi) {
+            const int m = pi >> 2, j = pi & 3;
+            const int e0 = (j & 1 ? 16 : 0) + 4 * m + (j >> 1);
+            const float sc = (j & 1) ? 0.0625f : 1.0f;
+            o[pi] = __builtin_bit_cast(uint32_t, h2{(_Float16)(v[e0] * sc), (_Float16)(v[e0 + 2] * sc)});
         }
         uint4 *dst = (uint4 *)(x16 + (size_t)t * H + 32 * b);
 #pragma unroll

@@ -9,7 +9,10 @@
 //    is built on the device (prepare kernel), so no host synchronisation;
 //  - K advances 64 elements (two GGUF blocks) per step: the activation rows
 //    (fp16) and the weight rows dequantised to fp16 (exact codes times the fp16
-//    scale, one rounding) are staged in double-buffered, padded LDS;
+//    scale, one rounding) are staged in double-buffered, padded LDS, both in
+//    the pair order of decode_pairs (the MFMA sums over K in any order, so
+//    permuting K the same way on both operands changes nothing), which lets a
+//    block dequantise with packed fp16 operations;
 //  - v_mfma_f32_16x16x32_f16 with fp32 accumulation; four wavefronts in 2x2,
 //    each owning 64 x 64 of the tile (4 x 4 MFMA tiles);
 //  - gate/up: the 128 weight rows are 64 gate rows and the same 64 up rows,
@@ -36,6 +39,7 @@ constexpr int kThreads = 256;
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 struct Smem {
     _Float16 a[2][BM * LDK];
@@ -57,63 +61,34 @@ __device__ __forceinline__ void fetch_block(const uint8_t *row, int kb, Raw<Q> &
     for (int i = 0; i < R; ++i) r.w[i] = p[i];
 }
 
-// The 32 values d * code of the fetched block as fp16 (one rounding each),
-// packed two per dword in element order.
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return __builtin_bit_cast(uint32_t, h2{(_Float16)a, (_Float16)b});
-}
-
+// The fetched block as 16 fp16 pairs in pair order (see decode_pairs), each
+// pair value times the block scale: d * code rounded once to fp16 (pairs
+// j = 1, 3 carry 16 * d * code, matched by activations stored / 16).
 template <int Q>
 __device__ __forceinline__ void dequant_block(const Raw<Q> &r, int s, uint32_t *dst) {
-    if constexpr (Q == FW_Q4_0) {
-        uint32_t q[4];
-        float d;
-        if (s == 0) {
+    constexpr int NQ = Q == FW_Q4_0 ? 4 : 8;
+    uint32_t q[NQ];
+    uint32_t dbits;
+    if (s == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) q[i] = funnel16(r.w[i], r.w[i + 1]);
-            d = half_bits_to_float(r.w[0] & 0xFFFFu);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) q[i] = r.w[i + 1];
-            d = half_bits_to_float(r.w[0] >> 16);
-        }
-        // element 4i+j is the low nibble of byte j of q[i], element 16+4i+j its high nibble
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t c = q[i];
-            auto lo = [&](int j) { return d * (float)((int)((c >> (8 * j)) & 15) - 8); };
-            auto hi = [&](int j) { return d * (float)((int)((c >> (8 * j + 4)) & 15) - 8); };
-            dst[2 * i] = pack2(lo(0), lo(1));
-            dst[2 * i + 1] = pack2(lo(2), lo(3));
-            dst[8 + 2 * i] = pack2(hi(0), hi(1));
-            dst[8 + 2 * i + 1] = pack2(hi(2), hi(3));
-        }
+        for (int i = 0; i < NQ; ++i) q[i] = funnel16(r.w[i], r.w[i + 1]);
+        dbits = r.w[0] & 0xFFFFu;
     } else {
-        uint32_t q[8];
-        float d;
-        if (s == 0) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = funnel16(r.w[i], r.w[i + 1]);
-            d = half_bits_to_float(r.w[0] & 0xFFFFu);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = r.w[i + 1];
-            d = half_bits_to_float(r.w[0] >> 16);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t c = q[i];
-            auto v = [&](int j) { return d * (float)(int)(int8_t)((c >> (8 * j)) & 0xFF); };
-            dst[2 * i] = pack2(v(0), v(1));
-            dst[2 * i + 1] = pack2(v(2), v(3));
-        }
+        for (int i = 0; i < NQ; ++i) q[i] = r.w[i + 1];
+        dbits = r.w[0] >> 16;
     }
+    h2 p[16];
+    codes_to_pairs<Q>(q, p, pair_magic<Q>());
+    const h2 d2 = as_h2(dbits | (dbits << 16));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dst[i] = __builtin_bit_cast(uint32_t, p[i] * d2);
 }
 
 // One (row tile, column tile) of one expert (or of the shared expert).
 //  GU:  A = x rows gathered through sorted_pairs (routed) or token rows
 //       (shared); weight rows = 64 gate + 64 up features; writes
-//       a = SiLU(g) * u (fp16) for 64 features;
+//       a = SiLU(g) * u (fp16, pair order) for 64 features;
 //  !GU: A = rows of a (fp16); weight rows = 128 outputs; writes y (fp32).
 template <int Q, bool GU>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
@@ -178,28 +153,29 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
         bsrc = wa + (size_t)expert * esz + (size_t)(ct * BN + brow) * rowbytes;
     }
 
-    // staging: fetch (global -> registers) before the step's MFMAs, commit
-    // (dequantise, registers -> LDS) after them
-    uint4 a0, a1, a2, a3;
-    Raw<Q> braw;
-#define FW_FETCH(step)                                                    \
+    // staging, two steps ahead: step s is fetched (global -> registers R[s&1])
+    // during the MFMAs of step s-2 and committed (dequantised, registers ->
+    // LDS) after the MFMAs of step s-1, so a load has two MFMA phases to land
+    u4 ra0[4], ra1[4];
+    Raw<Q> rw0, rw1;
+#define FW_FETCH(step, R)                                                 \
     do {                                                                  \
-        const uint4 *ap = (const uint4 *)(asrc + (step) * BK);            \
-        a0 = ap[0];                                                       \
-        a1 = ap[1];                                                       \
-        a2 = ap[2];                                                       \
-        a3 = ap[3];                                                       \
-        fetch_block<Q>(bsrc, 2 * (step) + bblk, braw);                    \
+        const u4 *ap = (const u4 *)(asrc + (step) * BK);                \
+        ra##R[0] = ap[0];                                                 \
+        ra##R[1] = ap[1];                                                 \
+        ra##R[2] = ap[2];                                                 \
+        ra##R[3] = ap[3];                                                 \
+        fetch_block<Q>(bsrc, 2 * (step) + bblk, rw##R);                   \
     } while (0)
-#define FW_COMMIT(buf)                                                                   \
+#define FW_COMMIT(buf, R)                                                                \
     do {                                                                                 \
-        uint4 *ad = (uint4 *)&sm.a[buf][arow * LDK + ahalf * 32];                        \
-        ad[0] = a0;                                                                      \
-        ad[1] = a1;                                                                      \
-        ad[2] = a2;                                                                      \
-        ad[3] = a3;                                                                      \
+        u4 *ad = (u4 *)&sm.a[buf][arow * LDK + ahalf * 32];                              \
+        ad[0] = ra##R[0];                                                                \
+        ad[1] = ra##R[1];                                                                \
+        ad[2] = ra##R[2];                                                                \
+        ad[3] = ra##R[3];                                                                \
         uint32_t t[16];                                                                  \
-        dequant_block<Q>(braw, bblk, t);                                                 \
+        dequant_block<Q>(rw##R, bblk, t);                                                \
         uint4 *bd = (uint4 *)&sm.b[buf][brow * LDK + bblk * 32];                         \
         bd[0] = uint4{t[0], t[1], t[2], t[3]};                                           \
         bd[1] = uint4{t[4], t[5], t[6], t[7]};                                           \
@@ -213,32 +189,34 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-    const int steps = K / BK;
-    FW_FETCH(0);
-    FW_COMMIT(0);
+    const int steps = K / BK;   // >= 4 (K >= 256)
+    FW_FETCH(0, 0);
+    FW_FETCH(1, 1);
+    FW_COMMIT(0, 0);
     __syncthreads();
     const int fr = lane & 15, fk = (lane >> 4) * 8;   // fragment row / k offset
-    for (int st = 0; st < steps; ++st) {
-        const int cur = st & 1;
-        const bool more = st + 1 < steps;
-        if (more) FW_FETCH(st + 1);
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 32) {
-            h8 af[4], bf[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *(const h8 *)&sm.a[cur][(wm * 64 + i * 16 + fr) * LDK + kk + fk];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bf[j] = *(const h8 *)&sm.b[cur][(wn * 64 + j * 16 + fr) * LDK + kk + fk];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    for (int st = 0; st < steps; st += 2) {
+        // even step st: LDS buf 0 holds st, registers R1 hold st+1
+#define FW_STEP(S, BUF, RNEXT, RFETCH)                                                          \
+        {                                                                                       \
+            FW_FETCH(min((S) + 2, steps - 1), RFETCH);   /* clamped: no conditional writes */ \
+            _Pragma("unroll") for (int kk = 0; kk < BK; kk += 32) {                             \
+                h8 af[4], bf[4];                                                                \
+                _Pragma("unroll") for (int i = 0; i < 4; ++i)                                   \
+                    af[i] = *(const h8 *)&sm.a[BUF][(wm * 64 + i * 16 + fr) * LDK + kk + fk];   \
+                _Pragma("unroll") for (int j = 0; j < 4; ++j)                                   \
+                    bf[j] = *(const h8 *)&sm.b[BUF][(wn * 64 + j * 16 + fr) * LDK + kk + fk];   \
+                _Pragma("unroll") for (int i = 0; i < 4; ++i)                                   \
+                    _Pragma("unroll") for (int j = 0; j < 4; ++j)                               \
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j],        \
+                                                                           acc[i][j], 0, 0, 0); \
+            }                                                                                   \
+            if ((S) + 1 < steps) FW_COMMIT((BUF) ^ 1, RNEXT);                                   \
+            __syncthreads();                                                                    \
         }
-        if (more) FW_COMMIT(cur ^ 1);
-        __syncthreads();
+        FW_STEP(st, 0, 1, 0)
+        FW_STEP(st + 1, 1, 0, 1)
+#undef FW_STEP
     }
 
 #undef FW_FETCH
@@ -255,10 +233,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float g = acc[i][j][r], u = acc[i][j + 2][r];
+                    const float g = acc[i][j][r], u = acc[i][j + 2][r];   // gate, up
                     const int row = wm * 64 + i * 16 + 4 * (lane >> 4) + r;
                     const int col = wn * 32 + j * 16 + (lane & 15);
-                    o[row * 64 + col] = (_Float16)(g / (1.0f + expf(-g)) * u);
+                    float a = g / (1.0f + __expf(-g)) * u;
+                    if (col & 16) a *= 0.0625f;   // pair order: pairs j = 1, 3 hold value / 16
+                    o[row * 64 + (col & ~31) + pair_pos(col & 31)] = (_Float16)a;
                 }
         __syncthreads();
         // 128 rows x 128 bytes: thread -> (row tid/2, 64 bytes)

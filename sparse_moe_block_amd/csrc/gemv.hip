@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kWave *kMaxSplit) void gemv_kernel(
                     const size_t r = (size_t)(rb + c0 + n);
                     if constexpr (GU) {
                         const float gv = acc[0][n], up = acc[NV - 1][n];
-                        float a = gv / (1.0f + expf(-gv)) * up;
+                        float a = gv / (1.0f + __expf(-gv)) * up;
                         if (row & 16) a *= 0.0625f;   // pairs j = 1, 3 hold value / 16
                         hout[r * N + (row & ~31) + pair_pos(row & 31)] = (_Float16)a;
                     } else {
