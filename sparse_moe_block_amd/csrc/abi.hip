@@ -178,18 +178,18 @@ int fw_moe_forward(const fw_moe_desc *desc, int32_t T, const void *x, const void
     a.ws = (char *)workspace;
     hipStream_t s = (hipStream_t)stream;
     const bool ev = g_events_on;
-    if (ev) hipEventRecord(g_events[0], s);
+    if (ev) (void)hipEventRecord(g_events[0], s);
     if ((rc = hip_status(launch_prepare(a, s))) != FW_OK) return rc;
-    if (ev) hipEventRecord(g_events[1], s);
+    if (ev) (void)hipEventRecord(g_events[1], s);
     const bool gemm = a.path == FW_PATH_GEMM;
     rc = hip_status(gemm ? launch_gemm_gate_up(a, s) : launch_gemv_gate_up(a, s));
     if (rc != FW_OK) return rc;
-    if (ev) hipEventRecord(g_events[2], s);
+    if (ev) (void)hipEventRecord(g_events[2], s);
     rc = hip_status(gemm ? launch_gemm_down(a, s) : launch_gemv_down(a, s));
     if (rc != FW_OK) return rc;
-    if (ev) hipEventRecord(g_events[3], s);
+    if (ev) (void)hipEventRecord(g_events[3], s);
     if ((rc = hip_status(launch_combine(a, s))) != FW_OK) return rc;
-    if (ev) hipEventRecord(g_events[4], s);
+    if (ev) (void)hipEventRecord(g_events[4], s);
     return FW_OK;
 }
 

@@ -12,66 +12,95 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// bf16 logits on MFMA.  A workgroup owns 16 tokens x (16*NE) experts; its four
-// waves split the reduction dimension H into interleaved 32-wide steps and
-// their partial tiles are summed in wave order through LDS.  bf16 x bf16
-// products are exact in fp32 and accumulate in fp32.
+// bf16 logits on MFMA.  A workgroup owns 16*MT tokens x 16*NE experts; its NW
+// waves split the reduction dimension H into interleaved 32-wide steps (wave
+// w takes steps w, w + NW, ...), issue the loads of U steps before their
+// MFMAs, and their partial tiles are summed in wave order through LDS.  bf16 x
+// bf16 products are exact in fp32 and accumulate in fp32.
+//
+// Decode-sized batches use one 16 x 16 tile per workgroup and 16 waves, so the
+// E x H router streams through E/16 workgroups with 16 loads in flight per
+// wave; prefill-sized batches use 32 x 64 tiles and 4 waves, so each router
+// row is re-read from L2 by fewer workgroups.
 //
 // v_mfma_f32_16x16x32_bf16: lane l supplies A[m = l%16][k = 8*(l/16) .. +7] and
 // B[k = 8*(l/16) .. +7][n = l%16]; it receives D[m = 4*(l/16) + i][n = l%16],
 // i = 0..3.  A = x rows (tokens), B = W_r rows (experts), both read as 16
 // contiguous bytes per lane.
-template <int NE>
-__global__ __launch_bounds__(256) void logits_bf16_kernel(
+template <int MT, int NE, int NW, int U>
+__global__ __launch_bounds__(NW *kWave) void logits_bf16_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
     const float *__restrict__ bias, float *__restrict__ logits, int T, int H, int E) {
-    __shared__ f32x4 red[3][NE][kWave];
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16 * NE;
+    __shared__ f32x4 red[NW - 1][MT * NE][kWave];
+    const int wave = wave_id(), lane = threadIdx.x % kWave;
+    const int t0 = blockIdx.x * 16 * MT, e0 = blockIdx.y * 16 * NE;
     const int r = lane % 16, kq = (lane / 16) * 8;
-    const int t = t0 + r;
-    const bool tv = t < T;
-    const uint16_t *xp = x + (size_t)(tv ? t : 0) * H + kq;
-    const uint16_t *wp[NE];
-    bool ev[NE];
+    const uint16_t *xp[MT], *wp[NE];
+    bool tv[MT], ev[NE];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int t = t0 + 16 * m + r;
+        tv[m] = t < T;
+        xp[m] = x + (size_t)(tv[m] ? t : 0) * H + kq;
+    }
 #pragma unroll
     for (int n = 0; n < NE; ++n) {
         const int e = e0 + 16 * n + r;
         ev[n] = e < E;
         wp[n] = wr + (size_t)(ev[n] ? e : 0) * H + kq;
     }
-    f32x4 acc[NE];
+    f32x4 acc[MT][NE];
 #pragma unroll
-    for (int n = 0; n < NE; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int n = 0; n < NE; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     const bf16x8 zero = {};
-    for (int k = wave * 32; k < H; k += 4 * 32) {
-        bf16x8 a = tv ? *(const bf16x8 *)(xp + k) : zero;
+    const int steps = H / 32;
+    for (int s0 = wave; s0 < steps; s0 += NW * U) {
+        bf16x8 a[U][MT], b[U][NE];
 #pragma unroll
-        for (int n = 0; n < NE; ++n) {
-            bf16x8 b = ev[n] ? *(const bf16x8 *)(wp[n] + k) : zero;
-            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[n], 0, 0, 0);
+        for (int u = 0; u < U; ++u) {
+            const int s = s0 + u * NW;
+            const bool in = s < steps;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                a[u][m] = (in && tv[m]) ? *(const bf16x8 *)(xp[m] + 32 * s) : zero;
+#pragma unroll
+            for (int n = 0; n < NE; ++n)
+                b[u][n] = (in && ev[n]) ? *(const bf16x8 *)(wp[n] + 32 * s) : zero;
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int n = 0; n < NE; ++n)
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][m], b[u][n],
+                                                                        acc[m][n], 0, 0, 0);
     }
     if (wave > 0) {
 #pragma unroll
-        for (int n = 0; n < NE; ++n) red[wave - 1][n][lane] = acc[n];
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int n = 0; n < NE; ++n) red[wave - 1][m * NE + n][lane] = acc[m][n];
     }
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
-    for (int n = 0; n < NE; ++n) {
-        f32x4 v = acc[n];
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int w = 0; w < 3; ++w) v += red[w][n][lane];
-        const int e = e0 + 16 * n + r;
-        if (e >= E) continue;
-        const float b = bias ? bias[e] : 0.f;
+        for (int n = 0; n < NE; ++n) {
+            f32x4 v = acc[m][n];
+            for (int w = 0; w < NW - 1; ++w) v += red[w][m * NE + n][lane];
+            const int e = e0 + 16 * n + r;
+            if (e >= E) continue;
+            const float b = bias ? bias[e] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tt = t0 + 4 * (lane / 16) + i;
-            if (tt < T) logits[(size_t)tt * E + e] = v[i] + b;
+            for (int i = 0; i < 4; ++i) {
+                const int tt = t0 + 16 * m + 4 * (lane / 16) + i;
+                if (tt < T) logits[(size_t)tt * E + e] = v[i] + b;
+            }
         }
-    }
 }
 
 // fp32 logits (small layers): one thread per (token, expert), sequential sum.
@@ -93,60 +122,100 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(
     logits[i] = acc + (bias ? bias[e] : 0.f);
 }
 
-// One wavefront per token.  Lane l holds the logits of experts l, l+64, ...;
-// k rounds of a wave-wide (value, index) arg-max with ties to the lower index
-// pick the experts in descending order; lane j keeps slot j.  Renormalised
-// weights: softmax -> exp(l_j - l_0) / sum over the slots (l_0 is the maximum);
-// sigmoid -> s_j / sum s.
+// Wave-wide reductions on the DPP network (no LDS round trip): quad
+// permutations, half-row and row mirrors leave every lane of a row with the
+// row's result; row broadcasts 15 and 31 carry it into rows 1..3; lane 63
+// holds the wave's result.  Fixed pattern, so sums are deterministic.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp<0xB1>(v));         // quad_perm [1,0,3,2]
+    v = max(v, dpp<0x4E>(v));         // quad_perm [2,3,0,1]
+    v = max(v, dpp<0x141>(v));        // row_half_mirror
+    v = max(v, dpp<0x140>(v));        // row_mirror
+    v = max(v, dpp<0x142, 0xA>(v));   // row_bcast:15 into rows 1, 3
+    v = max(v, dpp<0x143, 0xC>(v));   // row_bcast:31 into rows 2, 3
+    return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ float fdpp_add(float v, uint32_t o) { return v + __uint_as_float(o); }
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v = fdpp_add(v, dpp<0xB1>(__float_as_uint(v)));
+    v = fdpp_add(v, dpp<0x4E>(__float_as_uint(v)));
+    v = fdpp_add(v, dpp<0x141>(__float_as_uint(v)));
+    v = fdpp_add(v, dpp<0x140>(__float_as_uint(v)));
+    // rows 1 and 3 add lane 15 / 47; rows 0 and 2 add nothing (the DPP keeps
+    // their own value, so subtract-free: mask them out of the add instead)
+    {
+        const uint32_t o = dpp<0x142, 0xA>(__float_as_uint(v));
+        const bool add = (__lane_id() >> 4) & 1;
+        v = add ? v + __uint_as_float(o) : v;
+    }
+    {
+        const uint32_t o = dpp<0x143, 0xC>(__float_as_uint(v));
+        const bool add = (__lane_id() >> 5) & 1;
+        v = add ? v + __uint_as_float(o) : v;
+    }
+    return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+
+// Total order of logits as unsigned keys: larger logit -> larger key; -0 and
+// +0 compare equal (both map to the key of +0), NaN maps below -inf.
+__device__ __forceinline__ uint32_t logit_key(float l) {
+    if (l != l) return 0u;
+    const uint32_t u = __float_as_uint(l + 0.0f);   // -0 + 0 = +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_logit(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// One wavefront per token.  Lane l holds the logits of experts l, l+64, ...
+// as keys; each of k rounds takes the wave maximum of the untaken keys (DPP),
+// then the lowest expert index holding it (one ballot per register), so the
+// experts come out in descending logit order with ties to the lower index;
+// lane j keeps slot j.  Renormalised weights: softmax -> exp(l_j - l_0) / sum
+// over the slots (l_0 is the maximum); sigmoid -> s_j / sum s.
 template <int EPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E,
                                                    int k, int score, int32_t *__restrict__ ids,
                                                    float *__restrict__ w) {
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int t = blockIdx.x * 4 + wave;
+    const int lane = threadIdx.x % kWave;
+    const int t = blockIdx.x * 4 + wave_id();
     if (t >= T) return;
-    float v[EPL];
+    uint32_t key[EPL];
+    uint32_t taken = 0;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + kWave * i;
-        float l = e < E ? logits[(size_t)t * E + e] : -INFINITY;
-        v[i] = (l == l) ? l : -INFINITY;   // NaN never outranks a number
+        key[i] = e < E ? logit_key(logits[(size_t)t * E + e]) : 0u;
+        if (e >= E) taken |= 1u << i;   // never selectable
     }
-    uint32_t taken = 0;
     int my_e = 0;
     float my_l = 0.f;
     for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int be = 0x7FFFFFFF;
+        uint32_t best = 0;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const int e = lane + kWave * i;
-            if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
-                bv = v[i];
-                be = e;
-            }
-        }
+        for (int i = 0; i < EPL; ++i)
+            if (!((taken >> i) & 1u)) best = max(best, key[i]);
+        const uint32_t m = wave_max_u32(best);
+        int sel = 0;
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oe = __shfl_xor(be, off);
-            if (ov > bv || (ov == bv && oe < be)) {
-                bv = ov;
-                be = oe;
-            }
+        for (int i = EPL - 1; i >= 0; --i) {   // the lowest i with a match wins
+            const unsigned long long b = __ballot(!((taken >> i) & 1u) && key[i] == m);
+            if (b) sel = kWave * i + __builtin_ctzll(b);
         }
-        if ((be % kWave) == lane) taken |= 1u << (be / kWave);
+        if ((sel % kWave) == lane) taken |= 1u << (sel / kWave);
         if (lane == j) {
-            my_e = be;
-            my_l = bv;
+            my_e = sel;
+            my_l = key_logit(m);
         }
     }
-    const float l0 = __shfl(my_l, 0);
+    const float l0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_l), 0));
     float s = 0.f;
     if (lane < k) s = score == FW_SOFTMAX_RENORM ? expf(my_l - l0) : 1.0f / (1.0f + expf(-my_l));
-    float sum = s;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    const float sum = wave_sum_f32(s);
     if (lane < k) {
         ids[(size_t)t * k + lane] = my_e;
         w[(size_t)t * k + lane] = s / sum;
@@ -158,18 +227,20 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 hipError_t launch_logits(const fw_moe_desc &d, int T, const void *x, const void *wr,
                          const float *bias, float *logits, hipStream_t s) {
     const int H = d.hidden, E = d.n_experts;
+    const uint16_t *xb = (const uint16_t *)x, *wb = (const uint16_t *)wr;
     if (d.act_dtype == FW_F32) {
         const int n = T * E;
         logits_f32_kernel<<<(n + 255) / 256, 256, 0, s>>>((const float *)x, (const float *)wr,
                                                           bias, logits, T, H, E);
-    } else if (E >= 64) {
-        dim3 grid((T + 15) / 16, (E + 63) / 64);
-        logits_bf16_kernel<4><<<grid, 256, 0, s>>>((const uint16_t *)x, (const uint16_t *)wr,
-                                                   bias, logits, T, H, E);
-    } else {
+    } else if (T <= kGemvMaxT) {
         dim3 grid((T + 15) / 16, (E + 15) / 16);
-        logits_bf16_kernel<1><<<grid, 256, 0, s>>>((const uint16_t *)x, (const uint16_t *)wr,
-                                                   bias, logits, T, H, E);
+        logits_bf16_kernel<1, 1, 16, 4><<<grid, 16 * kWave, 0, s>>>(xb, wb, bias, logits, T, H, E);
+    } else if (E >= 64) {
+        dim3 grid((T + 31) / 32, (E + 63) / 64);
+        logits_bf16_kernel<2, 4, 4, 2><<<grid, 4 * kWave, 0, s>>>(xb, wb, bias, logits, T, H, E);
+    } else {
+        dim3 grid((T + 31) / 32, (E + 15) / 16);
+        logits_bf16_kernel<2, 1, 4, 4><<<grid, 4 * kWave, 0, s>>>(xb, wb, bias, logits, T, H, E);
     }
     return hipGetLastError();
 }

@@ -125,3 +125,29 @@ def test_repeat_is_bitwise_identical(path):
         off, sp, inv = G.permute(desc, cfg, ids, ws)
         outs.append(G.forward(desc, cfg, dl, x, w, off, sp, inv, ws).cpu())
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 4), (128, 8), (256, 8), (512, 16), (100, 16)])
+def test_route_ties_and_signed_zeros(ref, E, k):
+    """Selection from logits with many exact ties (a handful of distinct values,
+    +0 and -0 among them): ids must equal the oracle's (descending, ties to the
+    lower index, -0 == +0) and the weights must agree."""
+    T = 37
+    rng = np.random.default_rng(E * 100 + k)
+    vals = np.array([-1.5, -0.0, 0.0, 0.25, 0.25, 1.0, 2.0, -3.0],
+                    dtype=np.float32)
+    lin = vals[rng.integers(0, len(vals), size=(T, E))]
+    lin[0] = 0.0
+    lin[1] = -0.0
+    lin[2, ::2] = -0.0        # alternate signed zeros
+    for score in ("softmax", "sigmoid"):
+        desc = fw.make_desc(256, E, k, 256, score=score)
+        ids = torch.full((T, k), -7, dtype=torch.int32, device=G.DEV)
+        w = torch.full((T, k), float("nan"), device=G.DEV)
+        fw.fw_moe_route(desc, T, None, None, None, torch.from_numpy(lin).to(G.DEV), None, ids, w)
+        x_dummy = np.zeros((T, 256), np.uint16)
+        r_dummy = np.zeros((E, 256), np.uint16)
+        _, rids, rw = ref.route(x_dummy, r_dummy, None, k=k, act_dtype="bf16",
+                                router_dtype="bf16", score=score, logits_in=lin)
+        assert np.array_equal(ids.cpu().numpy(), rids), score
+        assert np.abs(w.cpu().numpy() - rw).max() <= G.W_MAX_ABS, score
