@@ -22,12 +22,16 @@ WsLayout ws_layout(const fw_moe_desc &d, int T) {
         off = align256(off + bytes);
         return at;
     };
-    L.max_tiles = (int)((P + kGemmBM - 1) / kGemmBM + E);
+    // row tiles of either family: GEMM tiles of kGemmBM rows, GEMV chunks of
+    // kGemvTokens rows (the larger count)
+    L.max_tiles = (int)((P + kGemvTokens - 1) / kGemvTokens + E);
     L.active = take((E + 1) * sizeof(int4));
     L.tiles = take((size_t)L.max_tiles * sizeof(int4));
     L.x16 = take((size_t)T * H * 2);
     L.h = take((P * F + (size_t)T * Fs) * 2);
     L.y = take((P + (Fs ? (size_t)T : 0)) * H * 4);
+    L.split_cnt = take((size_t)kSplitTiles * 4);
+    L.split_part = take((size_t)kSplitTiles * kSplitSlicesMax * 2 * kGemvTokens * kWave * 4);
     L.total = off;
     return L;
 }

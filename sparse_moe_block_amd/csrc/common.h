@@ -14,15 +14,19 @@ constexpr int kWave = 64;
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 16;
 constexpr int kUnit = 256;        // elements per 16-byte-aligned run of 8 blocks
-constexpr int kGemvTokens = 4;    // tokens a GEMV lane accumulates at once
+constexpr int kGemvTokens = 2;    // token rows a GEMV work item carries
 constexpr int kGemmBM = 128;      // token rows per grouped-GEMM tile
 constexpr int kGemvMaxT = 64;     // AUTO: GEMV family up to this many tokens
+// GEMV split-K: at most this many (row chunk, weight tile) pairs are split,
+// into at most kSplitSlicesMax reduction slices each
+constexpr int kSplitTiles = 1024;
+constexpr int kSplitSlicesMax = 8;
 
 // First 256 bytes of every workspace.
 struct WsHeader {
     int32_t status;     // sticky FW_STATUS_* bits
     int32_t n_active;   // experts with at least one routed pair
-    int32_t n_tiles;    // grouped-GEMM row tiles (routed experts)
+    int32_t n_tiles;    // row tiles of the routed experts (GEMM tiles or GEMV chunks)
     int32_t reserved[61];
 };
 static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
@@ -30,10 +34,12 @@ static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 // Byte offsets of the per-call scratch areas inside the workspace.
 struct WsLayout {
     size_t active;   // int4 [E + 1]              (expert, first row, rows) per active expert
-    size_t tiles;    // int4 [max_tiles]          (expert, first row, rows) per GEMM tile
+    size_t tiles;    // int4 [max_tiles]          (expert, first row, rows) per row tile
     size_t x16;      // f16  [T][H]               x in pair order
     size_t h;        // f16  [P][F] then [T][Fs]  SiLU(g)*u in pair order
     size_t y;        // f32  [P][H] then [T][H]   per-pair expert outputs
+    size_t split_cnt;   // int [kSplitTiles]      split-K arrival counters
+    size_t split_part;  // f32 [kSplitTiles * kSplitSlicesMax][2 * kGemvTokens][64] partials
     size_t total;
     int max_tiles;
 };

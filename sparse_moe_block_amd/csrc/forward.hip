@@ -8,16 +8,20 @@ namespace {
 constexpr int kPrepThreads = 256;
 
 // Block 0 turns expert_offsets into the list of active experts
-// (expert, first row, rows) and the grouped-GEMM tile list, clamping anything
-// out of range (FW_STATUS_BAD_OFFSETS).  Blocks 1..T stage one token row each
+// (expert, first row, rows) and the row-tile list -- each active expert's rows
+// cut into tiles of at most tile_rows (the grouped GEMM's 128-row tiles, or the
+// GEMV's token chunks) -- clamping anything out of range
+// (FW_STATUS_BAD_OFFSETS).  Blocks 1..T stage one token row each
 // in fp16 (bf16 values are exact in fp16), in the pair order both kernel
 // families consume (see decode_pairs).
 __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(
     const int32_t *__restrict__ offsets, int E, int P, const void *__restrict__ x, int act_bf16,
-    int H, int T, int gemm, int max_tiles, int4 *__restrict__ active, int4 *__restrict__ tiles,
-    _Float16 *__restrict__ x16, WsHeader *__restrict__ hdr) {
+    int H, int T, int tile_rows, int max_tiles, int4 *__restrict__ active, int4 *__restrict__ tiles,
+    _Float16 *__restrict__ x16, int *__restrict__ split_cnt, WsHeader *__restrict__ hdr) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     if (blockIdx.x == 0) {
+        // the GEMV's split-K arrival counters start every call at zero
+        for (int i = tid; i < kSplitTiles; i += kPrepThreads) split_cnt[i] = 0;
         __shared__ int wsum_a[kPrepThreads / kWave], wsum_t[kPrepThreads / kWave];
         // each thread owns experts 2*tid and 2*tid+1
         int beg[2], cnt[2], na = 0, nt = 0;
@@ -35,7 +39,7 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(
                 beg[i] = b;
                 cnt[i] = n - b;
                 na += cnt[i] > 0;
-                nt += (cnt[i] + kGemmBM - 1) / kGemmBM;
+                nt += (cnt[i] + tile_rows - 1) / tile_rows;
             }
         }
         if (bad) atomicOr(&hdr->status, FW_STATUS_BAD_OFFSETS);
@@ -63,9 +67,9 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(
         for (int i = 0; i < 2; ++i) {
             if (cnt[i] > 0) {
                 active[pa++] = int4{2 * tid + i, beg[i], cnt[i], 0};
-                if (gemm)   // bounded: overlapping (invalid) offsets can claim more
-                    for (int m = 0; m < cnt[i] && pt < max_tiles; m += kGemmBM)
-                        tiles[pt++] = int4{2 * tid + i, beg[i] + m, min(kGemmBM, cnt[i] - m), 0};
+                // bounded: overlapping (invalid) offsets can claim more
+                for (int m = 0; m < cnt[i] && pt < max_tiles; m += tile_rows)
+                    tiles[pt++] = int4{2 * tid + i, beg[i] + m, min(tile_rows, cnt[i] - m), 0};
             }
         }
         if (tid == kPrepThreads - 1) {
@@ -153,11 +157,11 @@ __global__ __launch_bounds__(256) void combine_kernel(
 }  // namespace
 
 hipError_t launch_prepare(const FwdArgs &a, hipStream_t s) {
-    const bool gemm = a.path == FW_PATH_GEMM;
+    const int tile_rows = a.path == FW_PATH_GEMM ? kGemmBM : kGemvTokens;
     prepare_kernel<<<1 + a.T, kPrepThreads, 0, s>>>(
-        a.offsets, a.d.n_experts, a.P, a.x, a.d.act_dtype == FW_BF16, a.d.hidden, a.T, gemm,
+        a.offsets, a.d.n_experts, a.P, a.x, a.d.act_dtype == FW_BF16, a.d.hidden, a.T, tile_rows,
         a.L.max_tiles, (int4 *)(a.ws + a.L.active), (int4 *)(a.ws + a.L.tiles),
-        (_Float16 *)(a.ws + a.L.x16), (WsHeader *)a.ws);
+        (_Float16 *)(a.ws + a.L.x16), (int *)(a.ws + a.L.split_cnt), (WsHeader *)a.ws);
     return hipGetLastError();
 }
 

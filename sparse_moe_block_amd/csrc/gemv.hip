@@ -3,19 +3,27 @@
 // pages' runtime counts its cost in weight bytes moved per token -- Flyweight
 // 0.2.0 "Quantization"), so the kernels are built around HBM streaming:
 //
-//  - a wavefront owns 64 consecutive weight rows of one expert and every S-th
-//    256-element unit (8 GGUF blocks, 16-byte aligned) along the reduction
-//    dimension; the S wavefronts of a workgroup interleave their units;
+//  - work items are (row chunk, 64-row weight tile) pairs: a row chunk is up to
+//    four rows of one expert's segment of the sorted pair list (built on the
+//    device), a weight tile 64 consecutive rows of that expert's matrix; the
+//    grid is sized to the resident capacity and each workgroup walks the items
+//    g, g + grid, ... so no workgroup pays a cold start twice;
+//  - the S wavefronts of a workgroup split the reduction dimension: wavefront w
+//    takes every S-th 256-element unit (8 GGUF blocks, 16-byte aligned), so the
+//    wavefronts fetch adjacent units of the same rows together;
 //  - weights move HBM -> LDS with global_load_lds_dwordx4 (each instruction
 //    reads 1 KB of consecutive row bytes, so every cache line fetched is used
-//    whole) through one buffer per wavefront (one batch in flight while the
-//    previous one is consumed from registers); lane r reads row r's unit from
-//    LDS (row strides of 144 / 272 bytes are bank-conflict-free for 16 lanes);
-//  - codes become exact fp16 pairs in registers (decode_pairs) and meet the
-//    activation pairs in v_dot2c_f32_f16 with fp32 accumulation; the fp16
-//    block scale multiplies each block's partial sum once;
-//  - the activations of the group's tokens are the same for every lane: they
-//    are read with scalar loads and enter each dot as the scalar operand;
+//    whole) through D buffers per wavefront; the batch stream runs across item
+//    boundaries, so D batches stay in flight while one is consumed from
+//    registers.  The LDS read of a batch waits only for that batch (vmcnt
+//    counts the younger ones), written with the wait in the same asm block;
+//  - lane r reads row r's unit from LDS (row strides of 144 / 272 bytes are
+//    bank-conflict-free for 16 lanes); codes become exact fp16 pairs in
+//    registers (decode_pairs) and meet the activation pairs in
+//    v_dot2c_f32_f16 with fp32 accumulation; the fp16 block scale multiplies
+//    each block's partial sum once;
+//  - the activations of the chunk's rows are the same for every lane: they are
+//    read with scalar loads and enter each dot as the scalar operand;
 //  - partial sums of the S wavefronts meet in LDS and are added in wavefront
 //    order, so results are deterministic.
 // Gate and up rows of the same feature share a lane, so SiLU(g)*u is formed in
@@ -28,11 +36,11 @@
 namespace fw {
 namespace {
 
-constexpr int NT = kGemvTokens;
-constexpr int kMaxSplit = 4;
 
 typedef __attribute__((address_space(4))) const uint32_t cu32;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const uint4 *lds_cptr;
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 // Stage unit u of the 64 rows starting at `tile` (row stride `rowbytes`) into
 // buf[64 * X4] as [row][X4 x 16 bytes]: instruction i moves chunks
@@ -50,17 +58,73 @@ __device__ __forceinline__ void stage_unit(uint4 *buf, const uint8_t *tile, uint
     }
 }
 
-template <int Q>
-__device__ __forceinline__ void read_unit(const uint4 *buf, int lane, uint32_t *w) {
-    constexpr int X4 = QT<Q>::kUnitX4;
+// Row `lane`'s unit from a staged batch, once at most N vector loads of this
+// wavefront are still outstanding (the batches staged after it).  The LDS
+// reads and both waits sit in one asm block: the compiler cannot tell the LDS
+// writes of global_load_lds apart and would otherwise wait for every batch.
+// The block ends with lgkmcnt(0), so its outputs are complete when it ends and
+// the buffer may be refilled right after.
+template <int N>
+__device__ __forceinline__ void wait_read_unit9(const uint4 *row, uint32_t *w) {
+    const uint32_t a = (uint32_t)(uintptr_t)(lds_cptr)row;
+    v4u r0, r1, r2, r3, r4, r5, r6, r7, r8;
+    asm volatile(
+        "s_waitcnt vmcnt(%9)\n\t"
+        "ds_read_b128 %0, %10\n\t"
+        "ds_read_b128 %1, %10 offset:16\n\t"
+        "ds_read_b128 %2, %10 offset:32\n\t"
+        "ds_read_b128 %3, %10 offset:48\n\t"
+        "ds_read_b128 %4, %10 offset:64\n\t"
+        "ds_read_b128 %5, %10 offset:80\n\t"
+        "ds_read_b128 %6, %10 offset:96\n\t"
+        "ds_read_b128 %7, %10 offset:112\n\t"
+        "ds_read_b128 %8, %10 offset:128\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6),
+          "=&v"(r7), "=&v"(r8)
+        : "n"(N), "v"(a)
+        : "memory");
+    const v4u r[9] = {r0, r1, r2, r3, r4, r5, r6, r7, r8};
 #pragma unroll
-    for (int i = 0; i < X4; ++i) {
-        const uint4 v = buf[lane * X4 + i];
-        w[4 * i] = v.x;
-        w[4 * i + 1] = v.y;
-        w[4 * i + 2] = v.z;
-        w[4 * i + 3] = v.w;
-    }
+    for (int i = 0; i < 9; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[4 * i + j] = r[i][j];
+}
+
+template <int N>
+__device__ __forceinline__ void wait_read_unit17(const uint4 *row, uint32_t *w) {
+    const uint32_t a = (uint32_t)(uintptr_t)(lds_cptr)row;
+    v4u r0, r1, r2, r3, r4, r5, r6, r7, r8, r9, r10, r11, r12, r13, r14, r15, r16;
+    asm volatile(
+        "s_waitcnt vmcnt(%17)\n\t"
+        "ds_read_b128 %0, %18\n\t"
+        "ds_read_b128 %1, %18 offset:16\n\t"
+        "ds_read_b128 %2, %18 offset:32\n\t"
+        "ds_read_b128 %3, %18 offset:48\n\t"
+        "ds_read_b128 %4, %18 offset:64\n\t"
+        "ds_read_b128 %5, %18 offset:80\n\t"
+        "ds_read_b128 %6, %18 offset:96\n\t"
+        "ds_read_b128 %7, %18 offset:112\n\t"
+        "ds_read_b128 %8, %18 offset:128\n\t"
+        "ds_read_b128 %9, %18 offset:144\n\t"
+        "ds_read_b128 %10, %18 offset:160\n\t"
+        "ds_read_b128 %11, %18 offset:176\n\t"
+        "ds_read_b128 %12, %18 offset:192\n\t"
+        "ds_read_b128 %13, %18 offset:208\n\t"
+        "ds_read_b128 %14, %18 offset:224\n\t"
+        "ds_read_b128 %15, %18 offset:240\n\t"
+        "ds_read_b128 %16, %18 offset:256\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6),
+          "=&v"(r7), "=&v"(r8), "=&v"(r9), "=&v"(r10), "=&v"(r11), "=&v"(r12), "=&v"(r13),
+          "=&v"(r14), "=&v"(r15), "=&v"(r16)
+        : "n"(N), "v"(a)
+        : "memory");
+    const v4u r[17] = {r0, r1, r2, r3, r4, r5, r6, r7, r8, r9, r10, r11, r12, r13, r14, r15, r16};
+#pragma unroll
+    for (int i = 0; i < 17; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[4 * i + j] = r[i][j];
 }
 
 // Activation pairs of block B of unit u for NTK token rows: one scalar load
@@ -89,168 +153,234 @@ __device__ __forceinline__ void dot_block(const uint32_t *w, const uint32_t (*x)
     }
 }
 
-// acc[n] += (row's unit u) . (activation row n's unit u), n < NTK.  For up to
-// two rows the next block's activations are loaded while the current block
-// is consumed (two sets of 16 SGPRs per row); scheduling barriers keep one
-// block's pairs live at a time.
+// acc[n] += (row's unit u) . (activation row n's unit u), n < NTK.  The next
+// block's activations are loaded while the current block is consumed (two
+// sets of 16 SGPRs per row); scheduling barriers keep one block's pairs live
+// at a time.
 template <int Q, int NTK>
 __device__ __forceinline__ void dot_unit(const uint32_t *w, int u, cu32 *const *in,
                                          float *acc) {
     const uint32_t magic = pair_magic<Q>();
     uint32_t xa[NTK][16], xb[NTK][16];
-    constexpr bool pre = NTK == 1;
     load_x<NTK>(xa, in, u, 0);
-#define FW_BLOCK(B, CUR, NXT)                                       \
-    if (pre && B < 7) load_x<NTK>(NXT, in, u, B + 1);              \
-    else if (!pre && B > 0) load_x<NTK>(CUR, in, u, B);            \
-    dot_block<Q, NTK, B>(w, CUR, magic, acc);                       \
+#define FW_BLOCK(B, CUR, NXT)                             \
+    if (B < 7) load_x<NTK>(NXT, in, u, B + 1);           \
+    dot_block<Q, NTK, B>(w, CUR, magic, acc);             \
     __builtin_amdgcn_sched_barrier(0);
     FW_BLOCK(0, xa, xb)
-    FW_BLOCK(1, (pre ? xb : xa), xa)
+    FW_BLOCK(1, xb, xa)
     FW_BLOCK(2, xa, xb)
-    FW_BLOCK(3, (pre ? xb : xa), xa)
+    FW_BLOCK(3, xb, xa)
     FW_BLOCK(4, xa, xb)
-    FW_BLOCK(5, (pre ? xb : xa), xa)
+    FW_BLOCK(5, xb, xa)
     FW_BLOCK(6, xa, xb)
-    FW_BLOCK(7, (pre ? xb : xa), xa)
+    FW_BLOCK(7, xb, xa)
 #undef FW_BLOCK
 }
 
-// The units of one wave (u = wave, wave + S, ...), staged one batch at a time
-// through `buf`.  A batch is read into registers, the next batch is issued
-// into the same buffer, and the registers are consumed while that batch is in
-// flight, so at every LDS read exactly one batch is outstanding.  With two
-// matrices (gate/up) the batches alternate between them for the same unit.
-// Interleaving units across the wavefronts of the workgroup makes the waves
-// fetch adjacent units of the same rows together, so the cache lines two
-// units share are fetched once.
-template <int Q, int NV, int NTK>
-__device__ __forceinline__ void stream_units(uint4 *buf, const uint8_t *ta, const uint8_t *tb,
-                                             uint32_t rowbytes, int wave, int S, int U, int lane,
-                                             cu32 *const *in, float (*acc)[NT]) {
-    constexpr int X4 = QT<Q>::kUnitX4;
-    uint32_t w[4 * X4];
-    // cur accumulates the batch being consumed; with two matrices the two
-    // accumulator sets swap after every batch (gate, up, gate, ...), which keeps
-    // a single dot_unit in the loop body
-    float cur[NTK], oth[NTK];
-#pragma unroll
-    for (int n = 0; n < NTK; ++n) cur[n] = oth[n] = 0.f;
-    const int nb = NV * (U / S);
-    stage_unit<Q>(buf, ta, rowbytes, wave, lane);
-    for (int i = 0; i < nb; ++i) {
-        const int u = wave + (i / NV) * S;
-        read_unit<Q>(buf, lane, w);
-        if (i + 1 < nb) {
-            const int un = wave + ((i + 1) / NV) * S;
-            stage_unit<Q>(buf, (NV == 2 && ((i + 1) & 1)) ? tb : ta, rowbytes, un, lane);
-        }
-        dot_unit<Q, NTK>(w, u, in, cur);
-        if (NV == 2) {
-#pragma unroll
-            for (int n = 0; n < NTK; ++n) {
-                const float t = cur[n];
-                cur[n] = oth[n];
-                oth[n] = t;
-            }
-        }
-    }
-    // nb is even for two matrices: cur holds gate, oth holds up
-#pragma unroll
-    for (int n = 0; n < NTK; ++n) {
-        acc[0][n] = cur[n];
-        if (NV == 2) acc[NV - 1][n] = oth[n];
-    }
+// What a wavefront needs of one work item: the 64-row weight tile of each
+// matrix, the activation rows of the item's chunk, and where outputs go.
+struct Item {
+    const uint8_t *ta, *tb;
+    cu32 *in[kGemvTokens];
+    int rb, nt, tile;
+    bool bad;
+};
+
+// The weight tiles (one per matrix) of work item `item`.
+__device__ __forceinline__ void tile_bases(int item, const uint8_t *wa, const uint8_t *wb,
+                                           const int4 *tiles, size_t rowbytes, size_t esz,
+                                           int tpg, int shared, const uint8_t *&ta,
+                                           const uint8_t *&tb) {
+    const int chunk = item / tpg;
+    size_t off = (size_t)(item % tpg) * kWave * rowbytes;
+    if (!shared) off += (size_t)ld_const(&tiles[chunk].x) * esz;
+    ta = wa + off;
+    tb = wb + off;
 }
 
-// One 64-row tile of one expert (or of the shared expert), for the expert's
-// rows [rb, rb + rc) of the sorted pair list.
-//  GU:  rows are gate/up features f; writes a = SiLU(W_g x) * (W_u x) as fp16
-//       in pair order (the down projection's activation layout);
-//  !GU: rows are outputs o; writes y = W_d a in fp32.
-template <int Q, bool GU>
-__global__ __launch_bounds__(kWave *kMaxSplit) void gemv_kernel(
+template <bool GU>
+__device__ __forceinline__ Item get_item(int item, const uint8_t *wa, const uint8_t *wb,
+                                         const int4 *tiles, const int32_t *sorted,
+                                         const _Float16 *xin, size_t rowbytes, size_t esz,
+                                         int tpg, int K, int k, int P, int shared,
+                                         int shared_rows) {
+    Item it;
+    const int chunk = item / tpg;
+    it.tile = item % tpg;
+    size_t off = (size_t)it.tile * kWave * rowbytes;
+    if (shared) {
+        it.rb = chunk * kGemvTokens;
+        it.nt = min(kGemvTokens, shared_rows - it.rb);
+    } else {
+        const int4 c = ld_const(tiles + chunk);   // (expert, first row, rows)
+        off += (size_t)c.x * esz;
+        it.rb = c.y;
+        it.nt = c.z;
+    }
+    it.ta = wa + off;
+    it.tb = wb + off;
+    it.bad = false;
+#pragma unroll
+    for (int n = 0; n < kGemvTokens; ++n) {
+        const int r = it.rb + min(n, it.nt - 1);
+        int t = r;   // the down projection reads row r of its input
+        if (GU && !shared) {
+            const int q = ld_const(sorted + r);
+            it.bad |= (unsigned)q >= (unsigned)P;
+            t = (unsigned)q < (unsigned)P ? q / k : 0;
+        }
+        it.in[n] = (cu32 *)(xin + (size_t)t * K);
+    }
+    return it;
+}
+
+// LDS read of a staged batch with at most `ahead` younger batches (LOADS
+// vector loads each) still in flight; D - 1 >= ahead.
+template <int Q, int D>
+__device__ __forceinline__ void wait_read(const uint4 *row, int ahead, uint32_t *w) {
+    constexpr int X4 = QT<Q>::kUnitX4;
+    static_assert(X4 * (D - 1) <= 63, "vmcnt holds at most 63");
+#define FW_WAIT(A)                                                                 \
+    if (D > A && ahead >= A) {                                                    \
+        if constexpr (X4 == 9) wait_read_unit9<(D > A ? A * X4 : 0)>(row, w);     \
+        else wait_read_unit17<(D > A ? A * X4 : 0)>(row, w);                      \
+        return;                                                                   \
+    }
+    FW_WAIT(3)
+    FW_WAIT(2)
+    FW_WAIT(1)
+#undef FW_WAIT
+    if constexpr (X4 == 9) wait_read_unit9<0>(row, w);
+    else wait_read_unit17<0>(row, w);
+}
+
+// Work items are (row chunk, 64-row weight tile) pairs, item = chunk * tpg +
+// tile; a chunk is up to kGemvTokens rows of one expert's segment of the
+// sorted pair list (routed) or of the token rows (shared expert).  Workgroup
+// g takes items g, g + grid, ...; its S wavefronts split each item's units,
+// and each streams its batches (NV matrices per unit) through D LDS buffers
+// with the stream running across item boundaries.
+template <int Q, bool GU, int S, int D>
+__global__ __launch_bounds__(kWave *S) void gemv_kernel(
     const uint8_t *__restrict__ wa, const uint8_t *__restrict__ wb,
-    const int4 *__restrict__ active, WsHeader *__restrict__ hdr,
+    const int4 *__restrict__ tiles, WsHeader *__restrict__ hdr,
     const int32_t *__restrict__ sorted, const _Float16 *__restrict__ xin,
     _Float16 *__restrict__ hout, float *__restrict__ yout, int K, int N, int k, int P,
-    int tiles_per_group, int shared, int shared_rows, int S) {
+    int tpg, int shared, int shared_rows, int ks, int *__restrict__ split_cnt,
+    float *__restrict__ split_part) {
     constexpr int X4 = QT<Q>::kUnitX4;
-    __shared__ uint4 stage[kMaxSplit][kWave * X4];
-    const int g = blockIdx.x / tiles_per_group, tile = blockIdx.x % tiles_per_group;
-    const size_t rowbytes = (size_t)(K / 32) * QT<Q>::kBlockBytes;
-    int rb = 0, rc = shared_rows;
-    const uint8_t *ta = wa, *tb = wb;
-    if (!shared) {
-        if (g >= ld_const(&hdr->n_active)) return;
-        const int4 ex = ld_const(active + g);   // (expert, first row, rows)
-        const size_t esz = (size_t)N * rowbytes;
-        ta += ex.x * esz;
-        if (GU) tb += ex.x * esz;
-        rb = ex.y;
-        rc = ex.z;
-    }
-    ta += (size_t)tile * kWave * rowbytes;
-    if (GU) tb += (size_t)tile * kWave * rowbytes;
-    const int wave = wave_id(), lane = threadIdx.x % kWave;
-    uint4 *buf = stage[wave];
-    const int U = K / kUnit;
     constexpr int NV = GU ? 2 : 1;
-    for (int c0 = 0; c0 < rc; c0 += NT) {
-        const int nt = min(NT, rc - c0);
-        cu32 *in[NT];
-        bool bad = false;
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            const int r = rb + c0 + min(n, nt - 1);
-            int t = r;   // the down projection reads row r of its input
-            if (GU && !shared) {
-                const int q = ld_const(sorted + r);
-                bad |= (unsigned)q >= (unsigned)P;
-                t = (unsigned)q < (unsigned)P ? q / k : 0;
-            }
-            in[n] = (cu32 *)(xin + (size_t)t * K);
-        }
-        if (bad && threadIdx.x == 0) atomicOr(&hdr->status, FW_STATUS_BAD_PAIR);
+    constexpr int NT = kGemvTokens;
+    __shared__ uint4 stage[S][D][kWave * X4];
+    __shared__ float red[S > 1 ? S - 1 : 1][NV * NT][kWave];
+    const int wave = wave_id(), lane = threadIdx.x % kWave;
+    const size_t rowbytes = (size_t)(K / 32) * QT<Q>::kBlockBytes;
+    const size_t esz = (size_t)N * rowbytes;
+    const uint8_t *wbb = GU ? wb : wa;
+    const int n_chunks = shared ? (shared_rows + NT - 1) / NT : ld_const(&hdr->n_tiles);
+    const int n_items = n_chunks * tpg * ks;
+    const int g0 = blockIdx.x, G = gridDim.x;
+    if (g0 >= n_items) return;
+    const int my_items = (n_items - g0 + G - 1) / G;
+    const int us = (K / kUnit) / ks;        // units per reduction slice
+    const int nb = NV * (us / S);           // batches per wavefront per item
+    const int total = my_items * nb;
+    const uint32_t rb32 = (uint32_t)rowbytes;
+    // staging cursor: batch js overall, bs within its item (D ahead of use);
+    // only the item's two weight tiles are needed to stage
+    int js = 0, is_ = 0, bs = 0;
+    const uint8_t *sa, *sb;
+    tile_bases(g0 / ks, wa, wbb, tiles, rowbytes, esz, tpg, shared, sa, sb);
+#define FW_STAGE_NEXT()                                                                     \
+    do {                                                                                    \
+        if (bs == nb) {                                                                     \
+            bs = 0;                                                                         \
+            ++is_;                                                                          \
+            tile_bases((g0 + is_ * G) / ks, wa, wbb, tiles, rowbytes, esz, tpg, shared, sa, sb); \
+        }                                                                                   \
+        stage_unit<Q>(stage[wave][js % D], (NV == 2 && (bs & 1)) ? sb : sa, rb32,           \
+                      ((g0 + is_ * G) % ks) * us + wave + (bs / NV) * S, lane);             \
+        ++bs;                                                                               \
+        ++js;                                                                               \
+    } while (0)
+    for (int j = 0; j < D && j < total; ++j) FW_STAGE_NEXT();
+
+    int j = 0;
+    for (int i = 0; i < my_items; ++i) {
+        const int item = g0 + i * G, ct = item / ks, slice = item % ks;
+        const Item it = get_item<GU>(ct, wa, wbb, tiles, sorted, xin, rowbytes, esz, tpg, K, k,
+                                     P, shared, shared_rows);
+        if (it.bad && threadIdx.x == 0) atomicOr(&hdr->status, FW_STATUS_BAD_PAIR);
         float acc[NV][NT];
 #pragma unroll
         for (int v = 0; v < NV; ++v)
 #pragma unroll
             for (int n = 0; n < NT; ++n) acc[v][n] = 0.f;
-        switch (nt) {
-            case 1: stream_units<Q, NV, 1>(buf, ta, tb, rowbytes, wave, S, U, lane, in, acc); break;
-            case 2: stream_units<Q, NV, 2>(buf, ta, tb, rowbytes, wave, S, U, lane, in, acc); break;
-            case 3: stream_units<Q, NV, 3>(buf, ta, tb, rowbytes, wave, S, U, lane, in, acc); break;
-            default: stream_units<Q, NV, 4>(buf, ta, tb, rowbytes, wave, S, U, lane, in, acc); break;
+        for (int b = 0; b < nb; ++b, ++j) {
+            uint32_t w[4 * X4];
+            wait_read<Q, D>(&stage[wave][j % D][lane * X4], min(D - 1, total - 1 - j), w);
+            if (js < total) FW_STAGE_NEXT();
+            const int u = slice * us + wave + (b / NV) * S;
+            float *a = acc[NV == 2 ? (b & 1) : 0];
+            if (it.nt == 1) dot_unit<Q, 1>(w, u, it.in, a);
+            else dot_unit<Q, 2>(w, u, it.in, a);
         }
-        // partial sums of waves 1..S-1 meet wave 0's in LDS (their idle stage
-        // buffers), added in wave order
+        // partial sums of waves 1..S-1 meet wave 0's in LDS, added in wave order
         if (S > 1) {
-            __syncthreads();
-            float *red = (float *)stage[wave];
             if (wave > 0) {
 #pragma unroll
                 for (int v = 0; v < NV; ++v)
 #pragma unroll
-                    for (int n = 0; n < NT; ++n) red[(v * NT + n) * kWave + lane] = acc[v][n];
+                    for (int n = 0; n < NT; ++n) red[wave - 1][v * NT + n][lane] = acc[v][n];
             }
             __syncthreads();
             if (wave == 0) {
-                for (int s = 1; s < S; ++s) {
-                    const float *o = (const float *)stage[s];
+#pragma unroll
+                for (int s = 0; s < S - 1; ++s)
 #pragma unroll
                     for (int v = 0; v < NV; ++v)
 #pragma unroll
-                        for (int n = 0; n < NT; ++n) acc[v][n] += o[(v * NT + n) * kWave + lane];
-                }
+                        for (int n = 0; n < NT; ++n) acc[v][n] += red[s][v * NT + n][lane];
             }
         }
-        if (wave == 0) {
-            const int row = tile * kWave + lane;
+        // split-K: every slice leaves its sums in split_part; the last slice
+        // of the tile to arrive (an integer counter) adds all slices in slice
+        // order and writes the outputs
+        bool out = wave == 0;
+        if (ks > 1 && wave == 0) {
+            float *part = split_part + (size_t)ct * ks * (NV * NT * kWave);
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int n = 0; n < NT; ++n)
+                    part[((size_t)slice * NV * NT + v * NT + n) * kWave + lane] = acc[v][n];
+            __threadfence();
+            int old = 0;
+            if (lane == 0) old = atomicAdd(&split_cnt[ct], 1);
+            old = __builtin_amdgcn_readfirstlane(old);
+            out = old == ks - 1;
+            if (out) {
+                __threadfence();
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) acc[v][n] = 0.f;
+                for (int sl = 0; sl < ks; ++sl)
+#pragma unroll
+                    for (int v = 0; v < NV; ++v)
+#pragma unroll
+                        for (int n = 0; n < NT; ++n)
+                            acc[v][n] += part[((size_t)sl * NV * NT + v * NT + n) * kWave + lane];
+                if (lane == 0) split_cnt[ct] = 0;   // ready for the next launch
+            }
+        }
+        if (out) {
+            const int row = it.tile * kWave + lane;
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
-                if (n < nt) {
-                    const size_t r = (size_t)(rb + c0 + n);
+                if (n < it.nt) {
+                    const size_t r = (size_t)(it.rb + n);
                     if constexpr (GU) {
                         const float gv = acc[0][n], up = acc[NV - 1][n];
                         float a = gv / (1.0f + __expf(-gv)) * up;
@@ -262,8 +392,9 @@ __global__ __launch_bounds__(kWave *kMaxSplit) void gemv_kernel(
                 }
             }
         }
-        if (S > 1) __syncthreads();   // stage[] is reused by the next chunk
+        if (S > 1) __syncthreads();   // red[] is reused by the next item
     }
+#undef FW_STAGE_NEXT
 }
 
 // Wavefronts per workgroup: the reduction dimension is split into S ranges of
@@ -274,13 +405,88 @@ int pick_split(int units) {
     return 1;
 }
 
+int g_cus = 0;
+
+int cu_count() {
+    if (!g_cus) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            n > 0)
+            g_cus = n;
+        else
+            g_cus = 256;
+    }
+    return g_cus;
+}
+
+template <int Q, bool GU, int S, int D>
+void launch_sd(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Float16 *xin,
+               _Float16 *hout, float *yout, int K, int N, long long items, int per_cu, int ks,
+               int shared, hipStream_t s) {
+    const int tpg = N / kWave;
+    const int grid = (int)std::max(1LL, std::min(items * ks, (long long)per_cu * cu_count()));
+    gemv_kernel<Q, GU, S, D><<<grid, kWave * S, 0, s>>>(
+        wa, wb, (const int4 *)(a.ws + a.L.tiles), (WsHeader *)a.ws, a.sorted, xin, hout, yout,
+        K, N, a.d.top_k, a.P, tpg, shared, shared ? a.T : 0, ks, (int *)(a.ws + a.L.split_cnt),
+        (float *)(a.ws + a.L.split_part));
+}
+
+// LDS is the in-flight buffer: about 144 KB of DMA batches per CU keeps HBM
+// busy.  Few items per CU (small batches, few active experts) get deep
+// per-wavefront pipelines; many items get more resident workgroups instead.
+template <int Q, bool GU, int S>
+void launch_s(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Float16 *xin,
+              _Float16 *hout, float *yout, int K, int N, int max_chunks, int shared,
+              hipStream_t s) {
+    constexpr int X4 = QT<Q>::kUnitX4;
+    const long long items = (long long)max_chunks * (N / kWave);
+    // far too few items to occupy the CUs (the shared expert of a one-token
+    // batch): split the reduction dimension into slices of whole units (each
+    // wavefront keeps at least one unit per slice).  The slices meet through
+    // memory with device-scope fences, which costs more than it gains once
+    // there are a few items per CU.
+    int ks = 1;
+    if (items <= kSplitTiles && items * 4 < cu_count()) {
+        const int per_wave = (K / kUnit) / S;
+        for (int c = kSplitSlicesMax; c > 1; --c)
+            if (per_wave % c == 0 && items * (c - 1) < 2LL * cu_count()) {
+                ks = c;
+                break;
+            }
+    }
+    const double per_cu = (double)items * ks / cu_count();
+    // workgroups per CU that the kernel's static LDS allows
+    const size_t batch = (size_t)S * kWave * X4 * 16;   // one batch of every wavefront
+    const size_t red = (size_t)std::max(S - 1, 1) * (GU ? 2 : 1) * kGemvTokens * kWave * 4;
+    auto fit = [&](int d) { return (int)std::max<size_t>(1, (160 * 1024) / (batch * d + red)); };
+    // Q4_0 batches are 9 KB per wavefront: depth 4, 2 or 1; Q8_0 batches are
+    // 17 KB: depth 2 or 1
+    constexpr int DMAX = Q == FW_Q4_0 ? 4 : 2;
+    if (per_cu < 1.5)
+        launch_sd<Q, GU, S, DMAX>(a, wa, wb, xin, hout, yout, K, N, items, fit(DMAX), ks, shared, s);
+    else if (Q == FW_Q4_0 && per_cu < 3.0)
+        launch_sd<Q, GU, S, 2>(a, wa, wb, xin, hout, yout, K, N, items, fit(2), ks, shared, s);
+    else
+        launch_sd<Q, GU, S, 1>(a, wa, wb, xin, hout, yout, K, N, items, fit(1), ks, shared, s);
+}
+
 template <int Q, bool GU>
 void launch(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Float16 *xin,
-            _Float16 *hout, float *yout, int K, int N, int groups, int shared, hipStream_t s) {
-    const int S = pick_split(K / kUnit), tpg = N / kWave;
-    gemv_kernel<Q, GU><<<groups * tpg, kWave * S, 0, s>>>(
-        wa, wb, (const int4 *)(a.ws + a.L.active), (WsHeader *)a.ws, a.sorted, xin, hout, yout,
-        K, N, a.d.top_k, a.P, tpg, shared, shared ? a.T : 0, S);
+            _Float16 *hout, float *yout, int K, int N, int max_chunks, int shared,
+            hipStream_t s) {
+    switch (pick_split(K / kUnit)) {
+        case 4: launch_s<Q, GU, 4>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, s); break;
+        case 3: launch_s<Q, GU, 3>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, s); break;
+        case 2: launch_s<Q, GU, 2>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, s); break;
+        default: launch_s<Q, GU, 1>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, s); break;
+    }
+}
+
+// Upper bound of the routed row chunks: every chunk holds at least one pair,
+// and at most one chunk per expert is partial.
+int max_routed_chunks(const FwdArgs &a) {
+    return std::min(a.P, a.P / kGemvTokens + std::min(a.d.n_experts, a.P));
 }
 
 }  // namespace
@@ -289,17 +495,18 @@ hipError_t launch_gemv_gate_up(const FwdArgs &a, hipStream_t s) {
     const fw_moe_desc &d = a.d;
     const _Float16 *x = (const _Float16 *)(a.ws + a.L.x16);
     _Float16 *h = (_Float16 *)(a.ws + a.L.h);
-    const int groups = std::min(d.n_experts, a.P);
+    const int mc = max_routed_chunks(a);
     if (d.expert_q == FW_Q4_0)
-        launch<FW_Q4_0, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, groups, 0, s);
+        launch<FW_Q4_0, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, mc, 0, s);
     else
-        launch<FW_Q8_0, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, groups, 0, s);
+        launch<FW_Q8_0, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, mc, 0, s);
     if (d.shared_ffn > 0) {
         _Float16 *hsh = h + (size_t)a.P * d.ffn;
+        const int sc = (a.T + kGemvTokens - 1) / kGemvTokens;
         if (d.shared_q == FW_Q4_0)
-            launch<FW_Q4_0, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, 1, 1, s);
+            launch<FW_Q4_0, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, sc, 1, s);
         else
-            launch<FW_Q8_0, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, 1, 1, s);
+            launch<FW_Q8_0, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, sc, 1, s);
     }
     return hipGetLastError();
 }
@@ -308,18 +515,19 @@ hipError_t launch_gemv_down(const FwdArgs &a, hipStream_t s) {
     const fw_moe_desc &d = a.d;
     const _Float16 *h = (const _Float16 *)(a.ws + a.L.h);
     float *y = (float *)(a.ws + a.L.y);
-    const int groups = std::min(d.n_experts, a.P);
+    const int mc = max_routed_chunks(a);
     if (d.expert_q == FW_Q4_0)
-        launch<FW_Q4_0, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, groups, 0, s);
+        launch<FW_Q4_0, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, mc, 0, s);
     else
-        launch<FW_Q8_0, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, groups, 0, s);
+        launch<FW_Q8_0, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, mc, 0, s);
     if (d.shared_ffn > 0) {
         const _Float16 *hsh = h + (size_t)a.P * d.ffn;
         float *ysh = y + (size_t)a.P * d.hidden;
+        const int sc = (a.T + kGemvTokens - 1) / kGemvTokens;
         if (d.shared_q == FW_Q4_0)
-            launch<FW_Q4_0, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, 1, 1, s);
+            launch<FW_Q4_0, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, sc, 1, s);
         else
-            launch<FW_Q8_0, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, 1, 1, s);
+            launch<FW_Q8_0, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, sc, 1, s);
     }
     return hipGetLastError();
 }
