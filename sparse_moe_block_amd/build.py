@@ -17,7 +17,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall",
          "-Wno-unused-result", "-I" + os.path.join(ROOT, "include"),
          # no packed fp32 arithmetic anywhere (v_pk_{add,mul,fma}_f32)
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA accumulators in ordinary VGPRs: the unified register file holds
+         # them, and the AGPR form made the allocator copy accumulators between
+         # register classes inside the K loops
+         "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src):

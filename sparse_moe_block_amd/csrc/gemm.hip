@@ -18,8 +18,11 @@
 //  - gate/up: the 128 weight rows are 64 gate rows and the same 64 up rows,
 //    arranged so a lane holds gate and up of the same (token, feature) and
 //    forms SiLU(g)*u in registers; outputs leave through LDS as whole rows;
-//  - consecutive workgroups of one XCD take the column tiles of one row tile,
-//    so its gathered activation rows stay in that XCD's L2.
+//  - the XCDs take the row tiles round-robin and consecutive workgroups of one
+//    XCD take the column tiles of one row tile, so its gathered activation rows
+//    stay in that XCD's L2;
+//  - a wavefront whose 64 tile rows hold fewer valid rows runs a specialisation
+//    with fewer MFMA row tiles (partial tiles of small experts cost less).
 //
 // fp16 rather than bf16 operands: bf16 (8-bit significand) roundings of the
 // dequantised weights cost ~3e-3 relative error on a layer output, above the
@@ -85,97 +88,51 @@ __device__ __forceinline__ void dequant_block(const Raw<Q> &r, int s, uint32_t *
     for (int i = 0; i < 16; ++i) dst[i] = __builtin_bit_cast(uint32_t, p[i] * d2);
 }
 
-// One (row tile, column tile) of one expert (or of the shared expert).
-//  GU:  A = x rows gathered through sorted_pairs (routed) or token rows
-//       (shared); weight rows = 64 gate + 64 up features; writes
-//       a = SiLU(g) * u (fp16, pair order) for 64 features;
-//  !GU: A = rows of a (fp16); weight rows = 128 outputs; writes y (fp32).
-template <int Q, bool GU>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(
-    const uint8_t *__restrict__ wa, const uint8_t *__restrict__ wb,
-    const int4 *__restrict__ tiles, WsHeader *__restrict__ hdr,
-    const int32_t *__restrict__ sorted, const _Float16 *__restrict__ ain,
-    _Float16 *__restrict__ hout, float *__restrict__ yout, int K, int N, int k, int P,
-    int col_tiles, int n_row_tiles_max, int shared, int shared_rows) {
-    __shared__ Smem sm;
-    // XCD-aware order: the workgroups one XCD runs (every 8th block) take a
-    // contiguous range of (row tile, column tile) pairs, column tiles fastest.
-    const int nblk = gridDim.x, per_xcd = nblk / 8;
-    const int lin = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    const int rt = lin / col_tiles, ct = lin % col_tiles;
-    if (rt >= n_row_tiles_max) return;
-    int expert = 0, rb = 0, rows = 0;
-    if (shared) {
-        rb = rt * BM;
-        rows = min(BM, shared_rows - rb);
-        if (rows <= 0) return;
-    } else {
-        if (rt >= ld_const(&hdr->n_tiles)) return;
-        const int4 tl = ld_const(tiles + rt);   // (expert, first row, rows)
-        expert = tl.x;
-        rb = tl.y;
-        rows = tl.z;
-    }
-    const size_t rowbytes = (size_t)(K / 32) * QT<Q>::kBlockBytes;
-    const size_t esz = (size_t)N * rowbytes;
-    const int tid = threadIdx.x, lane = tid % kWave, wave = wave_id();
-    const int wm = wave >> 1, wn = wave & 1;
+// What one thread of a tile needs through the K loop and the epilogue.
+struct TileCtx {
+    const _Float16 *asrc;   // this thread's activation row, at its half of a K step
+    const uint8_t *bsrc;    // this thread's weight row
+    _Float16 *hout;
+    float *yout;
+    int arow, ahalf, brow, bblk, wm, wn, lane, tid, steps, rows, rb, ct, N;
+};
 
-    // ---- per-thread load roles (fixed over the K loop) ----
-    // A: thread -> tile row tid/2, 32 of the 64 K-step halfs
-    const int arow = tid >> 1, ahalf = tid & 1;
-    int src_row;
-    {
-        const int r = rb + min(arow, rows - 1);
-        src_row = r;
-        if (GU && !shared) {
-            const int q = ld_const(sorted + r);
-            if ((unsigned)q >= (unsigned)P) {
-                if (arow < rows) atomicOr(&hdr->status, FW_STATUS_BAD_PAIR);
-                src_row = 0;
-            } else {
-                src_row = q / k;
-            }
-        }
-    }
-    const _Float16 *asrc = ain + (size_t)src_row * K + ahalf * 32;
-    // B: thread -> weight row tid/2 of the tile, block (tid&1) of the step
-    const int brow = tid >> 1, bblk = tid & 1;
-    const uint8_t *bsrc;
-    if (GU) {
-        // tile rows: wn*64 + [0,32) gate features, wn*64 + [32,64) up features,
-        // features ct*64 + wn*32 + [0,32)
-        const int grp = brow >> 6, within = brow & 63;
-        const int f = ct * 64 + grp * 32 + (within & 31);
-        const uint8_t *base = (within < 32) ? wa : wb;
-        bsrc = base + (size_t)expert * esz + (size_t)f * rowbytes;
-    } else {
-        bsrc = wa + (size_t)expert * esz + (size_t)(ct * BN + brow) * rowbytes;
-    }
+// The K loop and epilogue of one tile for a wavefront whose 64 tile rows hold
+// MI 16-row MFMA tiles of valid rows (rows past the expert's segment cost no
+// matrix work).  Every instantiation passes the same barriers in the same
+// order, so waves of one workgroup may run different MI.
+template <int Q, bool GU, int MI>
+__device__ __forceinline__ void tile_run(Smem &sm, const TileCtx &c) {
+    const _Float16 *const asrc = c.asrc;
+    const uint8_t *const bsrc = c.bsrc;
+    const int arow = c.arow, ahalf = c.ahalf, brow = c.brow, bblk = c.bblk;
+    const int wm = c.wm, wn = c.wn, lane = c.lane, tid = c.tid, steps = c.steps;
+    const int rows = c.rows, rb = c.rb, ct = c.ct, N = c.N;
 
-    // staging, two steps ahead: step s is fetched (global -> registers R[s&1])
-    // during the MFMAs of step s-2 and committed (dequantised, registers ->
-    // LDS) after the MFMAs of step s-1, so a load has two MFMA phases to land
+    // staging: the weight blocks of step s (from HBM) are fetched into
+    // registers B[s % 4] during the MFMAs of step s-3, the activation rows
+    // (mostly L2 hits) into A[s % 2] during step s-2; both are committed
+    // (dequantised, registers -> LDS) after the MFMAs of step s-1
     u4 ra0[4], ra1[4];
-    Raw<Q> rw0, rw1;
-#define FW_FETCH(step, R)                                                 \
+    Raw<Q> rw0, rw1, rw2, rw3;
+#define FW_FETCH_A(step, R)                                               \
     do {                                                                  \
         const u4 *ap = (const u4 *)(asrc + (step) * BK);                \
         ra##R[0] = ap[0];                                                 \
         ra##R[1] = ap[1];                                                 \
         ra##R[2] = ap[2];                                                 \
         ra##R[3] = ap[3];                                                 \
-        fetch_block<Q>(bsrc, 2 * (step) + bblk, rw##R);                   \
     } while (0)
-#define FW_COMMIT(buf, R)                                                                \
+#define FW_FETCH_B(step, R) fetch_block<Q>(bsrc, 2 * (step) + bblk, rw##R)
+#define FW_COMMIT(buf, RA, RB)                                                           \
     do {                                                                                 \
         u4 *ad = (u4 *)&sm.a[buf][arow * LDK + ahalf * 32];                              \
-        ad[0] = ra##R[0];                                                                \
-        ad[1] = ra##R[1];                                                                \
-        ad[2] = ra##R[2];                                                                \
-        ad[3] = ra##R[3];                                                                \
+        ad[0] = ra##RA[0];                                                               \
+        ad[1] = ra##RA[1];                                                               \
+        ad[2] = ra##RA[2];                                                               \
+        ad[3] = ra##RA[3];                                                               \
         uint32_t t[16];                                                                  \
-        dequant_block<Q>(rw##R, bblk, t);                                                \
+        dequant_block<Q>(rw##RB, bblk, t);                                               \
         uint4 *bd = (uint4 *)&sm.b[buf][brow * LDK + bblk * 32];                         \
         bd[0] = uint4{t[0], t[1], t[2], t[3]};                                           \
         bd[1] = uint4{t[4], t[5], t[6], t[7]};                                           \
@@ -183,52 +140,61 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
         bd[3] = uint4{t[12], t[13], t[14], t[15]};                                       \
     } while (0)
 
-    f4 acc[4][4];
+    f4 acc[MI > 0 ? MI : 1][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-    const int steps = K / BK;   // >= 4 (K >= 256)
-    FW_FETCH(0, 0);
-    FW_FETCH(1, 1);
-    FW_COMMIT(0, 0);
+    FW_FETCH_A(0, 0);
+    FW_FETCH_A(1, 1);
+    FW_FETCH_B(0, 0);
+    FW_FETCH_B(1, 1);
+    FW_FETCH_B(2, 2);
+    FW_COMMIT(0, 0, 0);
     __syncthreads();
     const int fr = lane & 15, fk = (lane >> 4) * 8;   // fragment row / k offset
-    for (int st = 0; st < steps; st += 2) {
-        // even step st: LDS buf 0 holds st, registers R1 hold st+1
-#define FW_STEP(S, BUF, RNEXT, RFETCH)                                                          \
+    for (int st = 0; st < steps; st += 4) {
+        // step S: LDS buffer S % 2 holds S; fetch A(S+2) into A[S % 2] and
+        // B(S+3) into B[(S+3) % 4] (clamped: no conditional writes); commit S+1
+#define FW_STEP(S, BUF, RA_F, RB_F, RA_N, RB_N)                                                 \
         {                                                                                       \
-            FW_FETCH(min((S) + 2, steps - 1), RFETCH);   /* clamped: no conditional writes */ \
-            _Pragma("unroll") for (int kk = 0; kk < BK; kk += 32) {                             \
-                h8 af[4], bf[4];                                                                \
-                _Pragma("unroll") for (int i = 0; i < 4; ++i)                                   \
-                    af[i] = *(const h8 *)&sm.a[BUF][(wm * 64 + i * 16 + fr) * LDK + kk + fk];   \
-                _Pragma("unroll") for (int j = 0; j < 4; ++j)                                   \
-                    bf[j] = *(const h8 *)&sm.b[BUF][(wn * 64 + j * 16 + fr) * LDK + kk + fk];   \
-                _Pragma("unroll") for (int i = 0; i < 4; ++i)                                   \
+            FW_FETCH_A(min((S) + 2, steps - 1), RA_F);                                          \
+            FW_FETCH_B(min((S) + 3, steps - 1), RB_F);                                          \
+            if constexpr (MI > 0) {                                                             \
+                _Pragma("unroll") for (int kk = 0; kk < BK; kk += 32) {                         \
+                    h8 af[MI > 0 ? MI : 1], bf[4];                                              \
                     _Pragma("unroll") for (int j = 0; j < 4; ++j)                               \
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j],        \
-                                                                           acc[i][j], 0, 0, 0); \
+                        bf[j] = *(const h8 *)&sm.b[BUF][(wn * 64 + j * 16 + fr) * LDK + kk + fk]; \
+                    _Pragma("unroll") for (int i = 0; i < MI; ++i)                              \
+                        af[i] = *(const h8 *)&sm.a[BUF][(wm * 64 + i * 16 + fr) * LDK + kk + fk]; \
+                    _Pragma("unroll") for (int i = 0; i < MI; ++i)                              \
+                        _Pragma("unroll") for (int j = 0; j < 4; ++j)                           \
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j],    \
+                                                                               acc[i][j], 0, 0, 0); \
+                }                                                                               \
             }                                                                                   \
-            if ((S) + 1 < steps) FW_COMMIT((BUF) ^ 1, RNEXT);                                   \
+            if ((S) + 1 < steps) FW_COMMIT((BUF) ^ 1, RA_N, RB_N);                              \
             __syncthreads();                                                                    \
         }
-        FW_STEP(st, 0, 1, 0)
-        FW_STEP(st + 1, 1, 0, 1)
+        FW_STEP(st, 0, 0, 3, 1, 1)
+        FW_STEP(st + 1, 1, 1, 0, 0, 2)
+        FW_STEP(st + 2, 0, 0, 1, 1, 3)
+        FW_STEP(st + 3, 1, 1, 2, 0, 0)
 #undef FW_STEP
     }
 
-#undef FW_FETCH
+#undef FW_FETCH_A
+#undef FW_FETCH_B
 #undef FW_COMMIT
 
     // ---- epilogue through LDS (the staging buffers are free now) ----
     // acc[i][j][r]: tile row wm*64 + i*16 + 4*(lane/16) + r, column wn*64 + j*16 + lane%16
-    if (GU) {
+    if constexpr (GU) {
         // a(row, feature) with feature index wn*32 + j*16 + lane%16, j = 0,1
         _Float16 *o = (_Float16 *)&sm;   // [BM][64] fp16
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -245,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
         const int row = tid >> 1, part = tid & 1;
         if (row < rows) {
             const uint4 *s = (const uint4 *)&o[row * 64 + part * 32];
-            uint4 *d = (uint4 *)(hout + (size_t)(rb + row) * N + ct * 64 + part * 32);
+            uint4 *d = (uint4 *)(c.hout + (size_t)(rb + row) * N + ct * 64 + part * 32);
 #pragma unroll
             for (int i = 0; i < 4; ++i) d[i] = s[i];
         }
@@ -256,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
         for (int half = 0; half < 2; ++half) {
             if (wm == half) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < MI; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -272,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
             const int grow = half * 64 + row;
             if (grow < rows) {
                 const uint4 *s = (const uint4 *)&o[row * BN + part * 32];
-                uint4 *d = (uint4 *)(yout + (size_t)(rb + grow) * N + ct * BN + part * 32);
+                uint4 *d = (uint4 *)(c.yout + (size_t)(rb + grow) * N + ct * BN + part * 32);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) d[i] = s[i];
             }
@@ -281,13 +247,107 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     }
 }
 
+// One (row tile, column tile) of one expert (or of the shared expert).
+//  GU:  A = x rows gathered through sorted_pairs (routed) or token rows
+//       (shared); weight rows = 64 gate + 64 up features; writes
+//       a = SiLU(g) * u (fp16, pair order) for 64 features;
+//  !GU: A = rows of a (fp16); weight rows = 128 outputs; writes y (fp32).
+template <int Q, bool GU>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(
+    const uint8_t *__restrict__ wa, const uint8_t *__restrict__ wb,
+    const int4 *__restrict__ tiles, WsHeader *__restrict__ hdr,
+    const int32_t *__restrict__ sorted, const _Float16 *__restrict__ ain,
+    _Float16 *__restrict__ hout, float *__restrict__ yout, int K, int N, int k, int P,
+    int col_tiles, int n_row_tiles_max, int shared, int shared_rows) {
+    __shared__ Smem sm;
+    // XCD-aware order: workgroup b runs on XCD b % 8; the XCDs take the row
+    // tiles round-robin (so the device-built list, a prefix of the row tiles,
+    // spreads over all eight), and consecutive workgroups of one XCD take the
+    // column tiles of one row tile (its gathered activation rows stay in that
+    // XCD's L2).
+    const int xcd = blockIdx.x % 8, i = blockIdx.x / 8;
+    const int rt = (i / col_tiles) * 8 + xcd, ct = i % col_tiles;
+    if (rt >= n_row_tiles_max) return;
+    int expert = 0, rb = 0, rows = 0;
+    if (shared) {
+        rb = rt * BM;
+        rows = min(BM, shared_rows - rb);
+        if (rows <= 0) return;
+    } else {
+        if (rt >= ld_const(&hdr->n_tiles)) return;
+        const int4 tl = ld_const(tiles + rt);   // (expert, first row, rows)
+        expert = tl.x;
+        rb = tl.y;
+        rows = tl.z;
+    }
+    const size_t rowbytes = (size_t)(K / 32) * QT<Q>::kBlockBytes;
+    const size_t esz = (size_t)N * rowbytes;
+    TileCtx c;
+    c.tid = threadIdx.x;
+    c.lane = c.tid % kWave;
+    const int wave = wave_id();
+    c.wm = wave >> 1;
+    c.wn = wave & 1;
+
+    // ---- per-thread load roles (fixed over the K loop) ----
+    // A: thread -> tile row tid/2, 32 of the 64 K-step halfs
+    c.arow = c.tid >> 1;
+    c.ahalf = c.tid & 1;
+    int src_row;
+    {
+        const int r = rb + min(c.arow, rows - 1);
+        src_row = r;
+        if (GU && !shared) {
+            const int q = ld_const(sorted + r);
+            if ((unsigned)q >= (unsigned)P) {
+                if (c.arow < rows) atomicOr(&hdr->status, FW_STATUS_BAD_PAIR);
+                src_row = 0;
+            } else {
+                src_row = q / k;
+            }
+        }
+    }
+    c.asrc = ain + (size_t)src_row * K + c.ahalf * 32;
+    // B: thread -> weight row tid/2 of the tile, block (tid&1) of the step
+    c.brow = c.tid >> 1;
+    c.bblk = c.tid & 1;
+    if (GU) {
+        // tile rows: wn*64 + [0,32) gate features, wn*64 + [32,64) up features,
+        // features ct*64 + wn*32 + [0,32)
+        const int grp = c.brow >> 6, within = c.brow & 63;
+        const int f = ct * 64 + grp * 32 + (within & 31);
+        const uint8_t *base = (within < 32) ? wa : wb;
+        c.bsrc = base + (size_t)expert * esz + (size_t)f * rowbytes;
+    } else {
+        c.bsrc = wa + (size_t)expert * esz + (size_t)(ct * BN + c.brow) * rowbytes;
+    }
+    c.hout = hout;
+    c.yout = yout;
+    c.steps = K / BK;   // a multiple of 4 (K is a multiple of 256)
+    c.rows = rows;
+    c.rb = rb;
+    c.ct = ct;
+    c.N = N;
+    // 16-row MFMA tiles of this wave that hold valid rows
+    const int mi = (min(max(rows - c.wm * 64, 0), 64) + 15) / 16;
+    switch (mi) {
+        case 4: tile_run<Q, GU, 4>(sm, c); break;
+        case 3: tile_run<Q, GU, 3>(sm, c); break;
+        case 2: tile_run<Q, GU, 2>(sm, c); break;
+        case 1: tile_run<Q, GU, 1>(sm, c); break;
+        default: tile_run<Q, GU, 0>(sm, c); break;
+    }
+}
+
 template <int Q, bool GU>
 void launch(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Float16 *ain,
             _Float16 *hout, float *yout, int K, int N, int shared, hipStream_t s) {
     const int col_tiles = GU ? N / 64 : N / BN;
-    const int row_tiles = shared ? (a.T + BM - 1) / BM : a.L.max_tiles;
-    int nblk = row_tiles * col_tiles;
-    nblk = (nblk + 7) / 8 * 8;   // the XCD mapping wants a multiple of 8
+    // routed: at most one partial tile per expert (the device list may hold
+    // fewer; the surplus workgroups return at once)
+    const int row_tiles = shared ? (a.T + BM - 1) / BM
+                                 : std::min(a.L.max_tiles, (a.P + BM - 1) / BM + a.d.n_experts);
+    const int nblk = (row_tiles + 7) / 8 * 8 * col_tiles;   // eight XCDs x whole row tiles
     gemm_kernel<Q, GU><<<nblk, kThreads, 0, s>>>(
         wa, wb, (const int4 *)(a.ws + a.L.tiles), (WsHeader *)a.ws, a.sorted, ain, hout, yout,
         K, N, a.d.top_k, a.P, col_tiles, row_tiles, shared, shared ? a.T : 0);
