@@ -186,10 +186,12 @@ int fw_moe_forward(const fw_moe_desc *desc, int32_t T, const void *x, const void
     if ((rc = hip_status(launch_prepare(a, s))) != FW_OK) return rc;
     if (ev) (void)hipEventRecord(g_events[1], s);
     const bool gemm = a.path == FW_PATH_GEMM;
-    rc = hip_status(gemm ? launch_gemm_gate_up(a, s) : launch_gemv_gate_up(a, s));
+    rc = hip_status(gemm ? (kUseGemm2 ? launch_gemm2_gate_up(a, s) : launch_gemm_gate_up(a, s))
+                         : launch_gemv_gate_up(a, s));
     if (rc != FW_OK) return rc;
     if (ev) (void)hipEventRecord(g_events[2], s);
-    rc = hip_status(gemm ? launch_gemm_down(a, s) : launch_gemv_down(a, s));
+    rc = hip_status(gemm ? (kUseGemm2 ? launch_gemm2_down(a, s) : launch_gemm_down(a, s))
+                         : launch_gemv_down(a, s));
     if (rc != FW_OK) return rc;
     if (ev) (void)hipEventRecord(g_events[3], s);
     if ((rc = hip_status(launch_combine(a, s))) != FW_OK) return rc;

@@ -15,7 +15,9 @@ constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 16;
 constexpr int kUnit = 256;        // elements per 16-byte-aligned run of 8 blocks
 constexpr int kGemvTokens = 2;    // token rows a GEMV work item carries
-constexpr int kGemmBM = 128;      // token rows per grouped-GEMM tile
+constexpr int kGemmBM = 128;      // token rows per tile of the LDS-dequant grouped GEMM
+constexpr int kGemm2BM = 64;      // token rows per tile of the register-dequant grouped GEMM
+constexpr bool kUseGemm2 = true;  // which grouped GEMM serves the GEMM path
 constexpr int kGemvMaxT = 64;     // AUTO: GEMV family up to this many tokens
 // GEMV split-K: at most this many (row chunk, weight tile) pairs are split,
 // into at most kSplitSlicesMax reduction slices each
@@ -222,6 +224,8 @@ hipError_t launch_gemv_gate_up(const FwdArgs &a, hipStream_t s);
 hipError_t launch_gemv_down(const FwdArgs &a, hipStream_t s);
 hipError_t launch_gemm_gate_up(const FwdArgs &a, hipStream_t s);
 hipError_t launch_gemm_down(const FwdArgs &a, hipStream_t s);
+hipError_t launch_gemm2_gate_up(const FwdArgs &a, hipStream_t s);
+hipError_t launch_gemm2_down(const FwdArgs &a, hipStream_t s);
 hipError_t launch_combine(const FwdArgs &a, hipStream_t s);
 
 }  // namespace fw

@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
 }  // namespace
 
 hipError_t launch_prepare(const FwdArgs &a, hipStream_t s) {
-    const int tile_rows = a.path == FW_PATH_GEMM ? kGemmBM : kGemvTokens;
+    const int tile_rows = a.path == FW_PATH_GEMM ? (kUseGemm2 ? kGemm2BM : kGemmBM) : kGemvTokens;
     prepare_kernel<<<1 + a.T, kPrepThreads, 0, s>>>(
         a.offsets, a.d.n_experts, a.P, a.x, a.d.act_dtype == FW_BF16, a.d.hidden, a.T, tile_rows,
         a.L.max_tiles, (int4 *)(a.ws + a.L.active), (int4 *)(a.ws + a.L.tiles),

@@ -48,6 +48,8 @@ struct Smem {
     _Float16 a[2][BM * LDK];
     _Float16 b[2][BN * LDK];
 };
+// the epilogues reuse the staging buffers: [BM][72] fp16 or [64][BN + 4] fp32
+static_assert(sizeof(Smem) >= BM * 72 * 2 && sizeof(Smem) >= 64 * (BN + 4) * 4, "epilogue fits");
 
 // Raw bytes of block kb of a weight row: the block pair starting at block
 // 2*(kb/2) is 4-byte aligned; block kb occupies dwords [R*s, R*s + R) of the
@@ -90,11 +92,11 @@ __device__ __forceinline__ void dequant_block(const Raw<Q> &r, int s, uint32_t *
 
 // What one thread of a tile needs through the K loop and the epilogue.
 struct TileCtx {
-    const _Float16 *asrc;   // this thread's activation row, at its half of a K step
+    const _Float16 *asrc[4];   // this thread's four activation rows, at its 16-byte chunk
     const uint8_t *bsrc;    // this thread's weight row
     _Float16 *hout;
     float *yout;
-    int arow, ahalf, brow, bblk, wm, wn, lane, tid, steps, rows, rb, ct, N;
+    int achunk, brow, bblk, wm, wn, lane, tid, steps, rows, rb, ct, N;
 };
 
 // The K loop and epilogue of one tile for a wavefront whose 64 tile rows hold
@@ -103,9 +105,10 @@ struct TileCtx {
 // order, so waves of one workgroup may run different MI.
 template <int Q, bool GU, int MI>
 __device__ __forceinline__ void tile_run(Smem &sm, const TileCtx &c) {
-    const _Float16 *const asrc = c.asrc;
+    const _Float16 *const as0 = c.asrc[0], *const as1 = c.asrc[1], *const as2 = c.asrc[2],
+                          *const as3 = c.asrc[3];
     const uint8_t *const bsrc = c.bsrc;
-    const int arow = c.arow, ahalf = c.ahalf, brow = c.brow, bblk = c.bblk;
+    const int achunk = c.achunk, brow = c.brow, bblk = c.bblk;
     const int wm = c.wm, wn = c.wn, lane = c.lane, tid = c.tid, steps = c.steps;
     const int rows = c.rows, rb = c.rb, ct = c.ct, N = c.N;
 
@@ -117,20 +120,16 @@ __device__ __forceinline__ void tile_run(Smem &sm, const TileCtx &c) {
     Raw<Q> rw0, rw1, rw2, rw3;
 #define FW_FETCH_A(step, R)                                               \
     do {                                                                  \
-        const u4 *ap = (const u4 *)(asrc + (step) * BK);                \
-        ra##R[0] = ap[0];                                                 \
-        ra##R[1] = ap[1];                                                 \
-        ra##R[2] = ap[2];                                                 \
-        ra##R[3] = ap[3];                                                 \
+        ra##R[0] = *(const u4 *)(as0 + (step) * BK);                      \
+        ra##R[1] = *(const u4 *)(as1 + (step) * BK);                      \
+        ra##R[2] = *(const u4 *)(as2 + (step) * BK);                      \
+        ra##R[3] = *(const u4 *)(as3 + (step) * BK);                      \
     } while (0)
 #define FW_FETCH_B(step, R) fetch_block<Q>(bsrc, 2 * (step) + bblk, rw##R)
 #define FW_COMMIT(buf, RA, RB)                                                           \
     do {                                                                                 \
-        u4 *ad = (u4 *)&sm.a[buf][arow * LDK + ahalf * 32];                              \
-        ad[0] = ra##RA[0];                                                               \
-        ad[1] = ra##RA[1];                                                               \
-        ad[2] = ra##RA[2];                                                               \
-        ad[3] = ra##RA[3];                                                               \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                    \
+            *(u4 *)&sm.a[buf][(tid / 8 + 32 * i) * LDK + achunk * 8] = ra##RA[i];            \
         uint32_t t[16];                                                                  \
         dequant_block<Q>(rw##RB, bblk, t);                                               \
         uint4 *bd = (uint4 *)&sm.b[buf][brow * LDK + bblk * 32];                         \
@@ -192,7 +191,9 @@ __device__ __forceinline__ void tile_run(Smem &sm, const TileCtx &c) {
     // acc[i][j][r]: tile row wm*64 + i*16 + 4*(lane/16) + r, column wn*64 + j*16 + lane%16
     if constexpr (GU) {
         // a(row, feature) with feature index wn*32 + j*16 + lane%16, j = 0,1
-        _Float16 *o = (_Float16 *)&sm;   // [BM][64] fp16
+        // [BM][OH] fp16; the 8-half pad keeps rows 4 apart off the same banks
+        constexpr int OH = 72;
+        _Float16 *o = (_Float16 *)&sm;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -204,20 +205,22 @@ __device__ __forceinline__ void tile_run(Smem &sm, const TileCtx &c) {
                     const int col = wn * 32 + j * 16 + (lane & 15);
                     float a = g / (1.0f + __expf(-g)) * u;
                     if (col & 16) a *= 0.0625f;   // pair order: pairs j = 1, 3 hold value / 16
-                    o[row * 64 + (col & ~31) + pair_pos(col & 31)] = (_Float16)a;
+                    o[row * OH + (col & ~31) + pair_pos(col & 31)] = (_Float16)a;
                 }
         __syncthreads();
         // 128 rows x 128 bytes: thread -> (row tid/2, 64 bytes)
         const int row = tid >> 1, part = tid & 1;
         if (row < rows) {
-            const uint4 *s = (const uint4 *)&o[row * 64 + part * 32];
+            const uint4 *s = (const uint4 *)&o[row * OH + part * 32];
             uint4 *d = (uint4 *)(c.hout + (size_t)(rb + row) * N + ct * 64 + part * 32);
 #pragma unroll
             for (int i = 0; i < 4; ++i) d[i] = s[i];
         }
     } else {
-        // fp32 [BM][BN] = 64 KB: two passes of 64 rows
-        float *o = (float *)&sm;   // [64][BN]
+        // fp32 outputs in two passes of 64 rows
+        // [64][OF] fp32; the 4-float pad keeps rows 4 apart off the same banks
+        constexpr int OF = BN + 4;
+        float *o = (float *)&sm;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             if (wm == half) {
@@ -229,7 +232,7 @@ __device__ __forceinline__ void tile_run(Smem &sm, const TileCtx &c) {
                         for (int r = 0; r < 4; ++r) {
                             const int row = i * 16 + 4 * (lane >> 4) + r;
                             const int col = wn * 64 + j * 16 + (lane & 15);
-                            o[row * BN + col] = acc[i][j][r];
+                            o[row * OF + col] = acc[i][j][r];
                         }
             }
             __syncthreads();
@@ -237,7 +240,7 @@ __device__ __forceinline__ void tile_run(Smem &sm, const TileCtx &c) {
             const int row = tid >> 2, part = tid & 3;
             const int grow = half * 64 + row;
             if (grow < rows) {
-                const uint4 *s = (const uint4 *)&o[row * BN + part * 32];
+                const uint4 *s = (const uint4 *)&o[row * OF + part * 32];
                 uint4 *d = (uint4 *)(c.yout + (size_t)(rb + grow) * N + ct * BN + part * 32);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) d[i] = s[i];
@@ -290,24 +293,25 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     c.wn = wave & 1;
 
     // ---- per-thread load roles (fixed over the K loop) ----
-    // A: thread -> tile row tid/2, 32 of the 64 K-step halfs
-    c.arow = c.tid >> 1;
-    c.ahalf = c.tid & 1;
-    int src_row;
-    {
-        const int r = rb + min(c.arow, rows - 1);
-        src_row = r;
+    // A: thread -> 16-byte chunk tid % 8 of tile rows tid/8 + 32 i, i < 4 (eight
+    // lanes read a row's 128 bytes of a K step together)
+    c.achunk = c.tid & 7;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int arow = c.tid / 8 + 32 * i;
+        const int r = rb + min(arow, rows - 1);
+        int src_row = r;
         if (GU && !shared) {
             const int q = ld_const(sorted + r);
             if ((unsigned)q >= (unsigned)P) {
-                if (c.arow < rows) atomicOr(&hdr->status, FW_STATUS_BAD_PAIR);
+                if (arow < rows) atomicOr(&hdr->status, FW_STATUS_BAD_PAIR);
                 src_row = 0;
             } else {
                 src_row = q / k;
             }
         }
+        c.asrc[i] = ain + (size_t)src_row * K + c.achunk * 8;
     }
-    c.asrc = ain + (size_t)src_row * K + c.ahalf * 32;
     // B: thread -> weight row tid/2 of the tile, block (tid&1) of the step
     c.brow = c.tid >> 1;
     c.bblk = c.tid & 1;

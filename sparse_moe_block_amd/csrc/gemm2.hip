@@ -1,0 +1,395 @@
+// Forward, GEMM family (prefill-sized batches), register-dequant form: grouped
+// expert GEMMs on MFMA whose weights never pass through LDS.
+//
+//  - a workgroup tile is up to 64 rows of one expert's segment of the sorted
+//    pair list (tokens gathered through sorted_pairs) times 256 weight rows;
+//    each of the four wavefronts owns 64 weight rows (four 16-row MFMA column
+//    groups) and all 64 token rows (four 16-row MFMA row groups);
+//  - K advances one 256-element unit (8 GGUF blocks) per step.  In the MFMA's
+//    k order, lane group g = lane / 16 covers blocks 2g and 2g + 1 of the unit
+//    and slice i (0..7) of a step covers block 2g + i / 4, fp16 pairs
+//    4 (i % 4) .. 4 (i % 4) + 3 in the pair order of decode_pairs (the MFMA
+//    sums over k in any order, so the activations are laid out the same way);
+//  - weights: lane (n = lane % 16, g) loads the 36-byte (Q4_0) or 68-byte
+//    (Q8_0) window of blocks 2g, 2g + 1 of its weight row (dword aligned), one
+//    step ahead, and turns one code dword into the four fp16 pairs of a B
+//    fragment (exact code times the fp16 scale, one rounding) right before the
+//    MFMAs that use it; no LDS traffic, no bank conflicts;
+//  - activations: the 64 x 256 fp16 tile of a step is staged through
+//    double-buffered, padded LDS (32 lanes read one row's 512 bytes together),
+//    loaded one step ahead; A fragments are read per slice;
+//  - v_mfma_f32_16x16x32_f16 with fp32 accumulation; gate/up: a wavefront's 64
+//    weight rows are 32 gate and the same 32 up features, so a lane holds gate
+//    and up of the same (token, feature) and forms SiLU(g)*u in registers;
+//    outputs leave through LDS as whole rows;
+//  - the XCDs take the row tiles round-robin and consecutive workgroups of one
+//    XCD take the column tiles of one row tile, so its gathered activation rows
+//    stay in that XCD's L2.
+#include <math.h>
+
+#include "common.h"
+
+namespace fw {
+namespace {
+
+constexpr int BM = kGemm2BM;   // 64 token rows
+constexpr int BN = 256;        // weight rows per workgroup
+constexpr int BK = kUnit;      // 256 elements per step
+constexpr int LDA = BK + 8;    // padded LDS activation row (halfs): 528 bytes
+constexpr int kThreads = 256;
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+struct Smem2 {
+    _Float16 a[2][BM * LDA];
+};
+// epilogues reuse the activation buffers: [64][136] fp16 or [64][260] fp32
+static_assert(sizeof(Smem2) >= BM * 136 * 2 && sizeof(Smem2) >= BM * (BN + 4) * 4,
+              "epilogue fits");
+
+// Dwords of the window of blocks 2g, 2g + 1 of a unit, per weight row.
+template <int Q> constexpr int win_dwords() { return Q == FW_Q4_0 ? 9 : 17; }
+
+template <int Q>
+__device__ __forceinline__ void load_window(const uint8_t *p, uint32_t *w) {
+    const uint32_t *q = (const uint32_t *)p;
+#pragma unroll
+    for (int i = 0; i < win_dwords<Q>(); ++i) w[i] = q[i];
+}
+
+// B fragment of slice I from a window: block I / 4 of the pair (even: 2 bytes
+// into the window, odd: dword aligned), pairs 4 (I % 4) .. + 3, times the
+// block's fp16 scale.
+template <int Q, int I>
+__device__ __forceinline__ h8 frag_b(const uint32_t *w) {
+    constexpr int m = I % 4;
+    uint32_t dbits, c0, c1 = 0;
+    if constexpr (Q == FW_Q4_0) {
+        if constexpr (I < 4) {
+            dbits = w[0] & 0xFFFFu;
+            c0 = funnel16(w[m], w[m + 1]);
+        } else {
+            dbits = w[4] >> 16;
+            c0 = w[5 + m];
+        }
+    } else {
+        if constexpr (I < 4) {
+            dbits = w[0] & 0xFFFFu;
+            c0 = funnel16(w[m], w[m + 1]);
+            c1 = funnel16(w[4 + m], w[5 + m]);
+        } else {
+            dbits = w[8] >> 16;
+            c0 = w[9 + m];
+            c1 = w[13 + m];
+        }
+    }
+    const uint32_t magic = pair_magic<Q>();
+    h2 p[4];
+    if constexpr (Q == FW_Q4_0) {
+        const h2 k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+        const h2 k1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
+        const uint32_t c8 = c0 >> 8;
+        p[0] = as_h2(and_or(c0, 0x000F000Fu, magic)) - k1032;
+        p[1] = as_h2(and_or(c0, 0x00F000F0u, magic)) - k1152;
+        p[2] = as_h2(and_or(c8, 0x000F000Fu, magic)) - k1032;
+        p[3] = as_h2(and_or(c8, 0x00F000F0u, magic)) - k1152;
+    } else {
+        const h2 k1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
+        const h2 k16 = {(_Float16)16.0f, (_Float16)16.0f};
+        const h2 k18432 = {(_Float16)18432.0f, (_Float16)18432.0f};
+        const uint32_t lo = c0 ^ 0x80808080u, hi = c1 ^ 0x80808080u;
+        p[0] = as_h2(__builtin_amdgcn_perm(magic, lo, 0x04020400u)) - k1152;
+        p[1] = as_h2(__builtin_amdgcn_perm(magic, hi, 0x04020400u)) * k16 - k18432;
+        p[2] = as_h2(__builtin_amdgcn_perm(magic, lo, 0x04030401u)) - k1152;
+        p[3] = as_h2(__builtin_amdgcn_perm(magic, hi, 0x04030401u)) * k16 - k18432;
+    }
+    const h2 d2 = as_h2(dbits | (dbits << 16));
+    h8 f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const h2 v = p[j] * d2;
+        f[2 * j] = v[0];
+        f[2 * j + 1] = v[1];
+    }
+    return f;
+}
+
+struct Tile2 {
+    const _Float16 *abase;     // activation rows (uniform)
+    uint32_t aoff[8];          // this thread's rows, at its 16-byte chunk: element offsets
+    const uint8_t *bbase[2];   // the expert's weight matrices (uniform): gate/up or down
+    uint32_t boff[4];          // this lane's rows (col groups), at its block pair: byte offsets
+    _Float16 *hout;
+    float *yout;
+    int tid, lane, wave, steps, rows, rb, ct, N;
+};
+
+// The K loop and epilogue of one tile, MI 16-row groups of token rows (a
+// specialisation per valid-row count would skip the empty groups of a partial
+// tile, but two of them in one kernel exceed 256 VGPRs).
+template <int Q, bool GU, int MI>
+__device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
+    constexpr int WD = win_dwords<Q>();
+    constexpr int UB = QT<Q>::kUnitBytes;
+    const int lane = c.lane, tid = c.tid, steps = c.steps;
+    const int g = lane >> 4, fr = lane & 15;
+
+    f4 acc[MI > 0 ? MI : 1][4];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+    u4 ra[8];                  // activation chunks of the next step
+    uint32_t wb0[4][WD], wb1[4][WD];   // weight windows: this step / next step
+
+    auto load_a = [&](int st) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ra[j] = *(const u4 *)(c.abase + c.aoff[j] + st * BK);
+    };
+    auto commit_a = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            *(u4 *)&sm.a[buf][(tid / 32 + 8 * j) * LDA + (tid & 31) * 8] = ra[j];
+    };
+#define FW_LOAD_B(W, st)                                                   \
+    _Pragma("unroll") for (int cg = 0; cg < 4; ++cg)                       \
+        load_window<Q>(c.bbase[GU ? cg >> 1 : 0] + c.boff[cg] + (st) * UB, W[cg]);
+
+    // one step: 8 slices x 4 column groups x MI row groups of MFMAs
+#define FW_MMA(BUF, W)                                                                        \
+    if constexpr (MI > 0) {                                                                   \
+        const _Float16 *abase = &sm.a[BUF][fr * LDA + 64 * g];                                \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                       \
+            h8 af[MI > 0 ? MI : 1];                                                           \
+            _Pragma("unroll") for (int r = 0; r < MI; ++r)                                    \
+                af[r] = *(const h8 *)(abase + 16 * r * LDA + 8 * i);                          \
+            _Pragma("unroll") for (int cg = 0; cg < 4; ++cg) {                                \
+                h8 bf;                                                                        \
+                switch (i) {                                                                  \
+                    case 0: bf = frag_b<Q, 0>(W[cg]); break;                                  \
+                    case 1: bf = frag_b<Q, 1>(W[cg]); break;                                  \
+                    case 2: bf = frag_b<Q, 2>(W[cg]); break;                                  \
+                    case 3: bf = frag_b<Q, 3>(W[cg]); break;                                  \
+                    case 4: bf = frag_b<Q, 4>(W[cg]); break;                                  \
+                    case 5: bf = frag_b<Q, 5>(W[cg]); break;                                  \
+                    case 6: bf = frag_b<Q, 6>(W[cg]); break;                                  \
+                    default: bf = frag_b<Q, 7>(W[cg]); break;                                 \
+                }                                                                             \
+                _Pragma("unroll") for (int r = 0; r < MI; ++r)                                \
+                    acc[r][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[r], bf, acc[r][cg], \
+                                                                        0, 0, 0);             \
+            }                                                                                 \
+            /* one slice's fragments live at a time */                                       \
+            __builtin_amdgcn_sched_barrier(0);                                                \
+        }                                                                                     \
+    }
+
+    load_a(0);
+    FW_LOAD_B(wb0, 0);
+    commit_a(0);
+    load_a(min(1, steps - 1));
+    __syncthreads();
+    // step s: LDS buffer s % 2 holds the activations of s, wb[s % 2] its
+    // weights; the next step's weights are loaded first, the activations of
+    // s + 1 committed and those of s + 2 loaded after the MFMAs (clamped loads
+    // past the last step are redundant, never conditional)
+    int st = 0;
+    for (; st + 1 < steps; st += 2) {
+        FW_LOAD_B(wb1, st + 1);
+        FW_MMA(0, wb0)
+        commit_a(1);
+        load_a(min(st + 2, steps - 1));
+        __syncthreads();
+        FW_LOAD_B(wb0, min(st + 2, steps - 1));
+        FW_MMA(1, wb1)
+        commit_a(0);
+        load_a(min(st + 3, steps - 1));
+        __syncthreads();
+    }
+    if (st < steps) {   // odd step count: the last step sits in buffer 0 / wb0
+        FW_MMA(0, wb0)
+        __syncthreads();
+    }
+#undef FW_LOAD_B
+#undef FW_MMA
+
+    // ---- epilogue through LDS (the activation buffers are free now) ----
+    // acc[r][cg][j]: token row 16 r + 4 g + j, weight row 64 wave + 16 cg + fr
+    const int rows = c.rows, rb = c.rb, ct = c.ct, N = c.N, wave = c.wave;
+    if constexpr (GU) {
+        // a(token, feature) for the workgroup's 128 features: [64][OH] fp16
+        constexpr int OH = 136;
+        _Float16 *o = (_Float16 *)&sm;
+#pragma unroll
+        for (int r = 0; r < MI; ++r)
+#pragma unroll
+            for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float gv = acc[r][cg][j], up = acc[r][cg + 2][j];   // gate, up
+                    const int row = 16 * r + 4 * g + j;
+                    const int col = 32 * wave + 16 * cg + fr;   // feature within the tile
+                    float a = gv / (1.0f + __expf(-gv)) * up;
+                    if (col & 16) a *= 0.0625f;   // pair order: pairs j = 1, 3 hold value / 16
+                    o[row * OH + (col & ~31) + pair_pos(col & 31)] = (_Float16)a;
+                }
+        __syncthreads();
+        // 64 rows x 256 bytes: thread -> (row tid / 4, 64 bytes)
+        const int row = tid >> 2, part = tid & 3;
+        if (row < rows) {
+            const uint4 *s = (const uint4 *)&o[row * OH + part * 32];
+            uint4 *d = (uint4 *)(c.hout + (size_t)(rb + row) * N + ct * 128 + part * 32);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d[i] = s[i];
+        }
+    } else {
+        // y rows: [64][OF] fp32
+        constexpr int OF = BN + 4;
+        float *o = (float *)&sm;
+#pragma unroll
+        for (int r = 0; r < MI; ++r)
+#pragma unroll
+            for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o[(16 * r + 4 * g + j) * OF + 64 * wave + 16 * cg + fr] = acc[r][cg][j];
+        __syncthreads();
+        // 64 rows x 1 KB: four threads per row, 256 bytes each
+        const int row = tid >> 2, part = tid & 3;
+        if (row < rows) {
+            const uint4 *s = (const uint4 *)&o[row * OF + part * 64];
+            uint4 *d = (uint4 *)(c.yout + (size_t)(rb + row) * N + ct * BN + part * 64);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) d[i] = s[i];
+        }
+    }
+}
+
+// One (row tile, column tile) of one expert (or of the shared expert).
+//  GU:  A = x rows gathered through sorted_pairs (routed) or token rows
+//       (shared); weight rows = 128 gate + 128 up features; writes
+//       a = SiLU(g) * u (fp16, pair order) for 128 features;
+//  !GU: A = rows of a (fp16); weight rows = 256 outputs; writes y (fp32).
+template <int Q, bool GU>
+__global__ __launch_bounds__(kThreads) void gemm2_kernel(
+    const uint8_t *__restrict__ wa, const uint8_t *__restrict__ wb,
+    const int4 *__restrict__ tiles, WsHeader *__restrict__ hdr,
+    const int32_t *__restrict__ sorted, const _Float16 *__restrict__ ain,
+    _Float16 *__restrict__ hout, float *__restrict__ yout, int K, int N, int k, int P,
+    int col_tiles, int n_row_tiles_max, int shared, int shared_rows) {
+    __shared__ Smem2 sm;
+    const int xcd = blockIdx.x % 8, bi = blockIdx.x / 8;
+    const int rt = (bi / col_tiles) * 8 + xcd, ct = bi % col_tiles;
+    if (rt >= n_row_tiles_max) return;
+    int expert = 0, rb = 0, rows = 0;
+    if (shared) {
+        rb = rt * BM;
+        rows = min(BM, shared_rows - rb);
+        if (rows <= 0) return;
+    } else {
+        if (rt >= ld_const(&hdr->n_tiles)) return;
+        const int4 tl = ld_const(tiles + rt);   // (expert, first row, rows)
+        expert = tl.x;
+        rb = tl.y;
+        rows = tl.z;
+    }
+    const size_t rowbytes = (size_t)(K / 32) * QT<Q>::kBlockBytes;
+    const size_t esz = (size_t)N * rowbytes;
+    Tile2 c;
+    c.tid = threadIdx.x;
+    c.lane = c.tid % kWave;
+    c.wave = wave_id();
+    // activations: thread -> 16-byte chunk tid % 32 of tile rows tid / 32 + 8 j
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int arow = c.tid / 32 + 8 * j;
+        const int r = rb + min(arow, rows - 1);
+        int src_row = r;
+        if (GU && !shared) {
+            const int q = ld_const(sorted + r);
+            if ((unsigned)q >= (unsigned)P) {
+                if (arow < rows) atomicOr(&hdr->status, FW_STATUS_BAD_PAIR);
+                src_row = 0;
+            } else {
+                src_row = q / k;
+            }
+        }
+        c.aoff[j] = (uint32_t)src_row * K + (c.tid & 31) * 8;
+    }
+    // weights: lane -> row 16 cg + lane % 16 of the wave's 64, block pair lane / 16
+    const int n = c.lane & 15, g = c.lane >> 4;
+    c.abase = ain;
+    c.bbase[0] = wa + (size_t)expert * esz;
+    c.bbase[1] = GU ? wb + (size_t)expert * esz : c.bbase[0];
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+        const int row = GU ? ct * 128 + 32 * c.wave + 16 * (cg & 1) + n   // feature (gate cg < 2)
+                           : ct * BN + 64 * c.wave + 16 * cg + n;          // output row
+        c.boff[cg] = (uint32_t)(row * rowbytes) + g * (2 * QT<Q>::kBlockBytes);
+    }
+    c.hout = hout;
+    c.yout = yout;
+    c.steps = K / BK;
+    c.rows = rows;
+    c.rb = rb;
+    c.ct = ct;
+    c.N = N;
+    tile2_run<Q, GU, 4>(sm, c);
+}
+
+template <int Q, bool GU>
+void launch2(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Float16 *ain,
+             _Float16 *hout, float *yout, int K, int N, int shared, hipStream_t s) {
+    const int col_tiles = GU ? N / 128 : N / BN;
+    // routed: at most one partial tile per expert
+    const int row_tiles = shared ? (a.T + BM - 1) / BM
+                                 : std::min(a.L.max_tiles, (a.P + BM - 1) / BM + a.d.n_experts);
+    const int nblk = (row_tiles + 7) / 8 * 8 * col_tiles;   // eight XCDs x whole row tiles
+    gemm2_kernel<Q, GU><<<nblk, kThreads, 0, s>>>(
+        wa, wb, (const int4 *)(a.ws + a.L.tiles), (WsHeader *)a.ws, a.sorted, ain, hout, yout,
+        K, N, a.d.top_k, a.P, col_tiles, row_tiles, shared, shared ? a.T : 0);
+}
+
+}  // namespace
+
+hipError_t launch_gemm2_gate_up(const FwdArgs &a, hipStream_t s) {
+    const fw_moe_desc &d = a.d;
+    const _Float16 *x = (const _Float16 *)(a.ws + a.L.x16);
+    _Float16 *h = (_Float16 *)(a.ws + a.L.h);
+    if (d.expert_q == FW_Q4_0)
+        launch2<FW_Q4_0, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, 0, s);
+    else
+        launch2<FW_Q8_0, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, 0, s);
+    if (d.shared_ffn > 0) {
+        _Float16 *hsh = h + (size_t)a.P * d.ffn;
+        if (d.shared_q == FW_Q4_0)
+            launch2<FW_Q4_0, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, 1, s);
+        else
+            launch2<FW_Q8_0, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, 1, s);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm2_down(const FwdArgs &a, hipStream_t s) {
+    const fw_moe_desc &d = a.d;
+    const _Float16 *h = (const _Float16 *)(a.ws + a.L.h);
+    float *y = (float *)(a.ws + a.L.y);
+    if (d.expert_q == FW_Q4_0)
+        launch2<FW_Q4_0, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, 0, s);
+    else
+        launch2<FW_Q8_0, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, 0, s);
+    if (d.shared_ffn > 0) {
+        const _Float16 *hsh = h + (size_t)a.P * d.ffn;
+        float *ysh = y + (size_t)a.P * d.hidden;
+        if (d.shared_q == FW_Q4_0)
+            launch2<FW_Q4_0, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, 1, s);
+        else
+            launch2<FW_Q8_0, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, 1, s);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fw
