@@ -12,6 +12,7 @@ Prints one JSON line: tokens/s, ms per step, the dominant kernel's roofline
 launch stream) and the CPU oracle's throughput on a bounded sample."""
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +29,10 @@ from sparse_moe_block_amd import fwmoe as fw  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MFMA_FP16_PEAK_TFLOPS = 2500.0
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)"
+CSRC = os.path.join(ROOT, "sparse_moe_block_amd", "csrc")
+# sources whose kernels the traffic counters describe (a change voids them)
+TRAFFIC_SOURCES = ["common.h", "gemv.hip", "gemm2.hip", "forward.hip"]
 
 WORKLOADS = {
     # name: (config, T, weight copies)
@@ -50,14 +55,21 @@ def parse():
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--reduce-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="instead of benchmarking: turn two rocprofv3 --pmc output "
+                         "directories (FETCH_SIZE, WRITE_SIZE) of this workload run "
+                         "with --copy-mib into profiles/traffic_<kernel>_<workload>.json")
     ap.add_argument("--copy-mib", type=int, default=0,
-                    help="also run one plain device copy of this many MiB (the "
-                         "reference kernel that scales hardware byte counters)")
+                    help="also run one plain device copy of this many MiB (a negation "
+                         "kernel, the reference that scales hardware byte counters)")
     return ap.parse_args()
 
 
 def main():
     a = parse()
+    if a.reduce_counters:
+        reduce_counters(a)
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported "
               f"(the layer is measured on one MI355X)", file=sys.stderr)
@@ -97,10 +109,11 @@ def main():
                           Li.s_down, w, off, sp, inv, out, ws, stream=stream)
 
     if a.copy_mib:
-        src = torch.empty(a.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        # reads and writes exactly copy_mib MiB in one elementwise kernel
+        src = torch.ones((a.copy_mib << 20) // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
     for i in range(a.warmup):
@@ -147,7 +160,7 @@ def main():
         # flops: 2 projections x 2 flops x P x H x F (+ the shared expert on T rows)
         gu_alg = 4 * P * H * cfg.ffn + 4 * T * H * cfg.shared_ffn
         achieved = gu_alg / (gu_ms * 1e-3) / 1e12
-        roof = {"kernel": "gemm_kernel<gate/up>", "bound": "mfma", "achieved": achieved,
+        roof = {"kernel": "gemm2_kernel<gate/up>", "bound": "mfma", "achieved": achieved,
                 "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / MFMA_FP16_PEAK_TFLOPS, "traffic": None,
                 "algorithmic_flops": gu_alg}
@@ -155,9 +168,9 @@ def main():
                    cfg.act_bytes(T) + T * H * 4)
     layer_flops = 6 * P * H * cfg.ffn + 6 * T * H * cfg.shared_ffn + 2 * T * H * E
 
+    roof["traffic"] = traffic(a.workload, roof)
     line = {
-        "metric": "MoE-layer tokens/s (" + ("decode; HBM-bound" if path == fw.FW_PATH_GEMV
-                                             else "prefill; MFMA-bound") + ")",
+        "metric": METRIC,
         "value": T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -167,7 +180,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q4_0 weights, fp32 accumulate" if cfg.expert_q == "q4_0" else "q8_0 weights, fp32 accumulate",
+        "dtype": "f16",
         "data": "synthetic (seeded N(0,0.02) weights quantized to GGUF blocks, N(0,1) bf16 tokens)",
         "config": {"workload": f"{cfg.name}, T={T}", "hidden": H, "experts": E, "top_k": k,
                    "ffn": cfg.ffn, "expert_format": cfg.expert_q, "shared_ffn": cfg.shared_ffn,
@@ -182,6 +195,80 @@ def main():
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, L, x, T, a.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# dominant kernel: label in the JSON line, mangled-name fragment in counter files
+KERNELS = {"gemv_kernel<gate/up>": ("gemv_gate_up", "gemv_kernelILi"),
+           "gemm2_kernel<gate/up>": ("gemm2_gate_up", "gemm2_kernelILi")}
+
+
+def traffic_path(workload, kernel):
+    return os.path.join(ROOT, "profiles", f"traffic_{KERNELS[kernel][0]}_{workload}.json")
+
+
+def traffic(workload, roof):
+    """HBM bytes per launch of the dominant kernel, from the committed
+    FETCH_SIZE / WRITE_SIZE counter summary of this workload (scaled by the
+    counters' reading of a plain copy of known size), or None when there is
+    none or the kernel sources changed since it was taken."""
+    p = traffic_path(workload, roof["kernel"])
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        t = json.load(fh)
+    if t.get("source_sha") != source_hash():
+        return None
+    return t["bytes_per_launch"]
+
+
+def reduce_counters(a):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the dominant gate/up
+    kernel, averaged over its dispatches, each scaled by what the counter read
+    for the --copy-mib negation kernel (which reads and writes exactly that
+    many bytes)."""
+    import csv
+    import glob
+    cfg, T, _ = WORKLOADS[a.workload]
+    path_gemv = T <= 64 if a.path == "auto" else a.path == "gemv"
+    kernel = "gemv_kernel<gate/up>" if path_gemv else "gemm2_kernel<gate/up>"
+    frag = KERNELS[kernel][1] + "1ELb1E" if cfg.expert_q == "q4_0" else KERNELS[kernel][1] + "0ELb1E"
+
+    def per_dispatch(d, counter, sub):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r["Counter_Name"] == counter and sub in r["Kernel_Name"]:
+                        key = (f, r["Dispatch_Id"])
+                        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        return list(vals.values())
+
+    fd, wd = a.reduce_counters
+    kf, kw = per_dispatch(fd, "FETCH_SIZE", frag), per_dispatch(wd, "WRITE_SIZE", frag)
+    cf, cw = per_dispatch(fd, "FETCH_SIZE", "neg_kernel"), per_dispatch(wd, "WRITE_SIZE", "neg_kernel")
+    if not (kf and kw and cf and cw):
+        sys.exit("counter files lack the kernel or the calibration copy")
+    copy_bytes = a.copy_mib << 20
+    ff, wf = copy_bytes / (max(cf) * 1024), copy_bytes / (max(cw) * 1024)
+    fetch = sum(kf) / len(kf) * 1024 * ff
+    write = sum(kw) / len(kw) * 1024 * wf
+    res = {"workload": a.workload, "kernel": kernel, "source_sha": source_hash(),
+           "dispatches": [len(kf), len(kw)], "fetch_kib_per_dispatch": sum(kf) / len(kf),
+           "write_kib_per_dispatch": sum(kw) / len(kw), "copy_mib": a.copy_mib,
+           "copy_fetch_kib": max(cf), "copy_write_kib": max(cw), "fetch_factor": ff,
+           "write_factor": wf, "fetch_bytes_per_launch": fetch,
+           "write_bytes_per_launch": write, "bytes_per_launch": fetch + write}
+    with open(traffic_path(a.workload, kernel), "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res))
 
 
 def cpu_baseline(cfg, L, x, T, seconds):
