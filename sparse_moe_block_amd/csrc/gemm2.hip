@@ -22,9 +22,9 @@
 //    weight rows are 32 gate and the same 32 up features, so a lane holds gate
 //    and up of the same (token, feature) and forms SiLU(g)*u in registers;
 //    outputs leave through LDS as whole rows;
-//  - the XCDs take the row tiles round-robin and consecutive workgroups of one
-//    XCD take the column tiles of one row tile, so its gathered activation rows
-//    stay in that XCD's L2.
+//  - each XCD takes a contiguous eighth of the row-tile list, so the row tiles
+//    of one expert share an L2 and its weights are fetched about once;
+//    consecutive workgroups of one XCD take the column tiles of one row tile.
 #include <math.h>
 
 #include "common.h"
@@ -158,31 +158,30 @@ __device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
     _Pragma("unroll") for (int cg = 0; cg < 4; ++cg)                       \
         load_window<Q>(c.bbase[GU ? cg >> 1 : 0] + c.boff[cg] + (st) * UB, W[cg]);
 
-    // one step: 8 slices x 4 column groups x MI row groups of MFMAs
+    // one step: 8 slices x 4 column groups x MI row groups of MFMAs; the A
+    // fragments of slice i + 1 are read from LDS while slice i's MFMAs run
+#define FW_FRAG_B(I, CG, W)                                                                   \
+    (I == 0 ? frag_b<Q, 0>(W[CG]) : I == 1 ? frag_b<Q, 1>(W[CG]) : I == 2 ? frag_b<Q, 2>(W[CG]) \
+     : I == 3 ? frag_b<Q, 3>(W[CG]) : I == 4 ? frag_b<Q, 4>(W[CG]) : I == 5 ? frag_b<Q, 5>(W[CG]) \
+     : I == 6 ? frag_b<Q, 6>(W[CG]) : frag_b<Q, 7>(W[CG]))
 #define FW_MMA(BUF, W)                                                                        \
     if constexpr (MI > 0) {                                                                   \
         const _Float16 *abase = &sm.a[BUF][fr * LDA + 64 * g];                                \
+        h8 afc[MI > 0 ? MI : 1], afn[MI > 0 ? MI : 1];                                        \
+        _Pragma("unroll") for (int r = 0; r < MI; ++r)                                        \
+            afc[r] = *(const h8 *)(abase + 16 * r * LDA);                                     \
         _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                       \
-            h8 af[MI > 0 ? MI : 1];                                                           \
-            _Pragma("unroll") for (int r = 0; r < MI; ++r)                                    \
-                af[r] = *(const h8 *)(abase + 16 * r * LDA + 8 * i);                          \
-            _Pragma("unroll") for (int cg = 0; cg < 4; ++cg) {                                \
-                h8 bf;                                                                        \
-                switch (i) {                                                                  \
-                    case 0: bf = frag_b<Q, 0>(W[cg]); break;                                  \
-                    case 1: bf = frag_b<Q, 1>(W[cg]); break;                                  \
-                    case 2: bf = frag_b<Q, 2>(W[cg]); break;                                  \
-                    case 3: bf = frag_b<Q, 3>(W[cg]); break;                                  \
-                    case 4: bf = frag_b<Q, 4>(W[cg]); break;                                  \
-                    case 5: bf = frag_b<Q, 5>(W[cg]); break;                                  \
-                    case 6: bf = frag_b<Q, 6>(W[cg]); break;                                  \
-                    default: bf = frag_b<Q, 7>(W[cg]); break;                                 \
-                }                                                                             \
+            if (i < 7)                                                                        \
                 _Pragma("unroll") for (int r = 0; r < MI; ++r)                                \
-                    acc[r][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[r], bf, acc[r][cg], \
+                    afn[r] = *(const h8 *)(abase + 16 * r * LDA + 8 * (i + 1));               \
+            _Pragma("unroll") for (int cg = 0; cg < 4; ++cg) {                                \
+                const h8 bf = FW_FRAG_B(i, cg, W);                                            \
+                _Pragma("unroll") for (int r = 0; r < MI; ++r)                                \
+                    acc[r][cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afc[r], bf, acc[r][cg], \
                                                                         0, 0, 0);             \
             }                                                                                 \
-            /* one slice's fragments live at a time */                                       \
+            _Pragma("unroll") for (int r = 0; r < MI; ++r) afc[r] = afn[r];                   \
+            /* one slice's B fragments live at a time */                                     \
             __builtin_amdgcn_sched_barrier(0);                                                \
         }                                                                                     \
     }
@@ -215,6 +214,7 @@ __device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
     }
 #undef FW_LOAD_B
 #undef FW_MMA
+#undef FW_FRAG_B
 
     // ---- epilogue through LDS (the activation buffers are free now) ----
     // acc[r][cg][j]: token row 16 r + 4 g + j, weight row 64 wave + 16 cg + fr
@@ -281,16 +281,23 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(
     _Float16 *__restrict__ hout, float *__restrict__ yout, int K, int N, int k, int P,
     int col_tiles, int n_row_tiles_max, int shared, int shared_rows) {
     __shared__ Smem2 sm;
+    // XCD-aware order: workgroup b runs on XCD b % 8.  Each XCD takes a
+    // contiguous eighth of the row tiles (the tiles of one expert are
+    // consecutive, so they share that XCD's L2 and its weights are fetched
+    // about once), column tiles fastest.
     const int xcd = blockIdx.x % 8, bi = blockIdx.x / 8;
-    const int rt = (bi / col_tiles) * 8 + xcd, ct = bi % col_tiles;
-    if (rt >= n_row_tiles_max) return;
+    const int n_rt = shared ? (shared_rows + BM - 1) / BM
+                            : min(ld_const(&hdr->n_tiles), n_row_tiles_max);
+    const int per = (n_rt + 7) / 8;
+    const int rl = bi / col_tiles, ct = bi % col_tiles;
+    if (rl >= per) return;
+    const int rt = xcd * per + rl;
+    if (rt >= n_rt) return;
     int expert = 0, rb = 0, rows = 0;
     if (shared) {
         rb = rt * BM;
         rows = min(BM, shared_rows - rb);
-        if (rows <= 0) return;
     } else {
-        if (rt >= ld_const(&hdr->n_tiles)) return;
         const int4 tl = ld_const(tiles + rt);   // (expert, first row, rows)
         expert = tl.x;
         rb = tl.y;
