@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--workload", default="decode16", choices=sorted(WORKLOADS))
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time direct launches only (value from the direct loop)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--reduce-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="instead of benchmarking: turn two rocprofv3 --pmc output "
@@ -101,12 +103,12 @@ def main():
     fw.fw_moe_clear_status(ws)
     stream = torch.cuda.current_stream()
 
-    def step(i):
+    def step(i, s=stream):
         Li = layers[i % copies]
-        fw.fw_moe_route(desc, T, x, Li.router, Li.bias, None, logits, ids, w, stream)
-        fw.fw_moe_permute(desc, T, ids, off, sp, inv, ws, stream=stream)
+        fw.fw_moe_route(desc, T, x, Li.router, Li.bias, None, logits, ids, w, s)
+        fw.fw_moe_permute(desc, T, ids, off, sp, inv, ws, stream=s)
         fw.fw_moe_forward(desc, T, x, Li.w_gate, Li.w_up, Li.w_down, Li.s_gate, Li.s_up,
-                          Li.s_down, w, off, sp, inv, out, ws, stream=stream)
+                          Li.s_down, w, off, sp, inv, out, ws, stream=s)
 
     if a.copy_mib:
         # reads and writes exactly copy_mib MiB in one elementwise kernel
@@ -138,9 +140,41 @@ def main():
     t1.record(stream)
     torch.cuda.synchronize()
     fw.fw_moe_set_stage_events(None)
-    ms = t0.elapsed_time(t1) / a.steps
+    direct_ms = t0.elapsed_time(t1) / a.steps
     stage_ms = np.array([[e[s].elapsed_time(e[s + 1]) for s in range(4)] for e in evs])
     stage_avg = stage_ms.mean(axis=0)
+
+    # the same K steps as HIP-graph replays (one captured step per weight copy;
+    # decode runtimes replay the layer as a graph).  Every ABI call is
+    # asynchronous and allocation-free, so the library captures as is.
+    graph_ms = None
+    if not a.no_graph:
+        graphs = []
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c, torch.cuda.current_stream())
+            graphs.append(g)
+        # a replay gives the eager result bit for bit
+        step(0)
+        torch.cuda.synchronize()
+        eager = out.clone()
+        out.fill_(float("nan"))
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), "graph replay differs from the eager step"
+        for i in range(a.warmup):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for i in range(a.steps):
+            graphs[(a.warmup + i) % copies].replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / a.steps
+    ms = graph_ms if graph_ms is not None else direct_ms
 
     # dominant kernel: the gate/up projection (2/3 of the expert bytes and flops)
     path = fw.fw_moe_forward_path(desc, T)
@@ -186,6 +220,8 @@ def main():
                    "ffn": cfg.ffn, "expert_format": cfg.expert_q, "shared_ffn": cfg.shared_ffn,
                    "tokens": T, "active_experts": n_active, "weight_copies": copies,
                    "path": "gemv" if path == fw.FW_PATH_GEMV else "gemm"},
+        "timing": "hip-graph replay per step" if graph_ms is not None else "direct launches",
+        "direct_ms_per_step": direct_ms,
         "layer_GBps": layer_bytes / (ms * 1e-3) / 1e9,
         "layer_TFLOPs": layer_flops / (ms * 1e-3) / 1e12,
         "stage_us": {n: round(float(v) * 1e3, 2) for n, v in
