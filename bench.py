@@ -32,7 +32,9 @@ MFMA_FP16_PEAK_TFLOPS = 2500.0
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)"
 CSRC = os.path.join(ROOT, "sparse_moe_block_amd", "csrc")
 # sources whose kernels the traffic counters describe (a change voids them)
-TRAFFIC_SOURCES = ["common.h", "gemv.hip", "gemm2.hip", "forward.hip"]
+# sources that decide each dominant kernel's memory traffic
+TRAFFIC_SOURCES = {"gemv_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "gemv.hip"],
+                   "gemm2_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "gemm2.hip"]}
 
 WORKLOADS = {
     # name: (config, T, weight copies)
@@ -233,9 +235,9 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def source_hash():
+def source_hash(kernel):
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
+    for f in TRAFFIC_SOURCES[kernel]:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -260,7 +262,7 @@ def traffic(workload, roof):
         return None
     with open(p) as fh:
         t = json.load(fh)
-    if t.get("source_sha") != source_hash():
+    if t.get("source_sha") != source_hash(roof["kernel"]):
         return None
     return t["bytes_per_launch"]
 
@@ -296,7 +298,7 @@ def reduce_counters(a):
     ff, wf = copy_bytes / (max(cf) * 1024), copy_bytes / (max(cw) * 1024)
     fetch = sum(kf) / len(kf) * 1024 * ff
     write = sum(kw) / len(kw) * 1024 * wf
-    res = {"workload": a.workload, "kernel": kernel, "source_sha": source_hash(),
+    res = {"workload": a.workload, "kernel": kernel, "source_sha": source_hash(kernel),
            "dispatches": [len(kf), len(kw)], "fetch_kib_per_dispatch": sum(kf) / len(kf),
            "write_kib_per_dispatch": sum(kw) / len(kw), "copy_mib": a.copy_mib,
            "copy_fetch_kib": max(cf), "copy_write_kib": max(cw), "fetch_factor": ff,

@@ -140,8 +140,10 @@ int fw_moe_route(const fw_moe_desc *desc, int32_t T, const void *x, const void *
  *                  an expert; entries past expert_offsets[E] are -1
  *   inv_pos        [P]   int32 out: sorted_pairs[inv_pos[q]] == q; -1 for a pair
  *                  whose id is out of range (and FW_STATUS_BAD_EXPERT_ID is set)
- * topk_ids [T][k] int32 in.  The workspace holds the status word only.
- * Bit-exact and unique for valid ids. */
+ * topk_ids [T][k] int32 in.  Up to 2048 pairs the workspace holds the status
+ * word only (256 bytes suffice); above that the sort keeps per-1024-pair-chunk
+ * expert counts in it and needs fw_moe_workspace_size(desc, T) bytes, else
+ * FW_EWORKSPACE.  Bit-exact and unique for valid ids. */
 int fw_moe_permute(const fw_moe_desc *desc, int32_t T, const int32_t *topk_ids,
                    int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *inv_pos,
                    void *workspace, size_t ws_bytes, void *stream);

@@ -32,6 +32,7 @@ WsLayout ws_layout(const fw_moe_desc &d, int T) {
     L.y = take((P + (Fs ? (size_t)T : 0)) * H * 4);
     L.split_cnt = take((size_t)kSplitTiles * 4);
     L.split_part = take((size_t)kSplitTiles * kSplitSlicesMax * 2 * kGemvTokens * kWave * 4);
+    L.perm = take(E * (size_t)(perm_blocks((long long)P) + 1) * 4);
     L.total = off;
     return L;
 }
@@ -135,8 +136,15 @@ int fw_moe_permute(const fw_moe_desc *desc, int32_t T, const int32_t *topk_ids,
         !al16(sorted_pairs) || !al16(inv_pos))))
         return FW_EALIGN;
     if (ws_bytes < sizeof(WsHeader)) return FW_EWORKSPACE;
+    const long long P = (long long)T * desc->top_k;
+    int32_t *perm = nullptr;
+    if (P > kPermOneBlockMaxP) {
+        const WsLayout L = ws_layout(*desc, T);
+        if (ws_bytes < L.total) return FW_EWORKSPACE;
+        perm = (int32_t *)((char *)workspace + L.perm);
+    }
     return hip_status(launch_permute(*desc, T, topk_ids, expert_offsets, sorted_pairs, inv_pos,
-                                     (WsHeader *)workspace, (hipStream_t)stream));
+                                     (WsHeader *)workspace, perm, (hipStream_t)stream));
 }
 
 int fw_moe_forward(const fw_moe_desc *desc, int32_t T, const void *x, const void *w_gate,

@@ -42,6 +42,8 @@ struct WsLayout {
     size_t y;        // f32  [P][H] then [T][H]   per-pair expert outputs
     size_t split_cnt;   // int [kSplitTiles]      split-K arrival counters
     size_t split_part;  // f32 [kSplitTiles * kSplitSlicesMax][2 * kGemvTokens][64] partials
+    size_t perm;     // int [E][nb + 1]              multi-block permutation: per-block
+                     //                              counts, then their prefix; totals
     size_t total;
     int max_tiles;
 };
@@ -203,8 +205,14 @@ hipError_t launch_logits(const fw_moe_desc &d, int T, const void *x, const void 
                          const float *bias, float *logits, hipStream_t s);
 hipError_t launch_topk(const fw_moe_desc &d, int T, const float *logits, int32_t *ids,
                        float *w, hipStream_t s);
+// Pair counts above which the permutation runs as three multi-workgroup
+// kernels (count, per-expert scan, scatter) instead of one workgroup.
+constexpr int kPermChunk = 1024;
+constexpr int kPermOneBlockMaxP = 2048;
+inline int perm_blocks(long long P) { return (int)((P + kPermChunk - 1) / kPermChunk); }
 hipError_t launch_permute(const fw_moe_desc &d, int T, const int32_t *ids, int32_t *offsets,
-                          int32_t *sorted, int32_t *inv, WsHeader *hdr, hipStream_t s);
+                          int32_t *sorted, int32_t *inv, WsHeader *hdr, int32_t *perm,
+                          hipStream_t s);
 hipError_t launch_clear_status(WsHeader *hdr, hipStream_t s);
 
 struct FwdArgs {
