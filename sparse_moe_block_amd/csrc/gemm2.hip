@@ -4,7 +4,8 @@
 //  - a workgroup tile is up to 64 rows of one expert's segment of the sorted
 //    pair list (tokens gathered through sorted_pairs) times 256 weight rows;
 //    each of the four wavefronts owns 64 weight rows (four 16-row MFMA column
-//    groups) and all 64 token rows (four 16-row MFMA row groups);
+//    groups) and all 64 token rows (four 16-row MFMA row groups; a tile with
+//    fewer rows runs only the row groups that hold rows: 1, 2 or 4);
 //  - K advances one 256-element unit (8 GGUF blocks) per step.  In the MFMA's
 //    k order, lane group g = lane / 16 covers blocks 2g and 2g + 1 of the unit
 //    and slice i (0..7) of a step covers block 2g + i / 4, fp16 pairs
@@ -32,7 +33,8 @@
 namespace fw {
 namespace {
 
-constexpr int BM = kGemm2BM;   // 64 token rows
+constexpr int BM = kGemm2BM;   // token rows per tile (a multiple of 64)
+constexpr int kMaxMI = BM / 16;   // 16-row MFMA row groups per tile
 constexpr int BN = 256;        // weight rows per workgroup
 constexpr int BK = kUnit;      // 256 elements per step
 constexpr int LDA = BK + 8;    // padded LDS activation row (halfs): 528 bytes
@@ -45,7 +47,7 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 struct Smem2 {
     _Float16 a[2][BM * LDA];
 };
-// epilogues reuse the activation buffers: [64][136] fp16 or [64][260] fp32
+// epilogues reuse the activation buffers: [BM][136] fp16 or [BM][260] fp32
 static_assert(sizeof(Smem2) >= BM * 136 * 2 && sizeof(Smem2) >= BM * (BN + 4) * 4,
               "epilogue fits");
 
@@ -118,7 +120,7 @@ __device__ __forceinline__ h8 frag_b(const uint32_t *w) {
 
 struct Tile2 {
     const _Float16 *abase;     // activation rows (uniform)
-    uint32_t aoff[8];          // this thread's rows, at its 16-byte chunk: element offsets
+    uint32_t aoff[BM / 8];     // this thread's rows, at its 16-byte chunk: element offsets
     const uint8_t *bbase[2];   // the expert's weight matrices (uniform): gate/up or down
     uint32_t boff[4];          // this lane's rows (col groups), at its block pair: byte offsets
     _Float16 *hout;
@@ -126,9 +128,9 @@ struct Tile2 {
     int tid, lane, wave, steps, rows, rb, ct, N;
 };
 
-// The K loop and epilogue of one tile, MI 16-row groups of token rows (a
-// specialisation per valid-row count would skip the empty groups of a partial
-// tile, but two of them in one kernel exceed 256 VGPRs).
+// The K loop and epilogue of one tile, MI 16-row groups of token rows.  The
+// kernel's register count is that of the largest MI; the smaller ones skip
+// the MFMAs and activation loads of a partial tile's empty row groups.
 template <int Q, bool GU, int MI>
 __device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
     constexpr int WD = win_dwords<Q>();
@@ -142,16 +144,17 @@ __device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-    u4 ra[8];                  // activation chunks of the next step
+    constexpr int NA = 2 * MI;   // activation chunks per thread: rows tid / 32 + 8 j
+    u4 ra[NA];                   // activation chunks of the next step
     uint32_t wb0[4][WD], wb1[4][WD];   // weight windows: this step / next step
 
     auto load_a = [&](int st) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ra[j] = *(const u4 *)(c.abase + c.aoff[j] + st * BK);
+        for (int j = 0; j < NA; ++j) ra[j] = *(const u4 *)(c.abase + c.aoff[j] + st * BK);
     };
     auto commit_a = [&](int buf) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < NA; ++j)
             *(u4 *)&sm.a[buf][(tid / 32 + 8 * j) * LDA + (tid & 31) * 8] = ra[j];
     };
 #define FW_LOAD_B(W, st)                                                   \
@@ -220,7 +223,7 @@ __device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
     // acc[r][cg][j]: token row 16 r + 4 g + j, weight row 64 wave + 16 cg + fr
     const int rows = c.rows, rb = c.rb, ct = c.ct, N = c.N, wave = c.wave;
     if constexpr (GU) {
-        // a(token, feature) for the workgroup's 128 features: [64][OH] fp16
+        // a(token, feature) for the workgroup's 128 features: [BM][OH] fp16
         constexpr int OH = 136;
         _Float16 *o = (_Float16 *)&sm;
 #pragma unroll
@@ -237,16 +240,20 @@ __device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
                     o[row * OH + (col & ~31) + pair_pos(col & 31)] = (_Float16)a;
                 }
         __syncthreads();
-        // 64 rows x 256 bytes: thread -> (row tid / 4, 64 bytes)
-        const int row = tid >> 2, part = tid & 3;
-        if (row < rows) {
-            const uint4 *s = (const uint4 *)&o[row * OH + part * 32];
-            uint4 *d = (uint4 *)(c.hout + (size_t)(rb + row) * N + ct * 128 + part * 32);
+        // rows x 256 bytes: thread -> (row r0 + tid / 4, 64 bytes)
+        const int part = tid & 3;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) d[i] = s[i];
+        for (int r0 = 0; r0 < 16 * MI; r0 += 64) {
+            const int row = r0 + (tid >> 2);
+            if (row < rows) {
+                const uint4 *s = (const uint4 *)&o[row * OH + part * 32];
+                uint4 *d = (uint4 *)(c.hout + (size_t)(rb + row) * N + ct * 128 + part * 32);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) d[i] = s[i];
+            }
         }
     } else {
-        // y rows: [64][OF] fp32
+        // y rows: [BM][OF] fp32
         constexpr int OF = BN + 4;
         float *o = (float *)&sm;
 #pragma unroll
@@ -257,13 +264,17 @@ __device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
                 for (int j = 0; j < 4; ++j)
                     o[(16 * r + 4 * g + j) * OF + 64 * wave + 16 * cg + fr] = acc[r][cg][j];
         __syncthreads();
-        // 64 rows x 1 KB: four threads per row, 256 bytes each
-        const int row = tid >> 2, part = tid & 3;
-        if (row < rows) {
-            const uint4 *s = (const uint4 *)&o[row * OF + part * 64];
-            uint4 *d = (uint4 *)(c.yout + (size_t)(rb + row) * N + ct * BN + part * 64);
+        // rows x 1 KB: four threads per row, 256 bytes each
+        const int part = tid & 3;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) d[i] = s[i];
+        for (int r0 = 0; r0 < 16 * MI; r0 += 64) {
+            const int row = r0 + (tid >> 2);
+            if (row < rows) {
+                const uint4 *s = (const uint4 *)&o[row * OF + part * 64];
+                uint4 *d = (uint4 *)(c.yout + (size_t)(rb + row) * N + ct * BN + part * 64);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) d[i] = s[i];
+            }
         }
     }
 }
@@ -311,7 +322,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(
     c.wave = wave_id();
     // activations: thread -> 16-byte chunk tid % 32 of tile rows tid / 32 + 8 j
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < BM / 8; ++j) {
         const int arow = c.tid / 32 + 8 * j;
         const int r = rb + min(arow, rows - 1);
         int src_row = r;
@@ -344,7 +355,13 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(
     c.rb = rb;
     c.ct = ct;
     c.N = N;
-    tile2_run<Q, GU, 4>(sm, c);
+    // only the row groups that hold rows of this tile run (an expert's last,
+    // partial tile of a skewed batch is often far below BM rows)
+    const int mi = (rows + 15) / 16;
+    if (kMaxMI >= 8 && mi > 4) tile2_run<Q, GU, kMaxMI>(sm, c);
+    else if (mi > 2) tile2_run<Q, GU, 4>(sm, c);
+    else if (mi > 1) tile2_run<Q, GU, 2>(sm, c);
+    else tile2_run<Q, GU, 1>(sm, c);
 }
 
 template <int Q, bool GU>
