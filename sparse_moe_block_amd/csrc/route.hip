@@ -235,9 +235,14 @@ hipError_t launch_logits(const fw_moe_desc &d, int T, const void *x, const void 
     } else if (T <= kGemvMaxT) {
         dim3 grid((T + 15) / 16, (E + 15) / 16);
         logits_bf16_kernel<1, 1, 16, 4><<<grid, 16 * kWave, 0, s>>>(xb, wb, bias, logits, T, H, E);
-    } else if (E >= 64) {
+    } else if (E >= 64 && (long long)((T + 31) / 32) * ((E + 63) / 64) >= 512) {
         dim3 grid((T + 31) / 32, (E + 63) / 64);
         logits_bf16_kernel<2, 4, 4, 2><<<grid, 4 * kWave, 0, s>>>(xb, wb, bias, logits, T, H, E);
+    } else if (E >= 32) {
+        // fewer than 512 of the 32 x 64 tiles: 32 x 32 tiles over 8 wavefronts
+        // keep more of the CUs busy (T = 2048, E = 128: 20 -> 13 us)
+        dim3 grid((T + 31) / 32, (E + 31) / 32);
+        logits_bf16_kernel<2, 2, 8, 2><<<grid, 8 * kWave, 0, s>>>(xb, wb, bias, logits, T, H, E);
     } else {
         dim3 grid((T + 31) / 32, (E + 15) / 16);
         logits_bf16_kernel<2, 1, 4, 4><<<grid, 4 * kWave, 0, s>>>(xb, wb, bias, logits, T, H, E);
