@@ -16,13 +16,14 @@ from typing import Optional, Tuple
 
 Q8_0 = "q8_0"
 Q4_0 = "q4_0"
+Q4_K = "q4_k"
 F32 = "f32"
 BF16 = "bf16"
 SOFTMAX = "softmax"
 SIGMOID = "sigmoid"
 
 # bytes per 32-element block
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18}
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 18}   # Q4_K: 144 per 256
 
 
 @dataclass(frozen=True)

@@ -2,7 +2,7 @@
 GGUF-blocked expert weights.
 
 Input generation only.  It contains none of the layer's arithmetic: no dequant,
-no routing, no FFN.  The quantizers below *produce* Q8_0 / Q4_0 blocks from fp32
+no routing, no FFN.  The quantizers below *produce* Q8_0 / Q4_0 / Q4_K blocks from fp32
 samples (the way a checkpoint converter would); the layer only ever *reads*
 blocks.  Both the GPU path and the CPU oracle are fed from here.
 
@@ -17,6 +17,11 @@ Block byte layout (GGUF, little-endian, no padding):
   Q4_0: [fp16 d][16 bytes of nibbles]    18 bytes, value = d*(q-8);
         byte i holds element i in its low nibble and element i+16 in its high
         nibble.
+  Q4_K: 256-element super-block, 144 bytes: [fp16 d][fp16 dmin][12 bytes of
+        six-bit (scale, min) pairs for the eight 32-element sub-blocks]
+        [128 bytes of nibbles: group c of 64 elements uses bytes 32c..32c+31,
+        low nibbles first 32 elements, high nibbles the next 32];
+        value = d*scale_j*q - dmin*min_j.
 """
 
 import math
@@ -26,7 +31,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-from .configs import BF16, F32, Q4_0, Q8_0, BLOCK_BYTES, LayerConfig
+from .configs import BF16, F32, Q4_0, Q4_K, Q8_0, BLOCK_BYTES, LayerConfig
 
 BASE_SEED = 20261202
 
@@ -91,7 +96,42 @@ def quantize_q4_0(w: torch.Tensor) -> torch.Tensor:
     return out.reshape(*lead, n // 32 * 18).contiguous()
 
 
-QUANTIZERS = {Q8_0: quantize_q8_0, Q4_0: quantize_q4_0}
+def quantize_q4_k(w: torch.Tensor) -> torch.Tensor:
+    """fp32 [..., n] -> uint8 [..., n/256*144] (GGUF Q4_K super-blocks).
+    Per 32-element sub-block j: scale_j = (max - min(min, 0)) / 15 and
+    min_j = -min(min, 0); per super-block d = max scale / 63 and dmin = max min
+    / 63, both stored as fp16; 6-bit codes sc_j = round(scale_j / d),
+    m_j = round(min_j / dmin); element codes round((x + dmin m_j) / (d sc_j))
+    clamped to 0..15.  Zero scales give zero codes."""
+    *lead, n = w.shape
+    assert n % 256 == 0
+    b = w.reshape(*lead, n // 256, 8, 32)
+    lo = b.amin(dim=-1).clamp(max=0.0)
+    hi = b.amax(dim=-1)
+    scale = (hi - lo) / 15.0
+    mn = -lo
+    d16 = (scale.amax(dim=-1) / 63.0).to(torch.float16)
+    dm16 = (mn.amax(dim=-1) / 63.0).to(torch.float16)
+    d, dm = d16.float().unsqueeze(-1), dm16.float().unsqueeze(-1)
+    safe = lambda v: torch.where(v > 0, v, torch.ones_like(v))
+    sc = torch.where(d > 0, _round_half_away(scale / safe(d)), torch.zeros_like(scale))
+    m = torch.where(dm > 0, _round_half_away(mn / safe(dm)), torch.zeros_like(mn))
+    sc, m = sc.clamp(0, 63), m.clamp(0, 63)
+    step = (d * sc).unsqueeze(-1)
+    off = (dm * m).unsqueeze(-1)
+    q = torch.where(step > 0, _round_half_away((b + off) / safe(step)), torch.zeros_like(b))
+    q = q.clamp(0, 15).to(torch.uint8).reshape(*lead, n // 256, 4, 2, 32)
+    qs = (q[..., 0, :] | (q[..., 1, :] << 4)).reshape(*lead, n // 256, 128)
+    sc, m = sc.to(torch.uint8), m.to(torch.uint8)
+    packed = torch.cat([sc[..., :4] | ((sc[..., 4:] >> 4) << 6),
+                        m[..., :4] | ((m[..., 4:] >> 4) << 6),
+                        (sc[..., 4:] & 15) | ((m[..., 4:] & 15) << 4)], dim=-1)
+    hdr = torch.stack([d16, dm16], dim=-1).view(torch.int16).view(torch.uint8)
+    out = torch.cat([hdr.reshape(*lead, n // 256, 4), packed, qs], dim=-1)
+    return out.reshape(*lead, n // 256 * 144).contiguous()
+
+
+QUANTIZERS = {Q8_0: quantize_q8_0, Q4_0: quantize_q4_0, Q4_K: quantize_q4_k}
 
 
 def quantized_normal(rows, cols, std, qtype, seed, device):

@@ -1,6 +1,6 @@
 /*
  * fwref.c -- CPU oracle for the routed mixture-of-experts FFN layer run on GGUF
- * Q8_0 / Q4_0 expert weights.
+ * Q8_0 / Q4_0 / Q4_K expert weights.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg load this library.  The GPU library shares no
@@ -8,8 +8,9 @@
  *
  * It is the plain definition of what the layer computes, written for a reader
  * to check by eye: straight loops, no blocking, no fusion, no reordering.
- * Dequantised weights are exact in fp32 (an fp16 scale times a code of at most
- * 8 significant bits fits in 24 bits); every sum is accumulated in fp64 in
+ * Dequantised Q8_0 / Q4_0 weights are exact in fp32 (an fp16 scale times a code
+ * of at most 8 significant bits fits in 24 bits); a Q4_K weight is formed
+ * exactly in fp64 and rounded once to fp32; every sum is accumulated in fp64 in
  * ascending index order and rounded to fp32 only where the layer's interface
  * hands a value over (logits, gate weights, output).
  *
@@ -20,6 +21,13 @@
  *  - Q8_0 and Q4_0 as expert formats (Flyweight 0.5.1, "Models and formats";
  *    Gemma 4's routed experts must be Q4_0, Flyweight 0.2.0 "Current
  *    limitations"); the byte layout is GGUF's, which the pages do not print;
+ *  - Q4_K, the K-quant the pages name as the smallest a MoE checkpoint packs
+ *    to and one of BailingMoE3's two grouped expert formats (Flyweight 0.2.0,
+ *    "Quantization" and "Current limitations"; Flyweight 0.5.1, "Models and
+ *    formats").  Its layout is again GGUF's and not printed by the pages:
+ *    PARITY UNPINNED against an outside encoder (none is available here);
+ *    the tests pin it by round trips, by the cases that reduce to Q4_0 and by
+ *    brute force over code positions;
  *  - SwiGLU expert FFNs (vOOM, module layout: layer_runner's block math);
  *  - top-k routing with k a tunable (vOOM notes: the request-local top-2
  *    expert schedule) and DeepSeek-shaped sigmoid routing with an always-on
@@ -40,7 +48,7 @@
 #endif
 
 enum { REF_F32 = 0, REF_BF16 = 1 };
-enum { REF_Q8_0 = 0, REF_Q4_0 = 1 };
+enum { REF_Q8_0 = 0, REF_Q4_0 = 1, REF_Q4_K = 2 };
 enum { REF_SOFTMAX = 0, REF_SIGMOID = 1 };
 
 /* IEEE 754 binary16 -> value: 1 sign bit, 5 exponent bits (bias 15), 10
@@ -67,14 +75,52 @@ float fwref_bf16_to_float(uint16_t b)
     return f;
 }
 
+/* Bytes per 32 elements (a Q4_K super-block is 144 bytes per 256). */
 static int block_bytes(int qtype) { return qtype == REF_Q8_0 ? 34 : 18; }
 
-/* Dequantise one row of n elements (n a multiple of 32).
+/* Q4_K sub-block j's 6-bit scale and min from the 12 packed bytes: j < 4 keep
+ * them in the low 6 bits of bytes j and j + 4; j >= 4 take their low 4 bits
+ * from byte j + 4 (scale: low nibble, min: high nibble) and their top 2 bits
+ * from the top 2 bits of bytes j - 4 (scale) and j (min). */
+static void q4k_scale_min(const uint8_t *sc, int j, int *scale, int *min)
+{
+    if (j < 4) {
+        *scale = sc[j] & 63;
+        *min = sc[j + 4] & 63;
+    } else {
+        *scale = (sc[j + 4] & 15) | (sc[j - 4] >> 6) << 4;
+        *min = (sc[j + 4] >> 4) | (sc[j] >> 6) << 4;
+    }
+}
+
+/* Dequantise one row of n elements (n a multiple of 32; of 256 for Q4_K).
  * Q8_0 block: [fp16 d][32 int8 q], value_i = d * q_i.
  * Q4_0 block: [fp16 d][16 bytes], byte i = q_i | q_{i+16} << 4,
- *             value_i = d * (q_i - 8). */
+ *             value_i = d * (q_i - 8).
+ * Q4_K super-block of 256 elements, 144 bytes: [fp16 d][fp16 dmin]
+ *             [12 bytes: eight 6-bit (scale, min) pairs][128 bytes of codes];
+ *             group c (0..3) of 64 elements reads code bytes 32c .. 32c + 31:
+ *             element 64c + l is the low nibble of byte 32c + l (sub-block
+ *             2c), element 64c + 32 + l its high nibble (sub-block 2c + 1);
+ *             value = d * scale_j * q - dmin * min_j for sub-block j. */
 void fwref_dequant_row(int qtype, const uint8_t *row, int n, float *out)
 {
+    if (qtype == REF_Q4_K) {
+        for (int b = 0; b < n / 256; ++b) {
+            const uint8_t *blk = row + (size_t)b * 144;
+            double d = fwref_half_to_float((uint16_t)(blk[0] | blk[1] << 8));
+            double dmin = fwref_half_to_float((uint16_t)(blk[2] | blk[3] << 8));
+            const uint8_t *sc = blk + 4, *qs = blk + 16;
+            for (int e = 0; e < 256; ++e) {
+                int c = e / 64, l = e % 32, high = (e % 64) >= 32;
+                int j = 2 * c + high, scale, min;
+                q4k_scale_min(sc, j, &scale, &min);
+                int q = high ? qs[32 * c + l] >> 4 : qs[32 * c + l] & 15;
+                out[256 * b + e] = (float)(d * scale * q - dmin * min);
+            }
+        }
+        return;
+    }
     for (int b = 0; b < n / 32; ++b) {
         const uint8_t *blk = row + (size_t)b * block_bytes(qtype);
         float d = fwref_half_to_float((uint16_t)(blk[0] | blk[1] << 8));

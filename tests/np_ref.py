@@ -4,13 +4,32 @@ itself pinned by the hand-decoded fixture in golden/q_blocks.txt."""
 
 import numpy as np
 
-BQ = {"q8_0": 34, "q4_0": 18}
+BQ = {"q8_0": 34, "q4_0": 18, "q4_k": 18}   # bytes per 32 elements (Q4_K: 144 per 256)
+
+
+def _q4k_scales(sc):
+    """[..., 12] packed bytes -> (scale, min) [..., 8] as int64: sub-blocks
+    0..3 in the low six bits of bytes 0..3 / 4..7; sub-blocks 4..7 combine the
+    nibbles of bytes 8..11 with the top two bits of bytes 0..3 / 4..7."""
+    sc = sc.astype(np.int64)
+    s = np.concatenate([sc[..., 0:4] & 63, (sc[..., 8:12] & 15) | ((sc[..., 0:4] >> 6) << 4)], -1)
+    m = np.concatenate([sc[..., 4:8] & 63, (sc[..., 8:12] >> 4) | ((sc[..., 4:8] >> 6) << 4)], -1)
+    return s, m
 
 
 def dequant(qtype, raw, n):
     """raw uint8 [..., n/32*Bq] -> float64 [..., n]."""
     raw = np.asarray(raw, dtype=np.uint8)
     lead = raw.shape[:-1]
+    if qtype == "q4_k":
+        sb = raw.reshape(*lead, n // 256, 144)
+        d = sb[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float64)
+        dmin = sb[..., 2:4].copy().view(np.float16)[..., 0].astype(np.float64)
+        s, m = _q4k_scales(sb[..., 4:16])
+        qs = sb[..., 16:].astype(np.int64).reshape(*lead, n // 256, 4, 32)
+        codes = np.stack([qs & 15, qs >> 4], axis=-2).reshape(*lead, n // 256, 8, 32)
+        v = (d[..., None, None] * s[..., None] * codes - dmin[..., None, None] * m[..., None])
+        return v.reshape(*lead, n)
     blocks = raw.reshape(*lead, n // 32, BQ[qtype])
     d = blocks[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float64)
     if qtype == "q8_0":

@@ -113,3 +113,121 @@ def test_q4_0_scale_sign_and_extreme():
     assert d == np.float16(-0.0625)
     assert raw[2 + 3] & 15 == 0                     # element 3 -> code 0 -> value 0.5
     assert raw[2 + 7] & 15 == 12                    # -0.25/-0.0625 + 8 = 12
+
+
+# ---------------------------------------------------------------------------
+# Q4_K (GGUF K-quant super-blocks).  The pages print no layout and no outside
+# encoder is available here: the oracle's Q4_K decoding is pinned by a
+# hand-packed super-block, by the case that reduces to Q4_0 (itself pinned by
+# the hand-decoded fixture above), by brute force over every six-bit
+# (scale, min) pair and every code position, and by the generator's error
+# bound.
+
+GOLDEN_K = os.path.join(os.path.dirname(__file__), "golden", "q4k_blocks.txt")
+
+
+def golden_q4k():
+    out = []
+    for line in open(GOLDEN_K):
+        if line.startswith("#") or not line.strip():
+            continue
+        name, d, dmin, sc, mn, rule, hx = [s.strip() for s in line.split("|")]
+        out.append((name, Fraction(d), Fraction(dmin), [int(v) for v in sc.split()],
+                    [int(v) for v in mn.split()], rule, bytes.fromhex(hx)))
+    return out
+
+
+@pytest.mark.parametrize("rec", golden_q4k(), ids=lambda r: r[0])
+def test_q4k_hand_packed_block(ref, rec):
+    name, d, dmin, sc, mn, rule, raw = rec
+    assert len(raw) == 144 and rule == "updown"
+    got = ref.dequant_row("q4_k", np.frombuffer(raw, dtype=np.uint8), 256)
+    want = []
+    for e in range(256):
+        j = 2 * (e // 64) + (e % 64 >= 32)        # sub-block
+        l = e % 32                                # byte within the group
+        q = l % 16 if e % 64 < 32 else 15 - l % 16
+        want.append(float(d * sc[j] * q - dmin * mn[j]))
+    assert np.array_equal(got.astype(np.float64), np.array(want))
+    assert np.array_equal(np_ref.dequant("q4_k", np.frombuffer(raw, dtype=np.uint8), 256),
+                          np.array(want))
+
+
+def _q4k_raw(d16, dmin16, scale_bytes, codes):
+    """A super-block from its fields: codes [256] in element order."""
+    codes = np.asarray(codes, dtype=np.uint8).reshape(4, 2, 32)
+    qs = (codes[:, 0, :] | (codes[:, 1, :] << 4)).reshape(-1)
+    hdr = np.array([d16, dmin16], dtype=np.float16).view(np.uint8)
+    return np.concatenate([hdr, np.asarray(scale_bytes, dtype=np.uint8), qs])
+
+
+def test_q4k_reduces_to_q4_0(ref):
+    """scale = min = 1 in every sub-block and dmin = 8 d give d * (q - 8): the
+    same values as eight Q4_0 blocks with scale d and the same codes."""
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 16, 256)
+    d = np.float16(0.0234)
+    ones = [1 | 0 << 6] * 4 + [1 | 0 << 6] * 4 + [1 | 1 << 4] * 4   # all scales, mins 1
+    got = ref.dequant_row("q4_k", _q4k_raw(d, np.float16(8 * float(d)), ones, codes), 256)
+    q40 = []
+    for b in range(8):
+        c = codes[32 * b:32 * b + 32]
+        q40.append(np.concatenate([np.array([d], np.float16).view(np.uint8),
+                                   (c[:16] | (c[16:] << 4)).astype(np.uint8)]))
+    want = ref.dequant_row("q4_0", np.concatenate(q40), 256)
+    assert np.array_equal(got, want)
+
+
+def test_q4k_every_scale_and_min(ref):
+    """Each sub-block j decodes every six-bit (scale, min) pair: with codes
+    q = 0 and q = 1 the values are -min and scale - min (d = dmin = 1)."""
+    for j in range(8):
+        for s in range(64):
+            m = (s * 37 + 11 * j) % 64
+            sc = np.zeros(12, np.int64)
+            if j < 4:
+                sc[j] |= s
+                sc[j + 4] |= m
+            else:
+                sc[j + 4] |= (s & 15) | (m & 15) << 4
+                sc[j - 4] |= (s >> 4) << 6
+                sc[j] |= (m >> 4) << 6
+            codes = np.zeros(256, np.int64)
+            e0 = 64 * (j // 2) + 32 * (j % 2)
+            codes[e0 + 1] = 1
+            v = ref.dequant_row("q4_k", _q4k_raw(1.0, 1.0, sc, codes), 256)
+            assert v[e0] == -m and v[e0 + 1] == s - m, (j, s, m)
+            others = np.delete(np.arange(256), np.arange(e0, e0 + 32))
+            assert not np.any(v[others] > 0)
+
+
+def test_q4k_every_code_position(ref):
+    """A single non-zero code at position p changes exactly element p."""
+    sc = [1] * 4 + [0] * 4 + [1] * 4          # scale 1, min 0 everywhere
+    for p in range(256):
+        codes = np.zeros(256, np.int64)
+        codes[p] = 7
+        v = ref.dequant_row("q4_k", _q4k_raw(1.0, 0.0, sc, codes), 256)
+        assert v[p] == 7 and np.count_nonzero(v) == 1, p
+
+
+def test_q4k_quantizer_error_bound(ref):
+    """The generator's Q4_K quantizer reproduces its input to within one code
+    step d * scale_j of each sub-block plus the six-bit rounding of the min;
+    the numpy decoder agrees with the oracle exactly."""
+    w = moegen.normal((16, 512), 0.02, 9)
+    w[0, :256] = 0.0
+    w[1, 40] = 0.3
+    raw = moegen.quantize_q4_k(w).numpy()
+    x = w.numpy().astype(np.float64)
+    for i in range(16):
+        v = ref.dequant_row("q4_k", raw[i], 512).astype(np.float64)
+        assert np.array_equal(v, np_ref.dequant("q4_k", raw[i], 512).astype(np.float32))
+        sb = raw[i].reshape(2, 144)
+        d = sb[:, 0:2].copy().view(np.float16)[:, 0].astype(np.float64)
+        dmin = sb[:, 2:4].copy().view(np.float16)[:, 0].astype(np.float64)
+        s, m = np_ref._q4k_scales(sb[:, 4:16])
+        err = np.abs(v - x[i]).reshape(2, 8, 32).max(axis=-1)
+        bound = d[:, None] * np.maximum(s, 1) + dmin[:, None] * 0.5 + 1e-3 * 2.0 ** -7
+        assert np.all(err <= bound), (i, err, bound)
+    assert not np.any(ref.dequant_row("q4_k", raw[0], 512)[:256])
