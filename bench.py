@@ -45,6 +45,9 @@ WORKLOADS = {
     "deepseek32": (moegen.DEEPSEEK, 32, 2),
     "prefill2048": (moegen.QWEN3_PREFILL, 2048, 4),
     "deepseek4096": (moegen.DEEPSEEK, 4096, 1),
+    # the same shapes on Q4_K experts (GGUF K-quant super-blocks)
+    "decode16_q4k": (moegen.QWEN3_DECODE.with_(expert_q=moegen.Q4_K), 16, 16),
+    "prefill2048_q4k": (moegen.QWEN3_PREFILL.with_(expert_q=moegen.Q4_K), 2048, 4),
 }
 
 
@@ -277,7 +280,7 @@ def reduce_counters(a):
     cfg, T, _ = WORKLOADS[a.workload]
     path_gemv = T <= 64 if a.path == "auto" else a.path == "gemv"
     kernel = "gemv_kernel<gate/up>" if path_gemv else "gemm2_kernel<gate/up>"
-    frag = KERNELS[kernel][1] + "1ELb1E" if cfg.expert_q == "q4_0" else KERNELS[kernel][1] + "0ELb1E"
+    frag = KERNELS[kernel][1] + {"q8_0": "0", "q4_0": "1", "q4_k": "2"}[cfg.expert_q] + "ELb1E"
 
     def per_dispatch(d, counter, sub):
         vals = {}

@@ -79,7 +79,7 @@ enum {
 };
 
 enum { FW_F32 = 0, FW_BF16 = 1 };                 /* activation / router dtype */
-enum { FW_Q8_0 = 0, FW_Q4_0 = 1 };                /* expert weight format      */
+enum { FW_Q8_0 = 0, FW_Q4_0 = 1, FW_Q4_K = 2 };   /* expert weight format      */
 enum { FW_SOFTMAX_RENORM = 0, FW_SIGMOID_RENORM = 1 };
 enum { FW_PATH_AUTO = 0, FW_PATH_GEMV = 1, FW_PATH_GEMM = 2 };
 
@@ -92,8 +92,8 @@ typedef struct {
     int32_t shared_ffn;   /* Fs: 0 = no shared expert, else multiple of 256        */
     int32_t act_dtype;    /* FW_F32 | FW_BF16: x                                   */
     int32_t router_dtype; /* FW_F32 | FW_BF16: router weights; must equal act_dtype */
-    int32_t expert_q;     /* FW_Q8_0 | FW_Q4_0: routed experts                     */
-    int32_t shared_q;     /* FW_Q8_0 | FW_Q4_0: shared expert (ignored if Fs = 0)  */
+    int32_t expert_q;     /* FW_Q8_0 | FW_Q4_0 | FW_Q4_K: routed experts          */
+    int32_t shared_q;     /* same choices: shared expert (ignored if Fs = 0)      */
     int32_t score;        /* FW_SOFTMAX_RENORM | FW_SIGMOID_RENORM                 */
     int32_t path;         /* FW_PATH_*: forward kernel family (AUTO picks by T)    */
 } fw_moe_desc;

@@ -63,6 +63,14 @@ template <> struct QT<FW_Q4_0> {
 template <> struct QT<FW_Q8_0> {
     static constexpr int kBlockBytes = 34, kUnitBytes = 272, kUnitX4 = 17;
 };
+// Q4_K: a unit is one 256-element super-block (144 bytes; kBlockBytes is the
+// per-32-element share used to size rows): [fp16 d][fp16 dmin][12 bytes of
+// six-bit (scale, min) pairs][128 code bytes], group c of 64 elements in code
+// bytes 32c .. 32c + 31 (low nibbles: sub-block 2c, high: 2c + 1).
+template <> struct QT<FW_Q4_K> {
+    static constexpr int kBlockBytes = 18, kUnitBytes = 144, kUnitX4 = 9;
+};
+
 
 // Uniform read of data no kernel writes while the reader runs (schedules,
 // pair lists, staged activations): through the constant address space, which
@@ -184,6 +192,46 @@ __device__ __forceinline__ void codes_to_pairs(const uint32_t *q, h2 *p, uint32_
     }
 }
 
+// Six-bit scale (first) and min of Q4_K sub-block J from the packed bytes held
+// as dwords s1 (bytes 0..3), s2 (4..7), s3 (8..11): J < 4 in the low six bits
+// of bytes J and J + 4; J >= 4 a nibble of byte J + 4 under the top two bits
+// of bytes J - 4 (scale) and J (min).
+template <int J>
+__device__ __forceinline__ void q4k_scale_min(uint32_t s1, uint32_t s2, uint32_t s3,
+                                              uint32_t &sc, uint32_t &mn) {
+    if constexpr (J < 4) {
+        sc = __builtin_amdgcn_ubfe(s1, 8 * J, 6);
+        mn = __builtin_amdgcn_ubfe(s2, 8 * J, 6);
+    } else {
+        constexpr int j = J - 4;
+        sc = __builtin_amdgcn_ubfe(s3, 8 * j, 4) | __builtin_amdgcn_ubfe(s1, 8 * j + 6, 2) << 4;
+        mn = __builtin_amdgcn_ubfe(s3, 8 * j + 4, 4) | __builtin_amdgcn_ubfe(s2, 8 * j + 6, 2) << 4;
+    }
+}
+
+// The 16 pairs (pair order) of Q4_K sub-block 2c + H from the group's code
+// dwords g[0..7], each pair = 1024 + q or, for pairs j = 1, 3, 1024 + 16 q
+// (the caller subtracts 1024).  Elements 4m.. of the sub-block sit in dword m,
+// elements 16 + 4m.. in dword 4 + m; low nibbles for H = 0, high for H = 1.
+template <int H>
+__device__ __forceinline__ void q4k_raw_pairs(const uint32_t *g, uint32_t *r, uint32_t magic) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t c0 = g[m], c1 = g[4 + m];
+        if constexpr (H == 0) {
+            r[4 * m + 0] = and_or(c0, 0x000F000Fu, magic);
+            r[4 * m + 1] = and_or(c1 << 4, 0x00F000F0u, magic);
+            r[4 * m + 2] = and_or(c0 >> 8, 0x000F000Fu, magic);
+            r[4 * m + 3] = and_or(c1 >> 4, 0x00F000F0u, magic);
+        } else {
+            r[4 * m + 0] = and_or(c0 >> 4, 0x000F000Fu, magic);
+            r[4 * m + 1] = and_or(c1, 0x00F000F0u, magic);
+            r[4 * m + 2] = and_or(c0 >> 12, 0x000F000Fu, magic);
+            r[4 * m + 3] = and_or(c1 >> 8, 0x00F000F0u, magic);
+        }
+    }
+}
+
 template <int Q, int B>
 __device__ __forceinline__ float decode_pairs(const uint32_t *w, h2 *p, uint32_t magic) {
     uint32_t q[Q == FW_Q4_0 ? 4 : 8];
@@ -192,10 +240,10 @@ __device__ __forceinline__ float decode_pairs(const uint32_t *w, h2 *p, uint32_t
     return d;
 }
 
-// The exponent bits decode_pairs ORs in: 0x6400 per half (fp16 1024).
+// The exponent bits decode_pairs ORs in: 0x6400 per half (fp16 1024), Q4_0 / Q4_K.
 // For Q8_0 the same register serves as the 0x64 byte source of v_perm.
 template <int Q> __device__ __forceinline__ uint32_t pair_magic() {
-    return Q == FW_Q4_0 ? 0x64006400u : 0x64646464u;
+    return Q == FW_Q8_0 ? 0x64646464u : 0x64006400u;
 }
 
 // ---------------------------------------------------------------------------

@@ -52,13 +52,73 @@ static_assert(sizeof(Smem2) >= BM * 136 * 2 && sizeof(Smem2) >= BM * (BN + 4) * 
               "epilogue fits");
 
 // Dwords of the window of blocks 2g, 2g + 1 of a unit, per weight row.
-template <int Q> constexpr int win_dwords() { return Q == FW_Q4_0 ? 9 : 17; }
+// Q4_K: the super-block's 16-byte header and the 32 code bytes of group g.
+template <int Q> constexpr int win_dwords() { return Q == FW_Q4_0 ? 9 : Q == FW_Q4_K ? 12 : 17; }
 
+// p: the lane's window (Q8_0 / Q4_0) or its row's unit (Q4_K, whose code bytes
+// sit qoff bytes in).
 template <int Q>
-__device__ __forceinline__ void load_window(const uint8_t *p, uint32_t *w) {
+__device__ __forceinline__ void load_window(const uint8_t *p, uint32_t qoff, uint32_t *w) {
     const uint32_t *q = (const uint32_t *)p;
+    if constexpr (Q == FW_Q4_K) {
+        const uint32_t *c = (const uint32_t *)(p + qoff);
 #pragma unroll
-    for (int i = 0; i < win_dwords<Q>(); ++i) w[i] = q[i];
+        for (int i = 0; i < 4; ++i) w[i] = q[i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[4 + i] = c[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < win_dwords<Q>(); ++i) w[i] = q[i];
+    }
+}
+
+// Per-step constants of a Q4_K window (sub-blocks A = 2g, B = 2g + 1 of the
+// lane's group g), as fp32 bits: k[2h] = d * scale, k[2h + 1] = -dmin * min
+// (both exact in fp32).
+__device__ __forceinline__ void q4k_consts(const uint32_t *w, int g, uint32_t *k) {
+    const float d = half_bits_to_float(w[0] & 0xFFFFu), dmin = half_bits_to_float(w[0] >> 16);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int j = 2 * g + h, jj = (j - 4) & 3;
+        const uint32_t lo_s = __builtin_amdgcn_ubfe(w[1], 8 * j, 6);
+        const uint32_t lo_m = __builtin_amdgcn_ubfe(w[2], 8 * j, 6);
+        const uint32_t hi_s = __builtin_amdgcn_ubfe(w[3], 8 * jj, 4) |
+                              __builtin_amdgcn_ubfe(w[1], 8 * jj + 6, 2) << 4;
+        const uint32_t hi_m = __builtin_amdgcn_ubfe(w[3], 8 * jj + 4, 4) |
+                              __builtin_amdgcn_ubfe(w[2], 8 * jj + 6, 2) << 4;
+        const uint32_t sc = j < 4 ? lo_s : hi_s, mn = j < 4 ? lo_m : hi_m;
+        k[2 * h] = __float_as_uint(d * (float)sc);
+        k[2 * h + 1] = __float_as_uint(-dmin * (float)mn);
+    }
+}
+
+// B fragment of slice I from a Q4_K window: sub-block H = I / 4 of the group,
+// pairs 4 (I % 4) .. + 3.  Each weight d * scale * q - dmin * min is formed in
+// fp32 (exact up to one fp32 rounding) and rounded once to fp16, like a Q4_0
+// weight; pairs j = 1, 3 then carry 16x (exact).
+template <int I>
+__device__ __forceinline__ h8 frag_b_q4k(const uint32_t *w, const uint32_t *k) {
+    constexpr int H = I / 4, m = I % 4;
+    const uint32_t c0 = w[4 + m] >> (4 * H), c1 = w[8 + m] >> (4 * H);
+    const uint32_t a0 = c0 & 0x0F0F0F0Fu, a1 = c1 & 0x0F0F0F0Fu;   // elements 4m.., 16+4m..
+    const float ds = __uint_as_float(k[2 * H]), nd = __uint_as_float(k[2 * H + 1]);
+    // (float)((v >> 8b) & 255) is one v_cvt_f32_ubyte<b>
+    auto e = [&](uint32_t v, int byte) {
+        return (_Float16)fmaf((float)((v >> (8 * byte)) & 255u), ds, nd);
+    };
+    const h2 k16 = {(_Float16)16.0f, (_Float16)16.0f};
+    h2 p[4];
+    p[0] = h2{e(a0, 0), e(a0, 2)};
+    p[1] = h2{e(a1, 0), e(a1, 2)} * k16;
+    p[2] = h2{e(a0, 1), e(a0, 3)};
+    p[3] = h2{e(a1, 1), e(a1, 3)} * k16;
+    h8 f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = p[j][0];
+        f[2 * j + 1] = p[j][1];
+    }
+    return f;
 }
 
 // B fragment of slice I from a window: block I / 4 of the pair (even: 2 bytes
@@ -118,11 +178,21 @@ __device__ __forceinline__ h8 frag_b(const uint32_t *w) {
     return f;
 }
 
+// B fragment of slice I of any format (kq: the Q4_K per-step constants).
+template <int Q, int I>
+__device__ __forceinline__ h8 frag_any(const uint32_t *w, const uint32_t *kq) {
+    if constexpr (Q == FW_Q4_K)
+        return frag_b_q4k<I>(w, kq);
+    else
+        return frag_b<Q, I>(w);
+}
+
 struct Tile2 {
     const _Float16 *abase;     // activation rows (uniform)
     uint32_t aoff[BM / 8];     // this thread's rows, at its 16-byte chunk: element offsets
     const uint8_t *bbase[2];   // the expert's weight matrices (uniform): gate/up or down
     uint32_t boff[4];          // this lane's rows (col groups), at its block pair: byte offsets
+    uint32_t qoff;             // Q4_K: byte offset of the lane's code group in a unit
     _Float16 *hout;
     float *yout;
     int tid, lane, wave, steps, rows, rb, ct, N;
@@ -159,16 +229,20 @@ __device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
     };
 #define FW_LOAD_B(W, st)                                                   \
     _Pragma("unroll") for (int cg = 0; cg < 4; ++cg)                       \
-        load_window<Q>(c.bbase[GU ? cg >> 1 : 0] + c.boff[cg] + (st) * UB, W[cg]);
+        load_window<Q>(c.bbase[GU ? cg >> 1 : 0] + c.boff[cg] + (st) * UB, c.qoff, W[cg]);
 
     // one step: 8 slices x 4 column groups x MI row groups of MFMAs; the A
     // fragments of slice i + 1 are read from LDS while slice i's MFMAs run
-#define FW_FRAG_B(I, CG, W)                                                                   \
-    (I == 0 ? frag_b<Q, 0>(W[CG]) : I == 1 ? frag_b<Q, 1>(W[CG]) : I == 2 ? frag_b<Q, 2>(W[CG]) \
-     : I == 3 ? frag_b<Q, 3>(W[CG]) : I == 4 ? frag_b<Q, 4>(W[CG]) : I == 5 ? frag_b<Q, 5>(W[CG]) \
-     : I == 6 ? frag_b<Q, 6>(W[CG]) : frag_b<Q, 7>(W[CG]))
+#define FW_FRAG_B(I, CG, W)                                                                  \
+    (I == 0 ? frag_any<Q, 0>(W[CG], kq[CG]) : I == 1 ? frag_any<Q, 1>(W[CG], kq[CG])          \
+     : I == 2 ? frag_any<Q, 2>(W[CG], kq[CG]) : I == 3 ? frag_any<Q, 3>(W[CG], kq[CG])        \
+     : I == 4 ? frag_any<Q, 4>(W[CG], kq[CG]) : I == 5 ? frag_any<Q, 5>(W[CG], kq[CG])        \
+     : I == 6 ? frag_any<Q, 6>(W[CG], kq[CG]) : frag_any<Q, 7>(W[CG], kq[CG]))
 #define FW_MMA(BUF, W)                                                                        \
     if constexpr (MI > 0) {                                                                   \
+        uint32_t kq[4][4];                                                                    \
+        if constexpr (Q == FW_Q4_K)                                                           \
+            _Pragma("unroll") for (int cg = 0; cg < 4; ++cg) q4k_consts(W[cg], g, kq[cg]);    \
         const _Float16 *abase = &sm.a[BUF][fr * LDA + 64 * g];                                \
         h8 afc[MI > 0 ? MI : 1], afn[MI > 0 ? MI : 1];                                        \
         _Pragma("unroll") for (int r = 0; r < MI; ++r)                                        \
@@ -346,8 +420,9 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(
     for (int cg = 0; cg < 4; ++cg) {
         const int row = GU ? ct * 128 + 32 * c.wave + 16 * (cg & 1) + n   // feature (gate cg < 2)
                            : ct * BN + 64 * c.wave + 16 * cg + n;          // output row
-        c.boff[cg] = (uint32_t)(row * rowbytes) + g * (2 * QT<Q>::kBlockBytes);
+        c.boff[cg] = (uint32_t)(row * rowbytes) + (Q == FW_Q4_K ? 0 : g * (2 * QT<Q>::kBlockBytes));
     }
+    c.qoff = 16 + 32 * g;
     c.hout = hout;
     c.yout = yout;
     c.steps = K / BK;
@@ -385,12 +460,16 @@ hipError_t launch_gemm2_gate_up(const FwdArgs &a, hipStream_t s) {
     _Float16 *h = (_Float16 *)(a.ws + a.L.h);
     if (d.expert_q == FW_Q4_0)
         launch2<FW_Q4_0, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, 0, s);
+    else if (d.expert_q == FW_Q4_K)
+        launch2<FW_Q4_K, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, 0, s);
     else
         launch2<FW_Q8_0, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, 0, s);
     if (d.shared_ffn > 0) {
         _Float16 *hsh = h + (size_t)a.P * d.ffn;
         if (d.shared_q == FW_Q4_0)
             launch2<FW_Q4_0, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, 1, s);
+        else if (d.shared_q == FW_Q4_K)
+            launch2<FW_Q4_K, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, 1, s);
         else
             launch2<FW_Q8_0, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, 1, s);
     }
@@ -403,6 +482,8 @@ hipError_t launch_gemm2_down(const FwdArgs &a, hipStream_t s) {
     float *y = (float *)(a.ws + a.L.y);
     if (d.expert_q == FW_Q4_0)
         launch2<FW_Q4_0, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, 0, s);
+    else if (d.expert_q == FW_Q4_K)
+        launch2<FW_Q4_K, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, 0, s);
     else
         launch2<FW_Q8_0, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, 0, s);
     if (d.shared_ffn > 0) {
@@ -410,6 +491,8 @@ hipError_t launch_gemm2_down(const FwdArgs &a, hipStream_t s) {
         float *ysh = y + (size_t)a.P * d.hidden;
         if (d.shared_q == FW_Q4_0)
             launch2<FW_Q4_0, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, 1, s);
+        else if (d.shared_q == FW_Q4_K)
+            launch2<FW_Q4_K, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, 1, s);
         else
             launch2<FW_Q8_0, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, 1, s);
     }

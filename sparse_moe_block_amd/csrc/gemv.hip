@@ -157,9 +157,53 @@ __device__ __forceinline__ void dot_block(const uint32_t *w, const uint32_t (*x)
 // block's activations are loaded while the current block is consumed (two
 // sets of 16 SGPRs per row); scheduling barriers keep one block's pairs live
 // at a time.
+// Q4_K unit (one super-block): sub-block J is block J of the unit in pair
+// order.  Its exact code pairs meet the activation pairs in fp32 dot products,
+// and the sub-block's scale and min apply once, in fp32:
+//   acc += d * scale_J * sum(q x) - dmin * min_J * sum(x).
+template <int NTK>
+__device__ __forceinline__ void dot_unit_q4k(const uint32_t *w, int u, cu32 *const *in,
+                                             float *acc) {
+    const uint32_t magic = pair_magic<FW_Q4_K>();
+    const float d = half_bits_to_float(w[0] & 0xFFFFu), dmin = half_bits_to_float(w[0] >> 16);
+    const h2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    const h2 one = {(_Float16)1.0f, (_Float16)1.0f}, k16 = {(_Float16)16.0f, (_Float16)16.0f};
+    uint32_t xa[NTK][16], xb[NTK][16];
+    load_x<NTK>(xa, in, u, 0);
+#define FW_SUB(J, CUR, NXT)                                                          \
+    {                                                                                \
+        if (J < 7) load_x<NTK>(NXT, in, u, J + 1);                                   \
+        uint32_t r[16], sc, mn;                                                      \
+        q4k_raw_pairs<J % 2>(w + 4 + 8 * (J / 2), r, magic);                         \
+        q4k_scale_min<J>(w[1], w[2], w[3], sc, mn);                                  \
+        const float ds = d * (float)sc, dm = dmin * (float)mn;                       \
+        _Pragma("unroll") for (int n = 0; n < NTK; ++n) {                            \
+            float s = 0.f, xs = 0.f;                                                 \
+            _Pragma("unroll") for (int i = 0; i < 16; ++i) {                         \
+                const h2 xv = as_h2(CUR[n][i]);                                      \
+                s = __builtin_amdgcn_fdot2(as_h2(r[i]) - k1024, xv, s, false);       \
+                /* pairs j = 1, 3 hold x / 16 */                                     \
+                xs = __builtin_amdgcn_fdot2((i & 1) ? k16 : one, xv, xs, false);     \
+            }                                                                        \
+            acc[n] = fmaf(ds, s, acc[n]);                                            \
+            acc[n] = fmaf(-dm, xs, acc[n]);                                          \
+        }                                                                            \
+    }                                                                                \
+    __builtin_amdgcn_sched_barrier(0);
+    FW_SUB(0, xa, xb)
+    FW_SUB(1, xb, xa)
+    FW_SUB(2, xa, xb)
+    FW_SUB(3, xb, xa)
+    FW_SUB(4, xa, xb)
+    FW_SUB(5, xb, xa)
+    FW_SUB(6, xa, xb)
+    FW_SUB(7, xb, xa)
+#undef FW_SUB
+}
+
 template <int Q, int NTK>
-__device__ __forceinline__ void dot_unit(const uint32_t *w, int u, cu32 *const *in,
-                                         float *acc) {
+__device__ __forceinline__ void dot_unit_blocks(const uint32_t *w, int u, cu32 *const *in,
+                                                float *acc) {
     const uint32_t magic = pair_magic<Q>();
     uint32_t xa[NTK][16], xb[NTK][16];
     load_x<NTK>(xa, in, u, 0);
@@ -176,6 +220,15 @@ __device__ __forceinline__ void dot_unit(const uint32_t *w, int u, cu32 *const *
     FW_BLOCK(6, xa, xb)
     FW_BLOCK(7, xb, xa)
 #undef FW_BLOCK
+}
+
+template <int Q, int NTK>
+__device__ __forceinline__ void dot_unit(const uint32_t *w, int u, cu32 *const *in,
+                                         float *acc) {
+    if constexpr (Q == FW_Q4_K)
+        dot_unit_q4k<NTK>(w, u, in, acc);
+    else
+        dot_unit_blocks<Q, NTK>(w, u, in, acc);
 }
 
 // What a wavefront needs of one work item: the 64-row weight tile of each
@@ -462,10 +515,10 @@ void launch_s(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Flo
     auto fit = [&](int d) { return (int)std::max<size_t>(1, (160 * 1024) / (batch * d + red)); };
     // Q4_0 batches are 9 KB per wavefront: depth 4, 2 or 1; Q8_0 batches are
     // 17 KB: depth 2 or 1
-    constexpr int DMAX = Q == FW_Q4_0 ? 4 : 2;
+    constexpr int DMAX = X4 == 9 ? 4 : 2;
     if (per_cu < 1.5)
         launch_sd<Q, GU, S, DMAX>(a, wa, wb, xin, hout, yout, K, N, items, fit(DMAX), ks, shared, s);
-    else if (Q == FW_Q4_0 && per_cu < 3.0)
+    else if (X4 == 9 && per_cu < 3.0)
         launch_sd<Q, GU, S, 2>(a, wa, wb, xin, hout, yout, K, N, items, fit(2), ks, shared, s);
     else
         launch_sd<Q, GU, S, 1>(a, wa, wb, xin, hout, yout, K, N, items, fit(1), ks, shared, s);
@@ -498,6 +551,8 @@ hipError_t launch_gemv_gate_up(const FwdArgs &a, hipStream_t s) {
     const int mc = max_routed_chunks(a);
     if (d.expert_q == FW_Q4_0)
         launch<FW_Q4_0, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, mc, 0, s);
+    else if (d.expert_q == FW_Q4_K)
+        launch<FW_Q4_K, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, mc, 0, s);
     else
         launch<FW_Q8_0, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, mc, 0, s);
     if (d.shared_ffn > 0) {
@@ -505,6 +560,8 @@ hipError_t launch_gemv_gate_up(const FwdArgs &a, hipStream_t s) {
         const int sc = (a.T + kGemvTokens - 1) / kGemvTokens;
         if (d.shared_q == FW_Q4_0)
             launch<FW_Q4_0, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, sc, 1, s);
+        else if (d.shared_q == FW_Q4_K)
+            launch<FW_Q4_K, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, sc, 1, s);
         else
             launch<FW_Q8_0, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, sc, 1, s);
     }
@@ -518,6 +575,8 @@ hipError_t launch_gemv_down(const FwdArgs &a, hipStream_t s) {
     const int mc = max_routed_chunks(a);
     if (d.expert_q == FW_Q4_0)
         launch<FW_Q4_0, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, mc, 0, s);
+    else if (d.expert_q == FW_Q4_K)
+        launch<FW_Q4_K, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, mc, 0, s);
     else
         launch<FW_Q8_0, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, mc, 0, s);
     if (d.shared_ffn > 0) {
@@ -526,6 +585,8 @@ hipError_t launch_gemv_down(const FwdArgs &a, hipStream_t s) {
         const int sc = (a.T + kGemvTokens - 1) / kGemvTokens;
         if (d.shared_q == FW_Q4_0)
             launch<FW_Q4_0, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, sc, 1, s);
+        else if (d.shared_q == FW_Q4_K)
+            launch<FW_Q4_K, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, sc, 1, s);
         else
             launch<FW_Q8_0, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, sc, 1, s);
     }
