@@ -32,6 +32,8 @@ WsLayout ws_layout(const fw_moe_desc &d, int T) {
     L.y = take((P + (Fs ? (size_t)T : 0)) * H * 4);
     L.split_cnt = take((size_t)kSplitTiles * 4);
     L.split_part = take((size_t)kSplitTiles * kSplitSlicesMax * 2 * kGemvTokens * kWave * 4);
+    L.xsum = take((size_t)T * (H / 32) * 4);
+    L.hsum = take((P * (F / 32) + (size_t)T * (Fs / 32)) * 4);
     L.perm = take(E * (size_t)(perm_blocks((long long)P) + 1) * 4);
     L.total = off;
     return L;

@@ -42,6 +42,8 @@ struct WsLayout {
     size_t y;        // f32  [P][H] then [T][H]   per-pair expert outputs
     size_t split_cnt;   // int [kSplitTiles]      split-K arrival counters
     size_t split_part;  // f32 [kSplitTiles * kSplitSlicesMax][2 * kGemvTokens][64] partials
+    size_t xsum;     // f32  [T][H/32]            32-element block sums of x16 (Q4_K GEMV)
+    size_t hsum;     // f32  [P][F/32] then [T][Fs/32]   block sums of h (Q4_K GEMV)
     size_t perm;     // int [E][nb + 1]              multi-block permutation: per-block
                      //                              counts, then their prefix; totals
     size_t total;

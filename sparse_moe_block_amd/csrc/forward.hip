@@ -17,7 +17,8 @@ constexpr int kPrepThreads = 256;
 __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(
     const int32_t *__restrict__ offsets, int E, int P, const void *__restrict__ x, int act_bf16,
     int H, int T, int tile_rows, int max_tiles, int4 *__restrict__ active, int4 *__restrict__ tiles,
-    _Float16 *__restrict__ x16, int *__restrict__ split_cnt, WsHeader *__restrict__ hdr) {
+    _Float16 *__restrict__ x16, float *__restrict__ xsum, int *__restrict__ split_cnt,
+    WsHeader *__restrict__ hdr) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     if (blockIdx.x == 0) {
         // the GEMV's split-K arrival counters start every call at zero
@@ -117,6 +118,19 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(
         uint4 *dst = (uint4 *)(x16 + (size_t)t * H + 32 * b);
 #pragma unroll
         for (int q = 0; q < 4; ++q) dst[q] = uint4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+        if (xsum) {
+            // the block's sum of the staged fp16 values (unscaled), in pair
+            // order: the min term of a Q4_K GEMV
+            float sum = 0.f;
+#pragma unroll
+            for (int pi = 0; pi < 16; ++pi) {
+                const h2 v = as_h2(o[pi]);
+                const float sc = (pi & 1) ? 16.0f : 1.0f;
+                sum += sc * (float)v[0];
+                sum += sc * (float)v[1];
+            }
+            xsum[(size_t)t * (H / 32) + b] = sum;
+        }
     }
 }
 
@@ -158,10 +172,14 @@ __global__ __launch_bounds__(256) void combine_kernel(
 
 hipError_t launch_prepare(const FwdArgs &a, hipStream_t s) {
     const int tile_rows = a.path == FW_PATH_GEMM ? (kUseGemm2 ? kGemm2BM : kGemmBM) : kGemvTokens;
+    // the Q4_K GEMV needs the activation rows' block sums
+    const bool sums = a.path == FW_PATH_GEMV &&
+                      (a.d.expert_q == FW_Q4_K || (a.d.shared_ffn > 0 && a.d.shared_q == FW_Q4_K));
     prepare_kernel<<<1 + a.T, kPrepThreads, 0, s>>>(
         a.offsets, a.d.n_experts, a.P, a.x, a.d.act_dtype == FW_BF16, a.d.hidden, a.T, tile_rows,
         a.L.max_tiles, (int4 *)(a.ws + a.L.active), (int4 *)(a.ws + a.L.tiles),
-        (_Float16 *)(a.ws + a.L.x16), (int *)(a.ws + a.L.split_cnt), (WsHeader *)a.ws);
+        (_Float16 *)(a.ws + a.L.x16), sums ? (float *)(a.ws + a.L.xsum) : nullptr,
+        (int *)(a.ws + a.L.split_cnt), (WsHeader *)a.ws);
     return hipGetLastError();
 }
 

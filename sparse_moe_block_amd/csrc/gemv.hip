@@ -160,33 +160,41 @@ __device__ __forceinline__ void dot_block(const uint32_t *w, const uint32_t (*x)
 // Q4_K unit (one super-block): sub-block J is block J of the unit in pair
 // order.  Its exact code pairs meet the activation pairs in fp32 dot products,
 // and the sub-block's scale and min apply once, in fp32:
-//   acc += d * scale_J * sum(q x) - dmin * min_J * sum(x).
+//   acc += d * scale_J * sum(q x) - dmin * min_J * sum(x),
+// sum(x) being the activation row's precomputed 32-element block sums (sum[n]:
+// one fp32 per block, written by the kernel that produced the row).
 template <int NTK>
 __device__ __forceinline__ void dot_unit_q4k(const uint32_t *w, int u, cu32 *const *in,
-                                             float *acc) {
+                                             cu32 *const *sum, float *acc) {
     const uint32_t magic = pair_magic<FW_Q4_K>();
     const float d = half_bits_to_float(w[0] & 0xFFFFu), dmin = half_bits_to_float(w[0] >> 16);
     const h2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-    const h2 one = {(_Float16)1.0f, (_Float16)1.0f}, k16 = {(_Float16)16.0f, (_Float16)16.0f};
-    uint32_t xa[NTK][16], xb[NTK][16];
-    load_x<NTK>(xa, in, u, 0);
+    // activation pairs of a sub-block plus the block's sum, one block ahead
+    uint32_t xa[NTK][17], xb[NTK][17];
+    auto load_xk = [&](uint32_t (*x)[17], int B) {
+#pragma unroll
+        for (int n = 0; n < NTK; ++n) {
+            cu32 *xp = in[n] + (u * kUnit + 32 * B) / 2;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[n][i] = xp[i];
+            x[n][16] = sum[n][8 * u + B];
+        }
+    };
+    load_xk(xa, 0);
 #define FW_SUB(J, CUR, NXT)                                                          \
     {                                                                                \
-        if (J < 7) load_x<NTK>(NXT, in, u, J + 1);                                   \
+        if (J < 7) load_xk(NXT, J + 1);                                              \
         uint32_t r[16], sc, mn;                                                      \
         q4k_raw_pairs<J % 2>(w + 4 + 8 * (J / 2), r, magic);                         \
         q4k_scale_min<J>(w[1], w[2], w[3], sc, mn);                                  \
         const float ds = d * (float)sc, dm = dmin * (float)mn;                       \
         _Pragma("unroll") for (int n = 0; n < NTK; ++n) {                            \
-            float s = 0.f, xs = 0.f;                                                 \
-            _Pragma("unroll") for (int i = 0; i < 16; ++i) {                         \
-                const h2 xv = as_h2(CUR[n][i]);                                      \
-                s = __builtin_amdgcn_fdot2(as_h2(r[i]) - k1024, xv, s, false);       \
-                /* pairs j = 1, 3 hold x / 16 */                                     \
-                xs = __builtin_amdgcn_fdot2((i & 1) ? k16 : one, xv, xs, false);     \
-            }                                                                        \
+            float s = 0.f;                                                           \
+            _Pragma("unroll") for (int i = 0; i < 16; ++i)                           \
+                s = __builtin_amdgcn_fdot2(as_h2(r[i]) - k1024, as_h2(CUR[n][i]), s, \
+                                           false);                                   \
             acc[n] = fmaf(ds, s, acc[n]);                                            \
-            acc[n] = fmaf(-dm, xs, acc[n]);                                          \
+            acc[n] = fmaf(-dm, __uint_as_float(CUR[n][16]), acc[n]);                 \
         }                                                                            \
     }                                                                                \
     __builtin_amdgcn_sched_barrier(0);
@@ -224,9 +232,9 @@ __device__ __forceinline__ void dot_unit_blocks(const uint32_t *w, int u, cu32 *
 
 template <int Q, int NTK>
 __device__ __forceinline__ void dot_unit(const uint32_t *w, int u, cu32 *const *in,
-                                         float *acc) {
+                                         cu32 *const *sum, float *acc) {
     if constexpr (Q == FW_Q4_K)
-        dot_unit_q4k<NTK>(w, u, in, acc);
+        dot_unit_q4k<NTK>(w, u, in, sum, acc);
     else
         dot_unit_blocks<Q, NTK>(w, u, in, acc);
 }
@@ -236,6 +244,7 @@ __device__ __forceinline__ void dot_unit(const uint32_t *w, int u, cu32 *const *
 struct Item {
     const uint8_t *ta, *tb;
     cu32 *in[kGemvTokens];
+    cu32 *sum[kGemvTokens];   // Q4_K: the rows' 32-element block sums
     int rb, nt, tile;
     bool bad;
 };
@@ -255,9 +264,9 @@ __device__ __forceinline__ void tile_bases(int item, const uint8_t *wa, const ui
 template <bool GU>
 __device__ __forceinline__ Item get_item(int item, const uint8_t *wa, const uint8_t *wb,
                                          const int4 *tiles, const int32_t *sorted,
-                                         const _Float16 *xin, size_t rowbytes, size_t esz,
-                                         int tpg, int K, int k, int P, int shared,
-                                         int shared_rows) {
+                                         const _Float16 *xin, const float *isum,
+                                         size_t rowbytes, size_t esz, int tpg, int K, int k,
+                                         int P, int shared, int shared_rows) {
     Item it;
     const int chunk = item / tpg;
     it.tile = item % tpg;
@@ -284,6 +293,7 @@ __device__ __forceinline__ Item get_item(int item, const uint8_t *wa, const uint
             t = (unsigned)q < (unsigned)P ? q / k : 0;
         }
         it.in[n] = (cu32 *)(xin + (size_t)t * K);
+        it.sum[n] = (cu32 *)(isum + (size_t)t * (K / 32));
     }
     return it;
 }
@@ -321,7 +331,7 @@ __global__ __launch_bounds__(kWave *S) void gemv_kernel(
     const int32_t *__restrict__ sorted, const _Float16 *__restrict__ xin,
     _Float16 *__restrict__ hout, float *__restrict__ yout, int K, int N, int k, int P,
     int tpg, int shared, int shared_rows, int ks, int *__restrict__ split_cnt,
-    float *__restrict__ split_part) {
+    float *__restrict__ split_part, const float *__restrict__ isum, float *__restrict__ osum) {
     constexpr int X4 = QT<Q>::kUnitX4;
     constexpr int NV = GU ? 2 : 1;
     constexpr int NT = kGemvTokens;
@@ -362,8 +372,8 @@ __global__ __launch_bounds__(kWave *S) void gemv_kernel(
     int j = 0;
     for (int i = 0; i < my_items; ++i) {
         const int item = g0 + i * G, ct = item / ks, slice = item % ks;
-        const Item it = get_item<GU>(ct, wa, wbb, tiles, sorted, xin, rowbytes, esz, tpg, K, k,
-                                     P, shared, shared_rows);
+        const Item it = get_item<GU>(ct, wa, wbb, tiles, sorted, xin, isum, rowbytes, esz, tpg,
+                                     K, k, P, shared, shared_rows);
         if (it.bad && threadIdx.x == 0) atomicOr(&hdr->status, FW_STATUS_BAD_PAIR);
         float acc[NV][NT];
 #pragma unroll
@@ -376,8 +386,8 @@ __global__ __launch_bounds__(kWave *S) void gemv_kernel(
             if (js < total) FW_STAGE_NEXT();
             const int u = slice * us + wave + (b / NV) * S;
             float *a = acc[NV == 2 ? (b & 1) : 0];
-            if (it.nt == 1) dot_unit<Q, 1>(w, u, it.in, a);
-            else dot_unit<Q, 2>(w, u, it.in, a);
+            if (it.nt == 1) dot_unit<Q, 1>(w, u, it.in, it.sum, a);
+            else dot_unit<Q, 2>(w, u, it.in, it.sum, a);
         }
         // partial sums of waves 1..S-1 meet wave 0's in LDS, added in wave order
         if (S > 1) {
@@ -438,7 +448,16 @@ __global__ __launch_bounds__(kWave *S) void gemv_kernel(
                         const float gv = acc[0][n], up = acc[NV - 1][n];
                         float a = gv / (1.0f + __expf(-gv)) * up;
                         if (row & 16) a *= 0.0625f;   // pairs j = 1, 3 hold value / 16
-                        hout[r * N + (row & ~31) + pair_pos(row & 31)] = (_Float16)a;
+                        const _Float16 ah = (_Float16)a;
+                        hout[r * N + (row & ~31) + pair_pos(row & 31)] = ah;
+                        if (osum) {
+                            // 32-element block sums of the stored values (a Q4_K
+                            // down projection's min term), in a fixed order
+                            float v = (row & 16) ? 16.0f * (float)ah : (float)ah;
+#pragma unroll
+                            for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o);
+                            if ((lane & 31) == 0) osum[r * (N / 32) + row / 32] = v;
+                        }
                     } else {
                         yout[r * N + row] = acc[0][n];
                     }
@@ -473,16 +492,19 @@ int cu_count() {
     return g_cus;
 }
 
+// isum: the input rows' 32-element block sums (Q4_K weights), osum: where
+// the gate/up pass leaves those of its output rows (a Q4_K down projection);
+// either may be null.
 template <int Q, bool GU, int S, int D>
 void launch_sd(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Float16 *xin,
                _Float16 *hout, float *yout, int K, int N, long long items, int per_cu, int ks,
-               int shared, hipStream_t s) {
+               int shared, const float *isum, float *osum, hipStream_t s) {
     const int tpg = N / kWave;
     const int grid = (int)std::max(1LL, std::min(items * ks, (long long)per_cu * cu_count()));
     gemv_kernel<Q, GU, S, D><<<grid, kWave * S, 0, s>>>(
         wa, wb, (const int4 *)(a.ws + a.L.tiles), (WsHeader *)a.ws, a.sorted, xin, hout, yout,
         K, N, a.d.top_k, a.P, tpg, shared, shared ? a.T : 0, ks, (int *)(a.ws + a.L.split_cnt),
-        (float *)(a.ws + a.L.split_part));
+        (float *)(a.ws + a.L.split_part), isum, osum);
 }
 
 // LDS is the in-flight buffer: about 144 KB of DMA batches per CU keeps HBM
@@ -491,7 +513,7 @@ void launch_sd(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Fl
 template <int Q, bool GU, int S>
 void launch_s(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Float16 *xin,
               _Float16 *hout, float *yout, int K, int N, int max_chunks, int shared,
-              hipStream_t s) {
+              const float *isum, float *osum, hipStream_t s) {
     constexpr int X4 = QT<Q>::kUnitX4;
     const long long items = (long long)max_chunks * (N / kWave);
     // far too few items to occupy the CUs (the shared expert of a one-token
@@ -517,22 +539,22 @@ void launch_s(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Flo
     // 17 KB: depth 2 or 1
     constexpr int DMAX = X4 == 9 ? 4 : 2;
     if (per_cu < 1.5)
-        launch_sd<Q, GU, S, DMAX>(a, wa, wb, xin, hout, yout, K, N, items, fit(DMAX), ks, shared, s);
+        launch_sd<Q, GU, S, DMAX>(a, wa, wb, xin, hout, yout, K, N, items, fit(DMAX), ks, shared, isum, osum, s);
     else if (X4 == 9 && per_cu < 3.0)
-        launch_sd<Q, GU, S, 2>(a, wa, wb, xin, hout, yout, K, N, items, fit(2), ks, shared, s);
+        launch_sd<Q, GU, S, 2>(a, wa, wb, xin, hout, yout, K, N, items, fit(2), ks, shared, isum, osum, s);
     else
-        launch_sd<Q, GU, S, 1>(a, wa, wb, xin, hout, yout, K, N, items, fit(1), ks, shared, s);
+        launch_sd<Q, GU, S, 1>(a, wa, wb, xin, hout, yout, K, N, items, fit(1), ks, shared, isum, osum, s);
 }
 
 template <int Q, bool GU>
 void launch(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Float16 *xin,
             _Float16 *hout, float *yout, int K, int N, int max_chunks, int shared,
-            hipStream_t s) {
+            const float *isum, float *osum, hipStream_t s) {
     switch (pick_split(K / kUnit)) {
-        case 4: launch_s<Q, GU, 4>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, s); break;
-        case 3: launch_s<Q, GU, 3>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, s); break;
-        case 2: launch_s<Q, GU, 2>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, s); break;
-        default: launch_s<Q, GU, 1>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, s); break;
+        case 4: launch_s<Q, GU, 4>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, isum, osum, s); break;
+        case 3: launch_s<Q, GU, 3>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, isum, osum, s); break;
+        case 2: launch_s<Q, GU, 2>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, isum, osum, s); break;
+        default: launch_s<Q, GU, 1>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, isum, osum, s); break;
     }
 }
 
@@ -544,26 +566,37 @@ int max_routed_chunks(const FwdArgs &a) {
 
 }  // namespace
 
+// One GEMV launch of format q (run-time) on the given matrices.
+template <bool GU>
+void launch_q(int q, const FwdArgs &a, const uint8_t *wa, const uint8_t *wb,
+              const _Float16 *xin, _Float16 *hout, float *yout, int K, int N, int max_chunks,
+              int shared, const float *isum, float *osum, hipStream_t s) {
+    if (q == FW_Q4_0)
+        launch<FW_Q4_0, GU>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, nullptr,
+                            nullptr, s);
+    else if (q == FW_Q8_0)
+        launch<FW_Q8_0, GU>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, nullptr,
+                            nullptr, s);
+    else
+        launch<FW_Q4_K, GU>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, isum, osum, s);
+}
+
+// Block sums: x rows (prepare), then h rows of the routed pairs [P][F/32]
+// followed by the shared expert's [T][Fs/32].
 hipError_t launch_gemv_gate_up(const FwdArgs &a, hipStream_t s) {
     const fw_moe_desc &d = a.d;
     const _Float16 *x = (const _Float16 *)(a.ws + a.L.x16);
     _Float16 *h = (_Float16 *)(a.ws + a.L.h);
+    const float *xs = (const float *)(a.ws + a.L.xsum);
+    float *hs = (float *)(a.ws + a.L.hsum);
     const int mc = max_routed_chunks(a);
-    if (d.expert_q == FW_Q4_0)
-        launch<FW_Q4_0, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, mc, 0, s);
-    else if (d.expert_q == FW_Q4_K)
-        launch<FW_Q4_K, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, mc, 0, s);
-    else
-        launch<FW_Q8_0, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, mc, 0, s);
+    launch_q<true>(d.expert_q, a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, mc, 0, xs, hs, s);
     if (d.shared_ffn > 0) {
         _Float16 *hsh = h + (size_t)a.P * d.ffn;
+        float *hssh = hs + (size_t)a.P * (d.ffn / 32);
         const int sc = (a.T + kGemvTokens - 1) / kGemvTokens;
-        if (d.shared_q == FW_Q4_0)
-            launch<FW_Q4_0, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, sc, 1, s);
-        else if (d.shared_q == FW_Q4_K)
-            launch<FW_Q4_K, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, sc, 1, s);
-        else
-            launch<FW_Q8_0, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, sc, 1, s);
+        launch_q<true>(d.shared_q, a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, sc, 1,
+                       xs, hssh, s);
     }
     return hipGetLastError();
 }
@@ -571,24 +604,18 @@ hipError_t launch_gemv_gate_up(const FwdArgs &a, hipStream_t s) {
 hipError_t launch_gemv_down(const FwdArgs &a, hipStream_t s) {
     const fw_moe_desc &d = a.d;
     const _Float16 *h = (const _Float16 *)(a.ws + a.L.h);
+    const float *hs = (const float *)(a.ws + a.L.hsum);
     float *y = (float *)(a.ws + a.L.y);
     const int mc = max_routed_chunks(a);
-    if (d.expert_q == FW_Q4_0)
-        launch<FW_Q4_0, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, mc, 0, s);
-    else if (d.expert_q == FW_Q4_K)
-        launch<FW_Q4_K, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, mc, 0, s);
-    else
-        launch<FW_Q8_0, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, mc, 0, s);
+    launch_q<false>(d.expert_q, a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, mc, 0, hs,
+                    nullptr, s);
     if (d.shared_ffn > 0) {
         const _Float16 *hsh = h + (size_t)a.P * d.ffn;
+        const float *hssh = hs + (size_t)a.P * (d.ffn / 32);
         float *ysh = y + (size_t)a.P * d.hidden;
         const int sc = (a.T + kGemvTokens - 1) / kGemvTokens;
-        if (d.shared_q == FW_Q4_0)
-            launch<FW_Q4_0, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, sc, 1, s);
-        else if (d.shared_q == FW_Q4_K)
-            launch<FW_Q4_K, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, sc, 1, s);
-        else
-            launch<FW_Q8_0, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, sc, 1, s);
+        launch_q<false>(d.shared_q, a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden,
+                        sc, 1, hssh, nullptr, s);
     }
     return hipGetLastError();
 }
