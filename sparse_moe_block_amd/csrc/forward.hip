@@ -11,9 +11,10 @@ constexpr int kPrepThreads = 256;
 // (expert, first row, rows) and the row-tile list -- each active expert's rows
 // cut into tiles of at most tile_rows (the grouped GEMM's 128-row tiles, or the
 // GEMV's token chunks) -- clamping anything out of range
-// (FW_STATUS_BAD_OFFSETS).  Blocks 1..T stage one token row each
-// in fp16 (bf16 values are exact in fp16), in the pair order both kernel
-// families consume (see decode_pairs).
+// (FW_STATUS_BAD_OFFSETS).  The other blocks stage the token rows in fp16
+// (bf16 values are exact in fp16), one 32-element block per thread over the
+// T * H / 32 blocks of x, in the pair order both kernel families consume (see
+// decode_pairs).
 __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(
     const int32_t *__restrict__ offsets, int E, int P, const void *__restrict__ x, int act_bf16,
     int H, int T, int tile_rows, int max_tiles, int4 *__restrict__ active, int4 *__restrict__ tiles,
@@ -79,10 +80,10 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(
         }
         return;
     }
-    const int t = blockIdx.x - 1;
-    if (t >= T) return;
-    // one 32-element block per thread
-    for (int b = tid; b < H / 32; b += kPrepThreads) {
+    const long long idx = (long long)(blockIdx.x - 1) * kPrepThreads + tid;
+    if (idx >= (long long)T * (H / 32)) return;
+    const int t = (int)(idx / (H / 32)), b = (int)(idx % (H / 32));
+    {
         float v[32];
         if (act_bf16) {
             const uint4 *src = (const uint4 *)((const uint16_t *)x + (size_t)t * H + 32 * b);
@@ -175,7 +176,8 @@ hipError_t launch_prepare(const FwdArgs &a, hipStream_t s) {
     // the Q4_K GEMV needs the activation rows' block sums
     const bool sums = a.path == FW_PATH_GEMV &&
                       (a.d.expert_q == FW_Q4_K || (a.d.shared_ffn > 0 && a.d.shared_q == FW_Q4_K));
-    prepare_kernel<<<1 + a.T, kPrepThreads, 0, s>>>(
+    const long long xblocks = (long long)a.T * (a.d.hidden / 32);
+    prepare_kernel<<<1 + (int)((xblocks + kPrepThreads - 1) / kPrepThreads), kPrepThreads, 0, s>>>(
         a.offsets, a.d.n_experts, a.P, a.x, a.d.act_dtype == FW_BF16, a.d.hidden, a.T, tile_rows,
         a.L.max_tiles, (int4 *)(a.ws + a.L.active), (int4 *)(a.ws + a.L.tiles),
         (_Float16 *)(a.ws + a.L.x16), sums ? (float *)(a.ws + a.L.xsum) : nullptr,

@@ -20,12 +20,16 @@
 //   scatter: every chunk workgroup scans the totals into expert_offsets (chunk
 //            0 writes them) and places its pairs at offset + prefix + the
 //            in-chunk rank of step 3.  Same positions as the one-workgroup sort.
+// Up to kPermFoldChunks chunks the scan is folded into the scatter: each
+// chunk workgroup sums the raw counts of the chunks before it itself (a few
+// KB of reads), which saves a launch.
 #include "common.h"
 
 namespace fw {
 namespace {
 
 constexpr int kThreads = 1024;
+constexpr int kPermFoldChunks = 64;
 constexpr int kWaves = kThreads / kWave;
 
 __global__ __launch_bounds__(kThreads) void permute_kernel(
@@ -196,16 +200,32 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int nb, int32_t *__restr
 
 __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
     const int32_t *__restrict__ ids, int P, int E, int nb, const int32_t *__restrict__ cnt_g,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted, int32_t *__restrict__ inv) {
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted, int32_t *__restrict__ inv,
+    int fold) {
     __shared__ int cursor[kMaxExperts];
     __shared__ int wave_tot[kMaxExperts / kWave];
     __shared__ int wcnt[kWaves][kMaxExperts];
     __shared__ int n_valid;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, b = blockIdx.x;
     for (int i = tid; i < kWaves * kMaxExperts; i += kThreads) (&wcnt[0][0])[i] = 0;
-    const int v = tid < E ? cnt_g[(size_t)tid * (nb + 1) + nb] : 0;
+    // this expert's total and its count in the chunks before this one: raw
+    // counts summed here (fold) or the scan kernel's prefix and total
+    int v = 0, before = 0;
+    if (tid < E) {
+        const int32_t *row = cnt_g + (size_t)tid * (nb + 1);
+        if (fold) {
+            for (int c = 0; c < nb; ++c) {
+                const int n = row[c];
+                v += n;
+                before += c < b ? n : 0;
+            }
+        } else {
+            v = row[nb];
+            before = row[b];
+        }
+    }
     const int ex = expert_scan(v, wave_tot, &n_valid);
-    if (tid < E) cursor[tid] = ex + cnt_g[(size_t)tid * (nb + 1) + b];
+    if (tid < E) cursor[tid] = ex + before;
     if (b == 0 && tid < E) offsets[tid] = ex;
     __syncthreads();
     if (b == 0 && tid == 0) offsets[E] = n_valid;
@@ -253,9 +273,10 @@ hipError_t launch_permute(const fw_moe_desc &d, int T, const int32_t *ids, int32
         return hipGetLastError();
     }
     const int nb = perm_blocks(P);
+    const int fold = nb <= kPermFoldChunks;
     perm_count_kernel<<<nb, kThreads, 0, s>>>(ids, P, E, nb, perm, hdr);
-    perm_scan_kernel<<<E, 256, 0, s>>>(nb, perm);
-    perm_scatter_kernel<<<nb, kThreads, 0, s>>>(ids, P, E, nb, perm, offsets, sorted, inv);
+    if (!fold) perm_scan_kernel<<<E, 256, 0, s>>>(nb, perm);
+    perm_scatter_kernel<<<nb, kThreads, 0, s>>>(ids, P, E, nb, perm, offsets, sorted, inv, fold);
     return hipGetLastError();
 }
 

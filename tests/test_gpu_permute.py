@@ -1,6 +1,7 @@
-"""GPU parity of fw_moe_permute on random id tables: both the one-workgroup sort
-(up to 2048 pairs) and the three-kernel sort above it, with ragged last
-chunks, extreme skew, every expert count up to 512 and out-of-range ids."""
+"""GPU parity of fw_moe_permute on random id tables: the one-workgroup sort (up
+to 2048 pairs), the multi-workgroup sort with the scan folded into the scatter
+(up to 64 chunks of 1024 pairs) and with a separate scan kernel, with ragged
+last chunks, extreme skew, every expert count up to 512 and out-of-range ids."""
 
 import numpy as np
 import pytest
@@ -21,6 +22,7 @@ CASES = [
     (128, 8, 2048, "one", 0.0),       # every pair to one expert
     (256, 8, 4096, "zipf", 0.0),      # skewed, 32 chunks
     (128, 8, 3000, "zipf", 0.02),     # skewed, ragged, bad ids
+    (64, 8, 9000, "zipf", 0.001),     # 71 chunks: the separate per-expert scan
 ]
 
 
