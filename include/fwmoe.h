@@ -158,6 +158,7 @@ int fw_moe_permute(const fw_moe_desc *desc, int32_t T, const int32_t *topk_ids,
  * expert path that changed the token stream was rejected).
  * x        [T][H]  act_dtype
  * w_gate, w_up [E][F][H/32] blocks of expert_q;  w_down [E][H][F/32] blocks
+ *          (Q4_K: [E][F][H/256] and [E][H][F/256] super-blocks, the same bytes)
  * ws_gate, ws_up [Fs][H/32], ws_down [H][Fs/32] blocks of shared_q, or NULL
  *          when shared_ffn == 0 (all three required when shared_ffn > 0)
  * topk_w   [T][k] fp32;  expert_offsets, sorted_pairs, inv_pos as produced by
@@ -166,11 +167,15 @@ int fw_moe_permute(const fw_moe_desc *desc, int32_t T, const int32_t *topk_ids,
  * workspace / ws_bytes: at least fw_moe_workspace_size(desc, T) bytes.
  * Numerics: both families round the activations x and the SwiGLU output h to
  * fp16 and accumulate in fp32.  The GEMV family (small T) multiplies the exact
- * weight codes (fp16 holds every Q8_0/Q4_0 code) by fp16 activations in fp32
- * dot products and applies each block's scale in fp32; the GEMM family (large
- * T) contracts on fp16 MFMA with weights dequantised to fp16 (code times scale,
- * one rounding).  Either way a layer output stays within 2e-3 max-abs and 1e-3
- * relative L2 of an fp64 evaluation of the same layer. */
+ * weight codes (fp16 holds every Q8_0/Q4_0/Q4_K code) by fp16 activations in
+ * fp32 dot products and applies each block's scale (Q4_K: each 32-element
+ * sub-block's d * scale, and dmin * min times the sub-block's activation sum)
+ * in fp32; the GEMM family (large T) contracts on fp16 MFMA with weights
+ * dequantised to fp16 (code times scale, or for Q4_K d * scale * q - dmin *
+ * min formed in fp32; one rounding).  Either way a layer output stays within
+ * 2e-3 max-abs and 1e-3 relative L2 of an fp64 evaluation of the same layer.
+ * Q4_K (GGUF K-quant, 144-byte super-blocks of 256 elements) needs H, F and
+ * Fs to be multiples of 256, which every descriptor already is. */
 int fw_moe_forward(const fw_moe_desc *desc, int32_t T, const void *x, const void *w_gate,
                    const void *w_up, const void *w_down, const void *ws_gate,
                    const void *ws_up, const void *ws_down, const float *topk_w,
