@@ -38,7 +38,7 @@ def good_desc(**kw):
 @pytest.mark.parametrize("field,value", [
     ("hidden", 300), ("hidden", 0), ("hidden", 16640), ("n_experts", 0), ("n_experts", 513),
     ("top_k", 0), ("top_k", 17), ("ffn", 100), ("ffn", 0), ("act_dtype", 7), ("expert_q", 5),
-    ("score", 3)])
+    ("expert_q", 3), ("expert_q", -1), ("shared_q", 3), ("score", 3)])
 def test_invalid_descriptors(field, value):
     d = good_desc()
     setattr(d, field, value)
@@ -52,6 +52,9 @@ def test_top_k_above_experts_and_mixed_dtypes():
         fw.FW_EUNSUPPORTED
     assert fw.fw_moe_validate(good_desc()) == fw.FW_OK
     assert fw.fw_moe_validate(good_desc(shared_ffn=2048, shared_q="q8_0")) == fw.FW_OK
+    assert fw.fw_moe_validate(good_desc(expert_q="q4_k")) == fw.FW_OK
+    assert fw.fw_moe_validate(good_desc(expert_q="q4_k", shared_ffn=2048,
+                                        shared_q="q4_k")) == fw.FW_OK
 
 
 def test_workspace_size_grows_with_T():
@@ -113,6 +116,10 @@ def test_permute_validation():
         fw.FW_EINVAL
     assert lib.fw_moe_permute(ctypes.byref(d), 4, 16, 16, 16, 16, 64, 256, None) == \
         fw.FW_EALIGN
+    # above 2048 pairs the sort needs the full workspace (checked before launching)
+    T = 4096 // d.top_k
+    assert lib.fw_moe_permute(ctypes.byref(d), T, 16, 16, 16, 16, 256, 256, None) == \
+        fw.FW_EWORKSPACE
 
 
 def test_status_strings_and_version():
