@@ -153,10 +153,11 @@ __device__ __forceinline__ void dot_block(const uint32_t *w, const uint32_t (*x)
     }
 }
 
-// acc[n] += (row's unit u) . (activation row n's unit u), n < NTK.  The next
-// block's activations are loaded while the current block is consumed (two
-// sets of 16 SGPRs per row); scheduling barriers keep one block's pairs live
-// at a time.
+// Activation sets a unit's dot keeps in SGPRs: one row prefetches three blocks
+// ahead (hiding a scalar-cache miss on long rows), two rows one block ahead
+// (16 SGPRs per row and block, plus the block sum for Q4_K).
+template <int NTK> constexpr int x_sets() { return NTK == 1 ? 4 : 2; }
+
 // Q4_K unit (one super-block): sub-block J is block J of the unit in pair
 // order.  Its exact code pairs meet the activation pairs in fp32 dot products,
 // and the sub-block's scale and min apply once, in fp32:
@@ -169,8 +170,9 @@ __device__ __forceinline__ void dot_unit_q4k(const uint32_t *w, int u, cu32 *con
     const uint32_t magic = pair_magic<FW_Q4_K>();
     const float d = half_bits_to_float(w[0] & 0xFFFFu), dmin = half_bits_to_float(w[0] >> 16);
     const h2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-    // activation pairs of a sub-block plus the block's sum, one block ahead
-    uint32_t xa[NTK][17], xb[NTK][17];
+    // activation pairs of a sub-block plus the block's sum, NB - 1 blocks ahead
+    constexpr int NB = x_sets<NTK>();
+    uint32_t xs[NB][NTK][17];
     auto load_xk = [&](uint32_t (*x)[17], int B) {
 #pragma unroll
         for (int n = 0; n < NTK; ++n) {
@@ -180,10 +182,12 @@ __device__ __forceinline__ void dot_unit_q4k(const uint32_t *w, int u, cu32 *con
             x[n][16] = sum[n][8 * u + B];
         }
     };
-    load_xk(xa, 0);
-#define FW_SUB(J, CUR, NXT)                                                          \
+#pragma unroll
+    for (int j = 0; j < NB - 1; ++j) load_xk(xs[j], j);
+#define FW_SUB(J)                                                                    \
     {                                                                                \
-        if (J < 7) load_xk(NXT, J + 1);                                              \
+        if (J + NB - 1 < 8) load_xk(xs[(J + NB - 1) % NB], J + NB - 1);              \
+        const uint32_t(*CUR)[17] = xs[J % NB];                                       \
         uint32_t r[16], sc, mn;                                                      \
         q4k_raw_pairs<J % 2>(w + 4 + 8 * (J / 2), r, magic);                         \
         q4k_scale_min<J>(w[1], w[2], w[3], sc, mn);                                  \
@@ -198,35 +202,40 @@ __device__ __forceinline__ void dot_unit_q4k(const uint32_t *w, int u, cu32 *con
         }                                                                            \
     }                                                                                \
     __builtin_amdgcn_sched_barrier(0);
-    FW_SUB(0, xa, xb)
-    FW_SUB(1, xb, xa)
-    FW_SUB(2, xa, xb)
-    FW_SUB(3, xb, xa)
-    FW_SUB(4, xa, xb)
-    FW_SUB(5, xb, xa)
-    FW_SUB(6, xa, xb)
-    FW_SUB(7, xb, xa)
+    FW_SUB(0)
+    FW_SUB(1)
+    FW_SUB(2)
+    FW_SUB(3)
+    FW_SUB(4)
+    FW_SUB(5)
+    FW_SUB(6)
+    FW_SUB(7)
 #undef FW_SUB
 }
 
+// acc[n] += (row's unit u) . (activation row n's unit u), n < NTK.  The
+// activations of block B + NB - 1 are loaded while block B is consumed;
+// scheduling barriers keep one block's pairs live at a time.
 template <int Q, int NTK>
 __device__ __forceinline__ void dot_unit_blocks(const uint32_t *w, int u, cu32 *const *in,
                                                 float *acc) {
     const uint32_t magic = pair_magic<Q>();
-    uint32_t xa[NTK][16], xb[NTK][16];
-    load_x<NTK>(xa, in, u, 0);
-#define FW_BLOCK(B, CUR, NXT)                             \
-    if (B < 7) load_x<NTK>(NXT, in, u, B + 1);           \
-    dot_block<Q, NTK, B>(w, CUR, magic, acc);             \
+    constexpr int NB = x_sets<NTK>();
+    uint32_t xs[NB][NTK][16];
+#pragma unroll
+    for (int j = 0; j < NB - 1; ++j) load_x<NTK>(xs[j], in, u, j);
+#define FW_BLOCK(B)                                                        \
+    if (B + NB - 1 < 8) load_x<NTK>(xs[(B + NB - 1) % NB], in, u, B + NB - 1); \
+    dot_block<Q, NTK, B>(w, xs[B % NB], magic, acc);                       \
     __builtin_amdgcn_sched_barrier(0);
-    FW_BLOCK(0, xa, xb)
-    FW_BLOCK(1, xb, xa)
-    FW_BLOCK(2, xa, xb)
-    FW_BLOCK(3, xb, xa)
-    FW_BLOCK(4, xa, xb)
-    FW_BLOCK(5, xb, xa)
-    FW_BLOCK(6, xa, xb)
-    FW_BLOCK(7, xb, xa)
+    FW_BLOCK(0)
+    FW_BLOCK(1)
+    FW_BLOCK(2)
+    FW_BLOCK(3)
+    FW_BLOCK(4)
+    FW_BLOCK(5)
+    FW_BLOCK(6)
+    FW_BLOCK(7)
 #undef FW_BLOCK
 }
 
@@ -535,12 +544,11 @@ void launch_s(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Flo
     const size_t batch = (size_t)S * kWave * X4 * 16;   // one batch of every wavefront
     const size_t red = (size_t)std::max(S - 1, 1) * (GU ? 2 : 1) * kGemvTokens * kWave * 4;
     auto fit = [&](int d) { return (int)std::max<size_t>(1, (160 * 1024) / (batch * d + red)); };
-    // Q4_0 batches are 9 KB per wavefront: depth 4, 2 or 1; Q8_0 batches are
-    // 17 KB: depth 2 or 1
-    constexpr int DMAX = X4 == 9 ? 4 : 2;
-    if (per_cu < 1.5)
-        launch_sd<Q, GU, S, DMAX>(a, wa, wb, xin, hout, yout, K, N, items, fit(DMAX), ks, shared, isum, osum, s);
-    else if (X4 == 9 && per_cu < 3.0)
+    // 9 KB batches (Q4_0, Q4_K): depth 2 between 1.5 and 3 items per CU, else
+    // 1 (deeper pipelines for one-token batches measured slower once the
+    // one-row dots prefetch their activations further ahead); 17 KB batches
+    // (Q8_0): depth 1
+    if (X4 == 9 && per_cu >= 1.5 && per_cu < 3.0)
         launch_sd<Q, GU, S, 2>(a, wa, wb, xin, hout, yout, K, N, items, fit(2), ks, shared, isum, osum, s);
     else
         launch_sd<Q, GU, S, 1>(a, wa, wb, xin, hout, yout, K, N, items, fit(1), ks, shared, isum, osum, s);
