@@ -12,6 +12,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Up to this many tokens the bf16 logits run one wavefront per dot product.
+constexpr int kLogitsDotMaxT = 16;
+
 // bf16 logits on MFMA.  A workgroup owns 16*MT tokens x 16*NE experts; its NW
 // waves split the reduction dimension H into interleaved 32-wide steps (wave
 // w takes steps w, w + NW, ...), issue the loads of U steps before their
@@ -101,6 +104,45 @@ __global__ __launch_bounds__(NW *kWave) void logits_bf16_kernel(
                 if (tt < T) logits[(size_t)tt * E + e] = v[i] + b;
             }
         }
+}
+
+// bf16 logits for a few tokens: one wavefront per (token, expert) dot product,
+// so the E x H router spreads over E * T wavefronts (a 16-token, 128-expert
+// batch: 512 workgroups) instead of E / 16 workgroups.  Each lane loads NC
+// 16-byte chunks of the router row and of the token row at once (all in
+// flight together), sums their exact bf16 x bf16 products in fp32 in element
+// order, and the wavefront's lanes are added in a fixed butterfly order.
+template <int NC>
+__global__ __launch_bounds__(256) void logits_dot_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
+    const float *__restrict__ bias, float *__restrict__ logits, int T, int H, int E) {
+    const int lane = threadIdx.x % kWave;
+    const int pair = blockIdx.x * 4 + wave_id();   // (token, expert)
+    if (pair >= T * E) return;
+    const int t = pair / E, e = pair % E;
+    const uint4 *wp = (const uint4 *)(wr + (size_t)e * H) + lane;
+    const uint4 *xp = (const uint4 *)(x + (size_t)t * H) + lane;
+    uint4 wv[NC], xv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        wv[c] = wp[c * kWave];
+        xv[c] = xp[c * kWave];
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const uint32_t a[4] = {wv[c].x, wv[c].y, wv[c].z, wv[c].w};
+        const uint32_t b[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc = fmaf(__uint_as_float(a[i] << 16), __uint_as_float(b[i] << 16), acc);
+            acc = fmaf(__uint_as_float(a[i] & 0xFFFF0000u), __uint_as_float(b[i] & 0xFFFF0000u),
+                       acc);
+        }
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) logits[(size_t)t * E + e] = acc + (bias ? bias[e] : 0.f);
 }
 
 // fp32 logits (small layers): one thread per (token, expert), sequential sum.
@@ -232,6 +274,20 @@ hipError_t launch_logits(const fw_moe_desc &d, int T, const void *x, const void 
         const int n = T * E;
         logits_f32_kernel<<<(n + 255) / 256, 256, 0, s>>>((const float *)x, (const float *)wr,
                                                           bias, logits, T, H, E);
+    } else if (T <= kLogitsDotMaxT && H % 512 == 0 && H <= 512 * 16) {
+        // 16-byte chunks per lane: H / 512
+        const int blocks = (T * E + 3) / 4;
+        switch (H / 512) {
+#define FW_LD(NC)                                                                              \
+    case NC:                                                                                   \
+        logits_dot_kernel<NC><<<blocks, 256, 0, s>>>(xb, wb, bias, logits, T, H, E);           \
+        break;
+            FW_LD(1) FW_LD(2) FW_LD(3) FW_LD(4) FW_LD(5) FW_LD(6) FW_LD(7) FW_LD(8)
+            FW_LD(9) FW_LD(10) FW_LD(11) FW_LD(12) FW_LD(13) FW_LD(14) FW_LD(15) FW_LD(16)
+#undef FW_LD
+            default:
+                return hipErrorInvalidValue;
+        }
     } else if (T <= kGemvMaxT) {
         dim3 grid((T + 15) / 16, (E + 15) / 16);
         logits_bf16_kernel<1, 1, 16, 4><<<grid, 16 * kWave, 0, s>>>(xb, wb, bias, logits, T, H, E);
