@@ -66,6 +66,12 @@ def parse():
                     help="instead of benchmarking: turn two rocprofv3 --pmc output "
                          "directories (FETCH_SIZE, WRITE_SIZE) of this workload run "
                          "with --copy-mib into profiles/traffic_<kernel>_<workload>.json")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the one-line benchmark: the hidden-4096 / 64-expert "
+                         "top-4 sweep layer over T = 1..8192 with Q8_0 and Q4_0 experts "
+                         "and uniform or Zipf(1.3) routing, both kernel families timed "
+                         "at each T; one JSON line per point, then the decode-to-prefill "
+                         "crossover of each variant")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a negation "
                          "kernel, the reference that scales hardware byte counters)")
@@ -81,6 +87,9 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported "
               f"(the layer is measured on one MI355X)", file=sys.stderr)
         sys.exit(2)
+    if a.sweep:
+        sweep(a)
+        return
     cfg, T, copies = WORKLOADS[a.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -238,6 +247,104 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def sweep(a):
+    """Step time of the sweep layer with each kernel family forced, over
+    T = 1, 2, 4, ..., 8192.  Each step is a HIP-graph replay of route ->
+    permute -> forward on one of 8 weight copies (cold Infinity Cache, as in
+    the main benchmark).  The GEMV family is timed while it is at most three
+    times slower than the grouped GEMM; the crossover of a variant is the
+    smallest T from which the GEMM step is faster at every larger T."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    copies = 8
+    steps, warm = min(a.steps, 30), min(a.warmup, 5)
+    summary = []
+    for base in (moegen.SWEEP_Q8, moegen.SWEEP_Q4):
+        for zipf in (None, 1.3):
+            cfg = base.with_(zipf=zipf)
+            L = moegen.make_layer(cfg, device=dev)
+            layers = [L] + [moegen.Layer(cfg, L.router, L.bias, L.w_gate.clone(),
+                                         L.w_up.clone(), L.w_down.clone(), None, None, None)
+                            for _ in range(copies - 1)]
+            E, k, H = cfg.n_experts, cfg.top_k, cfg.hidden
+            times = {}
+            gemv_on = True
+            for T in cfg.tokens:
+                x = moegen.make_x(cfg, T, device=dev)
+                P = T * k
+                bufs = dict(logits=torch.empty(T, E, device=dev),
+                            ids=torch.empty(T, k, dtype=torch.int32, device=dev),
+                            w=torch.empty(T, k, device=dev),
+                            off=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                            sp=torch.empty(P, dtype=torch.int32, device=dev),
+                            inv=torch.empty(P, dtype=torch.int32, device=dev),
+                            out=torch.empty(T, H, device=dev))
+                row = {"variant": f"{cfg.expert_q} {'zipf1.3' if zipf else 'uniform'}",
+                       "T": T}
+                for path in ("gemv", "gemm"):
+                    if path == "gemv" and not gemv_on:
+                        continue
+                    desc = fw.make_desc(H, E, k, cfg.ffn, 0, cfg.act_dtype, cfg.router_dtype,
+                                        cfg.expert_q, cfg.shared_q, cfg.score, path)
+                    ws = torch.empty(fw.fw_moe_workspace_size(desc, T), dtype=torch.uint8,
+                                     device=dev)
+                    fw.fw_moe_clear_status(ws)
+                    b = bufs
+
+                    def step(i, s):
+                        Li = layers[i % copies]
+                        fw.fw_moe_route(desc, T, x, Li.router, Li.bias, None, b["logits"],
+                                        b["ids"], b["w"], s)
+                        fw.fw_moe_permute(desc, T, b["ids"], b["off"], b["sp"], b["inv"], ws,
+                                          stream=s)
+                        fw.fw_moe_forward(desc, T, x, Li.w_gate, Li.w_up, Li.w_down, None,
+                                          None, None, b["w"], b["off"], b["sp"], b["inv"],
+                                          b["out"], ws, stream=s)
+
+                    step(0, torch.cuda.current_stream())
+                    torch.cuda.synchronize()
+                    assert fw.fw_moe_read_status(ws) == 0
+                    graphs = []
+                    for c in range(copies):
+                        g = torch.cuda.CUDAGraph()
+                        with torch.cuda.graph(g):
+                            step(c, torch.cuda.current_stream())
+                        graphs.append(g)
+                    for i in range(warm):
+                        graphs[i % copies].replay()
+                    torch.cuda.synchronize()
+                    g0 = torch.cuda.Event(enable_timing=True)
+                    g1 = torch.cuda.Event(enable_timing=True)
+                    g0.record()
+                    for i in range(steps):
+                        graphs[(warm + i) % copies].replay()
+                    g1.record()
+                    torch.cuda.synchronize()
+                    ms = g0.elapsed_time(g1) / steps
+                    row[f"{path}_us"] = round(ms * 1e3, 1)
+                    row[f"{path}_tok_s"] = round(T / (ms * 1e-3))
+                    del graphs, ws
+                times[T] = row
+                if "gemv_us" in row and row["gemv_us"] > 3 * row["gemm_us"]:
+                    gemv_on = False
+                row["auto"] = "gemv" if fw.fw_moe_forward_path(
+                    fw.make_desc(H, E, k, cfg.ffn, 0, cfg.act_dtype, cfg.router_dtype,
+                                 cfg.expert_q, cfg.shared_q, cfg.score, "auto"), T) == \
+                    fw.FW_PATH_GEMV else "gemm"
+                print(json.dumps(row), flush=True)
+            cross = None
+            for T in sorted(times, reverse=True):
+                r = times[T]
+                if "gemv_us" in r and r["gemv_us"] <= r["gemm_us"]:
+                    break
+                cross = T
+            summary.append({"variant": row["variant"], "crossover_T": cross})
+            del layers, L
+            torch.cuda.empty_cache()
+    print(json.dumps({"sweep": "hidden 4096, 64 experts top-4, ffn 1536",
+                      "crossover": summary}), flush=True)
+
+
 def source_hash(kernel):
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES[kernel]:
@@ -278,7 +385,10 @@ def reduce_counters(a):
     import csv
     import glob
     cfg, T, _ = WORKLOADS[a.workload]
-    path_gemv = T <= 64 if a.path == "auto" else a.path == "gemv"
+    desc = fw.make_desc(cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn, cfg.shared_ffn,
+                        cfg.act_dtype, cfg.router_dtype, cfg.expert_q, cfg.shared_q,
+                        cfg.score, a.path)
+    path_gemv = fw.fw_moe_forward_path(desc, T) == fw.FW_PATH_GEMV
     kernel = "gemv_kernel<gate/up>" if path_gemv else "gemm2_kernel<gate/up>"
     frag = KERNELS[kernel][1] + {"q8_0": "0", "q4_0": "1", "q4_k": "2"}[cfg.expert_q] + "ELb1E"
 

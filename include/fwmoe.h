@@ -184,7 +184,9 @@ int fw_moe_forward(const fw_moe_desc *desc, int32_t T, const void *x, const void
                    void *stream);
 
 /* The forward kernel family AUTO picks for T tokens (FW_PATH_GEMV or
- * FW_PATH_GEMM), or a negative error for an invalid descriptor. */
+ * FW_PATH_GEMM), or a negative error for an invalid descriptor.  AUTO takes
+ * the GEMV family up to T = 32 and the grouped GEMM above (measured crossover
+ * of the hidden-4096, 64-expert top-4 layer: between 32 and 64 tokens). */
 int fw_moe_forward_path(const fw_moe_desc *desc, int32_t T);
 
 /* Reset the workspace's status word (a fill kernel on `stream`). */

@@ -288,7 +288,7 @@ hipError_t launch_logits(const fw_moe_desc &d, int T, const void *x, const void 
             default:
                 return hipErrorInvalidValue;
         }
-    } else if (T <= kGemvMaxT) {
+    } else if (T <= kLogitsTileMaxT) {
         dim3 grid((T + 15) / 16, (E + 15) / 16);
         logits_bf16_kernel<1, 1, 16, 4><<<grid, 16 * kWave, 0, s>>>(xb, wb, bias, logits, T, H, E);
     } else if (E >= 64 && (long long)((T + 31) / 32) * ((E + 63) / 64) >= 512) {

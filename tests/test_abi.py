@@ -68,6 +68,9 @@ def test_path_choice():
     d = good_desc()
     assert fw.fw_moe_forward_path(d, 1) == fw.FW_PATH_GEMV
     assert fw.fw_moe_forward_path(d, 4096) == fw.FW_PATH_GEMM
+    # the measured decode-to-prefill crossover of the sweep layer lies between 32 and 64
+    assert fw.fw_moe_forward_path(d, 32) == fw.FW_PATH_GEMV
+    assert fw.fw_moe_forward_path(d, 33) == fw.FW_PATH_GEMM
     assert fw.fw_moe_forward_path(good_desc(path="gemv"), 4096) == fw.FW_PATH_GEMV
     assert fw.fw_moe_forward_path(good_desc(path="gemm"), 1) == fw.FW_PATH_GEMM
 
