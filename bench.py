@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode16", choices=sorted(WORKLOADS))
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
+    ap.add_argument("--three-calls", action="store_true",
+                    help="time the layer as fw_moe_route + fw_moe_permute + fw_moe_forward "
+                         "instead of the one fw_moe_layer call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="time direct launches only (value from the direct loop)")
@@ -119,10 +122,15 @@ def main():
 
     def step(i, s=stream):
         Li = layers[i % copies]
-        fw.fw_moe_route(desc, T, x, Li.router, Li.bias, None, logits, ids, w, s)
-        fw.fw_moe_permute(desc, T, ids, off, sp, inv, ws, stream=s)
-        fw.fw_moe_forward(desc, T, x, Li.w_gate, Li.w_up, Li.w_down, Li.s_gate, Li.s_up,
-                          Li.s_down, w, off, sp, inv, out, ws, stream=s)
+        if a.three_calls:
+            fw.fw_moe_route(desc, T, x, Li.router, Li.bias, None, logits, ids, w, s)
+            fw.fw_moe_permute(desc, T, ids, off, sp, inv, ws, stream=s)
+            fw.fw_moe_forward(desc, T, x, Li.w_gate, Li.w_up, Li.w_down, Li.s_gate, Li.s_up,
+                              Li.s_down, w, off, sp, inv, out, ws, stream=s)
+        else:
+            fw.fw_moe_layer(desc, T, x, Li.router, Li.bias, Li.w_gate, Li.w_up, Li.w_down,
+                            Li.s_gate, Li.s_up, Li.s_down, logits, ids, w, off, sp, inv, out,
+                            ws, stream=s)
 
     if a.copy_mib:
         # reads and writes exactly copy_mib MiB in one elementwise kernel
@@ -214,6 +222,8 @@ def main():
                 "algorithmic_flops": gu_alg}
     layer_bytes = (n_active * cfg.expert_bytes + cfg.shared_bytes + cfg.router_bytes +
                    cfg.act_bytes(T) + T * H * 4)
+    fused = (not a.three_calls and path == fw.FW_PATH_GEMV and P <= 2048)
+    stage0 = "front (top-k + permute + staging)" if fused else "prepare"
     layer_flops = 6 * P * H * cfg.ffn + 6 * T * H * cfg.shared_ffn + 2 * T * H * E
 
     roof["traffic"] = traffic(a.workload, roof)
@@ -235,11 +245,12 @@ def main():
                    "tokens": T, "active_experts": n_active, "weight_copies": copies,
                    "path": "gemv" if path == fw.FW_PATH_GEMV else "gemm"},
         "timing": "hip-graph replay per step" if graph_ms is not None else "direct launches",
+        "entry": "three calls" if a.three_calls else "fw_moe_layer",
         "direct_ms_per_step": direct_ms,
         "layer_GBps": layer_bytes / (ms * 1e-3) / 1e9,
         "layer_TFLOPs": layer_flops / (ms * 1e-3) / 1e12,
         "stage_us": {n: round(float(v) * 1e3, 2) for n, v in
-                     zip(["prepare", "gate_up", "down", "combine"], stage_avg)},
+                     zip([stage0, "gate_up", "down", "combine"], stage_avg)},
         "roofline": roof,
     }
     if not a.no_cpu_baseline:
@@ -293,13 +304,10 @@ def sweep(a):
 
                     def step(i, s):
                         Li = layers[i % copies]
-                        fw.fw_moe_route(desc, T, x, Li.router, Li.bias, None, b["logits"],
-                                        b["ids"], b["w"], s)
-                        fw.fw_moe_permute(desc, T, b["ids"], b["off"], b["sp"], b["inv"], ws,
-                                          stream=s)
-                        fw.fw_moe_forward(desc, T, x, Li.w_gate, Li.w_up, Li.w_down, None,
-                                          None, None, b["w"], b["off"], b["sp"], b["inv"],
-                                          b["out"], ws, stream=s)
+                        fw.fw_moe_layer(desc, T, x, Li.router, Li.bias, Li.w_gate, Li.w_up,
+                                        Li.w_down, None, None, None, b["logits"], b["ids"],
+                                        b["w"], b["off"], b["sp"], b["inv"], b["out"], ws,
+                                        stream=s)
 
                     step(0, torch.cuda.current_stream())
                     torch.cuda.synchronize()

@@ -183,6 +183,31 @@ int fw_moe_forward(const fw_moe_desc *desc, int32_t T, const void *x, const void
                    const int32_t *inv_pos, float *out, void *workspace, size_t ws_bytes,
                    void *stream);
 
+/* The whole layer in one call: fw_moe_route (logits computed, logits_in
+ * NULL), fw_moe_permute and fw_moe_forward on the same arguments, with the
+ * same results bit for bit (the route of fw_moe_route, the sort of
+ * fw_moe_permute, the expert FFNs and combine of fw_moe_forward, as stated
+ * above).  When the forward runs the GEMV family (AUTO up to T = 32, or
+ * FW_PATH_GEMV) and T*k <= 2048, the top-k, the permutation and the forward's
+ * activation staging run as one kernel, so a decode step is five launches
+ * instead of seven; otherwise the launches are those of the three calls.
+ * Persistent, single-launch decode kernels are listed among the pages' open
+ * work (Flyweight 0.2.0 "Current limitations").
+ * Arguments: as in the three calls.  logits [T][E] fp32 out, topk_ids
+ * [T][k] int32 out, topk_w [T][k] fp32 out, expert_offsets [E+1],
+ * sorted_pairs [T*k] and inv_pos [T*k] int32 out are caller-owned device
+ * buffers, all required (the layer's intermediate results stay readable);
+ * workspace / ws_bytes: at least fw_moe_workspace_size(desc, T) bytes.
+ * Every argument is checked before the first launch: an error return means
+ * nothing was enqueued.  Asynchronous on `stream`, allocation-free, capturable
+ * in a HIP graph. */
+int fw_moe_layer(const fw_moe_desc *desc, int32_t T, const void *x, const void *router_w,
+                 const float *logit_bias, const void *w_gate, const void *w_up,
+                 const void *w_down, const void *ws_gate, const void *ws_up,
+                 const void *ws_down, float *logits, int32_t *topk_ids, float *topk_w,
+                 int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *inv_pos, float *out,
+                 void *workspace, size_t ws_bytes, void *stream);
+
 /* The forward kernel family AUTO picks for T tokens (FW_PATH_GEMV or
  * FW_PATH_GEMM), or a negative error for an invalid descriptor.  AUTO takes
  * the GEMV family up to T = 32 and the grouped GEMM above (measured crossover
@@ -203,7 +228,9 @@ const char *fw_moe_status_string(int status);
  * FW_N_STAGE_EVENTS hipEvent_t handles; every later fw_moe_forward records
  * events[0] before its first kernel and events[s+1] after stage s, s in
  * {0: prepare, 1: gate/up projection, 2: down projection, 3: combine}, on its
- * stream.  NULL turns recording off.  Process-wide and not thread-safe. */
+ * stream; fw_moe_layer records the same five (stage 0 is then the fused
+ * front end or the staging kernel; the logits, top-k and permutation
+ * launches that precede it fall outside).  NULL turns recording off.  Process-wide and not thread-safe. */
 enum { FW_N_STAGE_EVENTS = 5 };
 int fw_moe_set_stage_events(void *const *events);
 

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfwmoe.so")
-SOURCES = ["abi.hip", "route.hip", "permute.hip", "forward.hip", "gemv.hip", "gemm.hip", "gemm2.hip"]
+SOURCES = ["abi.hip", "route.hip", "permute.hip", "forward.hip", "gemv.hip", "gemm.hip", "gemm2.hip", "layer.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall",

@@ -82,6 +82,81 @@ int resolve_path(const fw_moe_desc *d, int32_t T) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FW_OK : FW_EHIP; }
 
+// Checks fw_moe_forward's arguments (desc and T already checked, T > 0) and
+// fills the launch arguments.
+int forward_args(const fw_moe_desc *desc, int32_t T, const void *x, const void *w_gate,
+                 const void *w_up, const void *w_down, const void *ws_gate, const void *ws_up,
+                 const void *ws_down, const float *topk_w, const int32_t *expert_offsets,
+                 const int32_t *sorted_pairs, const int32_t *inv_pos, float *out,
+                 void *workspace, size_t ws_bytes, FwdArgs *out_args) {
+    const bool shared = desc->shared_ffn > 0;
+    if (!x || !w_gate || !w_up || !w_down || !topk_w || !expert_offsets || !sorted_pairs ||
+        !inv_pos || !out || !workspace)
+        return FW_EINVAL;
+    if (shared && (!ws_gate || !ws_up || !ws_down)) return FW_EINVAL;
+    const void *ptrs[] = {x, w_gate, w_up, w_down, topk_w, expert_offsets, sorted_pairs,
+                          inv_pos, out};
+    for (const void *p : ptrs)
+        if (!al16(p)) return FW_EALIGN;
+    if (shared && (!al16(ws_gate) || !al16(ws_up) || !al16(ws_down))) return FW_EALIGN;
+    if (!al256(workspace)) return FW_EALIGN;
+    FwdArgs &a = *out_args;
+    a.d = *desc;
+    a.T = T;
+    a.P = T * desc->top_k;
+    a.path = resolve_path(desc, T);
+    a.L = ws_layout(*desc, T);
+    if (ws_bytes < a.L.total) return FW_EWORKSPACE;
+    a.x = x;
+    a.wg = (const uint8_t *)w_gate;
+    a.wu = (const uint8_t *)w_up;
+    a.wd = (const uint8_t *)w_down;
+    a.sg = shared ? (const uint8_t *)ws_gate : nullptr;
+    a.su = shared ? (const uint8_t *)ws_up : nullptr;
+    a.sd = shared ? (const uint8_t *)ws_down : nullptr;
+    a.topk_w = topk_w;
+    a.offsets = expert_offsets;
+    a.sorted = sorted_pairs;
+    a.inv = inv_pos;
+    a.out = out;
+    a.ws = (char *)workspace;
+    return FW_OK;
+}
+
+// The routing buffers the fused decode front end writes.
+struct FrontArgs {
+    const float *logits;
+    int32_t *ids;
+    float *w;
+    int32_t *offsets, *sorted, *inv;
+};
+
+// The forward's launches: staging (or, with `front`, the fused top-k +
+// permutation + staging kernel), gate/up, down, combine; stage events around
+// each when they are on.
+int enqueue_forward(const FwdArgs &a, const FrontArgs *front, hipStream_t s) {
+    int rc;
+    const bool ev = g_events_on;
+    if (ev) (void)hipEventRecord(g_events[0], s);
+    rc = hip_status(front ? launch_decode_front(a, front->logits, front->ids, front->w,
+                                                front->offsets, front->sorted, front->inv, s)
+                          : launch_prepare(a, s));
+    if (rc != FW_OK) return rc;
+    if (ev) (void)hipEventRecord(g_events[1], s);
+    const bool gemm = a.path == FW_PATH_GEMM;
+    rc = hip_status(gemm ? (kUseGemm2 ? launch_gemm2_gate_up(a, s) : launch_gemm_gate_up(a, s))
+                         : launch_gemv_gate_up(a, s));
+    if (rc != FW_OK) return rc;
+    if (ev) (void)hipEventRecord(g_events[2], s);
+    rc = hip_status(gemm ? (kUseGemm2 ? launch_gemm2_down(a, s) : launch_gemm_down(a, s))
+                         : launch_gemv_down(a, s));
+    if (rc != FW_OK) return rc;
+    if (ev) (void)hipEventRecord(g_events[3], s);
+    if ((rc = hip_status(launch_combine(a, s))) != FW_OK) return rc;
+    if (ev) (void)hipEventRecord(g_events[4], s);
+    return FW_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -161,54 +236,45 @@ int fw_moe_forward(const fw_moe_desc *desc, int32_t T, const void *x, const void
     if (rc != FW_OK) return rc;
     if ((rc = check_T(desc, T)) != FW_OK) return rc;
     if (T == 0) return FW_OK;
-    const bool shared = desc->shared_ffn > 0;
-    if (!x || !w_gate || !w_up || !w_down || !topk_w || !expert_offsets || !sorted_pairs ||
-        !inv_pos || !out || !workspace)
-        return FW_EINVAL;
-    if (shared && (!ws_gate || !ws_up || !ws_down)) return FW_EINVAL;
-    const void *ptrs[] = {x, w_gate, w_up, w_down, topk_w, expert_offsets, sorted_pairs,
-                          inv_pos, out};
-    for (const void *p : ptrs)
-        if (!al16(p)) return FW_EALIGN;
-    if (shared && (!al16(ws_gate) || !al16(ws_up) || !al16(ws_down))) return FW_EALIGN;
-    if (!al256(workspace)) return FW_EALIGN;
     FwdArgs a;
-    a.d = *desc;
-    a.T = T;
-    a.P = T * desc->top_k;
-    a.path = resolve_path(desc, T);
-    a.L = ws_layout(*desc, T);
-    if (ws_bytes < a.L.total) return FW_EWORKSPACE;
-    a.x = x;
-    a.wg = (const uint8_t *)w_gate;
-    a.wu = (const uint8_t *)w_up;
-    a.wd = (const uint8_t *)w_down;
-    a.sg = shared ? (const uint8_t *)ws_gate : nullptr;
-    a.su = shared ? (const uint8_t *)ws_up : nullptr;
-    a.sd = shared ? (const uint8_t *)ws_down : nullptr;
-    a.topk_w = topk_w;
-    a.offsets = expert_offsets;
-    a.sorted = sorted_pairs;
-    a.inv = inv_pos;
-    a.out = out;
-    a.ws = (char *)workspace;
+    rc = forward_args(desc, T, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, topk_w,
+                      expert_offsets, sorted_pairs, inv_pos, out, workspace, ws_bytes, &a);
+    if (rc != FW_OK) return rc;
+    return enqueue_forward(a, nullptr, (hipStream_t)stream);
+}
+
+int fw_moe_layer(const fw_moe_desc *desc, int32_t T, const void *x, const void *router_w,
+                 const float *logit_bias, const void *w_gate, const void *w_up,
+                 const void *w_down, const void *ws_gate, const void *ws_up,
+                 const void *ws_down, float *logits, int32_t *topk_ids, float *topk_w,
+                 int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *inv_pos, float *out,
+                 void *workspace, size_t ws_bytes, void *stream) {
+    int rc = check_desc(desc);
+    if (rc != FW_OK) return rc;
+    if ((rc = check_T(desc, T)) != FW_OK) return rc;
+    if (T == 0) return FW_OK;
+    // every argument of the three stages is checked before anything is enqueued
+    if (!router_w || !logits || !topk_ids || !topk_w || !expert_offsets) return FW_EINVAL;
+    if (!al16(router_w) || !al16(logits) || !al16(topk_ids) || (logit_bias && !al16(logit_bias)))
+        return FW_EALIGN;
+    FwdArgs a;
+    rc = forward_args(desc, T, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, topk_w,
+                      expert_offsets, sorted_pairs, inv_pos, out, workspace, ws_bytes, &a);
+    if (rc != FW_OK) return rc;
     hipStream_t s = (hipStream_t)stream;
-    const bool ev = g_events_on;
-    if (ev) (void)hipEventRecord(g_events[0], s);
-    if ((rc = hip_status(launch_prepare(a, s))) != FW_OK) return rc;
-    if (ev) (void)hipEventRecord(g_events[1], s);
-    const bool gemm = a.path == FW_PATH_GEMM;
-    rc = hip_status(gemm ? (kUseGemm2 ? launch_gemm2_gate_up(a, s) : launch_gemm_gate_up(a, s))
-                         : launch_gemv_gate_up(a, s));
+    if ((rc = hip_status(launch_logits(*desc, T, x, router_w, logit_bias, logits, s))) != FW_OK)
+        return rc;
+    if (decode_front_fits(*desc, T, a.path)) {
+        FrontArgs f{logits, topk_ids, topk_w, expert_offsets, sorted_pairs, inv_pos};
+        return enqueue_forward(a, &f, s);
+    }
+    if ((rc = hip_status(launch_topk(*desc, T, logits, topk_ids, topk_w, s))) != FW_OK) return rc;
+    const long long P = (long long)T * desc->top_k;
+    int32_t *perm = P > kPermOneBlockMaxP ? (int32_t *)(a.ws + a.L.perm) : nullptr;
+    rc = hip_status(launch_permute(*desc, T, topk_ids, expert_offsets, sorted_pairs, inv_pos,
+                                   (WsHeader *)workspace, perm, s));
     if (rc != FW_OK) return rc;
-    if (ev) (void)hipEventRecord(g_events[2], s);
-    rc = hip_status(gemm ? (kUseGemm2 ? launch_gemm2_down(a, s) : launch_gemm_down(a, s))
-                         : launch_gemv_down(a, s));
-    if (rc != FW_OK) return rc;
-    if (ev) (void)hipEventRecord(g_events[3], s);
-    if ((rc = hip_status(launch_combine(a, s))) != FW_OK) return rc;
-    if (ev) (void)hipEventRecord(g_events[4], s);
-    return FW_OK;
+    return enqueue_forward(a, nullptr, s);
 }
 
 int fw_moe_clear_status(void *workspace, void *stream) {

@@ -290,5 +290,11 @@ hipError_t launch_gemm_down(const FwdArgs &a, hipStream_t s);
 hipError_t launch_gemm2_gate_up(const FwdArgs &a, hipStream_t s);
 hipError_t launch_gemm2_down(const FwdArgs &a, hipStream_t s);
 hipError_t launch_combine(const FwdArgs &a, hipStream_t s);
+// fw_moe_layer's fused decode front end (top-k + permutation + staging in one
+// launch): taken when the forward runs the GEMV family and the pairs fit the
+// one-workgroup permutation.
+bool decode_front_fits(const fw_moe_desc &d, int T, int path);
+hipError_t launch_decode_front(const FwdArgs &a, const float *logits, int32_t *ids, float *w,
+                               int32_t *offsets, int32_t *sorted, int32_t *inv, hipStream_t s);
 
 }  // namespace fw

@@ -1,11 +1,10 @@
 // Forward, stages 0 and 3: the per-call schedule / activation staging, and the
 // deterministic per-token weighted combine.
 #include "common.h"
+#include "stages.h"
 
 namespace fw {
 namespace {
-
-constexpr int kPrepThreads = 256;
 
 // Block 0 turns expert_offsets into the list of active experts
 // (expert, first row, rows) and the row-tile list -- each active expert's rows
@@ -20,119 +19,13 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(
     int H, int T, int tile_rows, int max_tiles, int4 *__restrict__ active, int4 *__restrict__ tiles,
     _Float16 *__restrict__ x16, float *__restrict__ xsum, int *__restrict__ split_cnt,
     WsHeader *__restrict__ hdr) {
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     if (blockIdx.x == 0) {
-        // the GEMV's split-K arrival counters start every call at zero
-        for (int i = tid; i < kSplitTiles; i += kPrepThreads) split_cnt[i] = 0;
-        __shared__ int wsum_a[kPrepThreads / kWave], wsum_t[kPrepThreads / kWave];
-        // each thread owns experts 2*tid and 2*tid+1
-        int beg[2], cnt[2], na = 0, nt = 0;
-        bool bad = false;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int e = 2 * tid + i;
-            beg[i] = cnt[i] = 0;
-            if (e < E) {
-                int b = offsets[e], n = offsets[e + 1];
-                if (e == 0 && b != 0) bad = true;
-                if (b < 0 || b > P || n < b || n > P) bad = true;
-                b = min(max(b, 0), P);
-                n = min(max(n, b), P);
-                beg[i] = b;
-                cnt[i] = n - b;
-                na += cnt[i] > 0;
-                nt += (cnt[i] + tile_rows - 1) / tile_rows;
-            }
-        }
-        if (bad) atomicOr(&hdr->status, FW_STATUS_BAD_OFFSETS);
-        int ia = na, it = nt;   // inclusive scans
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int oa = __shfl_up(ia, off), ot = __shfl_up(it, off);
-            if (lane >= off) {
-                ia += oa;
-                it += ot;
-            }
-        }
-        if (lane == kWave - 1) {
-            wsum_a[wave] = ia;
-            wsum_t[wave] = it;
-        }
-        __syncthreads();
-        int ba = 0, bt = 0;
-        for (int w = 0; w < wave; ++w) {
-            ba += wsum_a[w];
-            bt += wsum_t[w];
-        }
-        int pa = ba + ia - na, pt = bt + it - nt;   // exclusive positions
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            if (cnt[i] > 0) {
-                active[pa++] = int4{2 * tid + i, beg[i], cnt[i], 0};
-                // bounded: overlapping (invalid) offsets can claim more
-                for (int m = 0; m < cnt[i] && pt < max_tiles; m += tile_rows)
-                    tiles[pt++] = int4{2 * tid + i, beg[i] + m, min(tile_rows, cnt[i] - m), 0};
-            }
-        }
-        if (tid == kPrepThreads - 1) {
-            hdr->n_active = ba + ia;
-            hdr->n_tiles = min(bt + it, max_tiles);
-        }
+        build_schedule(offsets, E, P, tile_rows, max_tiles, active, tiles, split_cnt, hdr);
         return;
     }
-    const long long idx = (long long)(blockIdx.x - 1) * kPrepThreads + tid;
+    const long long idx = (long long)(blockIdx.x - 1) * kPrepThreads + threadIdx.x;
     if (idx >= (long long)T * (H / 32)) return;
-    const int t = (int)(idx / (H / 32)), b = (int)(idx % (H / 32));
-    {
-        float v[32];
-        if (act_bf16) {
-            const uint4 *src = (const uint4 *)((const uint16_t *)x + (size_t)t * H + 32 * b);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint4 raw = src[q];
-                const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v[8 * q + 2 * i] = __uint_as_float(wd[i] << 16);
-                    v[8 * q + 2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
-                }
-            }
-        } else {
-            const float4 *src = (const float4 *)((const float *)x + (size_t)t * H + 32 * b);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const float4 f = src[q];
-                v[4 * q] = f.x;
-                v[4 * q + 1] = f.y;
-                v[4 * q + 2] = f.z;
-                v[4 * q + 3] = f.w;
-            }
-        }
-        uint32_t o[16];
-#pragma unroll
-        for (int pi = 0; pi < 16; ++pi) {
-            const int m = pi >> 2, j = pi & 3;
-            const int e0 = (j & 1 ? 16 : 0) + 4 * m + (j >> 1);
-            const float sc = (j & 1) ? 0.0625f : 1.0f;
-            o[pi] = __builtin_bit_cast(uint32_t, h2{(_Float16)(v[e0] * sc), (_Float16)(v[e0 + 2] * sc)});
-        }
-        uint4 *dst = (uint4 *)(x16 + (size_t)t * H + 32 * b);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dst[q] = uint4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
-        if (xsum) {
-            // the block's sum of the staged fp16 values (unscaled), in pair
-            // order: the min term of a Q4_K GEMV
-            float sum = 0.f;
-#pragma unroll
-            for (int pi = 0; pi < 16; ++pi) {
-                const h2 v = as_h2(o[pi]);
-                const float sc = (pi & 1) ? 16.0f : 1.0f;
-                sum += sc * (float)v[0];
-                sum += sc * (float)v[1];
-            }
-            xsum[(size_t)t * (H / 32) + b] = sum;
-        }
-    }
+    stage_x_block(x, act_bf16, H, (int)(idx / (H / 32)), (int)(idx % (H / 32)), x16, xsum);
 }
 
 // out[t][o] = sum_{j<k} w[t][j] * y[inv[t*k+j]][o]  (slot order)  + y_shared[t][o]

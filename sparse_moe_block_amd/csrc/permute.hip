@@ -24,6 +24,7 @@
 // chunk workgroup sums the raw counts of the chunks before it itself (a few
 // KB of reads), which saves a launch.
 #include "common.h"
+#include "stages.h"
 
 namespace fw {
 namespace {
@@ -35,95 +36,7 @@ constexpr int kWaves = kThreads / kWave;
 __global__ __launch_bounds__(kThreads) void permute_kernel(
     const int32_t *__restrict__ ids, int P, int E, int32_t *__restrict__ offsets,
     int32_t *__restrict__ sorted, int32_t *__restrict__ inv, WsHeader *__restrict__ hdr) {
-    __shared__ int cnt[kMaxExperts];
-    __shared__ int cursor[kMaxExperts];
-    __shared__ int wave_tot[kMaxExperts / kWave];
-    __shared__ int wcnt[kWaves][kMaxExperts];
-    __shared__ int n_valid;
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-
-    for (int e = tid; e < kMaxExperts; e += kThreads) cnt[e] = 0;
-    for (int i = tid; i < kWaves * kMaxExperts; i += kThreads) (&wcnt[0][0])[i] = 0;
-    __syncthreads();
-
-    bool bad = false;
-    for (int q = tid; q < P; q += kThreads) {
-        const int e = ids[q];
-        if ((unsigned)e < (unsigned)E)
-            atomicAdd(&cnt[e], 1);
-        else
-            bad = true;
-    }
-    if (bad) atomicOr(&hdr->status, FW_STATUS_BAD_EXPERT_ID);
-    __syncthreads();
-
-    // exclusive scan over E <= 512 counts: waves 0..7 scan 64 experts each
-    if (tid < kMaxExperts) {
-        const int v = tid < E ? cnt[tid] : 0;
-        int incl = v;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int o = __shfl_up(incl, off);
-            if (lane >= off) incl += o;
-        }
-        if (lane == kWave - 1) wave_tot[wave] = incl;
-        cnt[tid] = incl - v;   // exclusive within the wave
-    }
-    __syncthreads();
-    if (tid < kMaxExperts) {
-        int base = 0;
-        for (int w = 0; w < wave; ++w) base += wave_tot[w];
-        const int ex = cnt[tid] + base;
-        if (tid <= E) offsets[tid] = ex;   // offsets[E] = total valid
-        if (tid == E) n_valid = ex;
-        if (tid < E) cursor[tid] = ex;
-    }
-    if (E == kMaxExperts && tid == 0) {
-        int tot = 0;
-        for (int w = 0; w < kMaxExperts / kWave; ++w) tot += wave_tot[w];
-        offsets[E] = tot;
-        n_valid = tot;
-    }
-    __syncthreads();
-
-    const unsigned long long lt_mask = (1ull << lane) - 1ull;
-    for (int c = 0; c * kThreads < P; ++c) {
-        const int q = c * kThreads + tid;
-        const int e = q < P ? ids[q] : -1;
-        const bool valid = (unsigned)e < (unsigned)E;
-        unsigned long long peers = __ballot(valid);
-#pragma unroll
-        for (int b = 0; b < 9; ++b) {   // E <= 512: 9 id bits
-            const bool bit = valid && ((e >> b) & 1);
-            const unsigned long long m = __ballot(bit);
-            peers &= bit ? m : ~m;
-        }
-        const int rank = __popcll(peers & lt_mask);
-        const int tag = (c + 1) << 8;   // counts are <= 64 < 256
-        if (valid && rank == 0) wcnt[wave][e] = tag | __popcll(peers);
-        __syncthreads();
-        int prefix = 0, total = 0;
-        if (valid) {
-            for (int w = 0; w < kWaves; ++w) {
-                const int v = wcnt[w][e];
-                const int n = (v & ~0xFF) == tag ? (v & 0xFF) : 0;
-                if (w < wave) prefix += n;
-                total += n;
-            }
-            const int pos = cursor[e] + prefix + rank;   // < offsets[e+1] <= P
-            if ((unsigned)pos < (unsigned)P) {
-                sorted[pos] = q;
-                inv[q] = pos;
-            }
-        } else if (q < P) {
-            inv[q] = -1;
-        }
-        __syncthreads();
-        if (valid && prefix + rank == total - 1) cursor[e] += total;
-        // the next chunk's LDS reads of cursor[] follow its first barrier
-    }
-    __syncthreads();
-    for (int p = n_valid + tid; p < P; p += kThreads) sorted[p] = -1;
+    permute_block(ids, P, E, offsets, sorted, inv, hdr);
 }
 
 // Exclusive scan of per-expert values v (threads tid < kMaxExperts hold one

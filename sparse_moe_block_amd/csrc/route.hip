@@ -5,6 +5,7 @@
 #include <math.h>
 
 #include "common.h"
+#include "stages.h"
 
 namespace fw {
 namespace {
@@ -164,104 +165,13 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(
     logits[i] = acc + (bias ? bias[e] : 0.f);
 }
 
-// Wave-wide reductions on the DPP network (no LDS round trip): quad
-// permutations, half-row and row mirrors leave every lane of a row with the
-// row's result; row broadcasts 15 and 31 carry it into rows 1..3; lane 63
-// holds the wave's result.  Fixed pattern, so sums are deterministic.
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ uint32_t dpp(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, dpp<0xB1>(v));         // quad_perm [1,0,3,2]
-    v = max(v, dpp<0x4E>(v));         // quad_perm [2,3,0,1]
-    v = max(v, dpp<0x141>(v));        // row_half_mirror
-    v = max(v, dpp<0x140>(v));        // row_mirror
-    v = max(v, dpp<0x142, 0xA>(v));   // row_bcast:15 into rows 1, 3
-    v = max(v, dpp<0x143, 0xC>(v));   // row_bcast:31 into rows 2, 3
-    return __builtin_amdgcn_readlane(v, 63);
-}
-__device__ __forceinline__ float fdpp_add(float v, uint32_t o) { return v + __uint_as_float(o); }
-__device__ __forceinline__ float wave_sum_f32(float v) {
-    v = fdpp_add(v, dpp<0xB1>(__float_as_uint(v)));
-    v = fdpp_add(v, dpp<0x4E>(__float_as_uint(v)));
-    v = fdpp_add(v, dpp<0x141>(__float_as_uint(v)));
-    v = fdpp_add(v, dpp<0x140>(__float_as_uint(v)));
-    // rows 1 and 3 add lane 15 / 47; rows 0 and 2 add nothing (the DPP keeps
-    // their own value, so subtract-free: mask them out of the add instead)
-    {
-        const uint32_t o = dpp<0x142, 0xA>(__float_as_uint(v));
-        const bool add = (__lane_id() >> 4) & 1;
-        v = add ? v + __uint_as_float(o) : v;
-    }
-    {
-        const uint32_t o = dpp<0x143, 0xC>(__float_as_uint(v));
-        const bool add = (__lane_id() >> 5) & 1;
-        v = add ? v + __uint_as_float(o) : v;
-    }
-    return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
-}
-
-// Total order of logits as unsigned keys: larger logit -> larger key; -0 and
-// +0 compare equal (both map to the key of +0), NaN maps below -inf.
-__device__ __forceinline__ uint32_t logit_key(float l) {
-    if (l != l) return 0u;
-    const uint32_t u = __float_as_uint(l + 0.0f);   // -0 + 0 = +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_logit(uint32_t k) {
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
-// One wavefront per token.  Lane l holds the logits of experts l, l+64, ...
-// as keys; each of k rounds takes the wave maximum of the untaken keys (DPP),
-// then the lowest expert index holding it (one ballot per register), so the
-// experts come out in descending logit order with ties to the lower index;
-// lane j keeps slot j.  Renormalised weights: softmax -> exp(l_j - l_0) / sum
-// over the slots (l_0 is the maximum); sigmoid -> s_j / sum s.
 template <int EPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E,
                                                    int k, int score, int32_t *__restrict__ ids,
                                                    float *__restrict__ w) {
-    const int lane = threadIdx.x % kWave;
     const int t = blockIdx.x * 4 + wave_id();
     if (t >= T) return;
-    uint32_t key[EPL];
-    uint32_t taken = 0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = lane + kWave * i;
-        key[i] = e < E ? logit_key(logits[(size_t)t * E + e]) : 0u;
-        if (e >= E) taken |= 1u << i;   // never selectable
-    }
-    int my_e = 0;
-    float my_l = 0.f;
-    for (int j = 0; j < k; ++j) {
-        uint32_t best = 0;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if (!((taken >> i) & 1u)) best = max(best, key[i]);
-        const uint32_t m = wave_max_u32(best);
-        int sel = 0;
-#pragma unroll
-        for (int i = EPL - 1; i >= 0; --i) {   // the lowest i with a match wins
-            const unsigned long long b = __ballot(!((taken >> i) & 1u) && key[i] == m);
-            if (b) sel = kWave * i + __builtin_ctzll(b);
-        }
-        if ((sel % kWave) == lane) taken |= 1u << (sel / kWave);
-        if (lane == j) {
-            my_e = sel;
-            my_l = key_logit(m);
-        }
-    }
-    const float l0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_l), 0));
-    float s = 0.f;
-    if (lane < k) s = score == FW_SOFTMAX_RENORM ? expf(my_l - l0) : 1.0f / (1.0f + expf(-my_l));
-    const float sum = wave_sum_f32(s);
-    if (lane < k) {
-        ids[(size_t)t * k + lane] = my_e;
-        w[(size_t)t * k + lane] = s / sum;
-    }
+    topk_token<EPL>(logits, t, E, k, score, ids, w, nullptr);
 }
 
 }  // namespace

@@ -68,6 +68,7 @@ def lib():
             "fw_moe_route": ([D, I] + [P] * 8, ctypes.c_int),
             "fw_moe_permute": ([D, I, P, P, P, P, P, ctypes.c_size_t, P], ctypes.c_int),
             "fw_moe_forward": ([D, I] + [P] * 13 + [ctypes.c_size_t, P], ctypes.c_int),
+            "fw_moe_layer": ([D, I] + [P] * 17 + [ctypes.c_size_t, P], ctypes.c_int),
             "fw_moe_clear_status": ([P, P], ctypes.c_int),
             "fw_moe_read_status": ([P, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
             "fw_moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -143,6 +144,18 @@ def fw_moe_forward(desc, T, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, to
         ctypes.byref(desc), T, _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(ws_gate),
         _ptr(ws_up), _ptr(ws_down), _ptr(topk_w), _ptr(expert_offsets), _ptr(sorted_pairs),
         _ptr(inv_pos), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def fw_moe_layer(desc, T, x, router_w, logit_bias, w_gate, w_up, w_down, ws_gate, ws_up,
+                 ws_down, logits, topk_ids, topk_w, expert_offsets, sorted_pairs, inv_pos, out,
+                 workspace, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    return _check("fw_moe_layer", lib().fw_moe_layer(
+        ctypes.byref(desc), T, _ptr(x), _ptr(router_w), _ptr(logit_bias), _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(logits),
+        _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(inv_pos),
+        _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def fw_moe_clear_status(workspace, stream=None):

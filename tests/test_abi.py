@@ -110,6 +110,31 @@ def test_forward_validation():
     assert _forward(ds, 8, fw.fw_moe_workspace_size(ds, 8)) == fw.FW_EINVAL   # no shared weights
 
 
+def _layer(d, T, ws_bytes, ws=256, x=16, router=16, logits=16, ids=16, out=16,
+           shared=(None, None, None)):
+    return fw.lib().fw_moe_layer(ctypes.byref(d), T, x, router, None, 16, 16, 16, *shared,
+                                 logits, ids, 16, 16, 16, 16, out, ws, ws_bytes, None)
+
+
+def test_layer_validation():
+    """Every refusal of fw_moe_layer happens before its first launch."""
+    d = good_desc()
+    need = fw.fw_moe_workspace_size(d, 8)
+    assert _layer(d, 0, 0) == fw.FW_OK                       # nothing to do
+    assert _layer(d, -1, need) == fw.FW_EINVAL
+    assert _layer(good_desc(hidden=100), 8, need) == fw.FW_EINVAL
+    assert _layer(d, 8, need, router=None) == fw.FW_EINVAL
+    assert _layer(d, 8, need, logits=None) == fw.FW_EINVAL   # logits are always written
+    assert _layer(d, 8, need, x=None) == fw.FW_EINVAL
+    assert _layer(d, 8, need, out=None) == fw.FW_EINVAL
+    assert _layer(d, 8, need, ids=24) == fw.FW_EALIGN
+    assert _layer(d, 8, need, router=40) == fw.FW_EALIGN
+    assert _layer(d, 8, need, ws=128) == fw.FW_EALIGN
+    assert _layer(d, 8, need - 1) == fw.FW_EWORKSPACE
+    ds = good_desc(shared_ffn=768)
+    assert _layer(ds, 8, fw.fw_moe_workspace_size(ds, 8)) == fw.FW_EINVAL   # no shared weights
+
+
 def test_permute_validation():
     d = good_desc()
     lib = fw.lib()
