@@ -1,4 +1,5 @@
-"""Graph capture: route -> permute -> forward captured once in a HIP graph and
+"""Graph capture: route -> permute -> forward (three calls, or the one
+fw_moe_layer call) captured once in a HIP graph and
 replayed several times, with eager work and synchronisations between the
 replays; every replay must equal the eager result bit for bit.  (The library
 issues no memset and no allocation, so it captures as is; split-K counters and
@@ -18,9 +19,10 @@ CASES = [(C.QWEN3_DECODE, 16, "auto"), (C.DEEPSEEK, 1, "auto"), (C.DEEPSEEK, 32,
          (C.QWEN3_PREFILL, 256, "gemm")]
 
 
+@pytest.mark.parametrize("one_call", [False, True], ids=["three-calls", "fw_moe_layer"])
 @pytest.mark.parametrize("cfg,T,path", CASES, ids=["c1-T16", "c3-T1", "c3-T32", "c2-T256-gemm"])
-def test_graph_replays_equal_eager(cfg, T, path):
-    print(f"graph {cfg.name} T={T} {path}", flush=True)
+def test_graph_replays_equal_eager(cfg, T, path, one_call):
+    print(f"graph {cfg.name} T={T} {path} one_call={one_call}", flush=True)
     dl = G.layer(cfg)
     L = dl.L
     desc = G.desc_of(cfg, path=path)
@@ -37,6 +39,11 @@ def test_graph_replays_equal_eager(cfg, T, path):
     ws = G.workspace(desc, T)
 
     def step(xin, s=None):
+        if one_call:
+            fw.fw_moe_layer(desc, T, xin, L.router, L.bias, L.w_gate, L.w_up, L.w_down,
+                            L.s_gate, L.s_up, L.s_down, logits, ids, w, off, sp, inv, out, ws,
+                            stream=s)
+            return
         fw.fw_moe_route(desc, T, xin, L.router, L.bias, None, logits, ids, w, s)
         fw.fw_moe_permute(desc, T, ids, off, sp, inv, ws, stream=s)
         fw.fw_moe_forward(desc, T, xin, L.w_gate, L.w_up, L.w_down, L.s_gate, L.s_up,
