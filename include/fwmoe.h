@@ -175,7 +175,12 @@ int fw_moe_permute(const fw_moe_desc *desc, int32_t T, const int32_t *topk_ids,
  * min formed in fp32; one rounding).  Either way a layer output stays within
  * 2e-3 max-abs and 1e-3 relative L2 of an fp64 evaluation of the same layer.
  * Q4_K (GGUF K-quant, 144-byte super-blocks of 256 elements) needs H, F and
- * Fs to be multiples of 256, which every descriptor already is. */
+ * Fs to be multiples of 256, which every descriptor already is.
+ * Batch limit: T * k * max(H, F, Fs) < 2^31 (the kernels' row offsets are
+ * 32-bit element counts); a larger batch returns FW_EINVAL before anything
+ * is enqueued and is to be split by the caller (DeepSeek-shaped layer:
+ * up to 37,449 tokens per call).  fw_moe_layer and fw_moe_forward_path apply
+ * the same limit. */
 int fw_moe_forward(const fw_moe_desc *desc, int32_t T, const void *x, const void *w_gate,
                    const void *w_up, const void *w_down, const void *ws_gate,
                    const void *ws_up, const void *ws_down, const float *topk_w,

@@ -75,6 +75,15 @@ int check_T(const fw_moe_desc *d, int32_t T) {
     return FW_OK;
 }
 
+// The forward kernels index activation and intermediate rows with 32-bit
+// element offsets (row * K): batches whose T * k * max(H, F, Fs) reaches 2^31
+// are refused; the caller splits them.
+int check_forward_T(const fw_moe_desc *d, int32_t T) {
+    const int64_t widest = std::max({d->hidden, d->ffn, d->shared_ffn});
+    if ((int64_t)T * d->top_k * widest >= (int64_t)1 << 31) return FW_EINVAL;
+    return FW_OK;
+}
+
 int resolve_path(const fw_moe_desc *d, int32_t T) {
     if (d->path != FW_PATH_AUTO) return d->path;
     return T <= kGemvMaxT ? FW_PATH_GEMV : FW_PATH_GEMM;
@@ -89,6 +98,7 @@ int forward_args(const fw_moe_desc *desc, int32_t T, const void *x, const void *
                  const void *ws_down, const float *topk_w, const int32_t *expert_offsets,
                  const int32_t *sorted_pairs, const int32_t *inv_pos, float *out,
                  void *workspace, size_t ws_bytes, FwdArgs *out_args) {
+    if (check_forward_T(desc, T) != FW_OK) return FW_EINVAL;
     const bool shared = desc->shared_ffn > 0;
     if (!x || !w_gate || !w_up || !w_down || !topk_w || !expert_offsets || !sorted_pairs ||
         !inv_pos || !out || !workspace)
@@ -174,6 +184,7 @@ int fw_moe_forward_path(const fw_moe_desc *desc, int32_t T) {
     int rc = check_desc(desc);
     if (rc != FW_OK) return rc;
     if ((rc = check_T(desc, T)) != FW_OK) return rc;
+    if ((rc = check_forward_T(desc, T)) != FW_OK) return rc;
     return resolve_path(desc, T);
 }
 

@@ -135,6 +135,25 @@ def test_layer_validation():
     assert _layer(ds, 8, fw.fw_moe_workspace_size(ds, 8)) == fw.FW_EINVAL   # no shared weights
 
 
+def test_forward_batch_limit():
+    """T * k * max(H, F, Fs) must stay below 2^31 (32-bit row offsets)."""
+    d = good_desc(hidden=7168, n_experts=256, top_k=8, ffn=2048)
+    t_max = ((1 << 31) - 1) // (8 * 7168)
+    assert t_max == 37449
+    assert fw.fw_moe_forward_path(d, t_max) == fw.FW_PATH_GEMM
+    assert fw.fw_moe_forward_path(d, t_max + 1) == fw.FW_EINVAL
+    big = t_max + 1
+    need = fw.fw_moe_workspace_size(d, big)
+    assert need > 0      # route / permute are not limited by it
+    assert _forward(d, big, need) == fw.FW_EINVAL
+    assert _layer(d, big, need) == fw.FW_EINVAL
+    # a wide shared expert sets the bound too
+    ds = good_desc(hidden=256, n_experts=8, top_k=1, ffn=256, shared_ffn=16384)
+    assert fw.fw_moe_forward_path(ds, (1 << 31) // 16384) == fw.FW_EINVAL
+    assert fw.fw_moe_forward_path(ds, (1 << 31) // 16384 - 1) in (fw.FW_PATH_GEMV,
+                                                                  fw.FW_PATH_GEMM)
+
+
 def test_permute_validation():
     d = good_desc()
     lib = fw.lib()
