@@ -75,6 +75,10 @@ def parse():
                          "and uniform or Zipf(1.3) routing, both kernel families timed "
                          "at each T; one JSON line per point, then the decode-to-prefill "
                          "crossover of each variant")
+    ap.add_argument("--sweep-layer", default="sweep", choices=["sweep", "qwen3", "deepseek"],
+                    help="layer of --sweep: the hidden-4096 sweep layer (default), the "
+                         "Qwen3-MoE-30B-A3B-shaped layer, or the DeepSeek-shaped layer "
+                         "(their own formats; T = 1..4096)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a negation "
                          "kernel, the reference that scales hardware byte counters)")
@@ -259,10 +263,12 @@ def main():
 
 
 def sweep(a):
-    """Step time of the sweep layer with each kernel family forced, over
-    T = 1, 2, 4, ..., 8192.  Each step is a HIP-graph replay of route ->
-    permute -> forward on one of 8 weight copies (cold Infinity Cache, as in
-    the main benchmark).  The GEMV family is timed while it is at most three
+    """Step time of a layer with each kernel family forced, over T = 1, 2, 3,
+    4, 6, 8, 12, ... (powers of two and the points halfway between, to 8192
+    for the sweep layer, 4096 for the others).  Each step is a
+    HIP-graph replay of one fw_moe_layer call on one of 8 weight copies (2 for
+    the DeepSeek-shaped layer; cold Infinity Cache either way, as in the main
+    benchmark).  The GEMV family is timed while it is at most three
     times slower than the grouped GEMM; the crossover of a variant is the
     smallest T from which the GEMM step is faster at every larger T."""
     dev = torch.device("cuda:0")
@@ -270,87 +276,103 @@ def sweep(a):
     copies = 8
     steps, warm = min(a.steps, 30), min(a.warmup, 5)
     summary = []
-    for base in (moegen.SWEEP_Q8, moegen.SWEEP_Q4):
-        for zipf in (None, 1.3):
-            cfg = base.with_(zipf=zipf)
-            L = moegen.make_layer(cfg, device=dev)
-            layers = [L] + [moegen.Layer(cfg, L.router, L.bias, L.w_gate.clone(),
-                                         L.w_up.clone(), L.w_down.clone(), None, None, None)
-                            for _ in range(copies - 1)]
-            E, k, H = cfg.n_experts, cfg.top_k, cfg.hidden
-            times = {}
-            gemv_on = True
-            for T in cfg.tokens:
-                x = moegen.make_x(cfg, T, device=dev)
-                P = T * k
-                bufs = dict(logits=torch.empty(T, E, device=dev),
-                            ids=torch.empty(T, k, dtype=torch.int32, device=dev),
-                            w=torch.empty(T, k, device=dev),
-                            off=torch.empty(E + 1, dtype=torch.int32, device=dev),
-                            sp=torch.empty(P, dtype=torch.int32, device=dev),
-                            inv=torch.empty(P, dtype=torch.int32, device=dev),
-                            out=torch.empty(T, H, device=dev))
-                row = {"variant": f"{cfg.expert_q} {'zipf1.3' if zipf else 'uniform'}",
-                       "T": T}
-                for path in ("gemv", "gemm"):
-                    if path == "gemv" and not gemv_on:
-                        continue
-                    desc = fw.make_desc(H, E, k, cfg.ffn, 0, cfg.act_dtype, cfg.router_dtype,
-                                        cfg.expert_q, cfg.shared_q, cfg.score, path)
-                    ws = torch.empty(fw.fw_moe_workspace_size(desc, T), dtype=torch.uint8,
-                                     device=dev)
-                    fw.fw_moe_clear_status(ws)
-                    b = bufs
+    if a.sweep_layer == "sweep":
+        variants = [b.with_(zipf=z) for b in (moegen.SWEEP_Q8, moegen.SWEEP_Q4)
+                    for z in (None, 1.3)]
+        t_max = 8192
+    elif a.sweep_layer == "qwen3":
+        variants = [moegen.QWEN3_DECODE, moegen.QWEN3_PREFILL]
+        t_max = 4096
+    else:
+        variants = [moegen.DEEPSEEK]
+        t_max = 4096
+        copies = 2
+    for cfg in variants:
+        zipf = cfg.zipf
+        L = moegen.make_layer(cfg, device=dev)
+        layers = [L] + [moegen.Layer(cfg, L.router, L.bias, L.w_gate.clone(),
+                                     L.w_up.clone(), L.w_down.clone(),
+                                     *(None if t is None else t.clone()
+                                       for t in (L.s_gate, L.s_up, L.s_down)))
+                        for _ in range(copies - 1)]
+        E, k, H = cfg.n_experts, cfg.top_k, cfg.hidden
+        times = {}
+        gemv_on = True
+        # powers of two and the points halfway between them (3 * 2^i)
+        for T in sorted({2 ** i for i in range(14)} | {3 << i for i in range(13)}):
+            if T > t_max:
+                continue
+            x = moegen.make_x(cfg, T, device=dev)
+            P = T * k
+            bufs = dict(logits=torch.empty(T, E, device=dev),
+                        ids=torch.empty(T, k, dtype=torch.int32, device=dev),
+                        w=torch.empty(T, k, device=dev),
+                        off=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                        sp=torch.empty(P, dtype=torch.int32, device=dev),
+                        inv=torch.empty(P, dtype=torch.int32, device=dev),
+                        out=torch.empty(T, H, device=dev))
+            row = {"variant": f"{cfg.name}, {cfg.expert_q}, "
+                              f"{'zipf' + str(zipf) if zipf else 'uniform'}", "T": T}
+            for path in ("gemv", "gemm"):
+                if path == "gemv" and not gemv_on:
+                    continue
+                desc = fw.make_desc(H, E, k, cfg.ffn, cfg.shared_ffn, cfg.act_dtype,
+                                    cfg.router_dtype, cfg.expert_q, cfg.shared_q, cfg.score,
+                                    path)
+                ws = torch.empty(fw.fw_moe_workspace_size(desc, T), dtype=torch.uint8,
+                                 device=dev)
+                fw.fw_moe_clear_status(ws)
+                b = bufs
 
-                    def step(i, s):
-                        Li = layers[i % copies]
-                        fw.fw_moe_layer(desc, T, x, Li.router, Li.bias, Li.w_gate, Li.w_up,
-                                        Li.w_down, None, None, None, b["logits"], b["ids"],
-                                        b["w"], b["off"], b["sp"], b["inv"], b["out"], ws,
-                                        stream=s)
+                def step(i, s):
+                    Li = layers[i % copies]
+                    fw.fw_moe_layer(desc, T, x, Li.router, Li.bias, Li.w_gate, Li.w_up,
+                                    Li.w_down, Li.s_gate, Li.s_up, Li.s_down, b["logits"],
+                                    b["ids"],
+                                    b["w"], b["off"], b["sp"], b["inv"], b["out"], ws,
+                                    stream=s)
 
-                    step(0, torch.cuda.current_stream())
-                    torch.cuda.synchronize()
-                    assert fw.fw_moe_read_status(ws) == 0
-                    graphs = []
-                    for c in range(copies):
-                        g = torch.cuda.CUDAGraph()
-                        with torch.cuda.graph(g):
-                            step(c, torch.cuda.current_stream())
-                        graphs.append(g)
-                    for i in range(warm):
-                        graphs[i % copies].replay()
-                    torch.cuda.synchronize()
-                    g0 = torch.cuda.Event(enable_timing=True)
-                    g1 = torch.cuda.Event(enable_timing=True)
-                    g0.record()
-                    for i in range(steps):
-                        graphs[(warm + i) % copies].replay()
-                    g1.record()
-                    torch.cuda.synchronize()
-                    ms = g0.elapsed_time(g1) / steps
-                    row[f"{path}_us"] = round(ms * 1e3, 1)
-                    row[f"{path}_tok_s"] = round(T / (ms * 1e-3))
-                    del graphs, ws
-                times[T] = row
-                if "gemv_us" in row and row["gemv_us"] > 3 * row["gemm_us"]:
-                    gemv_on = False
-                row["auto"] = "gemv" if fw.fw_moe_forward_path(
-                    fw.make_desc(H, E, k, cfg.ffn, 0, cfg.act_dtype, cfg.router_dtype,
-                                 cfg.expert_q, cfg.shared_q, cfg.score, "auto"), T) == \
-                    fw.FW_PATH_GEMV else "gemm"
-                print(json.dumps(row), flush=True)
-            cross = None
-            for T in sorted(times, reverse=True):
-                r = times[T]
-                if "gemv_us" in r and r["gemv_us"] <= r["gemm_us"]:
-                    break
-                cross = T
-            summary.append({"variant": row["variant"], "crossover_T": cross})
-            del layers, L
-            torch.cuda.empty_cache()
-    print(json.dumps({"sweep": "hidden 4096, 64 experts top-4, ffn 1536",
-                      "crossover": summary}), flush=True)
+                step(0, torch.cuda.current_stream())
+                torch.cuda.synchronize()
+                assert fw.fw_moe_read_status(ws) == 0
+                graphs = []
+                for c in range(copies):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        step(c, torch.cuda.current_stream())
+                    graphs.append(g)
+                for i in range(warm):
+                    graphs[i % copies].replay()
+                torch.cuda.synchronize()
+                g0 = torch.cuda.Event(enable_timing=True)
+                g1 = torch.cuda.Event(enable_timing=True)
+                g0.record()
+                for i in range(steps):
+                    graphs[(warm + i) % copies].replay()
+                g1.record()
+                torch.cuda.synchronize()
+                ms = g0.elapsed_time(g1) / steps
+                row[f"{path}_us"] = round(ms * 1e3, 1)
+                row[f"{path}_tok_s"] = round(T / (ms * 1e-3))
+                del graphs, ws
+            times[T] = row
+            if "gemv_us" in row and row["gemv_us"] > 3 * row["gemm_us"]:
+                gemv_on = False
+            row["auto"] = "gemv" if fw.fw_moe_forward_path(
+                fw.make_desc(H, E, k, cfg.ffn, cfg.shared_ffn, cfg.act_dtype,
+                             cfg.router_dtype, cfg.expert_q, cfg.shared_q, cfg.score,
+                             "auto"), T) == fw.FW_PATH_GEMV else "gemm"
+            print(json.dumps(row), flush=True)
+        cross = None
+        for T in sorted(times, reverse=True):
+            r = times[T]
+            if "gemv_us" in r and r["gemv_us"] <= r["gemm_us"]:
+                break
+            cross = T
+        summary.append({"variant": row["variant"], "crossover_T": cross})
+        del layers, L
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": a.sweep_layer, "crossover": summary}), flush=True)
 
 
 def source_hash(kernel):

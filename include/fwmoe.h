@@ -192,7 +192,7 @@ int fw_moe_forward(const fw_moe_desc *desc, int32_t T, const void *x, const void
  * NULL), fw_moe_permute and fw_moe_forward on the same arguments, with the
  * same results bit for bit (the route of fw_moe_route, the sort of
  * fw_moe_permute, the expert FFNs and combine of fw_moe_forward, as stated
- * above).  When the forward runs the GEMV family (AUTO up to T = 32, or
+ * above).  When the forward runs the GEMV family (AUTO up to T*k = 2E, or
  * FW_PATH_GEMV) and T*k <= 2048, the top-k, the permutation and the forward's
  * activation staging run as one kernel, so a decode step is five launches
  * instead of seven; otherwise the launches are those of the three calls.
@@ -215,8 +215,10 @@ int fw_moe_layer(const fw_moe_desc *desc, int32_t T, const void *x, const void *
 
 /* The forward kernel family AUTO picks for T tokens (FW_PATH_GEMV or
  * FW_PATH_GEMM), or a negative error for an invalid descriptor.  AUTO takes
- * the GEMV family up to T = 32 and the grouped GEMM above (measured crossover
- * of the hidden-4096, 64-expert top-4 layer: between 32 and 64 tokens). */
+ * the GEMV family while T * k <= 2 * E (at most two routed rows per expert on
+ * average) and the grouped GEMM above: the measured crossovers of the
+ * hidden-4096 / 64-expert, Qwen3-shaped and DeepSeek-shaped layers lie
+ * between 1.5 and 3 rows per expert. */
 int fw_moe_forward_path(const fw_moe_desc *desc, int32_t T);
 
 /* Reset the workspace's status word (a fill kernel on `stream`). */

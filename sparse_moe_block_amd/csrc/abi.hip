@@ -86,7 +86,8 @@ int check_forward_T(const fw_moe_desc *d, int32_t T) {
 
 int resolve_path(const fw_moe_desc *d, int32_t T) {
     if (d->path != FW_PATH_AUTO) return d->path;
-    return T <= kGemvMaxT ? FW_PATH_GEMV : FW_PATH_GEMM;
+    const int64_t pairs = (int64_t)T * d->top_k;
+    return pairs <= (int64_t)kGemvMaxRowsPerExpert * d->n_experts ? FW_PATH_GEMV : FW_PATH_GEMM;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FW_OK : FW_EHIP; }

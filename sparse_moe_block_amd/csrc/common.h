@@ -18,10 +18,12 @@ constexpr int kGemvTokens = 2;    // token rows a GEMV work item carries
 constexpr int kGemmBM = 128;      // token rows per tile of the LDS-dequant grouped GEMM
 constexpr int kGemm2BM = 64;      // token rows per tile of the register-dequant grouped GEMM
 constexpr bool kUseGemm2 = true;  // which grouped GEMM serves the GEMM path
-// AUTO: GEMV family up to this many tokens.  On the hidden-4096 / 64-expert
-// top-4 layer (Q8_0 and Q4_0, uniform and Zipf(1.3) routing) the grouped GEMM
-// step is faster from T = 64 on and the GEMV step up to T = 32.
-constexpr int kGemvMaxT = 32;
+// AUTO: the GEMV family while the routed pairs average at most this many rows
+// per expert (T * k <= 2 E), the grouped GEMM above.  Measured crossovers, in
+// rows per expert: the hidden-4096 / 64-expert top-4 layer between 2 and 3
+// (Q8_0 and Q4_0, uniform and Zipf(1.3) routing), the Qwen3-shaped layer
+// between 1.5 and 2 (a tie at 2), the DeepSeek-shaped layer between 1.5 and 2.
+constexpr int kGemvMaxRowsPerExpert = 2;
 // router logits: the 16-token-tile kernel up to this many tokens
 constexpr int kLogitsTileMaxT = 64;
 // GEMV split-K: at most this many (row chunk, weight tile) pairs are split,

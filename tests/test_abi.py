@@ -68,9 +68,16 @@ def test_path_choice():
     d = good_desc()
     assert fw.fw_moe_forward_path(d, 1) == fw.FW_PATH_GEMV
     assert fw.fw_moe_forward_path(d, 4096) == fw.FW_PATH_GEMM
-    # the measured decode-to-prefill crossover of the sweep layer lies between 32 and 64
+    # the measured decode-to-prefill crossover of the sweep layer lies between 32 and 48
     assert fw.fw_moe_forward_path(d, 32) == fw.FW_PATH_GEMV
     assert fw.fw_moe_forward_path(d, 33) == fw.FW_PATH_GEMM
+    # the rule follows routed rows per expert (T * k <= 2 E), not T
+    ds = good_desc(hidden=7168, n_experts=256, top_k=8, ffn=2048)
+    assert fw.fw_moe_forward_path(ds, 64) == fw.FW_PATH_GEMV
+    assert fw.fw_moe_forward_path(ds, 65) == fw.FW_PATH_GEMM
+    dt = good_desc(hidden=256, n_experts=8, top_k=2, ffn=512)
+    assert fw.fw_moe_forward_path(dt, 8) == fw.FW_PATH_GEMV
+    assert fw.fw_moe_forward_path(dt, 9) == fw.FW_PATH_GEMM
     assert fw.fw_moe_forward_path(good_desc(path="gemv"), 4096) == fw.FW_PATH_GEMV
     assert fw.fw_moe_forward_path(good_desc(path="gemm"), 1) == fw.FW_PATH_GEMM
 
