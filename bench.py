@@ -48,6 +48,9 @@ WORKLOADS = {
     # the same shapes on Q4_K experts (GGUF K-quant super-blocks)
     "decode16_q4k": (moegen.QWEN3_DECODE.with_(expert_q=moegen.Q4_K), 16, 16),
     "prefill2048_q4k": (moegen.QWEN3_PREFILL.with_(expert_q=moegen.Q4_K), 2048, 4),
+    # and on Q8_0 experts (the sweep's other format)
+    "decode16_q8": (moegen.QWEN3_DECODE.with_(expert_q=moegen.Q8_0), 16, 8),
+    "prefill2048_q8": (moegen.QWEN3_PREFILL.with_(expert_q=moegen.Q8_0), 2048, 2),
 }
 
 

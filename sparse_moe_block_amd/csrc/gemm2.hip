@@ -12,10 +12,15 @@
 //    4 (i % 4) .. 4 (i % 4) + 3 in the pair order of decode_pairs (the MFMA
 //    sums over k in any order, so the activations are laid out the same way);
 //  - weights: lane (n = lane % 16, g) loads the 36-byte (Q4_0) or 68-byte
-//    (Q8_0) window of blocks 2g, 2g + 1 of its weight row (dword aligned), one
-//    step ahead, and turns one code dword into the four fp16 pairs of a B
-//    fragment (exact code times the fp16 scale, one rounding) right before the
-//    MFMAs that use it; no LDS traffic, no bank conflicts;
+//    (Q8_0) window of blocks 2g, 2g + 1 of its weight row (dword aligned) and
+//    turns one code dword into the four fp16 pairs of a B fragment (exact code
+//    times the fp16 scale, one rounding) right before the MFMAs that use it;
+//    no LDS traffic, no bank conflicts.  Q4_0 windows are loaded one step
+//    ahead into a second buffer; the wider Q8_0 and Q4_K windows (17 and 12
+//    dwords per column group) have one buffer, refilled after the step's
+//    MFMAs, which keeps those kernels within 256 VGPRs at two waves per SIMD
+//    (with two buffers they spilled into AGPRs at one wave per SIMD: Q4_K
+//    prefill T=2048 545 -> 446 us, Q8_0 560 -> 515 us);
 //  - activations: the 64 x 256 fp16 tile of a step is staged through
 //    double-buffered, padded LDS (32 lanes read one row's 512 bytes together),
 //    loaded one step ahead; A fragments are read per slice;
@@ -273,6 +278,20 @@ __device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
     // s + 1 committed and those of s + 2 loaded after the MFMAs (clamped loads
     // past the last step are redundant, never conditional)
     int st = 0;
+    if constexpr (Q != FW_Q4_0) {
+        // wide windows (Q8_0, Q4_K): one weight buffer, the next step's
+        // windows loaded after this step's MFMAs; LDS buffer st % 2 holds
+        // step st's activations, and buffer (st + 1) % 2 is refilled only
+        // after the barrier that ends step st - 1's reads of it
+        for (; st < steps; ++st) {
+            const int cur = st & 1;
+            FW_MMA(cur, wb0)
+            FW_LOAD_B(wb0, min(st + 1, steps - 1));
+            commit_a(cur ^ 1);
+            load_a(min(st + 2, steps - 1));
+            __syncthreads();
+        }
+    } else {
     for (; st + 1 < steps; st += 2) {
         FW_LOAD_B(wb1, st + 1);
         FW_MMA(0, wb0)
@@ -288,6 +307,7 @@ __device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
     if (st < steps) {   // odd step count: the last step sits in buffer 0 / wb0
         FW_MMA(0, wb0)
         __syncthreads();
+    }
     }
 #undef FW_LOAD_B
 #undef FW_MMA
