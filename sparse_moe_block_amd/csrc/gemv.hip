@@ -509,6 +509,17 @@ void launch_sd(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Fl
                _Float16 *hout, float *yout, int K, int N, long long items, int per_cu, int ks,
                int shared, const float *isum, float *osum, hipStream_t s) {
     const int tpg = N / kWave;
+    // workgroups per CU: what the LDS pipeline asks for, but no more than
+    // registers and LDS let be resident at once (the schedule is persistent)
+    static int resident = 0;
+    if (!resident) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_kernel<Q, GU, S, D>, kWave * S,
+                                                         0) != hipSuccess || n < 1)
+            n = 1;
+        resident = n;
+    }
+    per_cu = std::min(per_cu, resident);
     const int grid = (int)std::max(1LL, std::min(items * ks, (long long)per_cu * cu_count()));
     gemv_kernel<Q, GU, S, D><<<grid, kWave * S, 0, s>>>(
         wa, wb, (const int4 *)(a.ws + a.L.tiles), (WsHeader *)a.ws, a.sorted, xin, hout, yout,
