@@ -27,8 +27,15 @@ CASES = [
     (C.DEEPSEEK, 1, "auto"),           # shared expert; 256 experts (4 per lane)
     (C.DEEPSEEK, 32, "auto"),          # 7 staging blocks beside the front block
     (C.QWEN3_PREFILL, 2048, "auto"),   # the GEMM path through the one call
+    (C.DEEPSEEK, 64, "auto"),          # 2 rows per expert: the last GEMV batch
+    (C.DEEPSEEK, 65, "auto"),          # the first GEMM batch
+    (C.DEEPSEEK, 4096, "auto"),
+    # every expert format at the benchmark's decode and prefill shapes
+    (C.QWEN3_DECODE.with_(expert_q=C.Q8_0), 16, "auto"),
+    (C.QWEN3_PREFILL.with_(expert_q=C.Q8_0), 2048, "auto"),
+    (C.QWEN3_PREFILL.with_(expert_q=C.Q4_K), 2048, "auto"),
 ]
-IDS = [f"c{c.cid}{'k' if c.expert_q == C.Q4_K else ''}-T{T}-{p}" for c, T, p in CASES]
+IDS = [f"c{c.cid}-{c.expert_q}-T{T}-{p}" for c, T, p in CASES]
 
 
 def _three_calls(desc, cfg, dl, x):
