@@ -27,7 +27,11 @@
 //  - v_mfma_f32_16x16x32_f16 with fp32 accumulation; gate/up: a wavefront's 64
 //    weight rows are 32 gate and the same 32 up features, so a lane holds gate
 //    and up of the same (token, feature) and forms SiLU(g)*u in registers;
-//    outputs leave through LDS as whole rows;
+//    that fp16 output (in pair order) leaves through LDS as whole rows, while
+//    the down projection's fp32 rows go straight from the accumulators to
+//    memory, 64 contiguous bytes per 16 lanes (through LDS they took a
+//    barrier and a 66 KB round trip per tile: prefill T=2048 down 117 -> 103
+//    us);
 //  - each XCD takes a contiguous eighth of the row-tile list, so the row tiles
 //    of one expert share an L2 and its weights are fetched about once;
 //    consecutive workgroups of one XCD take the column tiles of one row tile.
@@ -347,29 +351,19 @@ __device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
             }
         }
     } else {
-        // y rows: [BM][OF] fp32
-        constexpr int OF = BN + 4;
-        float *o = (float *)&sm;
+        // y rows straight from the accumulators: for each (row group, j, cg)
+        // the 16 lanes of a lane group write 64 contiguous bytes of one row
 #pragma unroll
         for (int r = 0; r < MI; ++r)
 #pragma unroll
-            for (int cg = 0; cg < 4; ++cg)
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * r + 4 * g + j;
+                if (row < rows) {
+                    float *d = c.yout + (size_t)(rb + row) * N + ct * BN + 64 * wave + fr;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    o[(16 * r + 4 * g + j) * OF + 64 * wave + 16 * cg + fr] = acc[r][cg][j];
-        __syncthreads();
-        // rows x 1 KB: four threads per row, 256 bytes each
-        const int part = tid & 3;
-#pragma unroll
-        for (int r0 = 0; r0 < 16 * MI; r0 += 64) {
-            const int row = r0 + (tid >> 2);
-            if (row < rows) {
-                const uint4 *s = (const uint4 *)&o[row * OF + part * 64];
-                uint4 *d = (uint4 *)(c.yout + (size_t)(rb + row) * N + ct * BN + part * 64);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) d[i] = s[i];
+                    for (int cg = 0; cg < 4; ++cg) d[16 * cg] = acc[r][cg][j];
+                }
             }
-        }
     }
 }
 
