@@ -36,6 +36,9 @@ CSRC = os.path.join(ROOT, "sparse_moe_block_amd", "csrc")
 TRAFFIC_SOURCES = {"gemv_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "gemv.hip"],
                    "gemm2_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "gemm2.hip"]}
 
+HEADLINE = "deepseek4096"   # the largest configuration, MFMA-bound (grouped GEMM)
+DECODE_EXTRA = "decode16"   # the metric's HBM-bound decode point, carried as "decode"
+
 WORKLOADS = {
     # name: (config, T, weight copies)
     "decode16": (moegen.QWEN3_DECODE, 16, 16),
@@ -57,9 +60,15 @@ WORKLOADS = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode16", choices=sorted(WORKLOADS))
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="deepseek4096", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-decode-extra", dest="decode_extra", action="store_false",
+                    help="skip the decode T=16 figures the default line carries under "
+                         "'decode' (the metric's HBM-bound point)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="instead of the layer: measure the fp16 MFMA and streaming-read "
+                         "peaks of this GPU with the microbenchmarks of libfwpeak.so")
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
     ap.add_argument("--three-calls", action="store_true",
                     help="time the layer as fw_moe_route + fw_moe_permute + fw_moe_forward "
@@ -67,7 +76,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="time direct launches only (value from the direct loop)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--reduce-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="instead of benchmarking: turn two rocprofv3 --pmc output "
                          "directories (FETCH_SIZE, WRITE_SIZE) of this workload run "
@@ -100,17 +109,53 @@ def main():
     if a.sweep:
         sweep(a)
         return
-    cfg, T, copies = WORKLOADS[a.workload]
+    if a.peaks:
+        peaks(a)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    line, ctx = measure(a, a.workload, a.steps, a.warmup)
+    if a.decode_extra and a.workload == HEADLINE:
+        # the decode point of the metric (HBM-bound GEMV family), same timing rules
+        free(ctx)
+        ctx = None
+        dline, dctx = measure(a, DECODE_EXTRA, max(a.steps, 50), max(a.warmup, 10))
+        free(dctx)
+        line["decode"] = {k: dline[k] for k in ("value", "unit", "ms_per_step", "config",
+                                                "direct_ms_per_step", "stage_us", "roofline")}
+    if not a.no_cpu_baseline:
+        if ctx is None:
+            ctx = measure(a, a.workload, 0, 0, setup_only=True)[1]
+        line["cpu_baseline"] = cpu_baseline(ctx["cfg"], ctx["L"], ctx["x"], ctx["T"],
+                                            a.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def free(ctx):
+    if ctx is not None:
+        ctx.clear()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def measure(a, workload, steps, warmup, setup_only=False):
+    """One workload: K timed steps of the layer (HIP-graph replays; the same K
+    steps as direct launches with per-stage events), the dominant kernel's
+    roofline.  Returns the JSON fields and the layer (for the CPU baseline)."""
+    cfg, T, copies = WORKLOADS[workload]
+    dev = torch.device("cuda:0")
     L = moegen.make_layer(cfg, device=dev)
     x = moegen.make_x(cfg, T, device=dev)
+    ctx = {"cfg": cfg, "L": L, "x": x, "T": T}
+    if setup_only:
+        return None, ctx
     layers = [L]
     for _ in range(copies - 1):
         layers.append(moegen.Layer(cfg, L.router, L.bias, L.w_gate.clone(), L.w_up.clone(),
                                    L.w_down.clone(),
                                    *(None if t is None else t.clone()
                                      for t in (L.s_gate, L.s_up, L.s_down))))
+    ctx["layers"] = layers
     desc = fw.make_desc(cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn, cfg.shared_ffn,
                         cfg.act_dtype, cfg.router_dtype, cfg.expert_q, cfg.shared_q,
                         cfg.score, a.path)
@@ -124,16 +169,21 @@ def main():
     inv = torch.empty(P, dtype=torch.int32, device=dev)
     out = torch.empty(T, H, device=dev)
     ws = torch.empty(fw.fw_moe_workspace_size(desc, T), dtype=torch.uint8, device=dev)
+    ctx["bufs"] = (logits, ids, w, off, sp, inv, out, ws)
     fw.fw_moe_clear_status(ws)
     stream = torch.cuda.current_stream()
 
-    def step(i, s=stream):
+    def step(i, s=stream, events=None):
         Li = layers[i % copies]
         if a.three_calls:
             fw.fw_moe_route(desc, T, x, Li.router, Li.bias, None, logits, ids, w, s)
             fw.fw_moe_permute(desc, T, ids, off, sp, inv, ws, stream=s)
             fw.fw_moe_forward(desc, T, x, Li.w_gate, Li.w_up, Li.w_down, Li.s_gate, Li.s_up,
                               Li.s_down, w, off, sp, inv, out, ws, stream=s)
+        elif events is not None:
+            fw.fw_moe_layer_timed(desc, T, x, Li.router, Li.bias, Li.w_gate, Li.w_up,
+                                  Li.w_down, Li.s_gate, Li.s_up, Li.s_down, logits, ids, w,
+                                  off, sp, inv, out, ws, events, stream=s)
         else:
             fw.fw_moe_layer(desc, T, x, Li.router, Li.bias, Li.w_gate, Li.w_up, Li.w_down,
                             Li.s_gate, Li.s_up, Li.s_down, logits, ids, w, off, sp, inv, out,
@@ -147,31 +197,32 @@ def main():
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    for i in range(a.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    assert fw.fw_moe_read_status(ws) == 0
+    status = fw.fw_moe_read_status(ws)
+    assert status == 0, f"device status {status}"
     n_active = int((torch.diff(off) > 0).sum())
 
-    # per-step stage events (HIP events recorded by the library on `stream`)
+    # the K steps launched directly, each with its own stage events (HIP events
+    # the library records on `stream` around the forward's stages); the
+    # three-call form has no stage events and its stages are not timed
+    timed = not a.three_calls
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(fw.FW_N_STAGE_EVENTS)]
-           for _ in range(a.steps)]
-    for e in evs:
-        fw.fw_moe_set_stage_events(e)   # creates the events
-    fw.fw_moe_set_stage_events(None)
-    torch.cuda.synchronize()
+           for _ in range(steps)] if timed else None
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
-    for i in range(a.steps):
-        fw.fw_moe_set_stage_events(evs[i])
-        step(a.warmup + i)
+    for i in range(steps):
+        step(warmup + i, events=evs[i] if timed else None)
     t1.record(stream)
     torch.cuda.synchronize()
-    fw.fw_moe_set_stage_events(None)
-    direct_ms = t0.elapsed_time(t1) / a.steps
-    stage_ms = np.array([[e[s].elapsed_time(e[s + 1]) for s in range(4)] for e in evs])
-    stage_avg = stage_ms.mean(axis=0)
+    direct_ms = t0.elapsed_time(t1) / steps
+    if timed:
+        stage_ms = np.array([[e[s].elapsed_time(e[s + 1]) for s in range(4)] for e in evs])
+        stage_avg = stage_ms.mean(axis=0)
+    else:
+        stage_avg = np.full(4, np.nan)
 
     # the same K steps as HIP-graph replays (one captured step per weight copy;
     # decode runtimes replay the layer as a graph).  Every ABI call is
@@ -192,18 +243,22 @@ def main():
         graphs[0].replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), "graph replay differs from the eager step"
-        for i in range(a.warmup):
+        del eager
+        for i in range(warmup):
             graphs[i % copies].replay()
         torch.cuda.synchronize()
         g0 = torch.cuda.Event(enable_timing=True)
         g1 = torch.cuda.Event(enable_timing=True)
         g0.record()
-        for i in range(a.steps):
-            graphs[(a.warmup + i) % copies].replay()
+        for i in range(steps):
+            graphs[(warmup + i) % copies].replay()
         g1.record()
         torch.cuda.synchronize()
-        graph_ms = g0.elapsed_time(g1) / a.steps
+        graph_ms = g0.elapsed_time(g1) / steps
+        del graphs
     ms = graph_ms if graph_ms is not None else direct_ms
+    status = fw.fw_moe_read_status(ws)
+    assert status == 0, f"device status {status}"
 
     # dominant kernel: the gate/up projection (2/3 of the expert bytes and flops)
     path = fw.fw_moe_forward_path(desc, T)
@@ -227,20 +282,21 @@ def main():
                 "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / MFMA_FP16_PEAK_TFLOPS, "traffic": None,
                 "algorithmic_flops": gu_alg}
+    roof["duration_us"] = gu_ms * 1e3
     layer_bytes = (n_active * cfg.expert_bytes + cfg.shared_bytes + cfg.router_bytes +
                    cfg.act_bytes(T) + T * H * 4)
     fused = (not a.three_calls and path == fw.FW_PATH_GEMV and P <= 2048)
     stage0 = "front (top-k + permute + staging)" if fused else "prepare"
     layer_flops = 6 * P * H * cfg.ffn + 6 * T * H * cfg.shared_ffn + 2 * T * H * E
 
-    roof["traffic"] = traffic(a.workload, roof)
+    roof["traffic"] = traffic(workload, roof)
     line = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
@@ -260,9 +316,7 @@ def main():
                      zip([stage0, "gate_up", "down", "combine"], stage_avg)},
         "roofline": roof,
     }
-    if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, L, x, T, a.cpu_seconds)
-    print(json.dumps(line), flush=True)
+    return line, ctx
 
 
 def sweep(a):
@@ -378,6 +432,69 @@ def sweep(a):
     print(json.dumps({"sweep": a.sweep_layer, "crossover": summary}), flush=True)
 
 
+def peaks(a):
+    """The two ceilings, measured on this GPU with libfwpeak.so: dense fp16
+    MFMA throughput (16x16x32 and 32x32x16, every SIMD busy, eight independent
+    accumulators per wavefront) and HBM streaming bandwidth (a 4 GiB read with
+    16-byte loads; a 2 GiB copy).  One JSON line per figure, each the best of
+    five timed launches after a warm-up."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_moe_block_amd", "libfwpeak.so"))
+    lib.fw_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    lib.fw_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    lib.fw_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                 ctypes.c_int, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    def best(launch, n=5):
+        launch()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts)
+
+    blocks = cus * 8          # two 4-wave workgroups per SIMD pair: every SIMD busy
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    for shape, per, flops in ((16, 8, 16384), (32, 4, 32768)):
+        iters = 4000
+        t = best(lambda: lib.fw_peak_mfma(shape, blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                                          ctypes.c_void_p(stream.cuda_stream)))
+        total = blocks * 4 * iters * per * flops
+        print(json.dumps({"peak": f"fp16 mfma {shape}x{shape}x{512 // shape}", "cus": cus,
+                          "workgroups": blocks, "seconds": t,
+                          "TFLOP/s": total / t / 1e12}), flush=True)
+    nbytes = 4 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    for blocks in (cus * 4, cus * 8, cus * 16):
+        o = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+        t = best(lambda: lib.fw_peak_read(ctypes.c_void_p(src.data_ptr()), nbytes, blocks,
+                                          ctypes.c_void_p(o.data_ptr()),
+                                          ctypes.c_void_p(stream.cuda_stream)))
+        print(json.dumps({"peak": "hbm streaming read", "bytes": nbytes, "workgroups": blocks,
+                          "seconds": t, "GB/s": nbytes / t / 1e9}), flush=True)
+    half = nbytes // 2
+    dst = torch.empty(half // 4, dtype=torch.int32, device=dev)
+    for blocks in (cus * 4, cus * 8):
+        t = best(lambda: lib.fw_peak_copy(ctypes.c_void_p(src.data_ptr()),
+                                          ctypes.c_void_p(dst.data_ptr()), half, blocks,
+                                          ctypes.c_void_p(stream.cuda_stream)))
+        print(json.dumps({"peak": "hbm copy (read + write)", "bytes_moved": 2 * half,
+                          "workgroups": blocks, "seconds": t,
+                          "GB/s": 2 * half / t / 1e9}), flush=True)
+
+
 def source_hash(kernel):
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES[kernel]:
@@ -455,30 +572,60 @@ def reduce_counters(a):
     print(json.dumps(res))
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, L, x, T, seconds):
-    """The CPU oracle (route + forward) on the same batch, repeated for about
-    `seconds`, on all host cores."""
+    """The CPU oracle (route + forward) on a bounded sample of the batch's
+    tokens: consecutive 16-token slices of the same batch, routed and run
+    through the layer, for about `seconds` on all host cores; then a few
+    tokens on one core.  Tokens are independent, so tokens/s of the sample is
+    the oracle's rate on the workload."""
     from oracle import fwref
     h = moegen.as_numpy_bits
     xh, wr, bias = h(x), h(L.router), h(L.bias)
     wg, wu, wd = h(L.w_gate), h(L.w_up), h(L.w_down)
     sg, su, sd = h(L.s_gate), h(L.s_up), h(L.s_down)
+
+    def run(tok, threads):
+        xs = np.ascontiguousarray(xh[tok])
+        _, ids, w = fwref.route(xs, wr, bias, k=cfg.top_k, act_dtype=cfg.act_dtype,
+                                router_dtype=cfg.router_dtype, score=cfg.score)
+        fwref.forward(xs, wg, wu, wd, ids, w, n_experts=cfg.n_experts, ffn=cfg.ffn,
+                      qtype=cfg.expert_q, act_dtype=cfg.act_dtype, s_gate=sg, s_up=su,
+                      s_down=sd, shared_ffn=cfg.shared_ffn, shared_q=cfg.shared_q,
+                      n_threads=threads)
+
     threads = fwref.threads(0)
+    chunk = min(T, 16)
     n = 0
     t0 = time.perf_counter()
     while True:
-        _, ids, w = fwref.route(xh, wr, bias, k=cfg.top_k, act_dtype=cfg.act_dtype,
-                                router_dtype=cfg.router_dtype, score=cfg.score)
-        fwref.forward(xh, wg, wu, wd, ids, w, n_experts=cfg.n_experts, ffn=cfg.ffn,
-                      qtype=cfg.expert_q, act_dtype=cfg.act_dtype, s_gate=sg, s_up=su,
-                      s_down=sd, shared_ffn=cfg.shared_ffn, shared_q=cfg.shared_q)
+        lo = (n * chunk) % T
+        run(np.arange(lo, min(lo + chunk, T)), 0)
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": n * T / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} passes of route+forward over the same {T}-token batch "
-                      f"({el:.1f} s)"}
+    tokens = n * chunk if T >= chunk else n * T
+    one = min(T, 2)
+    t1 = time.perf_counter()
+    run(np.arange(one), 1)
+    el1 = time.perf_counter() - t1
+    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} slices of {chunk} consecutive tokens of the {T}-token batch "
+                      f"({tokens} tokens, route + forward, {el:.1f} s)",
+            "cpu_model": cpu_model(),
+            "one_core": {"value": one / el1, "unit": "tokens/s",
+                         "sample": f"tokens 0..{one - 1}, route + forward ({el1:.1f} s)"}}
 
 
 if __name__ == "__main__":

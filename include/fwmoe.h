@@ -38,6 +38,10 @@
  *    workspace.  fw_moe_read_status reads it; fw_moe_clear_status resets it.
  *  - Results are deterministic: repeated calls on the same inputs are bitwise
  *    identical (no floating-point atomics; fixed summation orders).
+ *  - Stateless and thread-safe: the library keeps no state between calls
+ *    beyond per-device properties it queries once (CU count, kernel
+ *    occupancy); calls from several host threads on their own streams and
+ *    workspaces do not interfere.
  *
  * GGUF block layouts (the pages name the formats but print no byte layout; the
  * layout is GGUF's, little-endian, no padding):
@@ -74,8 +78,14 @@ enum {
     FW_STATUS_BAD_EXPERT_ID = 1, /* fw_moe_permute met an id outside [0, E)      */
     FW_STATUS_BAD_OFFSETS = 2,   /* fw_moe_forward met non-monotone / out-of-range
                                     expert_offsets (clamped)                     */
-    FW_STATUS_BAD_PAIR = 4       /* fw_moe_forward met a sorted_pairs / inv_pos
+    FW_STATUS_BAD_PAIR = 4,      /* fw_moe_forward met a sorted_pairs / inv_pos
                                     entry out of range (skipped)                 */
+    FW_STATUS_RANGE = 8          /* fw_moe_forward met a value its fp16 operands
+                                    cannot hold: a non-finite activation, a
+                                    SwiGLU output beyond +-65504 after the
+                                    per-token scaling, or (grouped GEMM) a block
+                                    scale whose dequantised codes exceed fp16;
+                                    the affected outputs are not reliable       */
 };
 
 enum { FW_F32 = 0, FW_BF16 = 1 };                 /* activation / router dtype */
@@ -166,14 +176,27 @@ int fw_moe_permute(const fw_moe_desc *desc, int32_t T, const int32_t *topk_ids,
  * out      [T][H] fp32 out (fully overwritten)
  * workspace / ws_bytes: at least fw_moe_workspace_size(desc, T) bytes.
  * Numerics: both families round the activations x and the SwiGLU output h to
- * fp16 and accumulate in fp32.  The GEMV family (small T) multiplies the exact
+ * fp16 and accumulate in fp32.  Each token row is first scaled by a power of
+ * two that puts its largest magnitude in [16, 32) (x * 2^e; g and u are
+ * scaled back exactly before SwiGLU, h is held at 2^(2e) and the down
+ * projection's sums are scaled back exactly), so a finite row of any
+ * magnitude uses fp16's normal range like a unit-scale row.  The GEMV family (small T) multiplies the exact
  * weight codes (fp16 holds every Q8_0/Q4_0/Q4_K code) by fp16 activations in
  * fp32 dot products and applies each block's scale (Q4_K: each 32-element
  * sub-block's d * scale, and dmin * min times the sub-block's activation sum)
  * in fp32; the GEMM family (large T) contracts on fp16 MFMA with weights
  * dequantised to fp16 (code times scale, or for Q4_K d * scale * q - dmin *
  * min formed in fp32; one rounding).  Either way a layer output stays within
- * 2e-3 max-abs and 1e-3 relative L2 of an fp64 evaluation of the same layer.
+ * 2e-3 max-abs and 1e-3 relative L2 of an fp64 evaluation of the same layer
+ * for unit-scale inputs like the workloads' (N(0,1) activations, weights of
+ * std 0.015-0.02), and each token row within the same relative error at any
+ * finite scale.  What fp16 cannot hold is reported, not clamped:
+ * FW_STATUS_RANGE is set for a non-finite x, for a scaled h beyond +-65504
+ * (very large weights), and, in the GEMM family, for a block scale above
+ * 31.98 (Q8_0) or 511.75 (Q4_0) -- 16x the extreme code times the scale must
+ * stay within fp16 -- or a Q4_K sub-block whose 16 (15 |d scale| + |dmin
+ * min|) exceeds 65504.  The GEMV family has no weight limit (codes stay
+ * exact, scales apply in fp32).
  * Q4_K (GGUF K-quant, 144-byte super-blocks of 256 elements) needs H, F and
  * Fs to be multiples of 256, which every descriptor already is.
  * Batch limit: T * k * max(H, F, Fs) < 2^31 (the kernels' row offsets are
@@ -231,15 +254,24 @@ int fw_moe_read_status(const void *workspace, int32_t *host_status);
 /* Human-readable text of a return code. */
 const char *fw_moe_status_string(int status);
 
-/* Benchmark instrumentation.  When `events` is non-NULL it must point to
- * FW_N_STAGE_EVENTS hipEvent_t handles; every later fw_moe_forward records
- * events[0] before its first kernel and events[s+1] after stage s, s in
- * {0: prepare, 1: gate/up projection, 2: down projection, 3: combine}, on its
- * stream; fw_moe_layer records the same five (stage 0 is then the fused
- * front end or the staging kernel; the logits, top-k and permutation
- * launches that precede it fall outside).  NULL turns recording off.  Process-wide and not thread-safe. */
+/* fw_moe_layer with timing events: the same validation, launches and results
+ * as fw_moe_layer, plus HIP events recorded on `stream` around the forward's
+ * stages: stage_events[0] before its first kernel and stage_events[s+1]
+ * after stage s, s in {0: the fused front end (GEMV batches) or the
+ * activation staging, 1: gate/up projection, 2: down projection, 3:
+ * combine}; the logits, top-k and permutation launches that precede stage 0
+ * fall outside.  stage_events: FW_N_STAGE_EVENTS caller-created hipEvent_t
+ * handles (required; FW_EINVAL if any is NULL).  For benchmarks and
+ * profilers: it keeps no state between calls, so concurrent callers with
+ * their own events and workspaces do not interfere. */
 enum { FW_N_STAGE_EVENTS = 5 };
-int fw_moe_set_stage_events(void *const *events);
+int fw_moe_layer_timed(const fw_moe_desc *desc, int32_t T, const void *x,
+                       const void *router_w, const float *logit_bias, const void *w_gate,
+                       const void *w_up, const void *w_down, const void *ws_gate,
+                       const void *ws_up, const void *ws_down, float *logits,
+                       int32_t *topk_ids, float *topk_w, int32_t *expert_offsets,
+                       int32_t *sorted_pairs, int32_t *inv_pos, float *out, void *workspace,
+                       size_t ws_bytes, void *const *stage_events, void *stream);
 
 #ifdef __cplusplus
 }

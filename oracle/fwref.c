@@ -310,9 +310,9 @@ int fwref_forward(int T, int H, int E, int k, int F, int qtype, int Fs, int qtyp
     int maxf = F > Fs ? F : Fs;
     int maxr = H > maxf ? H : maxf;
 #ifdef _OPENMP
-    if (n_threads > 0)
-        omp_set_num_threads(n_threads);
-#pragma omp parallel
+    /* a per-region thread count: a request here does not change later calls */
+    int nt = n_threads > 0 ? n_threads : omp_get_max_threads();
+#pragma omp parallel num_threads(nt)
 #endif
     {
         float *xf = malloc(sizeof(float) * (size_t)H);

@@ -11,7 +11,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfwmoe.so")
-SOURCES = ["abi.hip", "route.hip", "permute.hip", "forward.hip", "gemv.hip", "gemm.hip", "gemm2.hip", "layer.hip"]
+# the peak microbenchmarks (fp16 MFMA, HBM streaming): a library of their own
+PEAK_SOURCE = "peak.hip"
+PEAK_LIB = os.path.join(PKG, "libfwpeak.so")
+SOURCES = ["abi.hip", "route.hip", "permute.hip", "forward.hip", "gemv.hip", "gemm2.hip", "layer.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall",
@@ -39,7 +42,8 @@ def build(jobs=None, verbose=False):
     os.makedirs(OBJ, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(_compile, SOURCES + [PEAK_SOURCE]))
+    peak_obj, _ = results.pop()
     for _, msg in results:
         if verbose and msg.strip():
             print(msg, file=sys.stderr)
@@ -47,6 +51,10 @@ def build(jobs=None, verbose=False):
     subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp]
                           + [o for o, _ in results])
     os.replace(tmp, LIB)
+    tmp = PEAK_LIB + ".tmp"
+    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
+                           peak_obj])
+    os.replace(tmp, PEAK_LIB)
     return LIB
 
 

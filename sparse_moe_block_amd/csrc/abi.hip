@@ -22,7 +22,7 @@ WsLayout ws_layout(const fw_moe_desc &d, int T) {
         off = align256(off + bytes);
         return at;
     };
-    // row tiles of either family: GEMM tiles of kGemmBM rows, GEMV chunks of
+    // row tiles of either family: GEMM tiles of kGemm2BM rows, GEMV chunks of
     // kGemvTokens rows (the larger count)
     L.max_tiles = (int)((P + kGemvTokens - 1) / kGemvTokens + E);
     L.active = take((E + 1) * sizeof(int4));
@@ -32,6 +32,8 @@ WsLayout ws_layout(const fw_moe_desc &d, int T) {
     L.y = take((P + (Fs ? (size_t)T : 0)) * H * 4);
     L.split_cnt = take((size_t)kSplitTiles * 4);
     L.split_part = take((size_t)kSplitTiles * kSplitSlicesMax * 2 * kGemvTokens * kWave * 4);
+    L.xe = take((size_t)T * 4);
+    L.he = take((P + (size_t)T) * 4);
     L.xsum = take((size_t)T * (H / 32) * 4);
     L.hsum = take((P * (F / 32) + (size_t)T * (Fs / 32)) * 4);
     L.perm = take(E * (size_t)(perm_blocks((long long)P) + 1) * 4);
@@ -44,9 +46,6 @@ WsLayout ws_layout(const fw_moe_desc &d, int T) {
 using namespace fw;
 
 namespace {
-
-hipEvent_t g_events[FW_N_STAGE_EVENTS];
-bool g_events_on = false;
 
 bool al16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 bool al256(const void *p) { return ((uintptr_t)p & 255) == 0; }
@@ -62,8 +61,6 @@ int check_desc(const fw_moe_desc *d) {
     if (d->router_dtype != FW_F32 && d->router_dtype != FW_BF16) return FW_EINVAL;
     if (d->expert_q < FW_Q8_0 || d->expert_q > FW_Q4_K) return FW_EINVAL;
     if (d->shared_q < FW_Q8_0 || d->shared_q > FW_Q4_K) return FW_EINVAL;
-    // the LDS-dequant grouped GEMM decodes Q8_0 / Q4_0 only
-    if (!kUseGemm2 && (d->expert_q == FW_Q4_K || d->shared_q == FW_Q4_K)) return FW_EUNSUPPORTED;
     if (d->score != FW_SOFTMAX_RENORM && d->score != FW_SIGMOID_RENORM) return FW_EINVAL;
     if (d->path < FW_PATH_AUTO || d->path > FW_PATH_GEMM) return FW_EINVAL;
     if (d->router_dtype != d->act_dtype) return FW_EUNSUPPORTED;
@@ -143,29 +140,61 @@ struct FrontArgs {
 };
 
 // The forward's launches: staging (or, with `front`, the fused top-k +
-// permutation + staging kernel), gate/up, down, combine; stage events around
-// each when they are on.
-int enqueue_forward(const FwdArgs &a, const FrontArgs *front, hipStream_t s) {
+// permutation + staging kernel), gate/up, down, combine; with `ev`
+// (FW_N_STAGE_EVENTS events) an event before the first and after each.
+int enqueue_forward(const FwdArgs &a, const FrontArgs *front, const hipEvent_t *ev,
+                    hipStream_t s) {
     int rc;
-    const bool ev = g_events_on;
-    if (ev) (void)hipEventRecord(g_events[0], s);
+    if (ev) (void)hipEventRecord(ev[0], s);
     rc = hip_status(front ? launch_decode_front(a, front->logits, front->ids, front->w,
                                                 front->offsets, front->sorted, front->inv, s)
                           : launch_prepare(a, s));
     if (rc != FW_OK) return rc;
-    if (ev) (void)hipEventRecord(g_events[1], s);
+    if (ev) (void)hipEventRecord(ev[1], s);
     const bool gemm = a.path == FW_PATH_GEMM;
-    rc = hip_status(gemm ? (kUseGemm2 ? launch_gemm2_gate_up(a, s) : launch_gemm_gate_up(a, s))
-                         : launch_gemv_gate_up(a, s));
+    rc = hip_status(gemm ? launch_gemm2_gate_up(a, s) : launch_gemv_gate_up(a, s));
     if (rc != FW_OK) return rc;
-    if (ev) (void)hipEventRecord(g_events[2], s);
-    rc = hip_status(gemm ? (kUseGemm2 ? launch_gemm2_down(a, s) : launch_gemm_down(a, s))
-                         : launch_gemv_down(a, s));
+    if (ev) (void)hipEventRecord(ev[2], s);
+    rc = hip_status(gemm ? launch_gemm2_down(a, s) : launch_gemv_down(a, s));
     if (rc != FW_OK) return rc;
-    if (ev) (void)hipEventRecord(g_events[3], s);
+    if (ev) (void)hipEventRecord(ev[3], s);
     if ((rc = hip_status(launch_combine(a, s))) != FW_OK) return rc;
-    if (ev) (void)hipEventRecord(g_events[4], s);
+    if (ev) (void)hipEventRecord(ev[4], s);
     return FW_OK;
+}
+
+// fw_moe_layer: every argument of the three stages is checked before anything
+// is enqueued; `ev` as in enqueue_forward.
+int layer_impl(const fw_moe_desc *desc, int32_t T, const void *x, const void *router_w,
+               const float *logit_bias, const void *w_gate, const void *w_up,
+               const void *w_down, const void *ws_gate, const void *ws_up, const void *ws_down,
+               float *logits, int32_t *topk_ids, float *topk_w, int32_t *expert_offsets,
+               int32_t *sorted_pairs, int32_t *inv_pos, float *out, void *workspace,
+               size_t ws_bytes, const hipEvent_t *ev, hipStream_t s) {
+    int rc = check_desc(desc);
+    if (rc != FW_OK) return rc;
+    if ((rc = check_T(desc, T)) != FW_OK) return rc;
+    if (T == 0) return FW_OK;
+    if (!router_w || !logits || !topk_ids || !topk_w || !expert_offsets) return FW_EINVAL;
+    if (!al16(router_w) || !al16(logits) || !al16(topk_ids) || (logit_bias && !al16(logit_bias)))
+        return FW_EALIGN;
+    FwdArgs a;
+    rc = forward_args(desc, T, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, topk_w,
+                      expert_offsets, sorted_pairs, inv_pos, out, workspace, ws_bytes, &a);
+    if (rc != FW_OK) return rc;
+    if ((rc = hip_status(launch_logits(*desc, T, x, router_w, logit_bias, logits, s))) != FW_OK)
+        return rc;
+    if (decode_front_fits(*desc, T, a.path)) {
+        FrontArgs f{logits, topk_ids, topk_w, expert_offsets, sorted_pairs, inv_pos};
+        return enqueue_forward(a, &f, ev, s);
+    }
+    if ((rc = hip_status(launch_topk(*desc, T, logits, topk_ids, topk_w, s))) != FW_OK) return rc;
+    const long long P = (long long)T * desc->top_k;
+    int32_t *perm = P > kPermOneBlockMaxP ? (int32_t *)(a.ws + a.L.perm) : nullptr;
+    rc = hip_status(launch_permute(*desc, T, topk_ids, expert_offsets, sorted_pairs, inv_pos,
+                                   (WsHeader *)workspace, perm, s));
+    if (rc != FW_OK) return rc;
+    return enqueue_forward(a, nullptr, ev, s);
 }
 
 }  // namespace
@@ -252,7 +281,7 @@ int fw_moe_forward(const fw_moe_desc *desc, int32_t T, const void *x, const void
     rc = forward_args(desc, T, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, topk_w,
                       expert_offsets, sorted_pairs, inv_pos, out, workspace, ws_bytes, &a);
     if (rc != FW_OK) return rc;
-    return enqueue_forward(a, nullptr, (hipStream_t)stream);
+    return enqueue_forward(a, nullptr, nullptr, (hipStream_t)stream);
 }
 
 int fw_moe_layer(const fw_moe_desc *desc, int32_t T, const void *x, const void *router_w,
@@ -261,32 +290,25 @@ int fw_moe_layer(const fw_moe_desc *desc, int32_t T, const void *x, const void *
                  const void *ws_down, float *logits, int32_t *topk_ids, float *topk_w,
                  int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *inv_pos, float *out,
                  void *workspace, size_t ws_bytes, void *stream) {
-    int rc = check_desc(desc);
-    if (rc != FW_OK) return rc;
-    if ((rc = check_T(desc, T)) != FW_OK) return rc;
-    if (T == 0) return FW_OK;
-    // every argument of the three stages is checked before anything is enqueued
-    if (!router_w || !logits || !topk_ids || !topk_w || !expert_offsets) return FW_EINVAL;
-    if (!al16(router_w) || !al16(logits) || !al16(topk_ids) || (logit_bias && !al16(logit_bias)))
-        return FW_EALIGN;
-    FwdArgs a;
-    rc = forward_args(desc, T, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, topk_w,
-                      expert_offsets, sorted_pairs, inv_pos, out, workspace, ws_bytes, &a);
-    if (rc != FW_OK) return rc;
-    hipStream_t s = (hipStream_t)stream;
-    if ((rc = hip_status(launch_logits(*desc, T, x, router_w, logit_bias, logits, s))) != FW_OK)
-        return rc;
-    if (decode_front_fits(*desc, T, a.path)) {
-        FrontArgs f{logits, topk_ids, topk_w, expert_offsets, sorted_pairs, inv_pos};
-        return enqueue_forward(a, &f, s);
-    }
-    if ((rc = hip_status(launch_topk(*desc, T, logits, topk_ids, topk_w, s))) != FW_OK) return rc;
-    const long long P = (long long)T * desc->top_k;
-    int32_t *perm = P > kPermOneBlockMaxP ? (int32_t *)(a.ws + a.L.perm) : nullptr;
-    rc = hip_status(launch_permute(*desc, T, topk_ids, expert_offsets, sorted_pairs, inv_pos,
-                                   (WsHeader *)workspace, perm, s));
-    if (rc != FW_OK) return rc;
-    return enqueue_forward(a, nullptr, s);
+    return layer_impl(desc, T, x, router_w, logit_bias, w_gate, w_up, w_down, ws_gate, ws_up,
+                      ws_down, logits, topk_ids, topk_w, expert_offsets, sorted_pairs, inv_pos,
+                      out, workspace, ws_bytes, nullptr, (hipStream_t)stream);
+}
+
+int fw_moe_layer_timed(const fw_moe_desc *desc, int32_t T, const void *x,
+                       const void *router_w, const float *logit_bias, const void *w_gate,
+                       const void *w_up, const void *w_down, const void *ws_gate,
+                       const void *ws_up, const void *ws_down, float *logits,
+                       int32_t *topk_ids, float *topk_w, int32_t *expert_offsets,
+                       int32_t *sorted_pairs, int32_t *inv_pos, float *out, void *workspace,
+                       size_t ws_bytes, void *const *stage_events, void *stream) {
+    if (!stage_events) return FW_EINVAL;
+    for (int i = 0; i < FW_N_STAGE_EVENTS; ++i)
+        if (!stage_events[i]) return FW_EINVAL;
+    return layer_impl(desc, T, x, router_w, logit_bias, w_gate, w_up, w_down, ws_gate, ws_up,
+                      ws_down, logits, topk_ids, topk_w, expert_offsets, sorted_pairs, inv_pos,
+                      out, workspace, ws_bytes, (const hipEvent_t *)stage_events,
+                      (hipStream_t)stream);
 }
 
 int fw_moe_clear_status(void *workspace, void *stream) {
@@ -311,19 +333,6 @@ const char *fw_moe_status_string(int status) {
         case FW_EHIP: return "HIP runtime error";
         default: return "unknown status";
     }
-}
-
-int fw_moe_set_stage_events(void *const *events) {
-    if (!events) {
-        g_events_on = false;
-        return FW_OK;
-    }
-    for (int i = 0; i < FW_N_STAGE_EVENTS; ++i) {
-        if (!events[i]) return FW_EINVAL;
-        g_events[i] = (hipEvent_t)events[i];
-    }
-    g_events_on = true;
-    return FW_OK;
 }
 
 }  // extern "C"

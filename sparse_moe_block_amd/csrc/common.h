@@ -11,13 +11,12 @@
 namespace fw {
 
 constexpr int kWave = 64;
+constexpr int kMaxDevices = 64;   // per-device caches of device properties
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 16;
 constexpr int kUnit = 256;        // elements per 16-byte-aligned run of 8 blocks
 constexpr int kGemvTokens = 2;    // token rows a GEMV work item carries
-constexpr int kGemmBM = 128;      // token rows per tile of the LDS-dequant grouped GEMM
 constexpr int kGemm2BM = 64;      // token rows per tile of the register-dequant grouped GEMM
-constexpr bool kUseGemm2 = true;  // which grouped GEMM serves the GEMM path
 // AUTO: the GEMV family while the routed pairs average at most this many rows
 // per expert (T * k <= 2 E), the grouped GEMM above.  Measured crossovers, in
 // rows per expert: the hidden-4096 / 64-expert top-4 layer between 2 and 3
@@ -30,6 +29,22 @@ constexpr int kLogitsTileMaxT = 64;
 // into at most kSplitSlicesMax reduction slices each
 constexpr int kSplitTiles = 1024;
 constexpr int kSplitSlicesMax = 8;
+
+// Per-token scaling of the fp16 operands.  Each token row of x is staged as
+// x * 2^e, e chosen so that its largest magnitude lands in
+// [2^(kXExp-1), 2^kXExp): any finite row then uses fp16's normal range the
+// same way, whatever its own scale.  The gate/up accumulators are multiplied
+// by 2^-e (exact) before SwiGLU, and the SwiGLU output h is stored as
+// h * 2^(2e) -- g and u scale with x, so that keeps h near the range of a
+// unit-scale row -- and the down projection's accumulators are multiplied by
+// 2^-2e.  kXExp = 5 leaves h about 16x of headroom below fp16's 65504 on
+// the workloads' weights; larger values set FW_STATUS_RANGE.
+constexpr int kXExp = 5;
+// Largest fp16 scale bits (magnitude) whose 16x-scaled extreme code stays
+// within fp16 in the grouped GEMM's dequantised weights: Q4_0 16 * 8 * d
+// <= 65504 (d <= 511.75), Q8_0 16 * 128 * d <= 65504 (d <= 31.984375).
+constexpr uint32_t kQ4DMaxBits = 0x5FFFu;
+constexpr uint32_t kQ8DMaxBits = 0x4FFFu;
 
 // First 256 bytes of every workspace.
 struct WsHeader {
@@ -49,6 +64,8 @@ struct WsLayout {
     size_t y;        // f32  [P][H] then [T][H]   per-pair expert outputs
     size_t split_cnt;   // int [kSplitTiles]      split-K arrival counters
     size_t split_part;  // f32 [kSplitTiles * kSplitSlicesMax][2 * kGemvTokens][64] partials
+    size_t xe;       // int  [T]                  power-of-two exponent x16 row t is scaled by
+    size_t he;       // int  [P + T]              the same for h rows (2 xe of the row's token)
     size_t xsum;     // f32  [T][H/32]            32-element block sums of x16 (Q4_K GEMV)
     size_t hsum;     // f32  [P][F/32] then [T][Fs/32]   block sums of h (Q4_K GEMV)
     size_t perm;     // int [E][nb + 1]              multi-block permutation: per-block
@@ -155,6 +172,14 @@ __device__ __forceinline__ int pair_pos(int i) {   // element i -> half index in
 
 // Block B of a unit as 16 exact fp16 pairs (in pair order) times its scale d:
 // value of element i = d * (pair value), pairs j = 1, 3 scaled by 16.
+// The integer-to-fp16 step is the published "magic number" conversion: OR the
+// code bits into the mantissa of an fp16 1024 (exponent 0x6400), then subtract
+// the constant, all exact (Kim et al., "Who Says Elephants Can't Run: Bringing
+// Large Scale MoE Models into Cloud Scale Production", arXiv 2211.10017, and
+// the interleaved int4 -> fp16 conversion of NVIDIA FasterTransformer).  What
+// is ours: the pair order below (one mask per pair, high nibbles kept in place
+// as 16 q with the matching activations pre-scaled by 1/16), the v_perm form
+// for Q8_0, and the block scale applied in one rounding.
 //  Q4_0: (c & 0x000F000F) | 0x6400_6400 is the pair 1024 + q; minus 1032 gives
 //        q - 8.  The high nibbles masked in place give 1024 + 16q; minus 1152
 //        gives 16(q - 8).
@@ -287,8 +312,6 @@ struct FwdArgs {
 hipError_t launch_prepare(const FwdArgs &a, hipStream_t s);
 hipError_t launch_gemv_gate_up(const FwdArgs &a, hipStream_t s);
 hipError_t launch_gemv_down(const FwdArgs &a, hipStream_t s);
-hipError_t launch_gemm_gate_up(const FwdArgs &a, hipStream_t s);
-hipError_t launch_gemm_down(const FwdArgs &a, hipStream_t s);
 hipError_t launch_gemm2_gate_up(const FwdArgs &a, hipStream_t s);
 hipError_t launch_gemm2_down(const FwdArgs &a, hipStream_t s);
 hipError_t launch_combine(const FwdArgs &a, hipStream_t s);

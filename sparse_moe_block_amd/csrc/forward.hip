@@ -8,24 +8,23 @@ namespace {
 
 // Block 0 turns expert_offsets into the list of active experts
 // (expert, first row, rows) and the row-tile list -- each active expert's rows
-// cut into tiles of at most tile_rows (the grouped GEMM's 128-row tiles, or the
+// cut into tiles of at most tile_rows (the grouped GEMM's 64-row tiles, or the
 // GEMV's token chunks) -- clamping anything out of range
-// (FW_STATUS_BAD_OFFSETS).  The other blocks stage the token rows in fp16
-// (bf16 values are exact in fp16), one 32-element block per thread over the
-// T * H / 32 blocks of x, in the pair order both kernel families consume (see
-// decode_pairs).
+// (FW_STATUS_BAD_OFFSETS).  In the other blocks each wavefront stages one
+// token row in fp16, scaled by its power-of-two exponent (stage_x_row), in
+// the pair order both kernel families consume (see decode_pairs).
 __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(
     const int32_t *__restrict__ offsets, int E, int P, const void *__restrict__ x, int act_bf16,
     int H, int T, int tile_rows, int max_tiles, int4 *__restrict__ active, int4 *__restrict__ tiles,
-    _Float16 *__restrict__ x16, float *__restrict__ xsum, int *__restrict__ split_cnt,
-    WsHeader *__restrict__ hdr) {
+    _Float16 *__restrict__ x16, float *__restrict__ xsum, int32_t *__restrict__ xe,
+    int *__restrict__ split_cnt, WsHeader *__restrict__ hdr) {
     if (blockIdx.x == 0) {
         build_schedule(offsets, E, P, tile_rows, max_tiles, active, tiles, split_cnt, hdr);
         return;
     }
-    const long long idx = (long long)(blockIdx.x - 1) * kPrepThreads + threadIdx.x;
-    if (idx >= (long long)T * (H / 32)) return;
-    stage_x_block(x, act_bf16, H, (int)(idx / (H / 32)), (int)(idx % (H / 32)), x16, xsum);
+    const int t = (blockIdx.x - 1) * (kPrepThreads / kWave) + wave_id();
+    if (t >= T) return;
+    stage_x_row(x, act_bf16, H, t, x16, xsum, xe, hdr);
 }
 
 // out[t][o] = sum_{j<k} w[t][j] * y[inv[t*k+j]][o]  (slot order)  + y_shared[t][o]
@@ -65,16 +64,16 @@ __global__ __launch_bounds__(256) void combine_kernel(
 }  // namespace
 
 hipError_t launch_prepare(const FwdArgs &a, hipStream_t s) {
-    const int tile_rows = a.path == FW_PATH_GEMM ? (kUseGemm2 ? kGemm2BM : kGemmBM) : kGemvTokens;
+    const int tile_rows = a.path == FW_PATH_GEMM ? kGemm2BM : kGemvTokens;
     // the Q4_K GEMV needs the activation rows' block sums
     const bool sums = a.path == FW_PATH_GEMV &&
                       (a.d.expert_q == FW_Q4_K || (a.d.shared_ffn > 0 && a.d.shared_q == FW_Q4_K));
-    const long long xblocks = (long long)a.T * (a.d.hidden / 32);
-    prepare_kernel<<<1 + (int)((xblocks + kPrepThreads - 1) / kPrepThreads), kPrepThreads, 0, s>>>(
+    constexpr int rows_per_block = kPrepThreads / kWave;   // one wavefront per token row
+    prepare_kernel<<<1 + (a.T + rows_per_block - 1) / rows_per_block, kPrepThreads, 0, s>>>(
         a.offsets, a.d.n_experts, a.P, a.x, a.d.act_dtype == FW_BF16, a.d.hidden, a.T, tile_rows,
         a.L.max_tiles, (int4 *)(a.ws + a.L.active), (int4 *)(a.ws + a.L.tiles),
         (_Float16 *)(a.ws + a.L.x16), sums ? (float *)(a.ws + a.L.xsum) : nullptr,
-        (int *)(a.ws + a.L.split_cnt), (WsHeader *)a.ws);
+        (int32_t *)(a.ws + a.L.xe), (int *)(a.ws + a.L.split_cnt), (WsHeader *)a.ws);
     return hipGetLastError();
 }
 

@@ -101,6 +101,24 @@ __device__ __forceinline__ void q4k_consts(const uint32_t *w, int g, uint32_t *k
     }
 }
 
+// Largest block-scale magnitude (fp16 bits) of a Q4_0 / Q8_0 window's two blocks.
+template <int Q>
+__device__ __forceinline__ uint32_t d_bits(const uint32_t *w) {
+    constexpr int hi = Q == FW_Q4_0 ? 4 : 8;   // dword holding the odd block's scale
+    return max(w[0] & 0x7FFFu, __builtin_amdgcn_ubfe(w[hi], 16, 15));
+}
+
+// Bound on the 16x-scaled magnitude of a Q4_K window's weights from its
+// per-step constants: 16 (15 |d scale| + |dmin min|) over both sub-blocks.
+__device__ __forceinline__ float q4k_bound(const uint32_t *k) {
+    float b = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        b = fmaxf(b, 16.0f * fmaf(15.0f, fabsf(__uint_as_float(k[2 * h])),
+                                  fabsf(__uint_as_float(k[2 * h + 1]))));
+    return b;
+}
+
 // B fragment of slice I from a Q4_K window: sub-block H = I / 4 of the group,
 // pairs 4 (I % 4) .. + 3.  Each weight d * scale * q - dmin * min is formed in
 // fp32 (exact up to one fp32 rounding) and rounded once to fp16, like a Q4_0
@@ -204,7 +222,13 @@ struct Tile2 {
     uint32_t qoff;             // Q4_K: byte offset of the lane's code group in a unit
     _Float16 *hout;
     float *yout;
-    int tid, lane, wave, steps, rows, rb, ct, N;
+    // row exponents: gate/up reads the token's x exponent (iexp[token]; the
+    // token of a routed row via sorted) and records 2x it per h row in oexp;
+    // the down projection reads iexp[row]
+    const int32_t *sorted, *iexp;
+    int32_t *oexp;
+    WsHeader *hdr;
+    int tid, lane, wave, steps, rows, rb, ct, N, k, P, shared;
 };
 
 // The K loop and epilogue of one tile, MI 16-row groups of token rows.  The
@@ -226,6 +250,8 @@ __device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
     constexpr int NA = 2 * MI;   // activation chunks per thread: rows tid / 32 + 8 j
     u4 ra[NA];                   // activation chunks of the next step
     uint32_t wb0[4][WD], wb1[4][WD];   // weight windows: this step / next step
+    uint32_t dmax = 0;           // largest block-scale magnitude bits met (Q8_0 / Q4_0)
+    float wmax = 0.f;            // largest Q4_K weight bound met
 
     auto load_a = [&](int st) {
 #pragma unroll
@@ -251,7 +277,12 @@ __device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
     if constexpr (MI > 0) {                                                                   \
         uint32_t kq[4][4];                                                                    \
         if constexpr (Q == FW_Q4_K)                                                           \
-            _Pragma("unroll") for (int cg = 0; cg < 4; ++cg) q4k_consts(W[cg], g, kq[cg]);    \
+            _Pragma("unroll") for (int cg = 0; cg < 4; ++cg) {                                \
+                q4k_consts(W[cg], g, kq[cg]);                                                 \
+                wmax = fmaxf(wmax, q4k_bound(kq[cg]));                                        \
+            }                                                                                 \
+        else                                                                                  \
+            _Pragma("unroll") for (int cg = 0; cg < 4; ++cg) dmax = max(dmax, d_bits<Q>(W[cg])); \
         const _Float16 *abase = &sm.a[BUF][fr * LDA + 64 * g];                                \
         h8 afc[MI > 0 ? MI : 1], afn[MI > 0 ? MI : 1];                                        \
         _Pragma("unroll") for (int r = 0; r < MI; ++r)                                        \
@@ -320,8 +351,29 @@ __device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
     // ---- epilogue through LDS (the activation buffers are free now) ----
     // acc[r][cg][j]: token row 16 r + 4 g + j, weight row 64 wave + 16 cg + fr
     const int rows = c.rows, rb = c.rb, ct = c.ct, N = c.N, wave = c.wave;
+    // a dequantised weight beyond fp16 (16x-scaled extreme code): the outputs
+    // of this tile are not reliable
+    const bool wbad = Q == FW_Q4_K ? !(wmax <= 65504.0f)
+                                   : dmax > (Q == FW_Q4_0 ? kQ4DMaxBits : kQ8DMaxBits);
+    bool range = wbad;
+    // each accumulator row's exponent (rows past the tile's end read its last row)
+    int ex[MI > 0 ? MI : 1][4];
+#pragma unroll
+    for (int r = 0; r < MI; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rr = rb + min(16 * r + 4 * g + j, rows - 1);
+            int src = rr;
+            if (GU && !c.shared) {
+                const int q = c.sorted[rr];
+                src = (unsigned)q < (unsigned)c.P ? q / c.k : 0;
+            }
+            ex[r][j] = c.iexp[src];
+        }
     if constexpr (GU) {
-        // a(token, feature) for the workgroup's 128 features: [BM][OH] fp16
+        // a(token, feature) for the workgroup's 128 features: [BM][OH] fp16;
+        // g and u at the token's own scale (exact), SwiGLU in fp32, h stored at
+        // 2^(2e) (pairs j = 1, 3 at 1/16)
         constexpr int OH = 136;
         _Float16 *o = (_Float16 *)&sm;
 #pragma unroll
@@ -330,13 +382,28 @@ __device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
             for (int cg = 0; cg < 2; ++cg)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float gv = acc[r][cg][j], up = acc[r][cg + 2][j];   // gate, up
+                    const int e = ex[r][j];
+                    const float gv = __builtin_amdgcn_ldexpf(acc[r][cg][j], -e);
+                    const float up = __builtin_amdgcn_ldexpf(acc[r][cg + 2][j], -e);
                     const int row = 16 * r + 4 * g + j;
                     const int col = 32 * wave + 16 * cg + fr;   // feature within the tile
-                    float a = gv / (1.0f + __expf(-gv)) * up;
-                    if (col & 16) a *= 0.0625f;   // pair order: pairs j = 1, 3 hold value / 16
-                    o[row * OH + (col & ~31) + pair_pos(col & 31)] = (_Float16)a;
+                    const float a = gv / (1.0f + __expf(-gv)) * up;
+                    const _Float16 ah =
+                        (_Float16)__builtin_amdgcn_ldexpf(a, 2 * e - ((col & 16) ? 4 : 0));
+                    range |= row < rows && (__builtin_bit_cast(uint16_t, ah) & 0x7C00u) == 0x7C00u;
+                    o[row * OH + (col & ~31) + pair_pos(col & 31)] = ah;
                 }
+        // h rows' exponents, once per row
+        if (ct == 0 && wave == 0 && fr == 0) {
+#pragma unroll
+            for (int r = 0; r < MI; ++r)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int row = 16 * r + 4 * g + j;
+                    if (row < rows) c.oexp[rb + row] = 2 * ex[r][j];
+                }
+        }
+        if (range) atomicOr(&c.hdr->status, FW_STATUS_RANGE);
         __syncthreads();
         // rows x 256 bytes: thread -> (row r0 + tid / 4, 64 bytes)
         const int part = tid & 3;
@@ -351,8 +418,10 @@ __device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
             }
         }
     } else {
-        // y rows straight from the accumulators: for each (row group, j, cg)
-        // the 16 lanes of a lane group write 64 contiguous bytes of one row
+        if (range) atomicOr(&c.hdr->status, FW_STATUS_RANGE);
+        // y rows straight from the accumulators at the row's scale: for each
+        // (row group, j, cg) the 16 lanes of a lane group write 64 contiguous
+        // bytes of one row
 #pragma unroll
         for (int r = 0; r < MI; ++r)
 #pragma unroll
@@ -361,7 +430,8 @@ __device__ __forceinline__ void tile2_run(Smem2 &sm, const Tile2 &c) {
                 if (row < rows) {
                     float *d = c.yout + (size_t)(rb + row) * N + ct * BN + 64 * wave + fr;
 #pragma unroll
-                    for (int cg = 0; cg < 4; ++cg) d[16 * cg] = acc[r][cg][j];
+                    for (int cg = 0; cg < 4; ++cg)
+                        d[16 * cg] = __builtin_amdgcn_ldexpf(acc[r][cg][j], -ex[r][j]);
                 }
             }
     }
@@ -378,7 +448,8 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(
     const int4 *__restrict__ tiles, WsHeader *__restrict__ hdr,
     const int32_t *__restrict__ sorted, const _Float16 *__restrict__ ain,
     _Float16 *__restrict__ hout, float *__restrict__ yout, int K, int N, int k, int P,
-    int col_tiles, int n_row_tiles_max, int shared, int shared_rows) {
+    int col_tiles, int n_row_tiles_max, int shared, int shared_rows,
+    const int32_t *__restrict__ iexp, int32_t *__restrict__ oexp) {
     __shared__ Smem2 sm;
     // XCD-aware order: workgroup b runs on XCD b % 8.  Each XCD takes a
     // contiguous eighth of the row tiles (the tiles of one expert are
@@ -439,6 +510,13 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(
     c.qoff = 16 + 32 * g;
     c.hout = hout;
     c.yout = yout;
+    c.sorted = sorted;
+    c.iexp = iexp;
+    c.oexp = oexp;
+    c.hdr = hdr;
+    c.k = k;
+    c.P = P;
+    c.shared = shared;
     c.steps = K / BK;
     c.rows = rows;
     c.rb = rb;
@@ -455,7 +533,8 @@ __global__ __launch_bounds__(kThreads) void gemm2_kernel(
 
 template <int Q, bool GU>
 void launch2(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Float16 *ain,
-             _Float16 *hout, float *yout, int K, int N, int shared, hipStream_t s) {
+             _Float16 *hout, float *yout, int K, int N, int shared, const int32_t *iexp,
+             int32_t *oexp, hipStream_t s) {
     const int col_tiles = GU ? N / 128 : N / BN;
     // routed: at most one partial tile per expert
     const int row_tiles = shared ? (a.T + BM - 1) / BM
@@ -463,30 +542,34 @@ void launch2(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Floa
     const int nblk = (row_tiles + 7) / 8 * 8 * col_tiles;   // eight XCDs x whole row tiles
     gemm2_kernel<Q, GU><<<nblk, kThreads, 0, s>>>(
         wa, wb, (const int4 *)(a.ws + a.L.tiles), (WsHeader *)a.ws, a.sorted, ain, hout, yout,
-        K, N, a.d.top_k, a.P, col_tiles, row_tiles, shared, shared ? a.T : 0);
+        K, N, a.d.top_k, a.P, col_tiles, row_tiles, shared, shared ? a.T : 0, iexp, oexp);
 }
 
 }  // namespace
+
+// One launch of format q (run-time) on the given matrices.
+template <bool GU>
+void launch2_q(int q, const FwdArgs &a, const uint8_t *wa, const uint8_t *wb,
+               const _Float16 *ain, _Float16 *hout, float *yout, int K, int N, int shared,
+               const int32_t *iexp, int32_t *oexp, hipStream_t s) {
+    if (q == FW_Q4_0)
+        launch2<FW_Q4_0, GU>(a, wa, wb, ain, hout, yout, K, N, shared, iexp, oexp, s);
+    else if (q == FW_Q4_K)
+        launch2<FW_Q4_K, GU>(a, wa, wb, ain, hout, yout, K, N, shared, iexp, oexp, s);
+    else
+        launch2<FW_Q8_0, GU>(a, wa, wb, ain, hout, yout, K, N, shared, iexp, oexp, s);
+}
 
 hipError_t launch_gemm2_gate_up(const FwdArgs &a, hipStream_t s) {
     const fw_moe_desc &d = a.d;
     const _Float16 *x = (const _Float16 *)(a.ws + a.L.x16);
     _Float16 *h = (_Float16 *)(a.ws + a.L.h);
-    if (d.expert_q == FW_Q4_0)
-        launch2<FW_Q4_0, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, 0, s);
-    else if (d.expert_q == FW_Q4_K)
-        launch2<FW_Q4_K, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, 0, s);
-    else
-        launch2<FW_Q8_0, true>(a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, 0, s);
-    if (d.shared_ffn > 0) {
-        _Float16 *hsh = h + (size_t)a.P * d.ffn;
-        if (d.shared_q == FW_Q4_0)
-            launch2<FW_Q4_0, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, 1, s);
-        else if (d.shared_q == FW_Q4_K)
-            launch2<FW_Q4_K, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, 1, s);
-        else
-            launch2<FW_Q8_0, true>(a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, 1, s);
-    }
+    const int32_t *xe = (const int32_t *)(a.ws + a.L.xe);
+    int32_t *he = (int32_t *)(a.ws + a.L.he);
+    launch2_q<true>(d.expert_q, a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, 0, xe, he, s);
+    if (d.shared_ffn > 0)
+        launch2_q<true>(d.shared_q, a, a.sg, a.su, x, h + (size_t)a.P * d.ffn, nullptr, d.hidden,
+                        d.shared_ffn, 1, xe, he + a.P, s);
     return hipGetLastError();
 }
 
@@ -494,22 +577,13 @@ hipError_t launch_gemm2_down(const FwdArgs &a, hipStream_t s) {
     const fw_moe_desc &d = a.d;
     const _Float16 *h = (const _Float16 *)(a.ws + a.L.h);
     float *y = (float *)(a.ws + a.L.y);
-    if (d.expert_q == FW_Q4_0)
-        launch2<FW_Q4_0, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, 0, s);
-    else if (d.expert_q == FW_Q4_K)
-        launch2<FW_Q4_K, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, 0, s);
-    else
-        launch2<FW_Q8_0, false>(a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, 0, s);
-    if (d.shared_ffn > 0) {
-        const _Float16 *hsh = h + (size_t)a.P * d.ffn;
-        float *ysh = y + (size_t)a.P * d.hidden;
-        if (d.shared_q == FW_Q4_0)
-            launch2<FW_Q4_0, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, 1, s);
-        else if (d.shared_q == FW_Q4_K)
-            launch2<FW_Q4_K, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, 1, s);
-        else
-            launch2<FW_Q8_0, false>(a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden, 1, s);
-    }
+    const int32_t *he = (const int32_t *)(a.ws + a.L.he);
+    launch2_q<false>(d.expert_q, a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, 0, he,
+                     nullptr, s);
+    if (d.shared_ffn > 0)
+        launch2_q<false>(d.shared_q, a, a.sd, nullptr, h + (size_t)a.P * d.ffn, nullptr,
+                         y + (size_t)a.P * d.hidden, d.shared_ffn, d.hidden, 1, he + a.P,
+                         nullptr, s);
     return hipGetLastError();
 }
 

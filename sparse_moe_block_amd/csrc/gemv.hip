@@ -4,7 +4,7 @@
 // 0.2.0 "Quantization"), so the kernels are built around HBM streaming:
 //
 //  - work items are (row chunk, 64-row weight tile) pairs: a row chunk is up to
-//    four rows of one expert's segment of the sorted pair list (built on the
+//    two rows of one expert's segment of the sorted pair list (built on the
 //    device), a weight tile 64 consecutive rows of that expert's matrix; the
 //    grid is sized to the resident capacity and each workgroup walks the items
 //    g, g + grid, ... so no workgroup pays a cold start twice;
@@ -30,6 +30,8 @@
 // registers (the fused gate/up pass that shares each activation load:
 // Flyweight 0.2.0 "Current limitations").
 #include <math.h>
+
+#include <mutex>
 
 #include "common.h"
 
@@ -254,6 +256,7 @@ struct Item {
     const uint8_t *ta, *tb;
     cu32 *in[kGemvTokens];
     cu32 *sum[kGemvTokens];   // Q4_K: the rows' 32-element block sums
+    int ex[kGemvTokens];      // power-of-two exponent each input row is scaled by
     int rb, nt, tile;
     bool bad;
 };
@@ -274,8 +277,9 @@ template <bool GU>
 __device__ __forceinline__ Item get_item(int item, const uint8_t *wa, const uint8_t *wb,
                                          const int4 *tiles, const int32_t *sorted,
                                          const _Float16 *xin, const float *isum,
-                                         size_t rowbytes, size_t esz, int tpg, int K, int k,
-                                         int P, int shared, int shared_rows) {
+                                         const int32_t *iexp, size_t rowbytes, size_t esz,
+                                         int tpg, int K, int k, int P, int shared,
+                                         int shared_rows) {
     Item it;
     const int chunk = item / tpg;
     it.tile = item % tpg;
@@ -303,6 +307,7 @@ __device__ __forceinline__ Item get_item(int item, const uint8_t *wa, const uint
         }
         it.in[n] = (cu32 *)(xin + (size_t)t * K);
         it.sum[n] = (cu32 *)(isum + (size_t)t * (K / 32));
+        it.ex[n] = ld_const(iexp + t);
     }
     return it;
 }
@@ -339,8 +344,9 @@ __global__ __launch_bounds__(kWave *S) void gemv_kernel(
     const int4 *__restrict__ tiles, WsHeader *__restrict__ hdr,
     const int32_t *__restrict__ sorted, const _Float16 *__restrict__ xin,
     _Float16 *__restrict__ hout, float *__restrict__ yout, int K, int N, int k, int P,
-    int tpg, int shared, int shared_rows, int ks, int *__restrict__ split_cnt,
-    float *__restrict__ split_part, const float *__restrict__ isum, float *__restrict__ osum) {
+    int tpg, int max_chunks, int shared, int shared_rows, int ks, int *__restrict__ split_cnt,
+    float *__restrict__ split_part, const float *__restrict__ isum, float *__restrict__ osum,
+    const int32_t *__restrict__ iexp, int32_t *__restrict__ oexp) {
     constexpr int X4 = QT<Q>::kUnitX4;
     constexpr int NV = GU ? 2 : 1;
     constexpr int NT = kGemvTokens;
@@ -350,7 +356,11 @@ __global__ __launch_bounds__(kWave *S) void gemv_kernel(
     const size_t rowbytes = (size_t)(K / 32) * QT<Q>::kBlockBytes;
     const size_t esz = (size_t)N * rowbytes;
     const uint8_t *wbb = GU ? wb : wa;
-    const int n_chunks = shared ? (shared_rows + NT - 1) / NT : ld_const(&hdr->n_tiles);
+    // the device-written chunk count is clamped to the bound the launch (its
+    // split-K slices and their counters and partials) was sized for: corrupt
+    // expert_offsets can make the schedule claim more
+    const int n_chunks = shared ? (shared_rows + NT - 1) / NT
+                                : min(ld_const(&hdr->n_tiles), max_chunks);
     const int n_items = n_chunks * tpg * ks;
     const int g0 = blockIdx.x, G = gridDim.x;
     if (g0 >= n_items) return;
@@ -381,8 +391,8 @@ __global__ __launch_bounds__(kWave *S) void gemv_kernel(
     int j = 0;
     for (int i = 0; i < my_items; ++i) {
         const int item = g0 + i * G, ct = item / ks, slice = item % ks;
-        const Item it = get_item<GU>(ct, wa, wbb, tiles, sorted, xin, isum, rowbytes, esz, tpg,
-                                     K, k, P, shared, shared_rows);
+        const Item it = get_item<GU>(ct, wa, wbb, tiles, sorted, xin, isum, iexp, rowbytes, esz,
+                                     tpg, K, k, P, shared, shared_rows);
         if (it.bad && threadIdx.x == 0) atomicOr(&hdr->status, FW_STATUS_BAD_PAIR);
         float acc[NV][NT];
 #pragma unroll
@@ -449,16 +459,23 @@ __global__ __launch_bounds__(kWave *S) void gemv_kernel(
         }
         if (out) {
             const int row = it.tile * kWave + lane;
+            bool range = false;
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
                 if (n < it.nt) {
                     const size_t r = (size_t)(it.rb + n);
+                    const int e = it.ex[n];
                     if constexpr (GU) {
-                        const float gv = acc[0][n], up = acc[NV - 1][n];
-                        float a = gv / (1.0f + __expf(-gv)) * up;
-                        if (row & 16) a *= 0.0625f;   // pairs j = 1, 3 hold value / 16
-                        const _Float16 ah = (_Float16)a;
+                        // g and u at the token's own scale (exact), SwiGLU in
+                        // fp32, h stored at 2^(2e) (pairs j = 1, 3 at 1/16)
+                        const float gv = __builtin_amdgcn_ldexpf(acc[0][n], -e);
+                        const float up = __builtin_amdgcn_ldexpf(acc[NV - 1][n], -e);
+                        const float a = gv / (1.0f + __expf(-gv)) * up;
+                        const _Float16 ah =
+                            (_Float16)__builtin_amdgcn_ldexpf(a, 2 * e - ((row & 16) ? 4 : 0));
+                        range |= (__builtin_bit_cast(uint16_t, ah) & 0x7C00u) == 0x7C00u;
                         hout[r * N + (row & ~31) + pair_pos(row & 31)] = ah;
+                        if (it.tile == 0 && lane == 0) oexp[r] = 2 * e;
                         if (osum) {
                             // 32-element block sums of the stored values (a Q4_K
                             // down projection's min term), in a fixed order
@@ -468,10 +485,11 @@ __global__ __launch_bounds__(kWave *S) void gemv_kernel(
                             if ((lane & 31) == 0) osum[r * (N / 32) + row / 32] = v;
                         }
                     } else {
-                        yout[r * N + row] = acc[0][n];
+                        yout[r * N + row] = __builtin_amdgcn_ldexpf(acc[0][n], -e);
                     }
                 }
             }
+            if (GU && range) atomicOr(&hdr->status, FW_STATUS_RANGE);
         }
         if (S > 1) __syncthreads();   // red[] is reused by the next item
     }
@@ -486,19 +504,34 @@ int pick_split(int units) {
     return 1;
 }
 
-int g_cus = 0;
-
+// Properties of the current device, queried once per device (thread-safe)
+// and read-only after that.
 int cu_count() {
-    if (!g_cus) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            n > 0)
-            g_cus = n;
-        else
-            g_cus = 256;
-    }
-    return g_cus;
+    static std::once_flag once[kMaxDevices];
+    static int cus[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    std::call_once(once[dev], [dev] {
+        int n = 0;
+        cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+                               hipSuccess && n > 0 ? n : 256;
+    });
+    return cus[dev];
+}
+
+// Resident workgroups per CU of one kernel, per device (registers and LDS).
+template <typename K>
+int resident_per_cu(K kernel, int threads) {
+    static std::once_flag once[kMaxDevices];
+    static int res[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1;
+    std::call_once(once[dev], [&] {
+        int n = 0;
+        res[dev] = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) ==
+                               hipSuccess && n > 0 ? n : 1;
+    });
+    return res[dev];
 }
 
 // isum: the input rows' 32-element block sums (Q4_K weights), osum: where
@@ -506,20 +539,14 @@ int cu_count() {
 // either may be null.
 template <int Q, bool GU, int S, int D>
 void launch_sd(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Float16 *xin,
-               _Float16 *hout, float *yout, int K, int N, long long items, int per_cu, int ks,
-               int shared, const float *isum, float *osum, hipStream_t s) {
+               _Float16 *hout, float *yout, int K, int N, int max_chunks, int per_cu, int ks,
+               int shared, const float *isum, float *osum, const int32_t *iexp, int32_t *oexp,
+               hipStream_t s) {
     const int tpg = N / kWave;
+    const long long items = (long long)max_chunks * tpg;
     // workgroups per CU: what the LDS pipeline asks for, but no more than
     // registers and LDS let be resident at once (the schedule is persistent)
-    static int resident = 0;
-    if (!resident) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemv_kernel<Q, GU, S, D>, kWave * S,
-                                                         0) != hipSuccess || n < 1)
-            n = 1;
-        resident = n;
-    }
-    per_cu = std::min(per_cu, resident);
+    per_cu = std::min(per_cu, resident_per_cu(gemv_kernel<Q, GU, S, D>, kWave * S));
     const long long work = items * ks, slots = (long long)per_cu * cu_count();
     // gate/up: equal rounds, every workgroup takes the same number of items,
     // so no last partial round of items runs latency-bound after the rest
@@ -530,8 +557,9 @@ void launch_sd(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Fl
     const int grid = (int)std::max(1LL, GU ? (work + rounds - 1) / rounds : std::min(work, slots));
     gemv_kernel<Q, GU, S, D><<<grid, kWave * S, 0, s>>>(
         wa, wb, (const int4 *)(a.ws + a.L.tiles), (WsHeader *)a.ws, a.sorted, xin, hout, yout,
-        K, N, a.d.top_k, a.P, tpg, shared, shared ? a.T : 0, ks, (int *)(a.ws + a.L.split_cnt),
-        (float *)(a.ws + a.L.split_part), isum, osum);
+        K, N, a.d.top_k, a.P, tpg, max_chunks, shared, shared ? a.T : 0, ks,
+        (int *)(a.ws + a.L.split_cnt),
+        (float *)(a.ws + a.L.split_part), isum, osum, iexp, oexp);
 }
 
 // LDS is the in-flight buffer: about 144 KB of DMA batches per CU keeps HBM
@@ -540,7 +568,8 @@ void launch_sd(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Fl
 template <int Q, bool GU, int S>
 void launch_s(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Float16 *xin,
               _Float16 *hout, float *yout, int K, int N, int max_chunks, int shared,
-              const float *isum, float *osum, hipStream_t s) {
+              const float *isum, float *osum, const int32_t *iexp, int32_t *oexp,
+              hipStream_t s) {
     constexpr int X4 = QT<Q>::kUnitX4;
     const long long items = (long long)max_chunks * (N / kWave);
     // far too few items to occupy the CUs (the shared expert of a one-token
@@ -567,20 +596,20 @@ void launch_s(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Flo
     // one-row dots prefetch their activations further ahead); 17 KB batches
     // (Q8_0): depth 1
     if (X4 == 9 && per_cu >= 1.5 && per_cu < 3.0)
-        launch_sd<Q, GU, S, 2>(a, wa, wb, xin, hout, yout, K, N, items, fit(2), ks, shared, isum, osum, s);
+        launch_sd<Q, GU, S, 2>(a, wa, wb, xin, hout, yout, K, N, max_chunks, fit(2), ks, shared, isum, osum, iexp, oexp, s);
     else
-        launch_sd<Q, GU, S, 1>(a, wa, wb, xin, hout, yout, K, N, items, fit(1), ks, shared, isum, osum, s);
+        launch_sd<Q, GU, S, 1>(a, wa, wb, xin, hout, yout, K, N, max_chunks, fit(1), ks, shared, isum, osum, iexp, oexp, s);
 }
 
 template <int Q, bool GU>
 void launch(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Float16 *xin,
             _Float16 *hout, float *yout, int K, int N, int max_chunks, int shared,
-            const float *isum, float *osum, hipStream_t s) {
+            const float *isum, float *osum, const int32_t *iexp, int32_t *oexp, hipStream_t s) {
     switch (pick_split(K / kUnit)) {
-        case 4: launch_s<Q, GU, 4>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, isum, osum, s); break;
-        case 3: launch_s<Q, GU, 3>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, isum, osum, s); break;
-        case 2: launch_s<Q, GU, 2>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, isum, osum, s); break;
-        default: launch_s<Q, GU, 1>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, isum, osum, s); break;
+        case 4: launch_s<Q, GU, 4>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, isum, osum, iexp, oexp, s); break;
+        case 3: launch_s<Q, GU, 3>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, isum, osum, iexp, oexp, s); break;
+        case 2: launch_s<Q, GU, 2>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, isum, osum, iexp, oexp, s); break;
+        default: launch_s<Q, GU, 1>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, isum, osum, iexp, oexp, s); break;
     }
 }
 
@@ -596,15 +625,17 @@ int max_routed_chunks(const FwdArgs &a) {
 template <bool GU>
 void launch_q(int q, const FwdArgs &a, const uint8_t *wa, const uint8_t *wb,
               const _Float16 *xin, _Float16 *hout, float *yout, int K, int N, int max_chunks,
-              int shared, const float *isum, float *osum, hipStream_t s) {
+              int shared, const float *isum, float *osum, const int32_t *iexp, int32_t *oexp,
+              hipStream_t s) {
     if (q == FW_Q4_0)
         launch<FW_Q4_0, GU>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, nullptr,
-                            nullptr, s);
+                            nullptr, iexp, oexp, s);
     else if (q == FW_Q8_0)
         launch<FW_Q8_0, GU>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, nullptr,
-                            nullptr, s);
+                            nullptr, iexp, oexp, s);
     else
-        launch<FW_Q4_K, GU>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, isum, osum, s);
+        launch<FW_Q4_K, GU>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, isum, osum,
+                            iexp, oexp, s);
 }
 
 // Block sums: x rows (prepare), then h rows of the routed pairs [P][F/32]
@@ -615,14 +646,17 @@ hipError_t launch_gemv_gate_up(const FwdArgs &a, hipStream_t s) {
     _Float16 *h = (_Float16 *)(a.ws + a.L.h);
     const float *xs = (const float *)(a.ws + a.L.xsum);
     float *hs = (float *)(a.ws + a.L.hsum);
+    const int32_t *xe = (const int32_t *)(a.ws + a.L.xe);
+    int32_t *he = (int32_t *)(a.ws + a.L.he);
     const int mc = max_routed_chunks(a);
-    launch_q<true>(d.expert_q, a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, mc, 0, xs, hs, s);
+    launch_q<true>(d.expert_q, a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, mc, 0, xs, hs, xe,
+                   he, s);
     if (d.shared_ffn > 0) {
         _Float16 *hsh = h + (size_t)a.P * d.ffn;
         float *hssh = hs + (size_t)a.P * (d.ffn / 32);
         const int sc = (a.T + kGemvTokens - 1) / kGemvTokens;
         launch_q<true>(d.shared_q, a, a.sg, a.su, x, hsh, nullptr, d.hidden, d.shared_ffn, sc, 1,
-                       xs, hssh, s);
+                       xs, hssh, xe, he + a.P, s);
     }
     return hipGetLastError();
 }
@@ -632,16 +666,17 @@ hipError_t launch_gemv_down(const FwdArgs &a, hipStream_t s) {
     const _Float16 *h = (const _Float16 *)(a.ws + a.L.h);
     const float *hs = (const float *)(a.ws + a.L.hsum);
     float *y = (float *)(a.ws + a.L.y);
+    const int32_t *he = (const int32_t *)(a.ws + a.L.he);
     const int mc = max_routed_chunks(a);
     launch_q<false>(d.expert_q, a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, mc, 0, hs,
-                    nullptr, s);
+                    nullptr, he, nullptr, s);
     if (d.shared_ffn > 0) {
         const _Float16 *hsh = h + (size_t)a.P * d.ffn;
         const float *hssh = hs + (size_t)a.P * (d.ffn / 32);
         float *ysh = y + (size_t)a.P * d.hidden;
         const int sc = (a.T + kGemvTokens - 1) / kGemvTokens;
         launch_q<false>(d.shared_q, a, a.sd, nullptr, hsh, nullptr, ysh, d.shared_ffn, d.hidden,
-                        sc, 1, hssh, nullptr, s);
+                        sc, 1, hssh, nullptr, he + a.P, nullptr, s);
     }
     return hipGetLastError();
 }

@@ -5,8 +5,8 @@
 // microseconds of mostly launch latency at decode sizes.  Here block 0 runs
 // them back to back -- one wavefront per token for the top-k (ids also kept
 // in LDS), then the counting sort over those LDS ids and the active-expert
-// list and row tiles -- while the other blocks stage the token rows in fp16,
-// which does not depend on the routing.  Up to 64 pairs one wavefront sorts
+// list and row tiles -- while the other blocks stage the token rows in fp16
+// (one wavefront per row), which does not depend on the routing.  Up to 64 pairs one wavefront sorts
 // and schedules without workgroup barriers; above that the block runs the
 // same workgroup sort and schedule as the separate kernels.  The sort is
 // stable and the schedule is in expert order either way, so the results are
@@ -147,8 +147,8 @@ __global__ __launch_bounds__(kPermThreads) void decode_front_kernel(
     float *__restrict__ w, int32_t *__restrict__ offsets, int32_t *__restrict__ sorted,
     int32_t *__restrict__ inv, const void *__restrict__ x, int act_bf16, int H, int tile_rows,
     int max_tiles, int4 *__restrict__ active, int4 *__restrict__ tiles,
-    _Float16 *__restrict__ x16, float *__restrict__ xsum, int *__restrict__ split_cnt,
-    WsHeader *__restrict__ hdr) {
+    _Float16 *__restrict__ x16, float *__restrict__ xsum, int32_t *__restrict__ xe,
+    int *__restrict__ split_cnt, WsHeader *__restrict__ hdr) {
     if (blockIdx.x == 0) {
         __shared__ int32_t s_ids[SMALL ? kSmallP : kPermOneBlockMaxP];   // T * k fits
         if constexpr (SMALL) {
@@ -175,9 +175,9 @@ __global__ __launch_bounds__(kPermThreads) void decode_front_kernel(
         }
         return;
     }
-    const long long idx = (long long)(blockIdx.x - 1) * kPermThreads + threadIdx.x;
-    if (idx >= (long long)T * (H / 32)) return;
-    stage_x_block(x, act_bf16, H, (int)(idx / (H / 32)), (int)(idx % (H / 32)), x16, xsum);
+    const int t = (blockIdx.x - 1) * kPermWaves + wave_id();   // one wavefront per token row
+    if (t >= T) return;
+    stage_x_row(x, act_bf16, H, t, x16, xsum, xe, hdr);
 }
 
 }  // namespace
@@ -191,8 +191,7 @@ hipError_t launch_decode_front(const FwdArgs &a, const float *logits, int32_t *i
     const fw_moe_desc &d = a.d;
     if (!decode_front_fits(d, a.T, a.path)) return hipErrorInvalidValue;
     const bool sums = d.expert_q == FW_Q4_K || (d.shared_ffn > 0 && d.shared_q == FW_Q4_K);
-    const long long xblocks = (long long)a.T * (d.hidden / 32);
-    const int grid = 1 + (int)((xblocks + kPermThreads - 1) / kPermThreads);
+    const int grid = 1 + (a.T + kPermWaves - 1) / kPermWaves;
     const int epl = (d.n_experts + kWave - 1) / kWave;
 #define FW_FRONT(N)                                                                            \
     case N:                                                                                    \
@@ -205,8 +204,8 @@ hipError_t launch_decode_front(const FwdArgs &a, const float *logits, int32_t *i
     logits, a.T, d.n_experts, d.top_k, d.score, ids, w, offsets, sorted, inv, a.x,             \
         d.act_dtype == FW_BF16, d.hidden, kGemvTokens, a.L.max_tiles,                          \
         (int4 *)(a.ws + a.L.active), (int4 *)(a.ws + a.L.tiles), (_Float16 *)(a.ws + a.L.x16), \
-        sums ? (float *)(a.ws + a.L.xsum) : nullptr, (int *)(a.ws + a.L.split_cnt),            \
-        (WsHeader *)a.ws
+        sums ? (float *)(a.ws + a.L.xsum) : nullptr, (int32_t *)(a.ws + a.L.xe),               \
+        (int *)(a.ws + a.L.split_cnt), (WsHeader *)a.ws
     const bool small = (long long)a.T * d.top_k <= kSmallP;
     switch (epl) {
         FW_FRONT(1)

@@ -282,13 +282,9 @@ __device__ __forceinline__ void build_schedule(const int32_t *offsets, int E, in
     }
 }
 
-// Stage one 32-element block b of token t in fp16 (bf16 values are exact in
-// fp16), in the pair order both kernel families consume (see decode_pairs),
-// and optionally its block sum (the min term of a Q4_K GEMV).
-__device__ __forceinline__ void stage_x_block(const void *__restrict__ x, int act_bf16, int H,
-                                              int t, int b, _Float16 *__restrict__ x16,
-                                              float *__restrict__ xsum) {
-    float v[32];
+// The 32 values of block b of token row t as fp32 (bf16 widened exactly).
+__device__ __forceinline__ void load_x_block(const void *__restrict__ x, int act_bf16, int H,
+                                             int t, int b, float *v) {
     if (act_bf16) {
         const uint4 *src = (const uint4 *)((const uint16_t *)x + (size_t)t * H + 32 * b);
 #pragma unroll
@@ -312,29 +308,67 @@ __device__ __forceinline__ void stage_x_block(const void *__restrict__ x, int ac
             v[4 * q + 3] = f.w;
         }
     }
-    uint32_t o[16];
+}
+
+// One wavefront stages token row t (called by the whole wavefront, t uniform):
+// the row's largest magnitude sets its exponent e (x * 2^e has its largest
+// magnitude in [2^(kXExp-1), 2^kXExp); e = 0 for an all-zero row), written to
+// xe[t]; then every 32-element block is stored as fp16 x * 2^e in the pair
+// order both kernel families consume (see decode_pairs; pairs j = 1, 3 at
+// 1/16), with, when xsum is set, the block's sum of the stored values (the
+// min term of a Q4_K GEMV).  A non-finite value sets FW_STATUS_RANGE.
+__device__ __forceinline__ void stage_x_row(const void *__restrict__ x, int act_bf16, int H,
+                                            int t, _Float16 *__restrict__ x16,
+                                            float *__restrict__ xsum, int32_t *__restrict__ xe,
+                                            WsHeader *__restrict__ hdr) {
+    const int lane = threadIdx.x % kWave, nb = H / 32;
+    // |v| as fp32 bits orders like |v| (NaN above +inf)
+    uint32_t m = 0;
+    for (int b = lane; b < nb; b += kWave) {
+        float v[32];
+        load_x_block(x, act_bf16, H, t, b, v);
 #pragma unroll
-    for (int pi = 0; pi < 16; ++pi) {
-        const int m = pi >> 2, j = pi & 3;
-        const int e0 = (j & 1 ? 16 : 0) + 4 * m + (j >> 1);
-        const float sc = (j & 1) ? 0.0625f : 1.0f;
-        o[pi] = __builtin_bit_cast(uint32_t, h2{(_Float16)(v[e0] * sc), (_Float16)(v[e0 + 2] * sc)});
+        for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
     }
-    uint4 *dst = (uint4 *)(x16 + (size_t)t * H + 32 * b);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) dst[q] = uint4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
-    if (xsum) {
-        // the block's sum of the staged fp16 values (unscaled), in pair
-        // order: the min term of a Q4_K GEMV
-        float sum = 0.f;
+    m = wave_max_u32(m);
+    int e = 0;
+    if (m >= 0x7F800000u) {
+        if (lane == 0) atomicOr(&hdr->status, FW_STATUS_RANGE);
+    } else if (m != 0) {
+        // amax = f * 2^E, f in [0.5, 1): amax * 2^(kXExp - E) in [2^(kXExp-1), 2^kXExp)
+        e = kXExp - __builtin_amdgcn_frexp_expf(__uint_as_float(m));
+    }
+    if (lane == 0) xe[t] = e;
+    for (int b = lane; b < nb; b += kWave) {
+        float v[32];
+        load_x_block(x, act_bf16, H, t, b, v);
+        uint32_t o[16];
 #pragma unroll
         for (int pi = 0; pi < 16; ++pi) {
-            const h2 v = as_h2(o[pi]);
-            const float sc = (pi & 1) ? 16.0f : 1.0f;
-            sum += sc * (float)v[0];
-            sum += sc * (float)v[1];
+            const int mm = pi >> 2, j = pi & 3;
+            const int e0 = (j & 1 ? 16 : 0) + 4 * mm + (j >> 1);
+            const int es = (j & 1) ? e - 4 : e;
+            o[pi] = __builtin_bit_cast(uint32_t,
+                                       h2{(_Float16)__builtin_amdgcn_ldexpf(v[e0], es),
+                                          (_Float16)__builtin_amdgcn_ldexpf(v[e0 + 2], es)});
         }
-        xsum[(size_t)t * (H / 32) + b] = sum;
+        uint4 *dst = (uint4 *)(x16 + (size_t)t * H + 32 * b);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            dst[q] = uint4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+        if (xsum) {
+            // the block's sum of the stored fp16 values (pairs j = 1, 3 back at
+            // full scale), in pair order
+            float sum = 0.f;
+#pragma unroll
+            for (int pi = 0; pi < 16; ++pi) {
+                const h2 hv = as_h2(o[pi]);
+                const float sc = (pi & 1) ? 16.0f : 1.0f;
+                sum += sc * (float)hv[0];
+                sum += sc * (float)hv[1];
+            }
+            xsum[(size_t)t * nb + b] = sum;
+        }
     }
 }
 

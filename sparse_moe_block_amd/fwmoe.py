@@ -13,7 +13,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfwmoe.so")
 
 FW_OK, FW_EINVAL, FW_EUNSUPPORTED, FW_EWORKSPACE, FW_EALIGN, FW_EHIP = 0, -1, -2, -3, -4, -5
-FW_STATUS_BAD_EXPERT_ID, FW_STATUS_BAD_OFFSETS, FW_STATUS_BAD_PAIR = 1, 2, 4
+FW_STATUS_BAD_EXPERT_ID, FW_STATUS_BAD_OFFSETS, FW_STATUS_BAD_PAIR, FW_STATUS_RANGE = 1, 2, 4, 8
 FW_F32, FW_BF16 = 0, 1
 FW_Q8_0, FW_Q4_0, FW_Q4_K = 0, 1, 2
 FW_SOFTMAX_RENORM, FW_SIGMOID_RENORM = 0, 1
@@ -72,7 +72,7 @@ def lib():
             "fw_moe_clear_status": ([P, P], ctypes.c_int),
             "fw_moe_read_status": ([P, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
             "fw_moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
-            "fw_moe_set_stage_events": ([P], ctypes.c_int),
+            "fw_moe_layer_timed": ([D, I] + [P] * 17 + [ctypes.c_size_t, P, P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -176,19 +176,19 @@ def fw_moe_status_string(code):
 status_string = fw_moe_status_string
 
 
-def fw_moe_set_stage_events(events):
-    """events: FW_N_STAGE_EVENTS torch.cuda.Event objects (created with
-    enable_timing=True), or None to stop recording."""
-    if events is None:
-        return _check("fw_moe_set_stage_events", lib().fw_moe_set_stage_events(None))
-    assert len(events) == FW_N_STAGE_EVENTS
-    for e in events:
+def fw_moe_layer_timed(desc, T, x, router_w, logit_bias, w_gate, w_up, w_down, ws_gate,
+                       ws_up, ws_down, logits, topk_ids, topk_w, expert_offsets, sorted_pairs,
+                       inv_pos, out, workspace, stage_events, ws_bytes=None, stream=None):
+    """stage_events: FW_N_STAGE_EVENTS torch.cuda.Event objects (enable_timing=True)."""
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    assert len(stage_events) == FW_N_STAGE_EVENTS
+    for e in stage_events:
         if e.cuda_event == 0:      # torch creates the HIP event lazily
             e.record()
-    arr = (ctypes.c_void_p * FW_N_STAGE_EVENTS)(*[e.cuda_event for e in events])
-    global _events_keepalive
-    _events_keepalive = (arr, events)
-    return _check("fw_moe_set_stage_events", lib().fw_moe_set_stage_events(arr))
-
-
-_events_keepalive = None
+    arr = (ctypes.c_void_p * FW_N_STAGE_EVENTS)(*[e.cuda_event for e in stage_events])
+    return _check("fw_moe_layer_timed", lib().fw_moe_layer_timed(
+        ctypes.byref(desc), T, _ptr(x), _ptr(router_w), _ptr(logit_bias), _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(logits),
+        _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(inv_pos),
+        _ptr(out), _ptr(workspace), ws_bytes, arr, _stream(stream)))

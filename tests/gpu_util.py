@@ -108,13 +108,28 @@ def small_gaps(logits, k):
     return (srt[:, k - 1] - srt[:, k]) < GAP
 
 
-def sample_tokens(T, n, seed=0):
-    if T <= n:
+# Batches up to this many tokens are compared with the oracle on every row.
+FULL_COMPARE_MAX_T = 2048
+
+
+def compare_tokens(T, ids, n_experts, n_random=48, seed=0):
+    """The tokens whose output rows are compared with the oracle: every token
+    up to FULL_COMPARE_MAX_T; above that, both ends, n_random tokens drawn at
+    random, and, for every expert, the token of its last routed row in the
+    expert-sorted pair order -- a row of the expert's last (usually partial)
+    64-row GEMM tile and of its last GEMV row chunk.  Relative L2 is then
+    computed over the rows of this sample."""
+    if T <= FULL_COMPARE_MAX_T:
         return np.arange(T)
+    k = ids.shape[1]
+    flat = ids.reshape(-1)
+    order = np.argsort(flat, kind="stable")          # expert-major, ascending pair id
+    counts = np.bincount(flat, minlength=n_experts)
+    ends = np.cumsum(counts)
+    last = [order[ends[e] - 1] // k for e in range(n_experts) if counts[e] > 0]
     rng = np.random.default_rng(seed + T)
-    s = np.sort(rng.choice(T, n, replace=False))
-    s[0], s[-1] = 0, T - 1     # always include both ends
-    return np.unique(s)
+    tok = np.concatenate([[0, T - 1], rng.choice(T, n_random, replace=False), last])
+    return np.unique(tok)
 
 
 def check_out(got, want):

@@ -182,3 +182,24 @@ def test_status_strings_and_version():
         assert fw.fw_moe_status_string(code) != "unknown status"
     assert fw.fw_moe_status_string(99) == "unknown status"
     assert "gfx950" in fw.fw_moe_version()
+
+
+def test_layer_timed_validation():
+    """fw_moe_layer_timed takes its events per call: missing events are
+    refused before anything is enqueued, and so is everything fw_moe_layer
+    refuses."""
+    d = good_desc()
+    need = fw.fw_moe_workspace_size(d, 8)
+    lib = fw.lib()
+    ev = (ctypes.c_void_p * fw.FW_N_STAGE_EVENTS)(*([16] * fw.FW_N_STAGE_EVENTS))
+    ev_missing = (ctypes.c_void_p * fw.FW_N_STAGE_EVENTS)(*([16] * 4 + [None]))
+
+    def call(events, T=8, router=16, ws=256):
+        return lib.fw_moe_layer_timed(ctypes.byref(d), T, 16, router, None, 16, 16, 16, None,
+                                      None, None, 16, 16, 16, 16, 16, 16, 16, ws, need, events,
+                                      None)
+    assert call(None) == fw.FW_EINVAL
+    assert call(ev_missing) == fw.FW_EINVAL
+    assert call(ev, router=None) == fw.FW_EINVAL
+    assert call(ev, ws=128) == fw.FW_EALIGN
+    assert call(ev, T=-1) == fw.FW_EINVAL

@@ -83,7 +83,7 @@ def test_layer_matches_three_calls_and_oracle(ref, cfg, T, path):
     ok = ~G.small_gaps(rl, cfg.top_k)
     assert np.array_equal(ids[ok], rids[ok])
     assert np.abs(w[ok] - rw[ok]).max() <= G.W_MAX_ABS
-    tok = np.intersect1d(G.sample_tokens(T, 48), np.nonzero(ok)[0])
+    tok = np.intersect1d(G.compare_tokens(T, rids, cfg.n_experts), np.nonzero(ok)[0])
     assert tok.size > 0
     want = G.oracle_forward(ref, cfg, dl, np.ascontiguousarray(xh[tok]), rids[tok], rw[tok])
     G.check_out(out[tok], want)

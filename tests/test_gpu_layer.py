@@ -1,6 +1,8 @@
 """GPU parity of the three C-ABI calls against the CPU oracle, on the seeded
-workloads (all five, at their full sizes; large batches compare sampled
-tokens, which the oracle computes one by one)."""
+workloads (all five, at their full sizes).  Outputs are compared on every row
+up to 2048 tokens; larger batches compare a sample that holds both ends, 48
+random tokens and, for every expert, the token of its last routed row (its
+last, partial GEMM tile), which the oracle computes one by one."""
 
 import numpy as np
 import pytest
@@ -14,11 +16,17 @@ pytestmark = pytest.mark.gpu
 
 C = moegen
 SWEEP_Z = C.SWEEP_Q8.with_(zipf=1.3)
-# (config, T): every batch size each workload names; the sweep at a spread of T
+SWEEP_Q4_Z = C.SWEEP_Q4.with_(zipf=1.3)
+# (config, T): every batch size each workload names; the sweep layer (Q8_0 and
+# Q4_0 experts, uniform and Zipf(1.3) routing) at a spread of T around its
+# decode-to-prefill crossover (32 / 48 tokens) and at both ends of its range
 CASES = [(C.TINY, 4), (C.QWEN3_DECODE, 1), (C.QWEN3_DECODE, 4), (C.QWEN3_DECODE, 16),
          (C.QWEN3_PREFILL, 2048), (C.DEEPSEEK, 1), (C.DEEPSEEK, 32), (C.DEEPSEEK, 4096),
-         (C.SWEEP_Q8, 1), (C.SWEEP_Q8, 64), (C.SWEEP_Q8, 1024), (SWEEP_Z, 8192)]
-IDS = [f"c{c.cid}{'z' if c.zipf and c.cid == 4 else ''}-T{T}" for c, T in CASES]
+         (C.SWEEP_Q8, 1), (C.SWEEP_Q8, 64), (C.SWEEP_Q8, 1024), (C.SWEEP_Q8, 8192),
+         (SWEEP_Z, 8192)]
+CASES += [(cfg, T) for cfg in (C.SWEEP_Q4, SWEEP_Q4_Z) for T in (1, 32, 48, 1024, 8192)]
+IDS = [f"c{c.cid}{'' if c.cid != 4 else '-' + c.expert_q}{'z' if c.zipf and c.cid == 4 else ''}"
+       f"-T{T}" for c, T in CASES]
 
 
 def _x(cfg, T):
@@ -84,7 +92,7 @@ def test_forward(ref, cfg, T, path):
     off, sp, inv = G.permute(desc, cfg, ids_d, ws)
     out = G.forward(desc, cfg, dl, x, w_d, off, sp, inv, ws).cpu().numpy()
     assert fw.fw_moe_read_status(ws) == 0
-    tok = G.sample_tokens(T, 48)
+    tok = G.compare_tokens(T, rids, cfg.n_experts)
     want = G.oracle_forward(ref, cfg, dl, np.ascontiguousarray(xh[tok]), rids[tok], rw[tok])
     G.check_out(out[tok], want)
 
@@ -107,7 +115,8 @@ def test_end_to_end(ref, cfg, T):
     ws = G.workspace(desc, T)
     off, sp, inv = G.permute(desc, cfg, ids, ws)
     out = G.forward(desc, cfg, dl, x, w, off, sp, inv, ws).cpu().numpy()
-    tok = G.sample_tokens(T, 48)
+    assert fw.fw_moe_read_status(ws) == 0
+    tok = G.compare_tokens(T, rids, cfg.n_experts)
     want = G.oracle_forward(ref, cfg, dl, np.ascontiguousarray(xh[tok]), rids[tok], rw[tok])
     G.check_out(out[tok], want)
 

@@ -37,7 +37,7 @@ def test_forward_q4k(ref, cfg, T, path):
     off, sp, inv = G.permute(desc, cfg, ids_d, ws)
     out = G.forward(desc, cfg, dl, x, w_d, off, sp, inv, ws).cpu().numpy()
     assert fw.fw_moe_read_status(ws) == 0
-    tok = G.sample_tokens(T, 24)
+    tok = G.compare_tokens(T, rids, cfg.n_experts, n_random=24)
     want = G.oracle_forward(ref, cfg, dl, np.ascontiguousarray(xh[tok]), rids[tok], rw[tok])
     err, rel = G.check_out(out[tok], want)
     print(f"  max-abs {err:.2e} rel-L2 {rel:.2e}", flush=True)

@@ -1,0 +1,167 @@
+"""The fp16 range contract of fw_moe_forward (fwmoe.h, "Numerics").
+
+Both kernel families hold activations and the SwiGLU output in fp16.  Each
+token row is scaled by a power of two before it is staged (and the scale is
+taken back out exactly), so rows of any finite magnitude keep the accuracy of a
+unit-scale row; what fp16 still cannot hold sets FW_STATUS_RANGE.  Checked
+here against the CPU oracle on the same bytes:
+  - token rows whose magnitudes span 1e-6 .. 1e5, through both families and
+    all three expert formats: each row within the layer's relative accuracy;
+  - the edge blocks of the pinned block-decode fixtures (subnormal and
+    negative scales, the extreme codes -128 / 0 / 15) placed in routed expert
+    weights: in range, so within the layer tolerance and no status bit;
+  - a block scale of 65504 (fp16's largest) and a non-finite activation: the
+    status bit is set.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import moegen
+from sparse_moe_block_amd import fwmoe as fw
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+C = moegen
+# a small layer: hidden 512, 8 experts, top-2, expert ffn 512, bf16 activations
+BASE = C.TINY.with_(name="range", hidden=512, ffn=512, act_dtype=C.BF16,
+                    router_dtype=C.BF16)
+SCALES = [1e-6, 1e-4, 1e-2, 1.0, 1.0, 1e2, 1e3, 1e4, 1e5, 3e-5, 7.0, 0.5]
+
+
+def _routing(cfg, T, seed=3):
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.choice(cfg.n_experts, cfg.top_k, replace=False) for _ in range(T)])
+    w = rng.uniform(0.2, 1.0, size=(T, cfg.top_k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    return ids.astype(np.int32), w
+
+
+def _run(cfg, qtype, path, L, xh, ids, w, ref):
+    """GPU permute + forward and the oracle on the same host bytes."""
+    T = xh.shape[0]
+    desc = G.desc_of(cfg, path=path, qtype=qtype)
+    dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(G.DEV)
+    x = dev(xh).view(torch.bfloat16)
+    ws = G.workspace(desc, T)
+    off, sp, inv = G.permute(desc, cfg, dev(ids), ws)
+    out = torch.full((T, cfg.hidden), float("nan"), device=G.DEV)
+    fw.fw_moe_forward(desc, T, x, dev(L["w_gate"]), dev(L["w_up"]), dev(L["w_down"]), None,
+                      None, None, dev(w), off, sp, inv, out, ws)
+    torch.cuda.synchronize()
+    status = fw.fw_moe_read_status(ws)
+    want = ref.forward(xh, L["w_gate"], L["w_up"], L["w_down"], ids, w,
+                       n_experts=cfg.n_experts, ffn=cfg.ffn, qtype=qtype, act_dtype="bf16")
+    return status, out.cpu().numpy(), want
+
+
+def _host_layer(cfg, qtype):
+    L = moegen.make_layer(cfg, device="cpu", qtype=qtype)
+    h = moegen.as_numpy_bits
+    return {"w_gate": h(L.w_gate).copy(), "w_up": h(L.w_up).copy(),
+            "w_down": h(L.w_down).copy()}
+
+
+def _x_rows(cfg, scales, seed=11):
+    g = torch.Generator().manual_seed(seed)
+    z = torch.randn((len(scales), cfg.hidden), generator=g)
+    x = (z * torch.tensor(scales, dtype=torch.float32)[:, None]).to(torch.bfloat16)
+    return moegen.as_numpy_bits(x)
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0", "q4_k"])
+def test_rows_of_any_scale(ref, qtype, path):
+    """Each row within relative L2 1e-3 and a max error of 4e-3 of its own
+    largest output; the unit-scale rows also within the absolute tolerance."""
+    print(f"row scales {qtype} {path}", flush=True)
+    cfg = BASE
+    L = _host_layer(cfg, qtype)
+    xh = _x_rows(cfg, SCALES)
+    ids, w = _routing(cfg, len(SCALES))
+    status, got, want = _run(cfg, qtype, path, L, xh, ids, w, ref)
+    assert status == 0, status
+    assert np.all(np.isfinite(got))
+    worst = [0.0, 0.0]
+    for t, sc in enumerate(SCALES):
+        d, r = got[t] - want[t], want[t]
+        rel = np.linalg.norm(d) / np.linalg.norm(r)
+        mx = np.abs(d).max() / np.abs(r).max()
+        worst = [max(worst[0], rel), max(worst[1], mx)]
+        assert rel <= G.OUT_REL_L2 and mx <= 4e-3, (t, sc, rel, mx)
+    print(f"  worst row: rel-L2 {worst[0]:.2e}, max error / row max {worst[1]:.2e}", flush=True)
+    unit = [t for t, sc in enumerate(SCALES) if sc == 1.0]
+    G.check_out(got[unit], want[unit])
+
+
+def _put_block(W, e, row, blk, bq, raw):
+    W[e, row, blk * bq:(blk + 1) * bq] = np.frombuffer(raw, np.uint8)
+
+
+def _edge_weights(cfg, qtype):
+    """The pinned fixtures' edge cases written into block 0 / 1 of a few rows
+    of every expert's three matrices."""
+    L = _host_layer(cfg, qtype)
+    bq = {"q8_0": 34, "q4_0": 18}[qtype]
+    rng = np.random.default_rng(5)
+    for e in range(cfg.n_experts):
+        for name in ("w_gate", "w_up", "w_down"):
+            W = L[name]
+            d_norm = W[e, 0, 0:2].view(np.uint16)[0]            # an ordinary scale
+            if qtype == "q8_0":
+                codes = rng.integers(-128, 128, 32).astype(np.int8)
+                codes[0] = -128
+                _put_block(W, e, 0, 0, bq, np.uint16(0x0001).tobytes() + codes.tobytes())
+                _put_block(W, e, 1, 1, bq, np.uint16(0x03FF).tobytes() + codes.tobytes())
+                _put_block(W, e, 2, 0, bq, np.uint16(d_norm ^ 0x8000).tobytes()
+                           + codes.tobytes())
+                full = np.full(32, -128, np.int8)
+                _put_block(W, e, 3, 2, bq, np.uint16(d_norm).tobytes() + full.tobytes())
+            else:
+                q = rng.integers(0, 16, 32).astype(np.uint8)
+                q[0], q[17] = 0, 15
+                packed = (q[:16] | (q[16:] << 4)).astype(np.uint8)
+                _put_block(W, e, 0, 0, bq, np.uint16(0x0001).tobytes() + packed.tobytes())
+                _put_block(W, e, 1, 1, bq, np.uint16(0x03FF).tobytes() + packed.tobytes())
+                _put_block(W, e, 2, 0, bq, np.uint16(d_norm ^ 0x8000).tobytes()
+                           + packed.tobytes())
+                zeros = np.zeros(16, np.uint8)                      # every code 0: -8 d
+                _put_block(W, e, 3, 2, bq, np.uint16(d_norm).tobytes() + zeros.tobytes())
+    return L
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+def test_edge_blocks_in_range(ref, qtype, path):
+    print(f"edge blocks {qtype} {path}", flush=True)
+    cfg = BASE
+    L = _edge_weights(cfg, qtype)
+    T = 24
+    xh = moegen.as_numpy_bits(moegen.make_x(cfg, T))
+    ids, w = _routing(cfg, T, seed=7)
+    status, got, want = _run(cfg, qtype, path, L, xh, ids, w, ref)
+    assert status == 0, status
+    G.check_out(got, want)
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+def test_out_of_range_is_flagged(ref, qtype, path):
+    print(f"out of range {qtype} {path}", flush=True)
+    cfg = BASE
+    T = 24
+    xh = moegen.as_numpy_bits(moegen.make_x(cfg, T))
+    ids, w = _routing(cfg, T, seed=9)
+    # a block scale of 65504 in gate row 0 of every expert
+    L = _host_layer(cfg, qtype)
+    L["w_gate"][:, 0, 0:2] = np.frombuffer(np.uint16(0x7BFF).tobytes(), np.uint8)
+    status, _, _ = _run(cfg, qtype, path, L, xh, ids, w, ref)
+    assert status & fw.FW_STATUS_RANGE, status
+    # a non-finite activation, ordinary weights
+    L = _host_layer(cfg, qtype)
+    xb = xh.copy()
+    xb[3, 17] = 0x7F80                                         # bf16 +inf
+    status, _, _ = _run(cfg, qtype, path, L, xb, ids, w, ref)
+    assert status & fw.FW_STATUS_RANGE, status
