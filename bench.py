@@ -31,10 +31,11 @@ HBM_PEAK_GBS = 8000.0
 MFMA_FP16_PEAK_TFLOPS = 2500.0
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)"
 CSRC = os.path.join(ROOT, "sparse_moe_block_amd", "csrc")
-# sources whose kernels the traffic counters describe (a change voids them)
-# sources that decide each dominant kernel's memory traffic
+# sources that decide each dominant kernel's memory traffic (a change to any
+# voids its counter figures)
 TRAFFIC_SOURCES = {"gemv_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "gemv.hip"],
-                   "gemm2_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "gemm2.hip"]}
+                   "gemm_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "gemm_frag.h",
+                                            "gemm.hip"]}
 
 HEADLINE = "deepseek4096"   # the largest configuration, MFMA-bound (grouped GEMM)
 DECODE_EXTRA = "decode16"   # the metric's HBM-bound decode point, carried as "decode"
@@ -278,7 +279,7 @@ def measure(a, workload, steps, warmup, setup_only=False):
         # flops: 2 projections x 2 flops x P x H x F (+ the shared expert on T rows)
         gu_alg = 4 * P * H * cfg.ffn + 4 * T * H * cfg.shared_ffn
         achieved = gu_alg / (gu_ms * 1e-3) / 1e12
-        roof = {"kernel": "gemm2_kernel<gate/up>", "bound": "mfma", "achieved": achieved,
+        roof = {"kernel": "gemm_kernel<gate/up>", "bound": "mfma", "achieved": achieved,
                 "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / MFMA_FP16_PEAK_TFLOPS, "traffic": None,
                 "algorithmic_flops": gu_alg}
@@ -440,8 +441,8 @@ def peaks(a):
     five timed launches after a warm-up."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "sparse_moe_block_amd", "libfwpeak.so"))
-    lib.fw_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                 ctypes.c_void_p]
+    lib.fw_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p, ctypes.c_void_p]
     lib.fw_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                  ctypes.c_void_p, ctypes.c_void_p]
     lib.fw_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
@@ -465,16 +466,20 @@ def peaks(a):
             ts.append(e0.elapsed_time(e1) * 1e-3)
         return min(ts)
 
-    blocks = cus * 8          # two 4-wave workgroups per SIMD pair: every SIMD busy
-    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
-    for shape, per, flops in ((16, 8, 16384), (32, 4, 32768)):
-        iters = 4000
-        t = best(lambda: lib.fw_peak_mfma(shape, blocks, iters, ctypes.c_void_p(out.data_ptr()),
-                                          ctypes.c_void_p(stream.cuda_stream)))
-        total = blocks * 4 * iters * per * flops
-        print(json.dumps({"peak": f"fp16 mfma {shape}x{shape}x{512 // shape}", "cus": cus,
-                          "workgroups": blocks, "seconds": t,
-                          "TFLOP/s": total / t / 1e12}), flush=True)
+    # 4 or 8 wavefronts per CU (one or two per SIMD), several accumulator chains
+    out = torch.empty(cus * 8 * 256, dtype=torch.float32, device=dev)
+    for shape, flops, chain_set in ((16, 16384, (4, 8, 16)), (32, 32768, (2, 4, 8))):
+        for per_simd in (1, 2):
+            blocks = cus * per_simd
+            for ch in chain_set:
+                iters = 32000 // ch
+                t = best(lambda: lib.fw_peak_mfma(shape, ch, blocks, iters,
+                                                  ctypes.c_void_p(out.data_ptr()),
+                                                  ctypes.c_void_p(stream.cuda_stream)))
+                total = blocks * 4 * iters * ch * flops
+                print(json.dumps({"peak": f"fp16 mfma {shape}x{shape}x{512 // shape}",
+                                  "waves_per_simd": per_simd, "chains": ch, "seconds": t,
+                                  "TFLOP/s": total / t / 1e12}), flush=True)
     nbytes = 4 << 30
     src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
     for blocks in (cus * 4, cus * 8, cus * 16):
@@ -505,7 +510,7 @@ def source_hash(kernel):
 
 # dominant kernel: label in the JSON line, mangled-name fragment in counter files
 KERNELS = {"gemv_kernel<gate/up>": ("gemv_gate_up", "gemv_kernelILi"),
-           "gemm2_kernel<gate/up>": ("gemm2_gate_up", "gemm2_kernelILi")}
+           "gemm_kernel<gate/up>": ("gemm_gate_up", "gemm_kernelILi")}
 
 
 def traffic_path(workload, kernel):
@@ -539,7 +544,7 @@ def reduce_counters(a):
                         cfg.act_dtype, cfg.router_dtype, cfg.expert_q, cfg.shared_q,
                         cfg.score, a.path)
     path_gemv = fw.fw_moe_forward_path(desc, T) == fw.FW_PATH_GEMV
-    kernel = "gemv_kernel<gate/up>" if path_gemv else "gemm2_kernel<gate/up>"
+    kernel = "gemv_kernel<gate/up>" if path_gemv else "gemm_kernel<gate/up>"
     frag = KERNELS[kernel][1] + {"q8_0": "0", "q4_0": "1", "q4_k": "2"}[cfg.expert_q] + "ELb1E"
 
     def per_dispatch(d, counter, sub):

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -22,7 +23,7 @@ WsLayout ws_layout(const fw_moe_desc &d, int T) {
         off = align256(off + bytes);
         return at;
     };
-    // row tiles of either family: GEMM tiles of kGemm2BM rows, GEMV chunks of
+    // row tiles of either family: GEMM tiles of kGemmBM rows, GEMV chunks of
     // kGemvTokens rows (the larger count)
     L.max_tiles = (int)((P + kGemvTokens - 1) / kGemvTokens + E);
     L.active = take((E + 1) * sizeof(int4));
@@ -152,10 +153,10 @@ int enqueue_forward(const FwdArgs &a, const FrontArgs *front, const hipEvent_t *
     if (rc != FW_OK) return rc;
     if (ev) (void)hipEventRecord(ev[1], s);
     const bool gemm = a.path == FW_PATH_GEMM;
-    rc = hip_status(gemm ? launch_gemm2_gate_up(a, s) : launch_gemv_gate_up(a, s));
+    rc = hip_status(gemm ? launch_gemm_gate_up(a, s) : launch_gemv_gate_up(a, s));
     if (rc != FW_OK) return rc;
     if (ev) (void)hipEventRecord(ev[2], s);
-    rc = hip_status(gemm ? launch_gemm2_down(a, s) : launch_gemv_down(a, s));
+    rc = hip_status(gemm ? launch_gemm_down(a, s) : launch_gemv_down(a, s));
     if (rc != FW_OK) return rc;
     if (ev) (void)hipEventRecord(ev[3], s);
     if ((rc = hip_status(launch_combine(a, s))) != FW_OK) return rc;
@@ -163,14 +164,38 @@ int enqueue_forward(const FwdArgs &a, const FrontArgs *front, const hipEvent_t *
     return FW_OK;
 }
 
+// The launches of fw_moe_layer after validation.
+int layer_launches(const FwdArgs &a, const fw_moe_desc *desc, int32_t T, const void *x,
+                   const void *router_w, const float *logit_bias, float *logits,
+                   int32_t *topk_ids, float *topk_w, int32_t *expert_offsets,
+                   int32_t *sorted_pairs, int32_t *inv_pos, const hipEvent_t *ev, hipStream_t s) {
+    int rc;
+    if ((rc = hip_status(launch_logits(*desc, T, x, router_w, logit_bias, logits, s))) != FW_OK)
+        return rc;
+    if (decode_front_fits(*desc, T, a.path)) {
+        FrontArgs f{logits, topk_ids, topk_w, expert_offsets, sorted_pairs, inv_pos};
+        return enqueue_forward(a, &f, ev, s);
+    }
+    if ((rc = hip_status(launch_topk(*desc, T, logits, topk_ids, topk_w, s))) != FW_OK) return rc;
+    const long long P = (long long)T * desc->top_k;
+    int32_t *perm = P > kPermOneBlockMaxP ? (int32_t *)(a.ws + a.L.perm) : nullptr;
+    rc = hip_status(launch_permute(*desc, T, topk_ids, expert_offsets, sorted_pairs, inv_pos,
+                                   (WsHeader *)a.ws, perm, s));
+    if (rc != FW_OK) return rc;
+    return enqueue_forward(a, nullptr, ev, s);
+}
+
 // fw_moe_layer: every argument of the three stages is checked before anything
-// is enqueued; `ev` as in enqueue_forward.
+// is enqueued; `ev` as in enqueue_forward.  With `fresh_status` the status
+// word is cleared first (a fill kernel) and, when `status_out` is set, copied
+// there after the last stage.
 int layer_impl(const fw_moe_desc *desc, int32_t T, const void *x, const void *router_w,
                const float *logit_bias, const void *w_gate, const void *w_up,
                const void *w_down, const void *ws_gate, const void *ws_up, const void *ws_down,
                float *logits, int32_t *topk_ids, float *topk_w, int32_t *expert_offsets,
                int32_t *sorted_pairs, int32_t *inv_pos, float *out, void *workspace,
-               size_t ws_bytes, const hipEvent_t *ev, hipStream_t s) {
+               size_t ws_bytes, const hipEvent_t *ev, hipStream_t s, bool fresh_status = false,
+               int32_t *status_out = nullptr) {
     int rc = check_desc(desc);
     if (rc != FW_OK) return rc;
     if ((rc = check_T(desc, T)) != FW_OK) return rc;
@@ -182,19 +207,13 @@ int layer_impl(const fw_moe_desc *desc, int32_t T, const void *x, const void *ro
     rc = forward_args(desc, T, x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, topk_w,
                       expert_offsets, sorted_pairs, inv_pos, out, workspace, ws_bytes, &a);
     if (rc != FW_OK) return rc;
-    if ((rc = hip_status(launch_logits(*desc, T, x, router_w, logit_bias, logits, s))) != FW_OK)
+    if (fresh_status &&
+        (rc = hip_status(launch_clear_status((WsHeader *)workspace, s))) != FW_OK)
         return rc;
-    if (decode_front_fits(*desc, T, a.path)) {
-        FrontArgs f{logits, topk_ids, topk_w, expert_offsets, sorted_pairs, inv_pos};
-        return enqueue_forward(a, &f, ev, s);
-    }
-    if ((rc = hip_status(launch_topk(*desc, T, logits, topk_ids, topk_w, s))) != FW_OK) return rc;
-    const long long P = (long long)T * desc->top_k;
-    int32_t *perm = P > kPermOneBlockMaxP ? (int32_t *)(a.ws + a.L.perm) : nullptr;
-    rc = hip_status(launch_permute(*desc, T, topk_ids, expert_offsets, sorted_pairs, inv_pos,
-                                   (WsHeader *)workspace, perm, s));
-    if (rc != FW_OK) return rc;
-    return enqueue_forward(a, nullptr, ev, s);
+    rc = layer_launches(a, desc, T, x, router_w, logit_bias, logits, topk_ids, topk_w,
+                        expert_offsets, sorted_pairs, inv_pos, ev, s);
+    if (rc != FW_OK || !status_out) return rc;
+    return hip_status(launch_copy_status((const WsHeader *)workspace, status_out, s));
 }
 
 }  // namespace

@@ -16,7 +16,8 @@ constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 16;
 constexpr int kUnit = 256;        // elements per 16-byte-aligned run of 8 blocks
 constexpr int kGemvTokens = 2;    // token rows a GEMV work item carries
-constexpr int kGemm2BM = 64;      // token rows per tile of the register-dequant grouped GEMM
+constexpr int kGemm2BM = 64;      // token rows per tile of the 16x16x32 grouped GEMM
+constexpr int kGemmBM = 128;      // token rows per tile of the 32x32x16 grouped GEMM
 // AUTO: the GEMV family while the routed pairs average at most this many rows
 // per expert (T * k <= 2 E), the grouped GEMM above.  Measured crossovers, in
 // rows per expert: the hidden-4096 / 64-expert top-4 layer between 2 and 3
@@ -296,6 +297,7 @@ hipError_t launch_permute(const fw_moe_desc &d, int T, const int32_t *ids, int32
                           int32_t *sorted, int32_t *inv, WsHeader *hdr, int32_t *perm,
                           hipStream_t s);
 hipError_t launch_clear_status(WsHeader *hdr, hipStream_t s);
+hipError_t launch_copy_status(const WsHeader *hdr, int32_t *status, hipStream_t s);
 
 struct FwdArgs {
     fw_moe_desc d;
@@ -312,8 +314,8 @@ struct FwdArgs {
 hipError_t launch_prepare(const FwdArgs &a, hipStream_t s);
 hipError_t launch_gemv_gate_up(const FwdArgs &a, hipStream_t s);
 hipError_t launch_gemv_down(const FwdArgs &a, hipStream_t s);
-hipError_t launch_gemm2_gate_up(const FwdArgs &a, hipStream_t s);
-hipError_t launch_gemm2_down(const FwdArgs &a, hipStream_t s);
+hipError_t launch_gemm_gate_up(const FwdArgs &a, hipStream_t s);
+hipError_t launch_gemm_down(const FwdArgs &a, hipStream_t s);
 hipError_t launch_combine(const FwdArgs &a, hipStream_t s);
 // fw_moe_layer's fused decode front end (top-k + permutation + staging in one
 // launch): taken when the forward runs the GEMV family and the pairs fit the

@@ -8,7 +8,7 @@ namespace {
 
 // Block 0 turns expert_offsets into the list of active experts
 // (expert, first row, rows) and the row-tile list -- each active expert's rows
-// cut into tiles of at most tile_rows (the grouped GEMM's 64-row tiles, or the
+// cut into tiles of at most tile_rows (the grouped GEMM's 128-row tiles, or the
 // GEMV's token chunks) -- clamping anything out of range
 // (FW_STATUS_BAD_OFFSETS).  In the other blocks each wavefront stages one
 // token row in fp16, scaled by its power-of-two exponent (stage_x_row), in
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
 }  // namespace
 
 hipError_t launch_prepare(const FwdArgs &a, hipStream_t s) {
-    const int tile_rows = a.path == FW_PATH_GEMM ? kGemm2BM : kGemvTokens;
+    const int tile_rows = a.path == FW_PATH_GEMM ? kGemmBM : kGemvTokens;
     // the Q4_K GEMV needs the activation rows' block sums
     const bool sums = a.path == FW_PATH_GEMV &&
                       (a.d.expert_q == FW_Q4_K || (a.d.shared_ffn > 0 && a.d.shared_q == FW_Q4_K));

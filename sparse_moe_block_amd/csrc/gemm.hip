@@ -1,0 +1,510 @@
+// Forward, GEMM family (prefill-sized batches): grouped expert GEMMs on the
+// 32x32x16 fp16 MFMA, weights dequantised in registers, activations fed to
+// LDS by DMA.
+//
+// What bounds it.  Every dequantised weight fragment costs about 14 VALU
+// instructions (code bits into fp16 pairs, exact, then times the block's
+// fp16 scale), so the VALU work per MFMA is 14 divided by the number of
+// token-row groups the fragment feeds.  Each wavefront here owns all 128
+// token rows of its tile (four 32-row groups) and 64 weight rows (two 32-row
+// groups), so a fragment feeds four 32x32x16 MFMAs (32768 flops each); the
+// accumulators take 128 VGPRs.
+//
+//  - a workgroup tile is up to 128 rows of one expert's segment of the sorted
+//    pair list (tokens gathered through sorted_pairs) times 256 weight rows;
+//    a tile with fewer rows runs only the 32-row groups that hold rows;
+//  - K advances 128 elements (half a 256-element unit, four GGUF blocks) per
+//    step, eight 16-wide MFMA slices.  Lane group g = lane / 32 covers blocks
+//    2g and 2g + 1 of the half unit, slice s block 2g + s / 4, fp16 pairs
+//    4 (s % 4) .. + 3 in the pair order of decode_pairs, on both operands (the
+//    MFMA sums over k in any order);
+//  - activations: the 128 x 128 fp16 tile of a step moves HBM/L2 -> LDS with
+//    global_load_lds_dwordx4 (no VGPRs, no LDS store instructions), two steps
+//    in flight in two LDS buffers; 16-byte chunk c of tile row r lands at
+//    chunk c ^ (r % 16) of the row, so the 32 lanes that read one chunk of 32
+//    rows hit distinct banks;
+//  - weights: lane (n = lane % 32, g) loads the dword-aligned window of blocks
+//    2g, 2g + 1 of its weight row (36 bytes Q4_0, 68 Q8_0; Q4_K: the
+//    super-block header and the group's 32 code bytes) one step ahead and
+//    turns one code dword into a B fragment right before its MFMAs;
+//  - gate/up: a wavefront's 64 weight rows are 32 gate and the same 32 up
+//    features, so a lane holds gate and up of the same (token, feature) and
+//    forms SiLU(g)*u in registers; the 32 features of a wavefront are one
+//    32-element block of h, stored in pair order straight from the registers;
+//    the down projection's fp32 rows go straight from the accumulators too;
+//  - each XCD takes a contiguous eighth of the row-tile list (the tiles of one
+//    expert share its L2, so the expert's weights are fetched about once);
+//    consecutive workgroups of one XCD take the column tiles of one row tile.
+#include <math.h>
+
+#include "common.h"
+#include "gemm_frag.h"
+
+namespace fw {
+namespace {
+
+constexpr int BM = kGemmBM;   // token rows per tile
+constexpr int BK = 128;       // k per step
+constexpr int kChunks = BM * BK / 8;   // 16-byte chunks of a step's activations: 2048
+constexpr int kMaxDma = kChunks / 256;  // DMA instructions per thread (4-wave workgroups)
+constexpr int kMaxPX = 9;               // 16-byte weight pieces per row and half unit (Q8_0)
+static_assert(BM == 128, "tile shape");
+
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Addresses are a uniform 64-bit base plus a 32-bit per-lane byte offset, the
+// form the scalar-base global loads take (one VGPR per address).
+struct Tile {
+    const uint8_t *abase;    // activation rows (uniform)
+    uint32_t aoff[kMaxDma];  // byte offsets of this thread's DMA rows, at its chunk
+    const uint8_t *bbase[2]; // the expert's gate and up matrices (down: both the one)
+    uint32_t woff[kMaxPX];   // byte offsets of this thread's weight pieces (unit 0, half 0)
+    uint32_t wk;             // Q4_K: bit i set where piece i is a code piece (moves for half 1)
+    _Float16 *hout;
+    float *yout;
+    const int32_t *s_ex;     // LDS: each tile row's exponent
+    WsHeader *hdr;
+    int lane, wave, steps, rows, rb, ct, N;
+};
+
+// Weight pieces in LDS.  Each step's half unit moves to LDS by DMA in whole
+// 16-byte pieces, PX per weight row (the smallest run of aligned pieces that
+// covers the half; for Q4_K the 16-byte header and the half's two code
+// groups): consecutive lanes take consecutive pieces of a row, a few cache
+// lines per instruction.  Two half-unit buffers: the next step's half loads
+// while this step's is used.
+template <int Q> constexpr int half_pieces() { return Q == FW_Q8_0 ? 9 : 5; }
+// source piece of LDS piece j (0 .. PX - 1) of half h of a unit
+template <int Q> __device__ __forceinline__ int src_piece(int h, int j) {
+    if constexpr (Q == FW_Q4_K) return h == 0 || j == 0 ? j : 4 + j;
+    else return j + h * (QT<Q>::kUnitX4 - half_pieces<Q>());
+}
+
+// A lane's window of half h (blocks 2g, 2g + 1 of the half; Q4_K: the
+// super-block header and code group 2h + g) from its weight row's pieces in
+// LDS (row: the row's first piece).
+template <int Q>
+__device__ __forceinline__ void lds_window(const uint8_t *row, int h, int g, uint32_t *w) {
+    if constexpr (Q == FW_Q4_K) {
+        const uint32_t *hd = (const uint32_t *)row;
+        const uint32_t *cd = (const uint32_t *)(row + 16 + 32 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = hd[i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[4 + i] = cd[i];
+    } else {
+        constexpr int kHalf = QT<Q>::kUnitBytes / 2;
+        const int first = h * kHalf - 16 * src_piece<Q>(h, 0);   // 0 or 8
+        const uint32_t *q = (const uint32_t *)(row + first + g * (2 * QT<Q>::kBlockBytes));
+#pragma unroll
+        for (int i = 0; i < win_dwords<Q>(); ++i) w[i] = q[i];
+    }
+}
+
+// LDS weight row Rl of a buffer holds the workgroup's weight row Rl:
+//   gate/up: Rl < 32 NW gate feature ct 32 NW + Rl, else up feature
+//            ct 32 NW + Rl - 32 NW; wavefront w reads rows 32 w + n (gate)
+//            and 32 NW + 32 w + n (up);
+//   down:    output row ct 64 NW + Rl; wavefront w reads 64 w + 32 cg + n.
+template <bool GU, int NW>
+__device__ __forceinline__ int lds_wrow(int wave, int cg, int n) {
+    return GU ? 32 * NW * cg + 32 * wave + n : 64 * wave + 32 * cg + n;
+}
+
+// NW wavefronts per workgroup, each owning 64 weight rows and all token rows.
+template <int Q, bool GU, int NW, int MI>
+__device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 *B1,
+                                          const Tile &c) {
+    constexpr int kThreads = 64 * NW;
+    // DMA instruction i of a thread covers tile rows [4 NW i, 4 NW (i + 1)):
+    // the ones the tile's MI 32-row groups need
+    constexpr int kDma = (32 * MI + 4 * NW - 1) / (4 * NW);
+    constexpr int WD = win_dwords<Q>();
+    constexpr int UB = QT<Q>::kUnitBytes, PX = half_pieces<Q>();
+    const int lane = c.lane, steps = c.steps;
+    const int g = lane >> 5, n = lane & 31, wave = c.wave;
+
+    f16v acc[MI][2];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    uint32_t wh[2][WD];      // this step's windows, per column group
+    uint32_t dmax = 0;       // largest block-scale magnitude bits met (Q8_0 / Q4_0)
+    float wmax = 0.f;        // largest Q4_K weight bound met
+
+    // activations of step st: rows 4 NW i + tid / 16, chunk (tid % 16) ^ (tid / 16 % 16)
+    auto dma_a = [&](uint4 *buf, int st, int i) {
+        if (i < kDma)
+            __builtin_amdgcn_global_load_lds(c.abase + (c.aoff[i] + (uint32_t)st * (BK * 2)),
+                                             (lds_void *)(buf + i * kThreads + 64 * wave), 16,
+                                             0, 0);
+    };
+    // instruction i of the weight pieces of step st: LDS pieces
+    // 64 (NW i + w) .. + 63 of the buffer, all of one matrix (the 32 NW rows
+    // of PX pieces of each matrix are a whole number of 64-piece instructions)
+    auto dma_w = [&](uint4 *buf, int st, int i) {
+        if (i < PX) {
+            const int h = st & 1;
+            const uint8_t *base = GU && (NW * i + wave >= NW * PX / 2) ? c.bbase[1] : c.bbase[0];
+            uint32_t off = c.woff[i] + (uint32_t)(st >> 1) * UB;
+            if constexpr (Q == FW_Q4_K) off += h && ((c.wk >> i) & 1) ? 64u : 0u;
+            else off += (uint32_t)h * (16 * (QT<Q>::kUnitX4 - PX));
+            __builtin_amdgcn_global_load_lds(base + off,
+                                             (lds_void *)(buf + i * kThreads + 64 * wave), 16,
+                                             0, 0);
+        }
+    };
+    const int wr0 = lds_wrow<GU, NW>(wave, 0, n) * (16 * PX);
+    const int wr1 = lds_wrow<GU, NW>(wave, 1, n) * (16 * PX);
+    auto read_w = [&](const uint4 *buf, int h) {
+        lds_window<Q>((const uint8_t *)buf + wr0, h, g, wh[0]);
+        lds_window<Q>((const uint8_t *)buf + wr1, h, g, wh[1]);
+    };
+    // A fragment of slice s, row group mi: row 32 mi + n, chunk 8 g + s,
+    // stored at chunk (8 g + s) ^ (n % 16) of the row
+    const int arow = n * 16, ax = n & 15;
+    const int ch = arow + (8 * g ^ (ax & 8));   // the chunk's row base and bit 3
+    const int xs = ax & 7;
+    // One step: eight slices, software-pipelined one slice deep -- slice S's
+    // MFMAs are issued with slice S + 1's A fragments already on their way
+    // from LDS and followed by slice S + 1's B fragments, so a wavefront's
+    // MFMAs run back to back without waiting on its own LDS reads or dequant.
+    // pf(S) issues the DMA instructions placed after slice S.
+    auto step = [&](const uint4 *buf, int h, auto &&pf) {
+        uint32_t kq[2][4];
+        if constexpr (Q == FW_Q4_K) {
+#pragma unroll
+            for (int cg = 0; cg < 2; ++cg) {
+                q4k_consts(wh[cg], 2 * h + g, kq[cg]);
+                wmax = fmaxf(wmax, q4k_bound(kq[cg]));
+            }
+        } else {
+#pragma unroll
+            for (int cg = 0; cg < 2; ++cg) dmax = max(dmax, d_bits<Q>(wh[cg]));
+        }
+        h8 a[2][MI], b[2][2];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) a[0][mi] = __builtin_bit_cast(h8, buf[ch + xs + mi * 512]);
+        b[0][0] = frag_any<Q, 0>(wh[0], kq[0]);
+        b[0][1] = frag_any<Q, 0>(wh[1], kq[1]);
+#define FW_SLICE(S)                                                                          \
+    {                                                                                        \
+        constexpr int X = (S) & 1, Y = X ^ 1;                                                \
+        if constexpr ((S) < 7) {                                                             \
+            _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                                \
+                a[Y][mi] = __builtin_bit_cast(h8, buf[ch + (((S) + 1) ^ xs) + mi * 512]);    \
+        }                                                                                    \
+        _Pragma("unroll") for (int cg = 0; cg < 2; ++cg)                                     \
+            _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                                \
+                acc[mi][cg] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[X][mi], b[X][cg],     \
+                                                                     acc[mi][cg], 0, 0, 0);  \
+        if constexpr ((S) < 7) {                                                             \
+            b[Y][0] = frag_any<Q, ((S) + 1) & 7>(wh[0], kq[0]);                              \
+            b[Y][1] = frag_any<Q, ((S) + 1) & 7>(wh[1], kq[1]);                              \
+        }                                                                                    \
+        pf(S);                                                                               \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+    }
+        FW_SLICE(0)
+        FW_SLICE(1)
+        FW_SLICE(2)
+        FW_SLICE(3)
+        FW_SLICE(4)
+        FW_SLICE(5)
+        FW_SLICE(6)
+        FW_SLICE(7)
+#undef FW_SLICE
+    };
+    // sync: everything issued so far has landed (one full wait, as a builtin
+    // so the compiler's own wait insertion knows of it) and every wavefront
+    // has reached the same point, so a buffer read before it may be refilled
+    // after it.  The loop body has no branch (the compiler's tracking of
+    // which LDS buffer a pending DMA writes does not survive one): past the
+    // last step the prefetches repeat the last step's addresses.
+    auto sync = [&]() {
+        __builtin_amdgcn_s_waitcnt(7 << 4);   // vmcnt(0) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // Step st reads activations A[st % 2] and weights B[st % 2] and loads
+    // step st + 1's into the other pair of buffers, which every wavefront
+    // finished reading before the sync that ended step st - 1.  The DMA
+    // instructions follow the first slices rather than all come at the
+    // step's start: a burst of every wavefront's DMA fills the memory
+    // pipeline's queues and holds up the MFMAs behind it.
+    auto issue = [&](uint4 *abuf, uint4 *bbuf, int st, int S) {
+        if (S < 4) {
+#pragma unroll
+            for (int i = 0; i < (PX + 3) / 4; ++i) dma_w(bbuf, st, S * ((PX + 3) / 4) + i);
+        }
+        if (S < 2) {
+#pragma unroll
+            for (int i = 0; i < (kDma + 1) / 2; ++i) dma_a(abuf, st, S * ((kDma + 1) / 2) + i);
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < PX; ++i) dma_w(B0, 0, i);
+#pragma unroll
+    for (int i = 0; i < kDma; ++i) dma_a(A0, 0, i);
+    sync();
+    for (int st = 0; st < steps; st += 2) {
+        read_w(B0, 0);
+        step(A0, 0, [&](int S) { issue(A1, B1, st + 1, S); });
+        sync();
+        read_w(B1, 1);
+        const int nx = min(st + 2, steps - 1);
+        step(A1, 1, [&](int S) { issue(A0, B0, nx, S); });
+        sync();
+    }
+
+    // ---- epilogue: acc[mi][cg][v] is tile row 32 mi + 8 (v / 4) + 4 g + v % 4,
+    // weight row (column group cg) n ----
+    const int rows = c.rows, rb = c.rb, N = c.N;
+    bool range = Q == FW_Q4_K ? !(wmax <= 65504.0f)
+                              : dmax > (Q == FW_Q4_0 ? kQ4DMaxBits : kQ8DMaxBits);
+    if constexpr (GU) {
+        // feature ct * 128 + 32 wave + n: gate in column group 0, up in 1; the
+        // wavefront's 32 features are one 32-element block of h (pair order)
+        _Float16 *hrow = c.hout + (size_t)c.ct * (32 * NW) + 32 * c.wave + pair_pos(n);
+        const int esc = (n & 16) ? 4 : 0;   // pairs j = 1, 3 hold value / 16
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = 32 * mi + 8 * (v >> 2) + 4 * g + (v & 3);
+                if (row < rows) {
+                    const int e = c.s_ex[row];
+                    const float gv = __builtin_amdgcn_ldexpf(acc[mi][0][v], -e);
+                    const float up = __builtin_amdgcn_ldexpf(acc[mi][1][v], -e);
+                    const float a = gv / (1.0f + __expf(-gv)) * up;
+                    const _Float16 ah = (_Float16)__builtin_amdgcn_ldexpf(a, 2 * e - esc);
+                    range |= (__builtin_bit_cast(uint16_t, ah) & 0x7C00u) == 0x7C00u;
+                    hrow[(size_t)(rb + row) * N] = ah;
+                }
+            }
+    } else {
+        // y rows at the row's scale: for each (mi, cg, v) the 32 lanes of a
+        // lane group write 128 contiguous bytes of one row
+        float *yrow = c.yout + (size_t)c.ct * (64 * NW) + 64 * c.wave + n;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = 32 * mi + 8 * (v >> 2) + 4 * g + (v & 3);
+                if (row < rows) {
+                    const int e = c.s_ex[row];
+#pragma unroll
+                    for (int cg = 0; cg < 2; ++cg)
+                        yrow[(size_t)(rb + row) * N + 32 * cg] =
+                            __builtin_amdgcn_ldexpf(acc[mi][cg][v], -e);
+                }
+            }
+    }
+    if (range) atomicOr(&c.hdr->status, FW_STATUS_RANGE);
+}
+
+// One (row tile, column tile) of one expert (or of the shared expert).
+//  GU:  A = x rows gathered through sorted_pairs (routed) or token rows
+//       (shared); weight rows = 128 gate + 128 up features; writes
+//       a = SiLU(g) * u (fp16, pair order, at 2^(2e)) for 128 features and
+//       each h row's exponent 2e (oexp);
+//  !GU: A = rows of a (fp16); weight rows = 256 outputs; writes y (fp32)
+//       scaled back by the h row's exponent (iexp).
+// Two half-unit weight buffers (64 NW rows) and two activation tiles (64 KB)
+// fill most of a CU's 160 KB, so one workgroup runs per CU.  Eight-wave workgroups
+// (two wavefronts per SIMD, within 256 registers) serve Q4_0 and Q4_K;
+// four-wave ones (one wavefront per SIMD, up to 512 registers) serve the
+// column counts eight waves do not divide and Q8_0, whose wider windows and
+// 272-byte units need the registers and the LDS.
+template <int Q, int NW> constexpr int waves_per_simd() { return NW == 8 ? 2 : 1; }
+template <int Q> constexpr bool eight_waves() { return Q != FW_Q8_0; }
+
+template <int Q, bool GU, int NW>
+__global__ __launch_bounds__(64 * NW, (waves_per_simd<Q, NW>() * 4 / NW)) void gemm_kernel(
+    const uint8_t *__restrict__ wa, const uint8_t *__restrict__ wb,
+    const int4 *__restrict__ tiles, WsHeader *__restrict__ hdr,
+    const int32_t *__restrict__ sorted, const _Float16 *__restrict__ ain,
+    _Float16 *__restrict__ hout, float *__restrict__ yout, int K, int N, int k, int P,
+    int col_tiles, int n_row_tiles_max, int shared, int shared_rows,
+    const int32_t *__restrict__ iexp, int32_t *__restrict__ oexp) {
+    constexpr int PX = half_pieces<Q>();
+    __shared__ uint4 A0[kChunks];
+    __shared__ uint4 A1[kChunks];
+    __shared__ uint4 B0[64 * NW * PX];   // half units of the workgroup's weight rows
+    __shared__ uint4 B1[64 * NW * PX];
+    __shared__ int s_ex[BM];
+    // XCD-aware order: workgroup b runs on XCD b % 8.  Each XCD takes a
+    // contiguous eighth of the row tiles (the tiles of one expert are
+    // consecutive), column tiles fastest.
+    const int xcd = blockIdx.x % 8, bi = blockIdx.x / 8;
+    const int n_rt = shared ? (shared_rows + BM - 1) / BM
+                            : min(ld_const(&hdr->n_tiles), n_row_tiles_max);
+    const int per = (n_rt + 7) / 8;
+    const int rl = bi / col_tiles, ct = bi % col_tiles;
+    if (rl >= per) return;
+    const int rt = xcd * per + rl;
+    if (rt >= n_rt) return;
+    int expert = 0, rb = 0, rows = 0;
+    if (shared) {
+        rb = rt * BM;
+        rows = min(BM, shared_rows - rb);
+    } else {
+        const int4 tl = ld_const(tiles + rt);   // (expert, first row, rows)
+        expert = tl.x;
+        rb = tl.y;
+        rows = tl.z;
+    }
+    constexpr int kThreads = 64 * NW;
+    const int tid = threadIdx.x;
+    // each row's source row (the token of a routed gate/up row) and exponent
+    auto src_row = [&](int r) {   // r < rows
+        if (GU && !shared) {
+            const int q = sorted[rb + r];
+            if ((unsigned)q >= (unsigned)P) {
+                atomicOr(&hdr->status, FW_STATUS_BAD_PAIR);
+                return 0;
+            }
+            return q / k;
+        }
+        return rb + r;
+    };
+    if (tid < rows) {
+        const int src = src_row(tid);
+        if (GU) {
+            const int e = iexp[src];   // the token's x exponent
+            s_ex[tid] = e;
+            if (ct == 0) oexp[rb + tid] = 2 * e;
+        } else {
+            s_ex[tid] = iexp[rb + tid];   // the h row's exponent
+        }
+    }
+    Tile c;
+    c.lane = tid % kWave;
+    c.wave = wave_id();
+    // DMA rows 4 NW i + tid / 16 (past the tile's end: its last row), chunk
+    // (tid % 16) ^ (tid / 16 % 16), as byte offsets into ain
+    const int chunk = (tid & 15) ^ ((tid >> 4) & 15);
+#pragma unroll
+    for (int i = 0; i < kChunks / kThreads; ++i) {
+        const int r = min(4 * NW * i + (tid >> 4), rows - 1);
+        int s = rb + r;
+        if (GU && !shared) {
+            const int q = sorted[s];
+            s = (unsigned)q < (unsigned)P ? q / k : 0;
+        }
+        c.aoff[i] = ((uint32_t)s * K + chunk * 8) * 2;
+    }
+    c.abase = (const uint8_t *)ain;
+    const size_t rowbytes = (size_t)(K / 32) * QT<Q>::kBlockBytes;
+    const size_t esz = (size_t)N * rowbytes;
+    const uint8_t *ba = wa + (size_t)expert * esz, *bb = (GU ? wb : wa) + (size_t)expert * esz;
+    c.bbase[0] = ba;
+    c.bbase[1] = bb;
+    // weight piece of DMA instruction i: LDS piece p = i kThreads + tid is
+    // piece p % PX of LDS row p / PX (gate/up: rows from 32 NW on are the up
+    // matrix's, read from bbase[1])
+    c.wk = 0;
+#pragma unroll
+    for (int i = 0; i < PX; ++i) {
+        const int p = i * kThreads + tid;
+        int Rl = p / PX;
+        const int j = p - Rl * PX;
+        if (GU && Rl >= 32 * NW) Rl -= 32 * NW;
+        const int row = GU ? ct * (32 * NW) + Rl : ct * (64 * NW) + Rl;
+        c.woff[i] = (uint32_t)(row * rowbytes) + (uint32_t)j * 16;
+        if (j > 0) c.wk |= 1u << i;
+    }
+    c.hout = hout;
+    c.yout = yout;
+    c.s_ex = s_ex;
+    c.hdr = hdr;
+    c.steps = K / BK;
+    c.rows = rows;
+    c.rb = rb;
+    c.ct = ct;
+    c.N = N;
+    __syncthreads();   // s_ex
+    // only the 32-row groups that hold rows of this tile run
+    const int mi = (rows + 31) / 32;
+    if (mi > 3) tile_run<Q, GU, NW, 4>(A0, A1, B0, B1, c);
+    else if (mi > 2) tile_run<Q, GU, NW, 3>(A0, A1, B0, B1, c);
+    else if (mi > 1) tile_run<Q, GU, NW, 2>(A0, A1, B0, B1, c);
+    else tile_run<Q, GU, NW, 1>(A0, A1, B0, B1, c);
+}
+
+template <int Q, bool GU, int NW>
+void launch_nw(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Float16 *ain,
+                _Float16 *hout, float *yout, int K, int N, int shared, const int32_t *iexp,
+                int32_t *oexp, hipStream_t s) {
+    const int col_tiles = GU ? N / (32 * NW) : N / (64 * NW);
+    // routed: at most one partial tile per expert
+    const int row_tiles = shared ? (a.T + BM - 1) / BM
+                                 : std::min(a.L.max_tiles, (a.P + BM - 1) / BM + a.d.n_experts);
+    const int nblk = (row_tiles + 7) / 8 * 8 * col_tiles;   // eight XCDs x whole row tiles
+    gemm_kernel<Q, GU, NW><<<nblk, 64 * NW, 0, s>>>(
+        wa, wb, (const int4 *)(a.ws + a.L.tiles), (WsHeader *)a.ws, a.sorted, ain, hout, yout,
+        K, N, a.d.top_k, a.P, col_tiles, row_tiles, shared, shared ? a.T : 0, iexp, oexp);
+}
+
+// Eight-wave workgroups wherever the format allows and the columns divide
+// (gate/up: 256 features, down: 512 output rows per workgroup).
+template <int Q, bool GU>
+void launch(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Float16 *ain,
+             _Float16 *hout, float *yout, int K, int N, int shared, const int32_t *iexp,
+             int32_t *oexp, hipStream_t s) {
+    if constexpr (eight_waves<Q>()) {
+        if (N % (GU ? 256 : 512) == 0) {
+            launch_nw<Q, GU, 8>(a, wa, wb, ain, hout, yout, K, N, shared, iexp, oexp, s);
+            return;
+        }
+    }
+    launch_nw<Q, GU, 4>(a, wa, wb, ain, hout, yout, K, N, shared, iexp, oexp, s);
+}
+
+template <bool GU>
+void launch_q(int q, const FwdArgs &a, const uint8_t *wa, const uint8_t *wb,
+               const _Float16 *ain, _Float16 *hout, float *yout, int K, int N, int shared,
+               const int32_t *iexp, int32_t *oexp, hipStream_t s) {
+    if (q == FW_Q4_0)
+        launch<FW_Q4_0, GU>(a, wa, wb, ain, hout, yout, K, N, shared, iexp, oexp, s);
+    else if (q == FW_Q4_K)
+        launch<FW_Q4_K, GU>(a, wa, wb, ain, hout, yout, K, N, shared, iexp, oexp, s);
+    else
+        launch<FW_Q8_0, GU>(a, wa, wb, ain, hout, yout, K, N, shared, iexp, oexp, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_gate_up(const FwdArgs &a, hipStream_t s) {
+    const fw_moe_desc &d = a.d;
+    const _Float16 *x = (const _Float16 *)(a.ws + a.L.x16);
+    _Float16 *h = (_Float16 *)(a.ws + a.L.h);
+    const int32_t *xe = (const int32_t *)(a.ws + a.L.xe);
+    int32_t *he = (int32_t *)(a.ws + a.L.he);
+    launch_q<true>(d.expert_q, a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, 0, xe, he, s);
+    if (d.shared_ffn > 0)
+        launch_q<true>(d.shared_q, a, a.sg, a.su, x, h + (size_t)a.P * d.ffn, nullptr, d.hidden,
+                        d.shared_ffn, 1, xe, he + a.P, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_down(const FwdArgs &a, hipStream_t s) {
+    const fw_moe_desc &d = a.d;
+    const _Float16 *h = (const _Float16 *)(a.ws + a.L.h);
+    float *y = (float *)(a.ws + a.L.y);
+    const int32_t *he = (const int32_t *)(a.ws + a.L.he);
+    launch_q<false>(d.expert_q, a, a.wd, nullptr, h, nullptr, y, d.ffn, d.hidden, 0, he,
+                     nullptr, s);
+    if (d.shared_ffn > 0)
+        launch_q<false>(d.shared_q, a, a.sd, nullptr, h + (size_t)a.P * d.ffn, nullptr,
+                         y + (size_t)a.P * d.hidden, d.shared_ffn, d.hidden, 1, he + a.P,
+                         nullptr, s);
+    return hipGetLastError();
+}
+
+}  // namespace fw

@@ -1,0 +1,150 @@
+// Weight fragments of the grouped GEMM: the fp16 MFMA B fragments (eight k
+// values) dequantised in registers from a lane's window -- the dword-aligned
+// bytes of two consecutive GGUF blocks of one weight row (Q4_K: the
+// super-block header and one 32-byte code group).
+#pragma once
+
+#include "common.h"
+
+namespace fw {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+
+// Dwords of the window of blocks 2g, 2g + 1 of a unit, per weight row.
+// Q4_K: the super-block's 16-byte header and the 32 code bytes of group g.
+template <int Q> constexpr int win_dwords() { return Q == FW_Q4_0 ? 9 : Q == FW_Q4_K ? 12 : 17; }
+
+// Per-step constants of a Q4_K window (sub-blocks A = 2g, B = 2g + 1 of the
+// lane's group g), as fp32 bits: k[2h] = d * scale, k[2h + 1] = -dmin * min
+// (both exact in fp32).
+__device__ __forceinline__ void q4k_consts(const uint32_t *w, int g, uint32_t *k) {
+    const float d = half_bits_to_float(w[0] & 0xFFFFu), dmin = half_bits_to_float(w[0] >> 16);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int j = 2 * g + h, jj = (j - 4) & 3;
+        const uint32_t lo_s = __builtin_amdgcn_ubfe(w[1], 8 * j, 6);
+        const uint32_t lo_m = __builtin_amdgcn_ubfe(w[2], 8 * j, 6);
+        const uint32_t hi_s = __builtin_amdgcn_ubfe(w[3], 8 * jj, 4) |
+                              __builtin_amdgcn_ubfe(w[1], 8 * jj + 6, 2) << 4;
+        const uint32_t hi_m = __builtin_amdgcn_ubfe(w[3], 8 * jj + 4, 4) |
+                              __builtin_amdgcn_ubfe(w[2], 8 * jj + 6, 2) << 4;
+        const uint32_t sc = j < 4 ? lo_s : hi_s, mn = j < 4 ? lo_m : hi_m;
+        k[2 * h] = __float_as_uint(d * (float)sc);
+        k[2 * h + 1] = __float_as_uint(-dmin * (float)mn);
+    }
+}
+
+// Largest block-scale magnitude (fp16 bits) of a Q4_0 / Q8_0 window's two blocks.
+template <int Q>
+__device__ __forceinline__ uint32_t d_bits(const uint32_t *w) {
+    constexpr int hi = Q == FW_Q4_0 ? 4 : 8;   // dword holding the odd block's scale
+    return max(w[0] & 0x7FFFu, __builtin_amdgcn_ubfe(w[hi], 16, 15));
+}
+
+// Bound on the 16x-scaled magnitude of a Q4_K window's weights from its
+// per-step constants: 16 (15 |d scale| + |dmin min|) over both sub-blocks.
+__device__ __forceinline__ float q4k_bound(const uint32_t *k) {
+    float b = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        b = fmaxf(b, 16.0f * fmaf(15.0f, fabsf(__uint_as_float(k[2 * h])),
+                                  fabsf(__uint_as_float(k[2 * h + 1]))));
+    return b;
+}
+
+// B fragment of slice I from a Q4_K window: sub-block H = I / 4 of the group,
+// pairs 4 (I % 4) .. + 3.  Each weight d * scale * q - dmin * min is formed in
+// fp32 (exact up to one fp32 rounding) and rounded once to fp16, like a Q4_0
+// weight; pairs j = 1, 3 then carry 16x (exact).
+template <int I>
+__device__ __forceinline__ h8 frag_b_q4k(const uint32_t *w, const uint32_t *k) {
+    constexpr int H = I / 4, m = I % 4;
+    const uint32_t c0 = w[4 + m] >> (4 * H), c1 = w[8 + m] >> (4 * H);
+    const uint32_t a0 = c0 & 0x0F0F0F0Fu, a1 = c1 & 0x0F0F0F0Fu;   // elements 4m.., 16+4m..
+    const float ds = __uint_as_float(k[2 * H]), nd = __uint_as_float(k[2 * H + 1]);
+    // (float)((v >> 8b) & 255) is one v_cvt_f32_ubyte<b>
+    auto e = [&](uint32_t v, int byte) {
+        return (_Float16)fmaf((float)((v >> (8 * byte)) & 255u), ds, nd);
+    };
+    const h2 k16 = {(_Float16)16.0f, (_Float16)16.0f};
+    h2 p[4];
+    p[0] = h2{e(a0, 0), e(a0, 2)};
+    p[1] = h2{e(a1, 0), e(a1, 2)} * k16;
+    p[2] = h2{e(a0, 1), e(a0, 3)};
+    p[3] = h2{e(a1, 1), e(a1, 3)} * k16;
+    h8 f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = p[j][0];
+        f[2 * j + 1] = p[j][1];
+    }
+    return f;
+}
+
+// B fragment of slice I from a window: block I / 4 of the pair (even: 2 bytes
+// into the window, odd: dword aligned), pairs 4 (I % 4) .. + 3, times the
+// block's fp16 scale.
+template <int Q, int I>
+__device__ __forceinline__ h8 frag_b(const uint32_t *w) {
+    constexpr int m = I % 4;
+    uint32_t dbits, c0, c1 = 0;
+    if constexpr (Q == FW_Q4_0) {
+        if constexpr (I < 4) {
+            dbits = w[0] & 0xFFFFu;
+            c0 = funnel16(w[m], w[m + 1]);
+        } else {
+            dbits = w[4] >> 16;
+            c0 = w[5 + m];
+        }
+    } else {
+        if constexpr (I < 4) {
+            dbits = w[0] & 0xFFFFu;
+            c0 = funnel16(w[m], w[m + 1]);
+            c1 = funnel16(w[4 + m], w[5 + m]);
+        } else {
+            dbits = w[8] >> 16;
+            c0 = w[9 + m];
+            c1 = w[13 + m];
+        }
+    }
+    const uint32_t magic = pair_magic<Q>();
+    h2 p[4];
+    if constexpr (Q == FW_Q4_0) {
+        const h2 k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+        const h2 k1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
+        const uint32_t c8 = c0 >> 8;
+        p[0] = as_h2(and_or(c0, 0x000F000Fu, magic)) - k1032;
+        p[1] = as_h2(and_or(c0, 0x00F000F0u, magic)) - k1152;
+        p[2] = as_h2(and_or(c8, 0x000F000Fu, magic)) - k1032;
+        p[3] = as_h2(and_or(c8, 0x00F000F0u, magic)) - k1152;
+    } else {
+        const h2 k1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
+        const h2 k16 = {(_Float16)16.0f, (_Float16)16.0f};
+        const h2 k18432 = {(_Float16)18432.0f, (_Float16)18432.0f};
+        const uint32_t lo = c0 ^ 0x80808080u, hi = c1 ^ 0x80808080u;
+        p[0] = as_h2(__builtin_amdgcn_perm(magic, lo, 0x04020400u)) - k1152;
+        p[1] = as_h2(__builtin_amdgcn_perm(magic, hi, 0x04020400u)) * k16 - k18432;
+        p[2] = as_h2(__builtin_amdgcn_perm(magic, lo, 0x04030401u)) - k1152;
+        p[3] = as_h2(__builtin_amdgcn_perm(magic, hi, 0x04030401u)) * k16 - k18432;
+    }
+    const h2 d2 = as_h2(dbits | (dbits << 16));
+    h8 f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const h2 v = p[j] * d2;
+        f[2 * j] = v[0];
+        f[2 * j + 1] = v[1];
+    }
+    return f;
+}
+
+// B fragment of slice I of any format (kq: the Q4_K per-step constants).
+template <int Q, int I>
+__device__ __forceinline__ h8 frag_any(const uint32_t *w, const uint32_t *kq) {
+    if constexpr (Q == FW_Q4_K)
+        return frag_b_q4k<I>(w, kq);
+    else
+        return frag_b<Q, I>(w);
+}
+
+}  // namespace fw

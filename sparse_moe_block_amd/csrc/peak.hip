@@ -20,8 +20,8 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 
-constexpr int kChains = 8;
-
+// CH independent accumulator chains per wavefront
+template <int CH>
 __global__ __launch_bounds__(256) void mfma16_kernel(int iters, float *out) {
     const int lane = threadIdx.x % 64;
     h8 a, b;
@@ -30,20 +30,21 @@ __global__ __launch_bounds__(256) void mfma16_kernel(int iters, float *out) {
         a[i] = (_Float16)(0.001f * (lane + i));
         b[i] = (_Float16)(0.002f * (lane - i));
     }
-    f4 acc[kChains];
+    f4 acc[CH];
 #pragma unroll
-    for (int c = 0; c < kChains; ++c) acc[c] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < CH; ++c) acc[c] = f4{0.f, 0.f, 0.f, 0.f};
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int c = 0; c < kChains; ++c)
+        for (int c = 0; c < CH; ++c)
             acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[c], 0, 0, 0);
     }
     float s = 0.f;
 #pragma unroll
-    for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+    for (int c = 0; c < CH; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
     out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+template <int CH>
 __global__ __launch_bounds__(256) void mfma32_kernel(int iters, float *out) {
     const int lane = threadIdx.x % 64;
     h8 a, b;
@@ -52,20 +53,19 @@ __global__ __launch_bounds__(256) void mfma32_kernel(int iters, float *out) {
         a[i] = (_Float16)(0.001f * (lane + i));
         b[i] = (_Float16)(0.002f * (lane - i));
     }
-    constexpr int C = kChains / 2;
-    f16v acc[C];
+    f16v acc[CH];
 #pragma unroll
-    for (int c = 0; c < C; ++c)
+    for (int c = 0; c < CH; ++c)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[c][i] = 0.f;
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int c = 0; c < C; ++c)
+        for (int c = 0; c < CH; ++c)
             acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[c], 0, 0, 0);
     }
     float s = 0.f;
 #pragma unroll
-    for (int c = 0; c < C; ++c)
+    for (int c = 0; c < CH; ++c)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s += acc[c][i];
     out[blockIdx.x * blockDim.x + threadIdx.x] = s;
@@ -101,15 +101,20 @@ __global__ __launch_bounds__(256) void copy_kernel(const uint4 *__restrict__ src
 extern "C" {
 
 /* fp16 MFMA throughput: `blocks` workgroups of 256 threads, each wavefront
- * issuing iters * 8 MFMAs of 16x16x32 (shape 16) or iters * 4 of 32x32x16
- * (shape 32) -- 16384 or 32768 flops each.  out: blocks * 256 floats.
- * Returns a hipError_t. */
-int fw_peak_mfma(int shape, int blocks, int iters, float *out, void *stream) {
-    if (blocks < 1 || iters < 1 || !out || (shape != 16 && shape != 32)) return hipErrorInvalidValue;
-    if (shape == 16)
-        mfma16_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>(iters, out);
-    else
-        mfma32_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>(iters, out);
+ * issuing iters * chains MFMAs of 16x16x32 (shape 16; chains 4, 8 or 16) or
+ * 32x32x16 (shape 32; chains 2, 4 or 8) -- 16384 or 32768 flops each -- on
+ * `chains` independent accumulators.  out: blocks * 256 floats.  Returns a
+ * hipError_t. */
+int fw_peak_mfma(int shape, int chains, int blocks, int iters, float *out, void *stream) {
+    if (blocks < 1 || iters < 1 || !out) return hipErrorInvalidValue;
+    hipStream_t s = (hipStream_t)stream;
+    if (shape == 16 && chains == 4) mfma16_kernel<4><<<blocks, 256, 0, s>>>(iters, out);
+    else if (shape == 16 && chains == 8) mfma16_kernel<8><<<blocks, 256, 0, s>>>(iters, out);
+    else if (shape == 16 && chains == 16) mfma16_kernel<16><<<blocks, 256, 0, s>>>(iters, out);
+    else if (shape == 32 && chains == 2) mfma32_kernel<2><<<blocks, 256, 0, s>>>(iters, out);
+    else if (shape == 32 && chains == 4) mfma32_kernel<4><<<blocks, 256, 0, s>>>(iters, out);
+    else if (shape == 32 && chains == 8) mfma32_kernel<8><<<blocks, 256, 0, s>>>(iters, out);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -175,6 +175,10 @@ __global__ void clear_status_kernel(WsHeader *hdr) {
     if (threadIdx.x == 0) hdr->status = 0;
 }
 
+__global__ void copy_status_kernel(const WsHeader *hdr, int32_t *status) {
+    if (threadIdx.x == 0) *status = hdr->status;
+}
+
 }  // namespace
 
 hipError_t launch_permute(const fw_moe_desc &d, int T, const int32_t *ids, int32_t *offsets,
@@ -195,6 +199,11 @@ hipError_t launch_permute(const fw_moe_desc &d, int T, const int32_t *ids, int32
 
 hipError_t launch_clear_status(WsHeader *hdr, hipStream_t s) {
     clear_status_kernel<<<1, 64, 0, s>>>(hdr);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_status(const WsHeader *hdr, int32_t *status, hipStream_t s) {
+    copy_status_kernel<<<1, 64, 0, s>>>(hdr, status);
     return hipGetLastError();
 }
 

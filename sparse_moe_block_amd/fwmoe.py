@@ -192,3 +192,4 @@ def fw_moe_layer_timed(desc, T, x, router_w, logit_bias, w_gate, w_up, w_down, w
         _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(logits),
         _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(inv_pos),
         _ptr(out), _ptr(workspace), ws_bytes, arr, _stream(stream)))
+
