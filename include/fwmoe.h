@@ -273,6 +273,32 @@ int fw_moe_layer_timed(const fw_moe_desc *desc, int32_t T, const void *x,
                        int32_t *sorted_pairs, int32_t *inv_pos, float *out, void *workspace,
                        size_t ws_bytes, void *const *stage_events, void *stream);
 
+/* fw_moe_layer without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture that must not call
+ * hipMalloc, tight serving loops, harnesses that forbid allocation).  The
+ * workspace is a static device array of FW_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per device, which the library holds from its first use on a
+ * device until the process ends; the call itself allocates nothing.
+ * Arguments and results: as fw_moe_layer (bit for bit the same outputs), minus
+ * workspace / ws_bytes, plus
+ *   status  int32 device pointer (4-byte aligned) or NULL: receives the call's
+ *           FW_STATUS_* bits when the stream reaches the end of the call.
+ * The status word in the array is cleared (a fill kernel) at the start of
+ * every call; everything else the kernels need zeroed they clear themselves.
+ * Batches whose fw_moe_workspace_size(desc, T) exceeds FW_NOALLOC_SCRATCH_BYTES
+ * are refused with FW_EWORKSPACE before anything is enqueued (every decode
+ * batch of the workloads here fits; DeepSeek-shaped prefill does not).
+ * All calls on one device share its array: calls that overlap on one device
+ * (two streams, two threads) race and must be serialised by the caller. */
+#define FW_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int fw_moe_layer_noalloc(const fw_moe_desc *desc, int32_t T, const void *x,
+                         const void *router_w, const float *logit_bias, const void *w_gate,
+                         const void *w_up, const void *w_down, const void *ws_gate,
+                         const void *ws_up, const void *ws_down, float *logits,
+                         int32_t *topk_ids, float *topk_w, int32_t *expert_offsets,
+                         int32_t *sorted_pairs, int32_t *inv_pos, float *out,
+                         int32_t *status, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,6 +9,13 @@
 
 #include "common.h"
 
+// Workspace of fw_moe_layer_noalloc, for callers that cannot allocate: one
+// array per device, held from the library's first use on that device until
+// the process ends.  Host code never names it in a launch or copy: its device
+// address comes from hipGetSymbolAddress, once per device (noalloc_scratch).
+constexpr size_t kNoAllocScratchBytes = FW_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
 namespace fw {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -216,6 +223,20 @@ int layer_impl(const fw_moe_desc *desc, int32_t T, const void *x, const void *ro
     return hip_status(launch_copy_status((const WsHeader *)workspace, status_out, s));
 }
 
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current (nullptr if the lookup failed).
+void *noalloc_scratch() {
+    static std::once_flag once[kMaxDevices];
+    static void *ptr[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(once[dev], [dev] {
+        void *p = nullptr;
+        ptr[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess ? p : nullptr;
+    });
+    return ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -328,6 +349,26 @@ int fw_moe_layer_timed(const fw_moe_desc *desc, int32_t T, const void *x,
                       ws_down, logits, topk_ids, topk_w, expert_offsets, sorted_pairs, inv_pos,
                       out, workspace, ws_bytes, (const hipEvent_t *)stage_events,
                       (hipStream_t)stream);
+}
+
+int fw_moe_layer_noalloc(const fw_moe_desc *desc, int32_t T, const void *x,
+                         const void *router_w, const float *logit_bias, const void *w_gate,
+                         const void *w_up, const void *w_down, const void *ws_gate,
+                         const void *ws_up, const void *ws_down, float *logits,
+                         int32_t *topk_ids, float *topk_w, int32_t *expert_offsets,
+                         int32_t *sorted_pairs, int32_t *inv_pos, float *out,
+                         int32_t *status, void *stream) {
+    int rc = check_desc(desc);
+    if (rc != FW_OK) return rc;
+    if ((rc = check_T(desc, T)) != FW_OK) return rc;
+    if (T == 0) return FW_OK;
+    if (ws_layout(*desc, T).total > kNoAllocScratchBytes) return FW_EWORKSPACE;
+    if (status && ((uintptr_t)status & 3)) return FW_EALIGN;
+    void *ws = noalloc_scratch();
+    if (!ws) return FW_EHIP;
+    return layer_impl(desc, T, x, router_w, logit_bias, w_gate, w_up, w_down, ws_gate, ws_up,
+                      ws_down, logits, topk_ids, topk_w, expert_offsets, sorted_pairs, inv_pos,
+                      out, ws, kNoAllocScratchBytes, nullptr, (hipStream_t)stream, true, status);
 }
 
 int fw_moe_clear_status(void *workspace, void *stream) {

@@ -19,6 +19,7 @@ FW_Q8_0, FW_Q4_0, FW_Q4_K = 0, 1, 2
 FW_SOFTMAX_RENORM, FW_SIGMOID_RENORM = 0, 1
 FW_PATH_AUTO, FW_PATH_GEMV, FW_PATH_GEMM = 0, 1, 2
 FW_N_STAGE_EVENTS = 5
+FW_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 DTYPES = {"f32": FW_F32, "bf16": FW_BF16}
 QTYPES = {"q8_0": FW_Q8_0, "q4_0": FW_Q4_0, "q4_k": FW_Q4_K}
@@ -73,6 +74,7 @@ def lib():
             "fw_moe_read_status": ([P, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
             "fw_moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "fw_moe_layer_timed": ([D, I] + [P] * 17 + [ctypes.c_size_t, P, P], ctypes.c_int),
+            "fw_moe_layer_noalloc": ([D, I] + [P] * 17 + [P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -193,3 +195,13 @@ def fw_moe_layer_timed(desc, T, x, router_w, logit_bias, w_gate, w_up, w_down, w
         _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(inv_pos),
         _ptr(out), _ptr(workspace), ws_bytes, arr, _stream(stream)))
 
+
+def fw_moe_layer_noalloc(desc, T, x, router_w, logit_bias, w_gate, w_up, w_down, ws_gate,
+                         ws_up, ws_down, logits, topk_ids, topk_w, expert_offsets,
+                         sorted_pairs, inv_pos, out, status=None, stream=None):
+    """status: an int32 device tensor of one element, or None."""
+    return _check("fw_moe_layer_noalloc", lib().fw_moe_layer_noalloc(
+        ctypes.byref(desc), T, _ptr(x), _ptr(router_w), _ptr(logit_bias), _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(logits),
+        _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(inv_pos),
+        _ptr(out), _ptr(status), _stream(stream)))
