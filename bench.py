@@ -264,12 +264,12 @@ def measure(a, workload, steps, warmup, setup_only=False):
     # dominant kernel: the gate/up projection (2/3 of the expert bytes and flops)
     path = fw.fw_moe_forward_path(desc, T)
     gu_ms = float(stage_avg[1])
-    bq = moegen.BLOCK_BYTES[cfg.expert_q]
     if path == fw.FW_PATH_GEMV:
         # bytes: the active experts' gate and up rows, x in (bf16), a out
-        gu_alg = n_active * 2 * cfg.ffn * (H // 32) * bq + T * H * 2 + P * cfg.ffn * 2
+        gu_alg = (n_active * 2 * cfg.ffn * moegen.row_bytes(cfg.expert_q, H) + T * H * 2 +
+                  P * cfg.ffn * 2)
         if cfg.shared_ffn:
-            gu_alg += 2 * cfg.shared_ffn * (H // 32) * moegen.BLOCK_BYTES[cfg.shared_q]
+            gu_alg += 2 * cfg.shared_ffn * moegen.row_bytes(cfg.shared_q, H)
             gu_alg += T * cfg.shared_ffn * 2
         achieved = gu_alg / (gu_ms * 1e-3) / 1e9
         roof = {"kernel": "gemv_kernel<gate/up>", "bound": "hbm", "achieved": achieved,

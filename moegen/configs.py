@@ -17,13 +17,23 @@ from typing import Optional, Tuple
 Q8_0 = "q8_0"
 Q4_0 = "q4_0"
 Q4_K = "q4_k"
+Q6_K = "q6_k"
 F32 = "f32"
 BF16 = "bf16"
 SOFTMAX = "softmax"
 SIGMOID = "sigmoid"
 
-# bytes per 32-element block
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 18}   # Q4_K: 144 per 256
+# bytes per 32-element block (Q4_K: 144 per 256-element super-block)
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_K: 18}
+# bytes per 256-element super-block of the K-quants
+SUPER_BYTES = {Q4_K: 144, Q6_K: 210}
+
+
+def row_bytes(qtype: str, n: int) -> int:
+    """Bytes of a GGUF row of n elements."""
+    if qtype in SUPER_BYTES:
+        return n // 256 * SUPER_BYTES[qtype]
+    return n // 32 * BLOCK_BYTES[qtype]
 
 
 @dataclass(frozen=True)
@@ -51,14 +61,13 @@ class LayerConfig:
     @property
     def expert_bytes(self):
         """Bytes of one routed expert (gate + up + down)."""
-        bq = BLOCK_BYTES[self.expert_q]
-        return 3 * self.ffn * self.hidden // 32 * bq
+        return 3 * self.ffn * row_bytes(self.expert_q, self.hidden)
 
     @property
     def shared_bytes(self):
         if not self.shared_ffn:
             return 0
-        return 3 * self.shared_ffn * self.hidden // 32 * BLOCK_BYTES[self.shared_q]
+        return 3 * self.shared_ffn * row_bytes(self.shared_q, self.hidden)
 
     @property
     def router_bytes(self):

@@ -2,7 +2,7 @@
 GGUF-blocked expert weights.
 
 Input generation only.  It contains none of the layer's arithmetic: no dequant,
-no routing, no FFN.  The quantizers below *produce* Q8_0 / Q4_0 / Q4_K blocks from fp32
+no routing, no FFN.  The quantizers below *produce* Q8_0 / Q4_0 / Q4_K / Q6_K blocks from fp32
 samples (the way a checkpoint converter would); the layer only ever *reads*
 blocks.  Both the GPU path and the CPU oracle are fed from here.
 
@@ -22,6 +22,12 @@ Block byte layout (GGUF, little-endian, no padding):
         [128 bytes of nibbles: group c of 64 elements uses bytes 32c..32c+31,
         low nibbles first 32 elements, high nibbles the next 32];
         value = d*scale_j*q - dmin*min_j.
+  Q6_K: 256-element super-block, 210 bytes: [128 bytes ql][64 bytes qh]
+        [16 int8 scales][fp16 d]; half h (128 elements) uses ql bytes
+        64h..64h+63 and qh bytes 32h..32h+31; its element 32k+l takes the
+        low nibble (k < 2) or high nibble (k >= 2) of ql byte 64h+32(k%2)+l
+        and bits 2k, 2k+1 of qh byte 32h+l: a six-bit code q; value =
+        d*scale_j*(q-32), j the 16-element sub-block.
 """
 
 import math
@@ -31,7 +37,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-from .configs import BF16, F32, Q4_0, Q4_K, Q8_0, BLOCK_BYTES, LayerConfig
+from .configs import BF16, F32, Q4_0, Q4_K, Q6_K, Q8_0, LayerConfig, row_bytes
 
 BASE_SEED = 20261202
 
@@ -131,7 +137,40 @@ def quantize_q4_k(w: torch.Tensor) -> torch.Tensor:
     return out.reshape(*lead, n // 256 * 144).contiguous()
 
 
-QUANTIZERS = {Q8_0: quantize_q8_0, Q4_0: quantize_q4_0, Q4_K: quantize_q4_k}
+def quantize_q6_k(w: torch.Tensor) -> torch.Tensor:
+    """fp32 [..., n] -> uint8 [..., n/256*210] (GGUF Q6_K super-blocks).
+    Per 16-element sub-block j: m_j = the element of largest magnitude (sign
+    kept) and s_j = m_j / -32, so m_j is code 0; per super-block d = max |s_j|
+    / 127 as fp16 and int8 scales sc_j = s_j / d rounded away from zero (so
+    |d sc_j| >= |s_j| and every element is within 32 steps); element codes
+    round(x / (d sc_j)) + 32 clamped to 0..63.  Zero scales give code 32."""
+    *lead, n = w.shape
+    assert n % 256 == 0
+    b = w.reshape(*lead, n // 256, 16, 16)
+    idx = b.abs().argmax(dim=-1, keepdim=True)
+    m = torch.gather(b, -1, idx).squeeze(-1)
+    s = m / -32.0
+    d16 = (s.abs().amax(dim=-1) / 127.0).to(torch.float16)
+    d = d16.float().unsqueeze(-1)
+    safe = lambda v: torch.where(v != 0, v, torch.ones_like(v))
+    r = s / safe(d)
+    sc = torch.where(d > 0, torch.sign(r) * torch.ceil(r.abs()), torch.zeros_like(s)).clamp(-127, 127)
+    step = (d * sc).unsqueeze(-1)
+    q = torch.where(step != 0, _round_half_away(b / safe(step)), torch.zeros_like(b)) + 32
+    q = q.clamp(0, 63).to(torch.int64).reshape(*lead, n // 256, 2, 4, 32)   # [h][k][l]
+    lo, hi = q & 15, q >> 4
+    ql = torch.stack([lo[..., 0, :] | (lo[..., 2, :] << 4),
+                      lo[..., 1, :] | (lo[..., 3, :] << 4)], dim=-2)         # [h][k%2][l]
+    qh = hi[..., 0, :] | (hi[..., 1, :] << 2) | (hi[..., 2, :] << 4) | (hi[..., 3, :] << 6)
+    scb = sc.to(torch.int8).view(torch.uint8)
+    d8 = d16.view(torch.int16).view(torch.uint8).reshape(*lead, n // 256, 2)
+    out = torch.cat([ql.reshape(*lead, n // 256, 128).to(torch.uint8),
+                     qh.reshape(*lead, n // 256, 64).to(torch.uint8), scb, d8], dim=-1)
+    return out.reshape(*lead, n // 256 * 210).contiguous()
+
+
+QUANTIZERS = {Q8_0: quantize_q8_0, Q4_0: quantize_q4_0, Q4_K: quantize_q4_k,
+              Q6_K: quantize_q6_k}
 
 
 def quantized_normal(rows, cols, std, qtype, seed, device):
@@ -180,10 +219,9 @@ def make_layer(cfg: LayerConfig, device="cpu", qtype: Optional[str] = None) -> L
     router = to_act_dtype(normal((E, H), cfg.router_std, seed_of(c, T_ROUTER, 0), device),
                           cfg.router_dtype)
     bias = zipf_bias(E, cfg.zipf).to(device) if cfg.zipf else None
-    bq = BLOCK_BYTES[q]
-    wg = torch.empty((E, F, H // 32 * bq), dtype=torch.uint8, device=device)
+    wg = torch.empty((E, F, row_bytes(q, H)), dtype=torch.uint8, device=device)
     wu = torch.empty_like(wg)
-    wd = torch.empty((E, H, F // 32 * bq), dtype=torch.uint8, device=device)
+    wd = torch.empty((E, H, row_bytes(q, F)), dtype=torch.uint8, device=device)
     for e in range(E):
         wg[e] = quantized_normal(F, H, cfg.w_std, q, seed_of(c, T_GATE, e), device)
         wu[e] = quantized_normal(F, H, cfg.w_std, q, seed_of(c, T_UP, e), device)

@@ -1,6 +1,6 @@
 /*
  * fwref.c -- CPU oracle for the routed mixture-of-experts FFN layer run on GGUF
- * Q8_0 / Q4_0 / Q4_K expert weights.
+ * Q8_0 / Q4_0 / Q4_K / Q6_K expert weights.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg load this library.  The GPU library shares no
@@ -10,7 +10,9 @@
  * to check by eye: straight loops, no blocking, no fusion, no reordering.
  * Dequantised Q8_0 / Q4_0 weights are exact in fp32 (an fp16 scale times a code
  * of at most 8 significant bits fits in 24 bits); a Q4_K weight is formed
- * exactly in fp64 and rounded once to fp32; every sum is accumulated in fp64 in
+ * exactly in fp64 and rounded once to fp32 (a Q6_K weight, d * scale * code
+ * with an fp16 d, an int8 scale and a six-bit code, is exact in fp32 too);
+ * every sum is accumulated in fp64 in
  * ascending index order and rounded to fp32 only where the layer's interface
  * hands a value over (logits, gate weights, output).
  *
@@ -28,6 +30,11 @@
  *    PARITY UNPINNED against an outside encoder (none is available here);
  *    the tests pin it by round trips, by the cases that reduce to Q4_0 and by
  *    brute force over code positions;
+ *  - Q6_K, the other of BailingMoE3's two grouped expert formats and one of
+ *    the K-quants the newer page lists grouped kernels for (Flyweight 0.2.0,
+ *    "Current limitations"; Flyweight 0.5.1, "Models and formats").  GGUF's
+ *    layout again, PARITY UNPINNED against an outside encoder; pinned the
+ *    same way as Q4_K;
  *  - SwiGLU expert FFNs (vOOM, module layout: layer_runner's block math);
  *  - top-k routing with k a tunable (vOOM notes: the request-local top-2
  *    expert schedule) and DeepSeek-shaped sigmoid routing with an always-on
@@ -48,7 +55,7 @@
 #endif
 
 enum { REF_F32 = 0, REF_BF16 = 1 };
-enum { REF_Q8_0 = 0, REF_Q4_0 = 1, REF_Q4_K = 2 };
+enum { REF_Q8_0 = 0, REF_Q4_0 = 1, REF_Q4_K = 2, REF_Q6_K = 3 };
 enum { REF_SOFTMAX = 0, REF_SIGMOID = 1 };
 
 /* IEEE 754 binary16 -> value: 1 sign bit, 5 exponent bits (bias 15), 10
@@ -75,8 +82,17 @@ float fwref_bf16_to_float(uint16_t b)
     return f;
 }
 
-/* Bytes per 32 elements (a Q4_K super-block is 144 bytes per 256). */
-static int block_bytes(int qtype) { return qtype == REF_Q8_0 ? 34 : 18; }
+/* Bytes of a row of n elements: 32-element blocks of 34 (Q8_0) or 18 (Q4_0)
+ * bytes, 256-element super-blocks of 144 (Q4_K) or 210 (Q6_K) bytes. */
+static size_t row_bytes(int qtype, int n)
+{
+    switch (qtype) {
+        case REF_Q8_0: return (size_t)n / 32 * 34;
+        case REF_Q4_0: return (size_t)n / 32 * 18;
+        case REF_Q4_K: return (size_t)n / 256 * 144;
+        default: return (size_t)n / 256 * 210;
+    }
+}
 
 /* Q4_K sub-block j's 6-bit scale and min from the 12 packed bytes: j < 4 keep
  * them in the low 6 bits of bytes j and j + 4; j >= 4 take their low 4 bits
@@ -102,9 +118,34 @@ static void q4k_scale_min(const uint8_t *sc, int j, int *scale, int *min)
  *             group c (0..3) of 64 elements reads code bytes 32c .. 32c + 31:
  *             element 64c + l is the low nibble of byte 32c + l (sub-block
  *             2c), element 64c + 32 + l its high nibble (sub-block 2c + 1);
- *             value = d * scale_j * q - dmin * min_j for sub-block j. */
+ *             value = d * scale_j * q - dmin * min_j for sub-block j.
+ * Q6_K super-block of 256 elements, 210 bytes: [128 bytes ql][64 bytes qh]
+ *             [16 int8 scales][fp16 d].  Each half (128 elements, h = 0, 1)
+ *             uses ql bytes 64h .. 64h + 63 and qh bytes 32h .. 32h + 31;
+ *             its element 32k + l (k = 0..3, l = 0..31) takes its low four
+ *             bits from ql byte 64h + 32 (k % 2) + l (low nibble for k < 2,
+ *             high for k >= 2) and its top two bits from bits 2k, 2k + 1 of
+ *             qh byte 32h + l: a six-bit code q.  Sub-block j = e / 16 of 16
+ *             elements has scale byte j; value = d * scale_j * (q - 32). */
 void fwref_dequant_row(int qtype, const uint8_t *row, int n, float *out)
 {
+    if (qtype == REF_Q6_K) {
+        for (int b = 0; b < n / 256; ++b) {
+            const uint8_t *blk = row + (size_t)b * 210;
+            const uint8_t *ql = blk, *qh = blk + 128;
+            const int8_t *sc = (const int8_t *)(blk + 192);
+            double d = fwref_half_to_float((uint16_t)(blk[208] | blk[209] << 8));
+            for (int e = 0; e < 256; ++e) {
+                int h = e / 128, k = (e % 128) / 32, l = e % 32;
+                int lo = ql[64 * h + 32 * (k % 2) + l];
+                lo = k < 2 ? lo & 15 : lo >> 4;
+                int hi = (qh[32 * h + l] >> (2 * k)) & 3;
+                int q = lo | hi << 4;
+                out[256 * b + e] = (float)(d * sc[e / 16] * (q - 32));
+            }
+        }
+        return;
+    }
     if (qtype == REF_Q4_K) {
         for (int b = 0; b < n / 256; ++b) {
             const uint8_t *blk = row + (size_t)b * 144;
@@ -122,7 +163,7 @@ void fwref_dequant_row(int qtype, const uint8_t *row, int n, float *out)
         return;
     }
     for (int b = 0; b < n / 32; ++b) {
-        const uint8_t *blk = row + (size_t)b * block_bytes(qtype);
+        const uint8_t *blk = row + (size_t)b * (qtype == REF_Q8_0 ? 34 : 18);
         float d = fwref_half_to_float((uint16_t)(blk[0] | blk[1] << 8));
         if (qtype == REF_Q8_0) {
             for (int i = 0; i < 32; ++i)
@@ -265,8 +306,8 @@ static void expert_ffn(int qtype, int F, int H, const uint8_t *wg, const uint8_t
                        const uint8_t *wd, const float *x, double *y, float *row,
                        double *a)
 {
-    size_t rb_h = (size_t)H / 32 * block_bytes(qtype);
-    size_t rb_f = (size_t)F / 32 * block_bytes(qtype);
+    size_t rb_h = row_bytes(qtype, H);
+    size_t rb_f = row_bytes(qtype, F);
     for (int f = 0; f < F; ++f) {
         double g = 0.0, u = 0.0;
         fwref_dequant_row(qtype, wg + f * rb_h, H, row);
@@ -289,8 +330,8 @@ static void expert_ffn(int qtype, int F, int H, const uint8_t *wg, const uint8_t
 /* The layer's output for T tokens:
  *   out[t] = fp32( sum_{j<k} w[t][j] * FFN_{ids[t][j]}(x_t)  +  FFN_shared(x_t) )
  * with the slot sum in order j = 0..k-1 and the shared expert (Fs > 0) last.
- * Expert e's tensors start at e * F * (H/32) blocks (gate, up) and
- * e * H * (F/32) blocks (down).  Tokens are independent, so they are spread over
+ * Expert e's tensors start at e * F rows of H elements (gate, up) and e * H
+ * rows of F elements (down).  Tokens are independent, so they are spread over
  * n_threads OpenMP threads (0: the runtime's default).
  * Returns 0, or -1 on a bad argument or id. */
 int fwref_forward(int T, int H, int E, int k, int F, int qtype, int Fs, int qtype_s,
@@ -302,11 +343,15 @@ int fwref_forward(int T, int H, int E, int k, int F, int qtype, int Fs, int qtyp
     if (T < 0 || H <= 0 || H % 32 || F <= 0 || F % 32 || k < 1 || k > E || Fs < 0 ||
         Fs % 32)
         return -1;
+    /* K-quant rows are whole 256-element super-blocks */
+    if ((qtype >= REF_Q4_K && (H % 256 || F % 256)) ||
+        (Fs > 0 && qtype_s >= REF_Q4_K && (H % 256 || Fs % 256)))
+        return -1;
     for (long q = 0; q < (long)T * k; ++q)
         if (ids[q] < 0 || ids[q] >= E)
             return -1;
-    size_t expert_gu = (size_t)F * (H / 32) * block_bytes(qtype);
-    size_t expert_d = (size_t)H * (F / 32) * block_bytes(qtype);
+    size_t expert_gu = (size_t)F * row_bytes(qtype, H);
+    size_t expert_d = (size_t)H * row_bytes(qtype, F);
     int maxf = F > Fs ? F : Fs;
     int maxr = H > maxf ? H : maxf;
 #ifdef _OPENMP

@@ -5,6 +5,7 @@ itself pinned by the hand-decoded fixture in golden/q_blocks.txt."""
 import numpy as np
 
 BQ = {"q8_0": 34, "q4_0": 18, "q4_k": 18}   # bytes per 32 elements (Q4_K: 144 per 256)
+SUPER = {"q4_k": 144, "q6_k": 210}           # bytes per 256-element super-block
 
 
 def _q4k_scales(sc):
@@ -21,6 +22,17 @@ def dequant(qtype, raw, n):
     """raw uint8 [..., n/32*Bq] -> float64 [..., n]."""
     raw = np.asarray(raw, dtype=np.uint8)
     lead = raw.shape[:-1]
+    if qtype == "q6_k":
+        sb = raw.reshape(*lead, n // 256, 210)
+        ql = sb[..., 0:128].astype(np.int64).reshape(*lead, n // 256, 2, 2, 32)   # [h][k%2][l]
+        qh = sb[..., 128:192].astype(np.int64).reshape(*lead, n // 256, 2, 1, 32)  # [h][.][l]
+        sc = sb[..., 192:208].copy().view(np.int8).astype(np.float64)           # [16]
+        d = sb[..., 208:210].copy().view(np.float16)[..., 0].astype(np.float64)
+        lo = np.concatenate([ql & 15, ql >> 4], axis=-2)                       # k = 0..3
+        hi = np.concatenate([(qh >> (2 * k)) & 3 for k in range(4)], axis=-2)
+        q = (lo | (hi << 4)).reshape(*lead, n // 256, 16, 16) - 32
+        v = d[..., None, None] * sc[..., None] * q
+        return v.reshape(*lead, n)
     if qtype == "q4_k":
         sb = raw.reshape(*lead, n // 256, 144)
         d = sb[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float64)

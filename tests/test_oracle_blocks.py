@@ -231,3 +231,114 @@ def test_q4k_quantizer_error_bound(ref):
         bound = d[:, None] * np.maximum(s, 1) + dmin[:, None] * 0.5 + 1e-3 * 2.0 ** -7
         assert np.all(err <= bound), (i, err, bound)
     assert not np.any(ref.dequant_row("q4_k", raw[0], 512)[:256])
+
+
+# Q6_K (GGUF K-quant super-blocks of 210 bytes).  As for Q4_K, no layout is
+# printed and no outside encoder is available: the oracle's Q6_K decoding is
+# pinned by hand-packed super-blocks, by the case that reduces to Q8_0 (pinned
+# by the hand-decoded fixture above), by brute force over every code position,
+# every code value and every int8 scale, and by the generator's error bound.
+
+GOLDEN_6K = os.path.join(os.path.dirname(__file__), "golden", "q6k_blocks.txt")
+
+
+def golden_q6k():
+    out = []
+    for line in open(GOLDEN_6K):
+        if line.startswith("#") or not line.strip():
+            continue
+        name, d, sc, rule, hx = [s.strip() for s in line.split("|")]
+        out.append((name, Fraction(d), [int(v) for v in sc.split()], rule, bytes.fromhex(hx)))
+    return out
+
+
+@pytest.mark.parametrize("rec", golden_q6k(), ids=lambda r: r[0])
+def test_q6k_hand_packed_block(ref, rec):
+    name, d, sc, rule, raw = rec
+    assert len(raw) == 210 and rule == "kq" and len(sc) == 16
+    want = []
+    for e in range(256):
+        k, l = (e % 128) // 32, e % 32
+        q = 16 * k + (l % 16 if k < 2 else 15 - l % 16)
+        want.append(float(d * sc[e // 16] * (q - 32)))
+    want = np.array(want)
+    got = ref.dequant_row("q6_k", np.frombuffer(raw, dtype=np.uint8), 256)
+    assert np.array_equal(got.astype(np.float64), want)
+    assert np.array_equal(np_ref.dequant("q6_k", np.frombuffer(raw, dtype=np.uint8), 256), want)
+
+
+def _q6k_raw(d16, scales, codes):
+    """A super-block from its fields, packed by the layout rule (codes [256]
+    in element order, 0..63)."""
+    q = np.asarray(codes, dtype=np.int64).reshape(2, 4, 32)      # [h][k][l]
+    ql = np.stack([(q[:, 0] & 15) | ((q[:, 2] & 15) << 4),
+                   (q[:, 1] & 15) | ((q[:, 3] & 15) << 4)], axis=1).reshape(-1)
+    hi = q >> 4
+    qh = (hi[:, 0] | hi[:, 1] << 2 | hi[:, 2] << 4 | hi[:, 3] << 6).reshape(-1)
+    sc = np.asarray(scales, dtype=np.int64).astype(np.int8).view(np.uint8)
+    dd = np.array([d16], dtype=np.float16).view(np.uint8)
+    return np.concatenate([ql.astype(np.uint8), qh.astype(np.uint8), sc, dd])
+
+
+def test_q6k_reduces_to_q8_0(ref):
+    """Every scale 1: the values are d * (q - 32), the same as Q8_0 blocks with
+    scale d and codes q - 32."""
+    rng = np.random.default_rng(6)
+    codes = rng.integers(0, 64, 256)
+    d = np.float16(0.0371)
+    got = ref.dequant_row("q6_k", _q6k_raw(d, [1] * 16, codes), 256)
+    q8 = []
+    for b in range(8):
+        c = (codes[32 * b:32 * b + 32] - 32).astype(np.int8)
+        q8.append(np.concatenate([np.array([d], np.float16).view(np.uint8), c.view(np.uint8)]))
+    assert np.array_equal(got, ref.dequant_row("q8_0", np.concatenate(q8), 256))
+
+
+def test_q6k_every_code_position(ref):
+    """A code of 33 (value d * scale) at position p and 32 (zero) elsewhere
+    changes exactly element p."""
+    for p in range(256):
+        codes = np.full(256, 32)
+        codes[p] = 33
+        v = ref.dequant_row("q6_k", _q6k_raw(1.0, [3] * 16, codes), 256)
+        assert v[p] == 3 and np.count_nonzero(v) == 1, p
+
+
+def test_q6k_every_code_value_and_scale(ref):
+    """Each of the 64 code values in every element slot of a 32-element run
+    (covering both nibbles and all four top-bit pairs), and each of the 256
+    int8 scales in every sub-block."""
+    for q in range(64):
+        codes = np.full(256, 32)
+        e = np.arange(q % 4 * 32 + 128 * (q % 2), q % 4 * 32 + 128 * (q % 2) + 32)
+        codes[e] = q
+        v = ref.dequant_row("q6_k", _q6k_raw(0.5, [2] * 16, codes), 256)
+        assert np.all(v[e] == q - 32) and np.count_nonzero(np.delete(v, e)) == 0, q
+    for j in range(16):
+        for s in range(-128, 128):
+            sc = [0] * 16
+            sc[j] = s
+            codes = np.full(256, 63)
+            v = ref.dequant_row("q6_k", _q6k_raw(0.25, sc, codes), 256)
+            assert np.all(v[16 * j:16 * j + 16] == 0.25 * s * 31), (j, s)
+            assert np.count_nonzero(np.delete(v, np.arange(16 * j, 16 * j + 16))) == 0
+
+
+def test_q6k_quantizer_error_bound(ref):
+    """The generator's Q6_K quantizer reproduces its input to within one code
+    step d * |scale_j| of each 16-element sub-block; the numpy decoder agrees
+    with the oracle exactly."""
+    w = moegen.normal((16, 512), 0.02, 9)
+    w[0, :256] = 0.0
+    w[1, 40] = 0.3
+    raw = moegen.quantize_q6_k(w).numpy()
+    x = w.numpy().astype(np.float64)
+    for i in range(16):
+        v = ref.dequant_row("q6_k", raw[i], 512).astype(np.float64)
+        assert np.array_equal(v, np_ref.dequant("q6_k", raw[i], 512).astype(np.float32))
+        sb = raw[i].reshape(2, 210)
+        d = sb[:, 208:210].copy().view(np.float16)[:, 0].astype(np.float64)
+        sc = sb[:, 192:208].copy().view(np.int8).astype(np.float64)
+        err = np.abs(v - x[i]).reshape(2, 16, 16).max(axis=-1)
+        assert np.all(err <= d[:, None] * np.abs(sc) + 1e-12), (i, err)
+    assert not np.any(ref.dequant_row("q6_k", raw[0], 512)[:256])

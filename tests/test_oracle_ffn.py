@@ -103,7 +103,7 @@ def _layer(qtype="q4_0", H=512, F=256, E=4, shared=0, std=0.05):
 
 
 @pytest.mark.parametrize("H,F", [(512, 256), (256, 768)])
-@pytest.mark.parametrize("qtype", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("qtype", ["q8_0", "q4_0", "q4_k", "q6_k"])
 def test_single_expert_is_dense_swiglu_float64(ref, qtype, H, F):
     """E = 1, k = 1: the layer is the textbook dense FFN
     W_d (silu(W_g x) * (W_u x)); checked with numpy float64 matrix products on
