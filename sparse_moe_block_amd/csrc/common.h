@@ -86,9 +86,11 @@ WsLayout ws_layout(const fw_moe_desc &d, int T);
 template <int Q> struct QT;
 template <> struct QT<FW_Q4_0> {
     static constexpr int kBlockBytes = 18, kUnitBytes = 144, kUnitX4 = 9;
+    static constexpr size_t row_bytes(int K) { return (size_t)(K / 32) * kBlockBytes; }
 };
 template <> struct QT<FW_Q8_0> {
     static constexpr int kBlockBytes = 34, kUnitBytes = 272, kUnitX4 = 17;
+    static constexpr size_t row_bytes(int K) { return (size_t)(K / 32) * kBlockBytes; }
 };
 // Q4_K: a unit is one 256-element super-block (144 bytes; kBlockBytes is the
 // per-32-element share used to size rows): [fp16 d][fp16 dmin][12 bytes of
@@ -96,6 +98,19 @@ template <> struct QT<FW_Q8_0> {
 // bytes 32c .. 32c + 31 (low nibbles: sub-block 2c, high: 2c + 1).
 template <> struct QT<FW_Q4_K> {
     static constexpr int kBlockBytes = 18, kUnitBytes = 144, kUnitX4 = 9;
+    static constexpr size_t row_bytes(int K) { return (size_t)(K / 256) * kUnitBytes; }
+};
+// Q6_K: a unit is one 256-element super-block of 210 bytes, [128 bytes ql]
+// [64 bytes qh][16 int8 scales][fp16 d]: half h (128 elements) uses ql bytes
+// 64h .. 64h + 63 and qh bytes 32h .. 32h + 31; element 32k + l of the half
+// takes the low (k < 2) or high (k >= 2) nibble of ql byte 64h + 32 (k % 2) + l
+// and bits 2k, 2k + 1 of qh byte 32h + l as a six-bit code q; value
+// d * scale_(e / 16) * (q - 32).  Units are 2-byte aligned only: a unit is
+// staged as the 14 aligned 16-byte pieces that cover it (kUnitX4), at a
+// per-row byte offset of 0 .. 14 into the first piece.
+template <> struct QT<FW_Q6_K> {
+    static constexpr int kUnitBytes = 210, kUnitX4 = 14;
+    static constexpr size_t row_bytes(int K) { return (size_t)(K / 256) * kUnitBytes; }
 };
 
 

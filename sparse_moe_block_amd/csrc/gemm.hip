@@ -48,6 +48,7 @@ constexpr int BK = 128;       // k per step
 constexpr int kChunks = BM * BK / 8;   // 16-byte chunks of a step's activations: 2048
 constexpr int kMaxDma = kChunks / 256;  // DMA instructions per thread (4-wave workgroups)
 constexpr int kMaxPX = 9;               // 16-byte weight pieces per row and half unit (Q8_0)
+constexpr int kQ6PX = 10;               // Q6_K: pieces per row and half (ql 5, qh 3, tail 2)
 static_assert(BM == 128, "tile shape");
 
 typedef float f16v __attribute__((ext_vector_type(16)));
@@ -61,6 +62,11 @@ struct Tile {
     const uint8_t *bbase[2]; // the expert's gate and up matrices (down: both the one)
     uint32_t woff[kMaxPX];   // byte offsets of this thread's weight pieces (unit 0, half 0)
     uint32_t wk;             // Q4_K: bit i set where piece i is a code piece (moves for half 1)
+    // Q6_K (2-byte aligned units; bbase 16-byte aligned): per DMA instruction
+    // i and half h, the byte offsets of the first and last byte of the
+    // region its piece covers (unit 0) and the piece's offset in that region;
+    // per column group, the offset of the lane's own row
+    uint32_t q6s[2][kQ6PX], q6e[2][kQ6PX], q6p[kQ6PX], q6r[2];
     _Float16 *hout;
     float *yout;
     const int32_t *s_ex;     // LDS: each tile row's exponent
@@ -74,7 +80,12 @@ struct Tile {
 // groups): consecutive lanes take consecutive pieces of a row, a few cache
 // lines per instruction.  Two half-unit buffers: the next step's half loads
 // while this step's is used.
-template <int Q> constexpr int half_pieces() { return Q == FW_Q8_0 ? 9 : 5; }
+// Q6_K's half is four separate regions at a 2-byte aligned row offset: its
+// 64 ql bytes (5 pieces), 32 qh bytes (3), and from its 8 scales to the
+// unit's end (2): kQ6PX pieces, a region's spare pieces repeating its last.
+template <int Q> constexpr int half_pieces() {
+    return Q == FW_Q8_0 ? 9 : Q == FW_Q6_K ? kQ6PX : 5;
+}
 // source piece of LDS piece j (0 .. PX - 1) of half h of a unit
 template <int Q> __device__ __forceinline__ int src_piece(int h, int j) {
     if constexpr (Q == FW_Q4_K) return h == 0 || j == 0 ? j : 4 + j;
@@ -85,8 +96,34 @@ template <int Q> __device__ __forceinline__ int src_piece(int h, int j) {
 // super-block header and code group 2h + g) from its weight row's pieces in
 // LDS (row: the row's first piece).
 template <int Q>
-__device__ __forceinline__ void lds_window(const uint8_t *row, int h, int g, uint32_t *w) {
-    if constexpr (Q == FW_Q4_K) {
+__device__ __forceinline__ void lds_window(const uint8_t *row, int h, int g, uint32_t *w,
+                                           uint32_t x = 0) {
+    if constexpr (Q == FW_Q6_K) {
+        // x: the unit's byte offset in its first piece (= that of its ql and
+        // qh halves in theirs); reads start at the dword holding a region's
+        // first byte, a 2-byte offset is taken out with v_alignbyte
+        const uint32_t sh = x & 3u;
+        const uint32_t *ql = (const uint32_t *)(row + ((x + 32 * g) & ~3u));
+        const uint32_t *qh = (const uint32_t *)(row + 80 + (x & ~3u));
+        uint32_t r[9];
+#pragma unroll
+        for (int i = 0; i < 9; ++i) r[i] = ql[i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = __builtin_amdgcn_alignbyte(r[i + 1], r[i], sh);
+#pragma unroll
+        for (int i = 0; i < 9; ++i) r[i] = qh[i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[8 + i] = __builtin_amdgcn_alignbyte(r[i + 1], r[i], sh) >> (2 * g);
+        // scales 8h .. 8h + 7, then d 16 - 8h bytes after them
+        const uint32_t t = (x + 8 * h) & 15u, st = t & 3u;
+        const uint32_t *tl = (const uint32_t *)(row + 128 + (t & ~3u));
+#pragma unroll
+        for (int i = 0; i < 5; ++i) r[i] = tl[i];
+        w[16] = __builtin_amdgcn_alignbyte(r[1], r[0], st) >> (16 * g);
+        w[17] = __builtin_amdgcn_alignbyte(r[2], r[1], st) >> (16 * g);
+        w[18] = h ? __builtin_amdgcn_alignbyte(r[3], r[2], st)
+                  : __builtin_amdgcn_alignbyte(r[4], r[4], st);
+    } else if constexpr (Q == FW_Q4_K) {
         const uint32_t *hd = (const uint32_t *)row;
         const uint32_t *cd = (const uint32_t *)(row + 16 + 32 * g);
 #pragma unroll
@@ -151,9 +188,19 @@ __device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 
         if (i < PX) {
             const int h = st & 1;
             const uint8_t *base = GU && (NW * i + wave >= NW * PX / 2) ? c.bbase[1] : c.bbase[0];
-            uint32_t off = c.woff[i] + (uint32_t)(st >> 1) * UB;
-            if constexpr (Q == FW_Q4_K) off += h && ((c.wk >> i) & 1) ? 64u : 0u;
-            else off += (uint32_t)h * (16 * (QT<Q>::kUnitX4 - PX));
+            uint32_t off;
+            if constexpr (Q == FW_Q6_K) {
+                // the piece's aligned address, clamped to its region's last
+                // piece: every piece holds a byte of its region
+                const uint32_t uo = (uint32_t)(st >> 1) * UB;
+                const uint32_t b0 = (h ? c.q6s[1][i] : c.q6s[0][i]) + uo;
+                const uint32_t e0 = (h ? c.q6e[1][i] : c.q6e[0][i]) + uo;
+                off = min((b0 & ~15u) + c.q6p[i], e0 & ~15u);
+            } else {
+                off = c.woff[i] + (uint32_t)(st >> 1) * UB;
+                if constexpr (Q == FW_Q4_K) off += h && ((c.wk >> i) & 1) ? 64u : 0u;
+                else off += (uint32_t)h * (16 * (QT<Q>::kUnitX4 - PX));
+            }
             __builtin_amdgcn_global_load_lds(base + off,
                                              (lds_void *)(buf + i * kThreads + 64 * wave), 16,
                                              0, 0);
@@ -161,15 +208,27 @@ __device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 
     };
     const int wr0 = lds_wrow<GU, NW>(wave, 0, n) * (16 * PX);
     const int wr1 = lds_wrow<GU, NW>(wave, 1, n) * (16 * PX);
-    auto read_w = [&](const uint4 *buf, int h) {
-        lds_window<Q>((const uint8_t *)buf + wr0, h, g, wh[0]);
-        lds_window<Q>((const uint8_t *)buf + wr1, h, g, wh[1]);
+    // the windows of step st (half st % 2) from buffer buf
+    auto read_w = [&](const uint4 *buf, int st) {
+        const int h = st & 1;
+        if constexpr (Q == FW_Q6_K) {
+            const uint32_t uo = (uint32_t)(st >> 1) * UB;
+            lds_window<Q>((const uint8_t *)buf + wr0, h, g, wh[0], (c.q6r[0] + uo) & 15u);
+            lds_window<Q>((const uint8_t *)buf + wr1, h, g, wh[1], (c.q6r[1] + uo) & 15u);
+        } else {
+            lds_window<Q>((const uint8_t *)buf + wr0, h, g, wh[0]);
+            lds_window<Q>((const uint8_t *)buf + wr1, h, g, wh[1]);
+        }
     };
-    // A fragment of slice s, row group mi: row 32 mi + n, chunk 8 g + s,
-    // stored at chunk (8 g + s) ^ (n % 16) of the row
+    // A fragment of slice s, row group mi: row 32 mi + n, chunk 8 g + s (Q6_K:
+    // 4 g + 8 (s / 4) + s % 4, the lane group's blocks being g and g + 2),
+    // stored at the chunk's index ^ (n % 16) in the row
     const int arow = n * 16, ax = n & 15;
-    const int ch = arow + (8 * g ^ (ax & 8));   // the chunk's row base and bit 3
-    const int xs = ax & 7;
+    constexpr int kGC = Q == FW_Q6_K ? 4 : 8;
+    auto apos = [&](int S) {
+        const int cs = Q == FW_Q6_K ? 8 * (S >> 2) + (S & 3) : S;
+        return arow + ((kGC * g + cs) ^ ax);
+    };
     // One step: eight slices, software-pipelined one slice deep -- slice S's
     // MFMAs are issued with slice S + 1's A fragments already on their way
     // from LDS and followed by slice S + 1's B fragments, so a wavefront's
@@ -183,13 +242,19 @@ __device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 
                 q4k_consts(wh[cg], 2 * h + g, kq[cg]);
                 wmax = fmaxf(wmax, q4k_bound(kq[cg]));
             }
+        } else if constexpr (Q == FW_Q6_K) {
+#pragma unroll
+            for (int cg = 0; cg < 2; ++cg) {
+                q6k_consts(wh[cg], kq[cg]);
+                wmax = fmaxf(wmax, q6k_bound(kq[cg]));
+            }
         } else {
 #pragma unroll
             for (int cg = 0; cg < 2; ++cg) dmax = max(dmax, d_bits<Q>(wh[cg]));
         }
         h8 a[2][MI], b[2][2];
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) a[0][mi] = __builtin_bit_cast(h8, buf[ch + xs + mi * 512]);
+        for (int mi = 0; mi < MI; ++mi) a[0][mi] = __builtin_bit_cast(h8, buf[apos(0) + mi * 512]);
         b[0][0] = frag_any<Q, 0>(wh[0], kq[0]);
         b[0][1] = frag_any<Q, 0>(wh[1], kq[1]);
 #define FW_SLICE(S)                                                                          \
@@ -197,7 +262,7 @@ __device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 
         constexpr int X = (S) & 1, Y = X ^ 1;                                                \
         if constexpr ((S) < 7) {                                                             \
             _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                                \
-                a[Y][mi] = __builtin_bit_cast(h8, buf[ch + (((S) + 1) ^ xs) + mi * 512]);    \
+                a[Y][mi] = __builtin_bit_cast(h8, buf[apos((S) + 1) + mi * 512]);            \
         }                                                                                    \
         _Pragma("unroll") for (int cg = 0; cg < 2; ++cg)                                     \
             _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                                \
@@ -253,10 +318,10 @@ __device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 
     for (int i = 0; i < kDma; ++i) dma_a(A0, 0, i);
     sync();
     for (int st = 0; st < steps; st += 2) {
-        read_w(B0, 0);
+        read_w(B0, st);
         step(A0, 0, [&](int S) { issue(A1, B1, st + 1, S); });
         sync();
-        read_w(B1, 1);
+        read_w(B1, st + 1);
         const int nx = min(st + 2, steps - 1);
         step(A1, 1, [&](int S) { issue(A0, B0, nx, S); });
         sync();
@@ -265,8 +330,9 @@ __device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 
     // ---- epilogue: acc[mi][cg][v] is tile row 32 mi + 8 (v / 4) + 4 g + v % 4,
     // weight row (column group cg) n ----
     const int rows = c.rows, rb = c.rb, N = c.N;
-    bool range = Q == FW_Q4_K ? !(wmax <= 65504.0f)
-                              : dmax > (Q == FW_Q4_0 ? kQ4DMaxBits : kQ8DMaxBits);
+    bool range = (Q == FW_Q4_K || Q == FW_Q6_K)
+                     ? !(wmax <= 65504.0f)
+                     : dmax > (Q == FW_Q4_0 ? kQ4DMaxBits : kQ8DMaxBits);
     if constexpr (GU) {
         // feature ct * 128 + 32 wave + n: gate in column group 0, up in 1; the
         // wavefront's 32 features are one 32-element block of h (pair order)
@@ -322,7 +388,7 @@ __device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 
 // column counts eight waves do not divide and Q8_0, whose wider windows and
 // 272-byte units need the registers and the LDS.
 template <int Q, int NW> constexpr int waves_per_simd() { return NW == 8 ? 2 : 1; }
-template <int Q> constexpr bool eight_waves() { return Q != FW_Q8_0; }
+template <int Q> constexpr bool eight_waves() { return Q == FW_Q4_0 || Q == FW_Q4_K; }
 
 template <int Q, bool GU, int NW>
 __global__ __launch_bounds__(64 * NW, (waves_per_simd<Q, NW>() * 4 / NW)) void gemm_kernel(
@@ -400,24 +466,62 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<Q, NW>() * 4 / NW)) void g
         c.aoff[i] = ((uint32_t)s * K + chunk * 8) * 2;
     }
     c.abase = (const uint8_t *)ain;
-    const size_t rowbytes = (size_t)(K / 32) * QT<Q>::kBlockBytes;
+    const size_t rowbytes = QT<Q>::row_bytes(K);
     const size_t esz = (size_t)N * rowbytes;
     const uint8_t *ba = wa + (size_t)expert * esz, *bb = (GU ? wb : wa) + (size_t)expert * esz;
-    c.bbase[0] = ba;
-    c.bbase[1] = bb;
     // weight piece of DMA instruction i: LDS piece p = i kThreads + tid is
     // piece p % PX of LDS row p / PX (gate/up: rows from 32 NW on are the up
     // matrix's, read from bbase[1])
-    c.wk = 0;
+    if constexpr (Q == FW_Q6_K) {
+        // 16-byte aligned bases; offsets carry the matrices' own misalignment
+        const uint32_t mis[2] = {(uint32_t)(uintptr_t)ba & 15u, (uint32_t)(uintptr_t)bb & 15u};
+        c.bbase[0] = ba - mis[0];
+        c.bbase[1] = bb - mis[1];
 #pragma unroll
-    for (int i = 0; i < PX; ++i) {
-        const int p = i * kThreads + tid;
-        int Rl = p / PX;
-        const int j = p - Rl * PX;
-        if (GU && Rl >= 32 * NW) Rl -= 32 * NW;
-        const int row = GU ? ct * (32 * NW) + Rl : ct * (64 * NW) + Rl;
-        c.woff[i] = (uint32_t)(row * rowbytes) + (uint32_t)j * 16;
-        if (j > 0) c.wk |= 1u << i;
+        for (int i = 0; i < PX; ++i) {
+            const int p = i * kThreads + tid;
+            int Rl = p / PX;
+            const int j = p - Rl * PX;
+            int m = 0;
+            if (GU && Rl >= 32 * NW) {
+                Rl -= 32 * NW;
+                m = 1;
+            }
+            const int row = GU ? ct * (32 * NW) + Rl : ct * (64 * NW) + Rl;
+            const uint32_t ro = mis[m] + (uint32_t)(row * rowbytes);
+            // regions: ql half [64h, 64h + 64), qh half [128 + 32h, + 32),
+            // scales of the half to the unit's end [192 + 8h, 210)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t b0 = j < 5 ? 64 * h : j < 8 ? 128 + 32 * h : 192 + 8 * h;
+                const uint32_t e0 = j < 5 ? 64 * h + 63 : j < 8 ? 159 + 32 * h : 209;
+                c.q6s[h][i] = ro + b0;
+                c.q6e[h][i] = ro + e0;
+            }
+            c.q6p[i] = 16u * (uint32_t)(j < 5 ? j : j < 8 ? j - 5 : j - 8);
+        }
+        // the rows this lane reads windows of (lds_wrow)
+        const int n = c.lane & 31;
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg) {
+            const int row = GU ? ct * (32 * NW) + 32 * c.wave + n
+                               : ct * (64 * NW) + 64 * c.wave + 32 * cg + n;
+            c.q6r[cg] = mis[GU ? cg : 0] + (uint32_t)(row * rowbytes);
+        }
+    } else {
+        c.bbase[0] = ba;
+        c.bbase[1] = bb;
+        c.wk = 0;
+#pragma unroll
+        for (int i = 0; i < PX; ++i) {
+            const int p = i * kThreads + tid;
+            int Rl = p / PX;
+            const int j = p - Rl * PX;
+            if (GU && Rl >= 32 * NW) Rl -= 32 * NW;
+            const int row = GU ? ct * (32 * NW) + Rl : ct * (64 * NW) + Rl;
+            c.woff[i] = (uint32_t)(row * rowbytes) + (uint32_t)j * 16;
+            if (j > 0) c.wk |= 1u << i;
+        }
     }
     c.hout = hout;
     c.yout = yout;
@@ -474,6 +578,8 @@ void launch_q(int q, const FwdArgs &a, const uint8_t *wa, const uint8_t *wb,
         launch<FW_Q4_0, GU>(a, wa, wb, ain, hout, yout, K, N, shared, iexp, oexp, s);
     else if (q == FW_Q4_K)
         launch<FW_Q4_K, GU>(a, wa, wb, ain, hout, yout, K, N, shared, iexp, oexp, s);
+    else if (q == FW_Q6_K)
+        launch<FW_Q6_K, GU>(a, wa, wb, ain, hout, yout, K, N, shared, iexp, oexp, s);
     else
         launch<FW_Q8_0, GU>(a, wa, wb, ain, hout, yout, K, N, shared, iexp, oexp, s);
 }

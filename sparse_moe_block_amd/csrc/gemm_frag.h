@@ -12,7 +12,12 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
 // Dwords of the window of blocks 2g, 2g + 1 of a unit, per weight row.
 // Q4_K: the super-block's 16-byte header and the 32 code bytes of group g.
-template <int Q> constexpr int win_dwords() { return Q == FW_Q4_0 ? 9 : Q == FW_Q4_K ? 12 : 17; }
+// Q6_K: 8 ql dwords (the lane group's 32 bytes of the half's low bits), 8
+// qh dwords (the half's top bits, shifted right by 2g), the half's 8 scales
+// (2 dwords, shifted right by 16g) and d.
+template <int Q> constexpr int win_dwords() {
+    return Q == FW_Q4_0 ? 9 : Q == FW_Q4_K ? 12 : Q == FW_Q6_K ? 19 : 17;
+}
 
 // Per-step constants of a Q4_K window (sub-blocks A = 2g, B = 2g + 1 of the
 // lane's group g), as fp32 bits: k[2h] = d * scale, k[2h + 1] = -dmin * min
@@ -138,11 +143,63 @@ __device__ __forceinline__ h8 frag_b(const uint32_t *w) {
     return f;
 }
 
-// B fragment of slice I of any format (kq: the Q4_K per-step constants).
+// Per-step constants of a Q6_K window, as fp32 bits: for the lane group's
+// blocks k = g + 2 k2 (k2 = 0, 1), k[2 k2] = d * scale of the block's first
+// 16 elements and k[2 k2 + 1] = 16 d * scale of its last 16 (their pairs
+// j = 1, 3 carry 16x).  Both exact in fp32.
+__device__ __forceinline__ void q6k_consts(const uint32_t *w, uint32_t *k) {
+    const float d = half_bits_to_float(w[18] & 0xFFFFu);
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+        k[2 * k2] = __float_as_uint(d * (float)(int)__builtin_amdgcn_sbfe(w[16 + k2], 0, 8));
+        k[2 * k2 + 1] = __float_as_uint(16.0f * d * (float)(int)__builtin_amdgcn_sbfe(w[16 + k2], 8, 8));
+    }
+}
+
+// Bound on the magnitude of a Q6_K window's fp16 weights: 32 |constant|.
+__device__ __forceinline__ float q6k_bound(const uint32_t *k) {
+    float b = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b = fmaxf(b, 32.0f * fabsf(__uint_as_float(k[i])));
+    return b;
+}
+
+// B fragment of slice I from a Q6_K window: block k = g + 2 (I / 4) of the
+// half, pairs 4 (I % 4) .. + 3.  Four six-bit codes form in the bytes of one
+// dword (low bits: nibble I / 4 of the ql dword; top bits: bits 4 (I / 4) of
+// the pre-shifted qh dword); each weight (q - 32) * d * scale is formed
+// exactly in fp32 and rounded once to fp16 (pairs j = 1, 3 at 16x).
+template <int I>
+__device__ __forceinline__ h8 frag_b_q6k(const uint32_t *w, const uint32_t *k) {
+    constexpr int K2 = I / 4, m = I % 4;
+    const uint32_t cl = (((w[m] >> (4 * K2)) & 0x0F0F0F0Fu) |
+                         (((w[8 + m] >> (4 * K2)) & 0x03030303u) << 4));
+    const uint32_t chh = (((w[4 + m] >> (4 * K2)) & 0x0F0F0F0Fu) |
+                          (((w[12 + m] >> (4 * K2)) & 0x03030303u) << 4));
+    const float ds = __uint_as_float(k[2 * K2]), ds16 = __uint_as_float(k[2 * K2 + 1]);
+    const float nds = -32.0f * ds, nds16 = -32.0f * ds16;
+    auto e = [&](uint32_t v, int byte, float a, float b) {
+        return (_Float16)fmaf((float)((v >> (8 * byte)) & 255u), a, b);
+    };
+    h8 f;
+    f[0] = e(cl, 0, ds, nds);
+    f[1] = e(cl, 2, ds, nds);
+    f[2] = e(chh, 0, ds16, nds16);
+    f[3] = e(chh, 2, ds16, nds16);
+    f[4] = e(cl, 1, ds, nds);
+    f[5] = e(cl, 3, ds, nds);
+    f[6] = e(chh, 1, ds16, nds16);
+    f[7] = e(chh, 3, ds16, nds16);
+    return f;
+}
+
+// B fragment of slice I of any format (kq: the Q4_K / Q6_K per-step constants).
 template <int Q, int I>
 __device__ __forceinline__ h8 frag_any(const uint32_t *w, const uint32_t *kq) {
     if constexpr (Q == FW_Q4_K)
         return frag_b_q4k<I>(w, kq);
+    else if constexpr (Q == FW_Q6_K)
+        return frag_b_q6k<I>(w, kq);
     else
         return frag_b<Q, I>(w);
 }

@@ -51,6 +51,23 @@ template <int Q>
 __device__ __forceinline__ void stage_unit(uint4 *buf, const uint8_t *tile, uint32_t rowbytes,
                                            int u, int lane) {
     constexpr int X4 = QT<Q>::kUnitX4;
+    if constexpr (Q == FW_Q6_K) {
+        // 2-byte aligned units: row r's unit starts at byte o_r = mis + r *
+        // rowbytes + 210 u of the 16-byte aligned base below the tile; its 14
+        // covering pieces start at o_r & ~15.  The first and last piece each
+        // hold a byte of the unit, so no 16-byte granule outside the unit's
+        // own is touched.
+        const uint8_t *base = (const uint8_t *)((uintptr_t)tile & ~(uintptr_t)15);
+        const uint32_t mis = (uint32_t)(uintptr_t)tile & 15u;
+#pragma unroll
+        for (int i = 0; i < X4; ++i) {
+            const uint32_t c = i * kWave + lane, row = c / X4, piece = c % X4;
+            const uint32_t o = mis + row * rowbytes + (uint32_t)u * QT<Q>::kUnitBytes;
+            __builtin_amdgcn_global_load_lds(base + ((o & ~15u) + piece * 16),
+                                             (lds_void *)(buf + i * kWave), 16, 0, 0);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < X4; ++i) {
         // uniform base + 32-bit lane offset: the SGPR-base addressing form
@@ -241,11 +258,95 @@ __device__ __forceinline__ void dot_unit_blocks(const uint32_t *w, int u, cu32 *
 #undef FW_BLOCK
 }
 
+// Row `lane`'s Q6_K unit from its staged pieces (the only batch in flight:
+// Q6_K runs one buffer per wavefront), realigned so that w[i] holds bytes
+// 4i .. 4i + 3 of the unit (i < 53).  sub: the unit's byte offset in the
+// first piece (even, 0 .. 14).  The reads start at the dword holding the
+// unit's first byte (a per-lane LDS address); a 2-byte offset is taken out
+// with v_alignbyte.
+__device__ __forceinline__ void read_unit_q6k(const uint4 *slot, uint32_t sub, uint32_t *w) {
+    __builtin_amdgcn_s_waitcnt(7 << 4);   // vmcnt(0): the batch has landed
+    const uint32_t *p = (const uint32_t *)((const uint8_t *)slot + (sub & 12u));
+    uint32_t r[54];
+#pragma unroll
+    for (int i = 0; i < 54; ++i) r[i] = p[i];
+    // every LDS read has returned before the buffer's next DMA is issued
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    const uint32_t sh = sub & 3u;
+#pragma unroll
+    for (int i = 0; i < 53; ++i) w[i] = __builtin_amdgcn_alignbyte(r[i + 1], r[i], sh);
+}
+
+// Q6_K unit (one super-block) in pair order: block B = 4h + k of the unit
+// (half h, k = 0..3) takes its codes' low four bits from ql dwords
+// 16h + 8 (k % 2) + m (elements 4m ..) and + 4 (elements 16 + 4m ..), nibble
+// k / 2, and their top two bits from qh dwords 32 + 8h + m (+ 4), bits 2k.
+// Four six-bit codes form in the bytes of one dword; two of them at a time
+// become the exact fp16 pair 1024 + q (pairs j = 0, 2) or 1024 + 16 q (pairs
+// j = 1, 3, whose activations carry 1/16).  Elements l < 16 of a block
+// (pairs j = 0, 2) are sub-block 2B, the others 2B + 1: two dot sums per
+// block, each scaled once by d * scale in fp32.
+template <int NTK>
+__device__ __forceinline__ void dot_unit_q6k(const uint32_t *w, int u, cu32 *const *in,
+                                             float *acc) {
+    const uint32_t magic = pair_magic<FW_Q6_K>();
+    const float d = half_bits_to_float(w[52] & 0xFFFFu);
+    const h2 k1056 = {(_Float16)1056.0f, (_Float16)1056.0f};
+    const h2 k1536 = {(_Float16)1536.0f, (_Float16)1536.0f};
+    constexpr int NB = x_sets<NTK>();
+    uint32_t xs[NB][NTK][16];
+#pragma unroll
+    for (int j = 0; j < NB - 1; ++j) load_x<NTK>(xs[j], in, u, j);
+#define FW_Q6B(B)                                                                        \
+    {                                                                                    \
+        if (B + NB - 1 < 8) load_x<NTK>(xs[(B + NB - 1) % NB], in, u, B + NB - 1);       \
+        const uint32_t(*X)[16] = xs[B % NB];                                             \
+        constexpr int H = (B) / 4, KK = (B) % 4;                                         \
+        const uint32_t *ql = w + 16 * H + 8 * (KK % 2), *qh = w + 32 + 8 * H;            \
+        h2 p[16];                                                                        \
+        _Pragma("unroll") for (int m = 0; m < 4; ++m) {                                  \
+            const uint32_t cl = and_or(ql[m] >> (4 * (KK / 2)), 0x0F0F0F0Fu,             \
+                                       ((qh[m] >> (2 * KK)) & 0x03030303u) << 4);        \
+            const uint32_t ch = and_or(ql[m + 4] >> (4 * (KK / 2)), 0x0F0F0F0Fu,         \
+                                       ((qh[m + 4] >> (2 * KK)) & 0x03030303u) << 4);    \
+            p[4 * m + 0] = as_h2(and_or(cl, 0x003F003Fu, magic)) - k1056;                \
+            p[4 * m + 1] = as_h2(and_or(ch << 4, 0x03F003F0u, magic)) - k1536;           \
+            p[4 * m + 2] = as_h2(and_or(cl >> 8, 0x003F003Fu, magic)) - k1056;           \
+            p[4 * m + 3] = as_h2(and_or(ch >> 4, 0x03F003F0u, magic)) - k1536;           \
+        }                                                                                \
+        const float s0 = d * (float)(int)__builtin_amdgcn_sbfe(w[48 + (B) / 2], 16 * ((B) & 1), 8); \
+        const float s1 = d * (float)(int)__builtin_amdgcn_sbfe(w[48 + (B) / 2], 16 * ((B) & 1) + 8, 8); \
+        _Pragma("unroll") for (int n = 0; n < NTK; ++n) {                                \
+            float lo = 0.f, hi = 0.f;                                                    \
+            _Pragma("unroll") for (int m = 0; m < 4; ++m) {                              \
+                lo = __builtin_amdgcn_fdot2(p[4 * m + 0], as_h2(X[n][4 * m + 0]), lo, false); \
+                lo = __builtin_amdgcn_fdot2(p[4 * m + 2], as_h2(X[n][4 * m + 2]), lo, false); \
+                hi = __builtin_amdgcn_fdot2(p[4 * m + 1], as_h2(X[n][4 * m + 1]), hi, false); \
+                hi = __builtin_amdgcn_fdot2(p[4 * m + 3], as_h2(X[n][4 * m + 3]), hi, false); \
+            }                                                                            \
+            acc[n] = fmaf(s0, lo, acc[n]);                                               \
+            acc[n] = fmaf(s1, hi, acc[n]);                                               \
+        }                                                                                \
+    }                                                                                    \
+    __builtin_amdgcn_sched_barrier(0);
+    FW_Q6B(0)
+    FW_Q6B(1)
+    FW_Q6B(2)
+    FW_Q6B(3)
+    FW_Q6B(4)
+    FW_Q6B(5)
+    FW_Q6B(6)
+    FW_Q6B(7)
+#undef FW_Q6B
+}
+
 template <int Q, int NTK>
 __device__ __forceinline__ void dot_unit(const uint32_t *w, int u, cu32 *const *in,
                                          cu32 *const *sum, float *acc) {
     if constexpr (Q == FW_Q4_K)
         dot_unit_q4k<NTK>(w, u, in, sum, acc);
+    else if constexpr (Q == FW_Q6_K)
+        dot_unit_q6k<NTK>(w, u, in, acc);
     else
         dot_unit_blocks<Q, NTK>(w, u, in, acc);
 }
@@ -353,7 +454,7 @@ __global__ __launch_bounds__(kWave *S) void gemv_kernel(
     __shared__ uint4 stage[S][D][kWave * X4];
     __shared__ float red[S > 1 ? S - 1 : 1][NV * NT][kWave];
     const int wave = wave_id(), lane = threadIdx.x % kWave;
-    const size_t rowbytes = (size_t)(K / 32) * QT<Q>::kBlockBytes;
+    const size_t rowbytes = QT<Q>::row_bytes(K);
     const size_t esz = (size_t)N * rowbytes;
     const uint8_t *wbb = GU ? wb : wa;
     // the device-written chunk count is clamped to the bound the launch (its
@@ -401,9 +502,16 @@ __global__ __launch_bounds__(kWave *S) void gemv_kernel(
             for (int n = 0; n < NT; ++n) acc[v][n] = 0.f;
         for (int b = 0; b < nb; ++b, ++j) {
             uint32_t w[4 * X4];
-            wait_read<Q, D>(&stage[wave][j % D][lane * X4], min(D - 1, total - 1 - j), w);
-            if (js < total) FW_STAGE_NEXT();
             const int u = slice * us + wave + (b / NV) * S;
+            if constexpr (Q == FW_Q6_K) {
+                const uint8_t *tl = (NV == 2 && (b & 1)) ? it.tb : it.ta;
+                const uint32_t sub =
+                    ((uint32_t)(uintptr_t)tl + (uint32_t)lane * rb32 + 210u * (uint32_t)u) & 15u;
+                read_unit_q6k(&stage[wave][j % D][lane * X4], sub, w);
+            } else {
+                wait_read<Q, D>(&stage[wave][j % D][lane * X4], min(D - 1, total - 1 - j), w);
+            }
+            if (js < total) FW_STAGE_NEXT();
             float *a = acc[NV == 2 ? (b & 1) : 0];
             if (it.nt == 1) dot_unit<Q, 1>(w, u, it.in, it.sum, a);
             else dot_unit<Q, 2>(w, u, it.in, it.sum, a);
@@ -633,9 +741,12 @@ void launch_q(int q, const FwdArgs &a, const uint8_t *wa, const uint8_t *wb,
     else if (q == FW_Q8_0)
         launch<FW_Q8_0, GU>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, nullptr,
                             nullptr, iexp, oexp, s);
-    else
+    else if (q == FW_Q4_K)
         launch<FW_Q4_K, GU>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, isum, osum,
                             iexp, oexp, s);
+    else
+        launch<FW_Q6_K, GU>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, nullptr,
+                            nullptr, iexp, oexp, s);
 }
 
 // Block sums: x rows (prepare), then h rows of the routed pairs [P][F/32]
