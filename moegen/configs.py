@@ -18,6 +18,7 @@ Q8_0 = "q8_0"
 Q4_0 = "q4_0"
 Q4_K = "q4_k"
 Q6_K = "q6_k"
+MXFP4 = "mxfp4"
 F32 = "f32"
 BF16 = "bf16"
 SOFTMAX = "softmax"
@@ -30,7 +31,10 @@ SUPER_BYTES = {Q4_K: 144, Q6_K: 210}
 
 
 def row_bytes(qtype: str, n: int) -> int:
-    """Bytes of a GGUF row of n elements."""
+    """Bytes a row of n elements takes (MXFP4: its codes and its share of the
+    scales, which sit after the whole matrix's codes)."""
+    if qtype == MXFP4:
+        return n // 2 + n // 32
     if qtype in SUPER_BYTES:
         return n // 256 * SUPER_BYTES[qtype]
     return n // 32 * BLOCK_BYTES[qtype]

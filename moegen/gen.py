@@ -2,7 +2,7 @@
 GGUF-blocked expert weights.
 
 Input generation only.  It contains none of the layer's arithmetic: no dequant,
-no routing, no FFN.  The quantizers below *produce* Q8_0 / Q4_0 / Q4_K / Q6_K blocks from fp32
+no routing, no FFN.  The quantizers below *produce* Q8_0 / Q4_0 / Q4_K / Q6_K / MXFP4 weights from fp32
 samples (the way a checkpoint converter would); the layer only ever *reads*
 blocks.  Both the GPU path and the CPU oracle are fed from here.
 
@@ -28,6 +28,9 @@ Block byte layout (GGUF, little-endian, no padding):
         low nibble (k < 2) or high nibble (k >= 2) of ql byte 64h+32(k%2)+l
         and bits 2k, 2k+1 of qh byte 32h+l: a six-bit code q; value =
         d*scale_j*(q-32), j the 16-element sub-block.
+  MXFP4 (MLX packing, group 32): a matrix of R rows is R x K/2 bytes of E2M1
+        codes (element j in nibble j%2 of byte j/2, low first) followed by
+        R x K/32 E8M0 scale bytes; value = E2M1(code) * 2^(scale-127).
 """
 
 import math
@@ -37,7 +40,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-from .configs import BF16, F32, Q4_0, Q4_K, Q6_K, Q8_0, LayerConfig, row_bytes
+from .configs import BF16, F32, MXFP4, Q4_0, Q4_K, Q6_K, Q8_0, LayerConfig, row_bytes
 
 BASE_SEED = 20261202
 
@@ -169,8 +172,35 @@ def quantize_q6_k(w: torch.Tensor) -> torch.Tensor:
     return out.reshape(*lead, n // 256 * 210).contiguous()
 
 
+# E2M1 magnitudes by code (bits 2..0); bit 3 is the sign
+E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def quantize_mxfp4(w: torch.Tensor) -> torch.Tensor:
+    """fp32 [R, n] -> uint8 [R*n/2 + R*n/32]: the MLX MXFP4 codes of all rows,
+    then their scales.  Per 32-element group (OCP MX): shared exponent
+    e = floor(log2(amax)) - 2 (E2M1's largest exponent), scale byte e + 127
+    clamped to 0..254; codes: the nearest E2M1 value to x / 2^e (ties to the
+    smaller magnitude), saturating at 6.  All-zero groups: scale 0, codes 0."""
+    R, n = w.shape
+    assert n % 32 == 0
+    b = w.reshape(R, n // 32, 32)
+    amax = b.abs().amax(dim=-1)
+    e = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax,
+                                                                  torch.ones_like(amax)))) - 2,
+                    torch.full_like(amax, -127.0)).clamp(-127, 127)
+    y = b / torch.exp2(e).unsqueeze(-1)
+    mag = torch.tensor(E2M1, dtype=torch.float32, device=w.device)
+    dist = (y.abs().unsqueeze(-1) - mag).abs()            # [R, G, 32, 8]
+    k = dist.argmin(dim=-1)                               # first (smaller) on ties
+    code = (k | torch.where(y < 0, 8, 0)).to(torch.uint8).reshape(R, n)
+    codes = (code[:, 0::2] | (code[:, 1::2] << 4)).reshape(-1)
+    scales = (e + 127).to(torch.uint8).reshape(-1)
+    return torch.cat([codes, scales]).contiguous()
+
+
 QUANTIZERS = {Q8_0: quantize_q8_0, Q4_0: quantize_q4_0, Q4_K: quantize_q4_k,
-              Q6_K: quantize_q6_k}
+              Q6_K: quantize_q6_k, MXFP4: quantize_mxfp4}
 
 
 def quantized_normal(rows, cols, std, qtype, seed, device):
@@ -219,13 +249,25 @@ def make_layer(cfg: LayerConfig, device="cpu", qtype: Optional[str] = None) -> L
     router = to_act_dtype(normal((E, H), cfg.router_std, seed_of(c, T_ROUTER, 0), device),
                           cfg.router_dtype)
     bias = zipf_bias(E, cfg.zipf).to(device) if cfg.zipf else None
-    wg = torch.empty((E, F, row_bytes(q, H)), dtype=torch.uint8, device=device)
-    wu = torch.empty_like(wg)
-    wd = torch.empty((E, H, row_bytes(q, F)), dtype=torch.uint8, device=device)
-    for e in range(E):
-        wg[e] = quantized_normal(F, H, cfg.w_std, q, seed_of(c, T_GATE, e), device)
-        wu[e] = quantized_normal(F, H, cfg.w_std, q, seed_of(c, T_UP, e), device)
-        wd[e] = quantized_normal(H, F, cfg.w_std, q, seed_of(c, T_DOWN, e), device)
+    if q == MXFP4:
+        # one matrix per projection over all experts' rows: codes, then scales
+        def stack(rows, cols, tid):
+            m = torch.empty(E * rows * (cols // 2 + cols // 32), dtype=torch.uint8, device=device)
+            cb, sb = rows * cols // 2, rows * cols // 32
+            for e in range(E):
+                one = quantized_normal(rows, cols, cfg.w_std, q, seed_of(c, tid, e), device)
+                m[e * cb:(e + 1) * cb] = one[:cb]
+                m[E * rows * cols // 2 + e * sb:E * rows * cols // 2 + (e + 1) * sb] = one[cb:]
+            return m
+        wg, wu, wd = stack(F, H, T_GATE), stack(F, H, T_UP), stack(H, F, T_DOWN)
+    else:
+        wg = torch.empty((E, F, row_bytes(q, H)), dtype=torch.uint8, device=device)
+        wu = torch.empty_like(wg)
+        wd = torch.empty((E, H, row_bytes(q, F)), dtype=torch.uint8, device=device)
+        for e in range(E):
+            wg[e] = quantized_normal(F, H, cfg.w_std, q, seed_of(c, T_GATE, e), device)
+            wu[e] = quantized_normal(F, H, cfg.w_std, q, seed_of(c, T_UP, e), device)
+            wd[e] = quantized_normal(H, F, cfg.w_std, q, seed_of(c, T_DOWN, e), device)
     layer = Layer(cfg, router, bias, wg, wu, wd)
     if cfg.shared_ffn:
         Fs, qs = cfg.shared_ffn, cfg.shared_q

@@ -1,6 +1,6 @@
 /*
  * fwref.c -- CPU oracle for the routed mixture-of-experts FFN layer run on GGUF
- * Q8_0 / Q4_0 / Q4_K / Q6_K expert weights.
+ * Q8_0 / Q4_0 / Q4_K / Q6_K / MXFP4 expert weights.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg load this library.  The GPU library shares no
@@ -35,6 +35,14 @@
  *    "Current limitations"; Flyweight 0.5.1, "Models and formats").  GGUF's
  *    layout again, PARITY UNPINNED against an outside encoder; pinned the
  *    same way as Q4_K;
+ *  - MXFP4 (group 32), the expert-only format of vOOM's lossy artifacts (vOOM,
+ *    the Qwen3.6-35B-A3B side-quest notes: routed expert matrices only, MLX
+ *    weight/scale pairs, --mode mxfp4 --group-size 32).  MLX's packing: a
+ *    matrix of R rows is its E2M1 codes, R x K/2 bytes (element j of a row in
+ *    nibble j % 2 of byte j / 2, low nibble first), followed by its E8M0
+ *    scales, R x K/32 bytes; value = E2M1(code) * 2^(scale - 127), exact in
+ *    fp32 below 2^128 (from scale 253 on the larger values are infinite);
+ *    scale 255 is NaN.  PARITY UNPINNED against an outside encoder;
  *  - SwiGLU expert FFNs (vOOM, module layout: layer_runner's block math);
  *  - top-k routing with k a tunable (vOOM notes: the request-local top-2
  *    expert schedule) and DeepSeek-shaped sigmoid routing with an always-on
@@ -55,7 +63,7 @@
 #endif
 
 enum { REF_F32 = 0, REF_BF16 = 1 };
-enum { REF_Q8_0 = 0, REF_Q4_0 = 1, REF_Q4_K = 2, REF_Q6_K = 3 };
+enum { REF_Q8_0 = 0, REF_Q4_0 = 1, REF_Q4_K = 2, REF_Q6_K = 3, REF_MXFP4 = 4 };
 enum { REF_SOFTMAX = 0, REF_SIGMOID = 1 };
 
 /* IEEE 754 binary16 -> value: 1 sign bit, 5 exponent bits (bias 15), 10
@@ -83,15 +91,49 @@ float fwref_bf16_to_float(uint16_t b)
 }
 
 /* Bytes of a row of n elements: 32-element blocks of 34 (Q8_0) or 18 (Q4_0)
- * bytes, 256-element super-blocks of 144 (Q4_K) or 210 (Q6_K) bytes. */
+ * bytes, 256-element super-blocks of 144 (Q4_K) or 210 (Q6_K) bytes; MXFP4
+ * rows hold their n / 2 code bytes here (the scales sit after the matrix). */
 static size_t row_bytes(int qtype, int n)
 {
     switch (qtype) {
         case REF_Q8_0: return (size_t)n / 32 * 34;
         case REF_Q4_0: return (size_t)n / 32 * 18;
         case REF_Q4_K: return (size_t)n / 256 * 144;
-        default: return (size_t)n / 256 * 210;
+        case REF_Q6_K: return (size_t)n / 256 * 210;
+        default: return (size_t)n / 2;
     }
+}
+
+/* OCP MX E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0; the
+ * exponent-0 codes are the subnormals 0 and 0.5. */
+static double e2m1_value(int code)
+{
+    int ex = (code >> 1) & 3, m = code & 1;
+    double v = ex == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, ex - 1);
+    return code & 8 ? -v : v;
+}
+
+/* Row r (of R) of an MXFP4 matrix of n-element rows starting at base. */
+static void mxfp4_row(const uint8_t *base, size_t R, size_t r, int n, float *out)
+{
+    const uint8_t *codes = base + r * (size_t)(n / 2);
+    const uint8_t *scales = base + R * (size_t)(n / 2) + r * (size_t)(n / 32);
+    for (int j = 0; j < n; ++j) {
+        int code = j % 2 ? codes[j / 2] >> 4 : codes[j / 2] & 15;
+        int s = scales[j / 32];
+        out[j] = s == 255 ? NAN : (float)ldexp(e2m1_value(code), s - 127);
+    }
+}
+
+void fwref_dequant_row(int qtype, const uint8_t *row, int n, float *out);
+
+/* Row r of a matrix of R rows of n elements in format qtype at base. */
+static void matrix_row(int qtype, const uint8_t *base, size_t R, size_t r, int n, float *out)
+{
+    if (qtype == REF_MXFP4)
+        mxfp4_row(base, R, r, n, out);
+    else
+        fwref_dequant_row(qtype, base + r * row_bytes(qtype, n), n, out);
 }
 
 /* Q4_K sub-block j's 6-bit scale and min from the 12 packed bytes: j < 4 keep
@@ -126,9 +168,14 @@ static void q4k_scale_min(const uint8_t *sc, int j, int *scale, int *min)
  *             bits from ql byte 64h + 32 (k % 2) + l (low nibble for k < 2,
  *             high for k >= 2) and its top two bits from bits 2k, 2k + 1 of
  *             qh byte 32h + l: a six-bit code q.  Sub-block j = e / 16 of 16
- *             elements has scale byte j; value = d * scale_j * (q - 32). */
+ *             elements has scale byte j; value = d * scale_j * (q - 32).
+ * MXFP4: the row's n / 2 code bytes followed by its n / 32 E8M0 scales. */
 void fwref_dequant_row(int qtype, const uint8_t *row, int n, float *out)
 {
+    if (qtype == REF_MXFP4) {   /* a one-row matrix: n / 2 code bytes, n / 32 scales */
+        mxfp4_row(row, 1, 0, n, out);
+        return;
+    }
     if (qtype == REF_Q6_K) {
         for (int b = 0; b < n / 256; ++b) {
             const uint8_t *blk = row + (size_t)b * 210;
@@ -300,27 +347,26 @@ int fwref_permute(int T, int E, int k, const int32_t *ids, int32_t *offsets,
  *   g_f = sum_h Wg[f][h] x_h,  u_f = sum_h Wu[f][h] x_h
  *   a_f = g_f * sigmoid(g_f) * u_f          (SiLU(gate) * up)
  *   y_o = sum_f Wd[o][f] a_f
- * Wg, Wu: F rows of H elements; Wd: H rows of F elements; blocked along the
- * row (the reduction dimension). */
+ * Wg, Wu: rows r0gu .. r0gu + F - 1 of matrices of Rgu rows of H elements;
+ * Wd: rows r0d .. r0d + H - 1 of a matrix of Rd rows of F elements; blocked
+ * along the row (the reduction dimension). */
 static void expert_ffn(int qtype, int F, int H, const uint8_t *wg, const uint8_t *wu,
-                       const uint8_t *wd, const float *x, double *y, float *row,
-                       double *a)
+                       const uint8_t *wd, size_t Rgu, size_t Rd, size_t r0gu, size_t r0d,
+                       const float *x, double *y, float *row, double *a)
 {
-    size_t rb_h = row_bytes(qtype, H);
-    size_t rb_f = row_bytes(qtype, F);
     for (int f = 0; f < F; ++f) {
         double g = 0.0, u = 0.0;
-        fwref_dequant_row(qtype, wg + f * rb_h, H, row);
+        matrix_row(qtype, wg, Rgu, r0gu + f, H, row);
         for (int h = 0; h < H; ++h)
             g += (double)row[h] * (double)x[h];
-        fwref_dequant_row(qtype, wu + f * rb_h, H, row);
+        matrix_row(qtype, wu, Rgu, r0gu + f, H, row);
         for (int h = 0; h < H; ++h)
             u += (double)row[h] * (double)x[h];
         a[f] = g / (1.0 + exp(-g)) * u;
     }
     for (int o = 0; o < H; ++o) {
         double acc = 0.0;
-        fwref_dequant_row(qtype, wd + o * rb_f, F, row);
+        matrix_row(qtype, wd, Rd, r0d + o, F, row);
         for (int f = 0; f < F; ++f)
             acc += (double)row[f] * a[f];
         y[o] = acc;
@@ -330,8 +376,8 @@ static void expert_ffn(int qtype, int F, int H, const uint8_t *wg, const uint8_t
 /* The layer's output for T tokens:
  *   out[t] = fp32( sum_{j<k} w[t][j] * FFN_{ids[t][j]}(x_t)  +  FFN_shared(x_t) )
  * with the slot sum in order j = 0..k-1 and the shared expert (Fs > 0) last.
- * Expert e's tensors start at e * F rows of H elements (gate, up) and e * H
- * rows of F elements (down).  Tokens are independent, so they are spread over
+ * Expert e's rows are rows e * F .. (gate, up: E * F rows of H elements) and
+ * e * H .. (down: E * H rows of F elements) of the routed matrices.  Tokens are independent, so they are spread over
  * n_threads OpenMP threads (0: the runtime's default).
  * Returns 0, or -1 on a bad argument or id. */
 int fwref_forward(int T, int H, int E, int k, int F, int qtype, int Fs, int qtype_s,
@@ -347,11 +393,11 @@ int fwref_forward(int T, int H, int E, int k, int F, int qtype, int Fs, int qtyp
     if ((qtype >= REF_Q4_K && (H % 256 || F % 256)) ||
         (Fs > 0 && qtype_s >= REF_Q4_K && (H % 256 || Fs % 256)))
         return -1;
+    if (qtype < REF_Q8_0 || qtype > REF_MXFP4 || (Fs > 0 && (qtype_s < REF_Q8_0 || qtype_s > REF_MXFP4)))
+        return -1;
     for (long q = 0; q < (long)T * k; ++q)
         if (ids[q] < 0 || ids[q] >= E)
             return -1;
-    size_t expert_gu = (size_t)F * row_bytes(qtype, H);
-    size_t expert_d = (size_t)H * row_bytes(qtype, F);
     int maxf = F > Fs ? F : Fs;
     int maxr = H > maxf ? H : maxf;
 #ifdef _OPENMP
@@ -375,13 +421,14 @@ int fwref_forward(int T, int H, int E, int k, int F, int qtype, int Fs, int qtyp
             }
             for (int j = 0; j < k; ++j) {
                 int e = ids[(size_t)t * k + j];
-                expert_ffn(qtype, F, H, wg + e * expert_gu, wu + e * expert_gu,
-                           wd + e * expert_d, xf, y, row, a);
+                expert_ffn(qtype, F, H, wg, wu, wd, (size_t)E * F, (size_t)E * H,
+                           (size_t)e * F, (size_t)e * H, xf, y, row, a);
                 for (int h = 0; h < H; ++h)
                     acc[h] += (double)w[(size_t)t * k + j] * y[h];
             }
             if (Fs > 0) {
-                expert_ffn(qtype_s, Fs, H, sg, su, sd, xf, y, row, a);
+                expert_ffn(qtype_s, Fs, H, sg, su, sd, (size_t)Fs, (size_t)H, 0, 0, xf, y,
+                           row, a);
                 for (int h = 0; h < H; ++h)
                     acc[h] += y[h];
             }

@@ -16,10 +16,11 @@ LIB_PATH = os.environ.get("FWREF_LIB") or os.path.join(HERE, "liboracle.so")
 SRC_PATH = os.path.join(HERE, "fwref.c")
 
 REF_F32, REF_BF16 = 0, 1
-REF_Q8_0, REF_Q4_0, REF_Q4_K, REF_Q6_K = 0, 1, 2, 3
+REF_Q8_0, REF_Q4_0, REF_Q4_K, REF_Q6_K, REF_MXFP4 = 0, 1, 2, 3, 4
 REF_SOFTMAX, REF_SIGMOID = 0, 1
 DTYPE = {"f32": REF_F32, "bf16": REF_BF16}
-QTYPE = {"q8_0": REF_Q8_0, "q4_0": REF_Q4_0, "q4_k": REF_Q4_K, "q6_k": REF_Q6_K}
+QTYPE = {"q8_0": REF_Q8_0, "q4_0": REF_Q4_0, "q4_k": REF_Q4_K, "q6_k": REF_Q6_K,
+         "mxfp4": REF_MXFP4}
 SCORE = {"softmax": REF_SOFTMAX, "sigmoid": REF_SIGMOID}
 
 GCC_CMD = ["gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",

@@ -18,10 +18,36 @@ def _q4k_scales(sc):
     return s, m
 
 
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def mxfp4_matrix(buf, R, n):
+    """MLX MXFP4 matrix (R rows: R*n/2 code bytes, then R*n/32 E8M0 scales)
+    -> float64 [R, n]."""
+    buf = np.asarray(buf, dtype=np.uint8).reshape(-1)
+    codes = buf[:R * n // 2].reshape(R, n // 2).astype(np.int64)
+    sc = buf[R * n // 2:R * n // 2 + R * n // 32].reshape(R, n // 32).astype(np.float64)
+    q = np.stack([codes & 15, codes >> 4], axis=-1).reshape(R, n)
+    v = E2M1[q & 7] * np.where(q & 8, -1.0, 1.0)
+    scale = np.where(sc == 255, np.nan, np.exp2(sc - 127.0))
+    return v * np.repeat(scale, 32, axis=-1)
+
+
+def dequant_matrix(qtype, buf, R, n):
+    """A whole R x n matrix of any format -> float64 [R, n]."""
+    if qtype == "mxfp4":
+        return mxfp4_matrix(buf, R, n)
+    return dequant(qtype, np.asarray(buf, dtype=np.uint8).reshape(R, -1), n)
+
+
 def dequant(qtype, raw, n):
-    """raw uint8 [..., n/32*Bq] -> float64 [..., n]."""
+    """raw uint8 [..., n/32*Bq] -> float64 [..., n] (MXFP4: one row, its
+    codes then its scales)."""
     raw = np.asarray(raw, dtype=np.uint8)
     lead = raw.shape[:-1]
+    if qtype == "mxfp4":
+        assert not lead
+        return mxfp4_matrix(raw, 1, n)[0]
     if qtype == "q6_k":
         sb = raw.reshape(*lead, n // 256, 210)
         ql = sb[..., 0:128].astype(np.int64).reshape(*lead, n // 256, 2, 2, 32)   # [h][k%2][l]

@@ -342,3 +342,103 @@ def test_q6k_quantizer_error_bound(ref):
         err = np.abs(v - x[i]).reshape(2, 16, 16).max(axis=-1)
         assert np.all(err <= d[:, None] * np.abs(sc) + 1e-12), (i, err)
     assert not np.any(ref.dequant_row("q6_k", raw[0], 512)[:256])
+
+
+# MXFP4 (group 32, MLX packing).  No layout is printed and no outside encoder
+# is available: the oracle's decoding is pinned by hand-packed rows, by the
+# case that reduces to Q8_0, by every code at several scales, by the NaN
+# scale, and by the generator's error bound.
+
+GOLDEN_MX = os.path.join(os.path.dirname(__file__), "golden", "mxfp4_blocks.txt")
+E2M1 = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+        Fraction(4), Fraction(6)]
+
+
+def golden_mxfp4():
+    out = []
+    for line in open(GOLDEN_MX):
+        if line.startswith("#") or not line.strip():
+            continue
+        name, sc, rule, hx = [s.strip() for s in line.split("|")]
+        out.append((name, [int(v) for v in sc.split()], rule, bytes.fromhex(hx)))
+    return out
+
+
+def _e2m1(code):
+    v = E2M1[code & 7]
+    return -v if code & 8 else v
+
+
+@pytest.mark.parametrize("rec", golden_mxfp4(), ids=lambda r: r[0])
+def test_mxfp4_hand_packed_row(ref, rec):
+    name, sc, rule, raw = rec
+    assert len(raw) == 34 and len(sc) == 2 and rule in ("ramp", "rev")
+    want = []
+    for j in range(64):
+        code = j % 16 if rule == "ramp" else 15 - j % 16
+        want.append(float(_e2m1(code) * Fraction(2) ** (sc[j // 32] - 127)))
+    got = ref.dequant_row("mxfp4", np.frombuffer(raw, dtype=np.uint8), 64)
+    assert np.array_equal(got.astype(np.float64), np.array(want))
+    assert np.array_equal(np_ref.dequant("mxfp4", np.frombuffer(raw, dtype=np.uint8), 64),
+                          np.array(want))
+
+
+def _mx_row(codes, scales):
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.concatenate([(c[0::2] | (c[1::2] << 4)).astype(np.uint8),
+                           np.asarray(scales, dtype=np.uint8)])
+
+
+def _mx_want(code, s):
+    """The exact value as fp32 would hold it: 2^128 and beyond are infinite."""
+    v = _e2m1(code) * Fraction(2) ** (s - 127)
+    if abs(v) >= 2 ** 128:
+        return -np.inf if v < 0 else np.inf
+    return float(v)
+
+
+def test_mxfp4_every_code_and_scale(ref):
+    """Each code in each element slot (both nibbles) at scales 1, 126, 127,
+    128, 253 and 254 (where the larger values exceed fp32 and are infinite);
+    scale 255 decodes to NaN."""
+    for s in (1, 126, 127, 128, 253, 254):
+        for code in range(16):
+            for j0 in (0, 1, 30, 31):
+                codes = np.zeros(32, np.int64)
+                codes[j0] = code
+                v = ref.dequant_row("mxfp4", _mx_row(codes, [s]), 32)
+                assert v[j0] == _mx_want(code, s), (s, code, j0)
+                assert np.count_nonzero(np.delete(v, j0)) == 0
+    v = ref.dequant_row("mxfp4", _mx_row(np.full(32, 2), [255]), 32)
+    assert np.all(np.isnan(v))
+
+
+def test_mxfp4_reduces_to_q8_0(ref):
+    """Scale 127: the values are the E2M1 values themselves, the same as a
+    Q8_0 block with d = 1/2 and codes 2 * value."""
+    rng = np.random.default_rng(8)
+    codes = rng.integers(0, 16, 32)
+    got = ref.dequant_row("mxfp4", _mx_row(codes, [127]), 32)
+    q8 = np.array([int(2 * _e2m1(c)) for c in codes], dtype=np.int8)
+    blk = np.concatenate([np.array([0.5], np.float16).view(np.uint8), q8.view(np.uint8)])
+    assert np.array_equal(got, ref.dequant_row("q8_0", blk, 32))
+
+
+def test_mxfp4_quantizer_error_bound(ref):
+    """The generator's MXFP4 quantizer reproduces its input within two E2M1
+    steps of the group's scale (the largest spacing, 4 -> 6, halved, or the
+    clip of values in (6, 8) x 2^e to 6); the matrix layout decodes row by row
+    like single rows."""
+    w = moegen.normal((16, 256), 0.02, 9)
+    w[0, :32] = 0.0
+    w[1, 40] = 0.3
+    buf = moegen.quantize_mxfp4(w).numpy()
+    m = np_ref.mxfp4_matrix(buf, 16, 256)
+    x = w.numpy().astype(np.float64)
+    sc = buf[16 * 128:].reshape(16, 8).astype(np.float64)
+    for r in range(16):
+        row = np.concatenate([buf[r * 128:(r + 1) * 128], buf[2048 + r * 8:2048 + (r + 1) * 8]])
+        assert np.array_equal(ref.dequant_row("mxfp4", row, 256).astype(np.float64), m[r])
+    err = np.abs(m - x).reshape(16, 8, 32).max(axis=-1)
+    assert np.all(err <= 2.0 * np.exp2(sc - 127))
+    assert not np.any(m[0, :32])

@@ -103,7 +103,7 @@ def _layer(qtype="q4_0", H=512, F=256, E=4, shared=0, std=0.05):
 
 
 @pytest.mark.parametrize("H,F", [(512, 256), (256, 768)])
-@pytest.mark.parametrize("qtype", ["q8_0", "q4_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("qtype", ["q8_0", "q4_0", "q4_k", "q6_k", "mxfp4"])
 def test_single_expert_is_dense_swiglu_float64(ref, qtype, H, F):
     """E = 1, k = 1: the layer is the textbook dense FFN
     W_d (silu(W_g x) * (W_u x)); checked with numpy float64 matrix products on
@@ -113,9 +113,9 @@ def test_single_expert_is_dense_swiglu_float64(ref, qtype, H, F):
     out = ref.forward(x, L.w_gate.numpy(), L.w_up.numpy(), L.w_down.numpy(),
                       np.zeros((6, 1), np.int32), np.ones((6, 1), np.float32),
                       n_experts=1, ffn=cfg.ffn, qtype=qtype, act_dtype="bf16")
-    Wg = np_ref.dequant(qtype, L.w_gate.numpy()[0], cfg.hidden)
-    Wu = np_ref.dequant(qtype, L.w_up.numpy()[0], cfg.hidden)
-    Wd = np_ref.dequant(qtype, L.w_down.numpy()[0], cfg.ffn)
+    Wg = np_ref.dequant_matrix(qtype, L.w_gate.numpy(), cfg.ffn, cfg.hidden)
+    Wu = np_ref.dequant_matrix(qtype, L.w_up.numpy(), cfg.ffn, cfg.hidden)
+    Wd = np_ref.dequant_matrix(qtype, L.w_down.numpy(), cfg.hidden, cfg.ffn)
     X = np_ref.act(x)
     want = (np_ref.silu(X @ Wg.T) * (X @ Wu.T)) @ Wd.T
     np.testing.assert_allclose(out, want, rtol=0, atol=1e-6 * np.abs(want).max())
