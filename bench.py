@@ -55,6 +55,9 @@ WORKLOADS = {
     # and on Q6_K experts (210-byte super-blocks)
     "decode16_q6k": (moegen.QWEN3_DECODE.with_(expert_q=moegen.Q6_K), 16, 16),
     "prefill2048_q6k": (moegen.QWEN3_PREFILL.with_(expert_q=moegen.Q6_K), 2048, 4),
+    # and on MXFP4 experts (MLX packing, group 32)
+    "decode16_mxfp4": (moegen.QWEN3_DECODE.with_(expert_q=moegen.MXFP4), 16, 16),
+    "prefill2048_mxfp4": (moegen.QWEN3_PREFILL.with_(expert_q=moegen.MXFP4), 2048, 4),
     # and on Q8_0 experts (the sweep's other format)
     "decode16_q8": (moegen.QWEN3_DECODE.with_(expert_q=moegen.Q8_0), 16, 8),
     "prefill2048_q8": (moegen.QWEN3_PREFILL.with_(expert_q=moegen.Q8_0), 2048, 2),
@@ -548,7 +551,7 @@ def reduce_counters(a):
                         cfg.score, a.path)
     path_gemv = fw.fw_moe_forward_path(desc, T) == fw.FW_PATH_GEMV
     kernel = "gemv_kernel<gate/up>" if path_gemv else "gemm_kernel<gate/up>"
-    frag = KERNELS[kernel][1] + {"q8_0": "0", "q4_0": "1", "q4_k": "2", "q6_k": "3"}[cfg.expert_q] + "ELb1E"
+    frag = KERNELS[kernel][1] + {"q8_0": "0", "q4_0": "1", "q4_k": "2", "q6_k": "3", "mxfp4": "4"}[cfg.expert_q] + "ELb1E"
 
     def per_dispatch(d, counter, sub):
         vals = {}

@@ -89,7 +89,7 @@ enum {
 };
 
 enum { FW_F32 = 0, FW_BF16 = 1 };                 /* activation / router dtype */
-enum { FW_Q8_0 = 0, FW_Q4_0 = 1, FW_Q4_K = 2, FW_Q6_K = 3 };   /* expert weight format */
+enum { FW_Q8_0 = 0, FW_Q4_0 = 1, FW_Q4_K = 2, FW_Q6_K = 3, FW_MXFP4 = 4 };  /* weight format */
 enum { FW_SOFTMAX_RENORM = 0, FW_SIGMOID_RENORM = 1 };
 enum { FW_PATH_AUTO = 0, FW_PATH_GEMV = 1, FW_PATH_GEMM = 2 };
 
@@ -102,7 +102,7 @@ typedef struct {
     int32_t shared_ffn;   /* Fs: 0 = no shared expert, else multiple of 256        */
     int32_t act_dtype;    /* FW_F32 | FW_BF16: x                                   */
     int32_t router_dtype; /* FW_F32 | FW_BF16: router weights; must equal act_dtype */
-    int32_t expert_q;     /* FW_Q8_0 | FW_Q4_0 | FW_Q4_K | FW_Q6_K: routed experts */
+    int32_t expert_q;     /* FW_Q8_0 | FW_Q4_0 | FW_Q4_K | FW_Q6_K | FW_MXFP4       */
     int32_t shared_q;     /* same choices: shared expert (ignored if Fs = 0)      */
     int32_t score;        /* FW_SOFTMAX_RENORM | FW_SIGMOID_RENORM                 */
     int32_t path;         /* FW_PATH_*: forward kernel family (AUTO picks by T)    */
@@ -170,7 +170,12 @@ int fw_moe_permute(const fw_moe_desc *desc, int32_t T, const int32_t *topk_ids,
  * w_gate, w_up [E][F][H/32] blocks of expert_q;  w_down [E][H][F/32] blocks
  *          (Q4_K, Q6_K: [E][F][H/256] and [E][H][F/256] super-blocks, 144 or
  *          210 bytes each; a Q6_K row is 2-byte aligned when H/256 or F/256
- *          is not a multiple of 8, which the kernels handle)
+ *          is not a multiple of 8, which the kernels handle.  MXFP4 (MLX
+ *          packing, group 32; vOOM notes: expert-only MXFP4, --group-size
+ *          32): each projection is its E2M1 codes, [E][F][H/2] bytes
+ *          (element j in nibble j % 2 of byte j / 2, low first), followed in
+ *          the same buffer by its E8M0 scales, [E][F][H/32] bytes; value =
+ *          E2M1(code) * 2^(scale - 127).  Shared: [Fs][H/2] then [Fs][H/32].)
  * ws_gate, ws_up [Fs][H/32], ws_down [H][Fs/32] blocks of shared_q, or NULL
  *          when shared_ffn == 0 (all three required when shared_ffn > 0)
  * topk_w   [T][k] fp32;  expert_offsets, sorted_pairs, inv_pos as produced by
@@ -183,13 +188,14 @@ int fw_moe_permute(const fw_moe_desc *desc, int32_t T, const int32_t *topk_ids,
  * scaled back exactly before SwiGLU, h is held at 2^(2e) and the down
  * projection's sums are scaled back exactly), so a finite row of any
  * magnitude uses fp16's normal range like a unit-scale row.  The GEMV family (small T) multiplies the exact
- * weight codes (fp16 holds every Q8_0/Q4_0/Q4_K/Q6_K code) by fp16
- * activations in fp32 dot products and applies each block's scale (Q4_K:
- * each 32-element sub-block's d * scale, and dmin * min times the sub-block's
- * activation sum; Q6_K: each 16-element sub-block's d * scale) in fp32; the
- * GEMM family (large T) contracts on fp16 MFMA with weights dequantised to
- * fp16 (code times scale, or for Q4_K d * scale * q - dmin * min and for
- * Q6_K d * scale * (q - 32) formed in fp32; one rounding).  Either way a layer output stays within
+ * weight codes (fp16 holds every Q8_0/Q4_0/Q4_K/Q6_K code, and every E2M1
+ * value times 2^-14) by fp16 activations in fp32 dot products and applies
+ * each block's scale (Q4_K: each 32-element sub-block's d * scale, and dmin *
+ * min times the sub-block's activation sum; Q6_K: each 16-element
+ * sub-block's d * scale; MXFP4: 2^(scale - 113), exactly) in fp32; the GEMM
+ * family (large T) contracts on fp16 MFMA with weights dequantised to fp16
+ * (code times scale, or for Q4_K d * scale * q - dmin * min and for Q6_K
+ * d * scale * (q - 32) formed in fp32; one rounding; MXFP4 exactly).  Either way a layer output stays within
  * 2e-3 max-abs and 1e-3 relative L2 of an fp64 evaluation of the same layer
  * for unit-scale inputs like the workloads' (N(0,1) activations, weights of
  * std 0.015-0.02), and each token row within the same relative error at any
@@ -198,11 +204,14 @@ int fw_moe_permute(const fw_moe_desc *desc, int32_t T, const int32_t *topk_ids,
  * (very large weights), and, in the GEMM family, for a block scale above
  * 31.98 (Q8_0) or 511.75 (Q4_0) -- 16x the extreme code times the scale must
  * stay within fp16 -- a Q4_K sub-block whose 16 (15 |d scale| + |dmin
- * min|) exceeds 65504, or a Q6_K sub-block whose 512 |d scale| does.  The GEMV family has no weight limit (codes stay
+ * min|) exceeds 65504, a Q6_K sub-block whose 512 |d scale| does, or an
+ * MXFP4 scale above 136 (96 x 2^(scale - 127) beyond fp16; scale 255, NaN
+ * by the format, included).  The GEMV family has no weight limit (codes stay
  * exact, scales apply in fp32).
  * Q4_K and Q6_K (GGUF K-quants, 144- and 210-byte super-blocks of 256
  * elements) need H, F and Fs to be multiples of 256, which every descriptor
- * already is.
+ * already is.  MXFP4 requires the routed and shared matrices to be stored
+ * as above; a scale of 255 (NaN) gives non-finite outputs in the GEMV.
  * Batch limit: T * k * max(H, F, Fs) < 2^31 (the kernels' row offsets are
  * 32-bit element counts); a larger batch returns FW_EINVAL before anything
  * is enqueued and is to be split by the caller (DeepSeek-shaped layer:

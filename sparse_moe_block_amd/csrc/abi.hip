@@ -67,8 +67,8 @@ int check_desc(const fw_moe_desc *d) {
     if (d->shared_ffn < 0 || d->shared_ffn > 16384 || d->shared_ffn % 256) return FW_EINVAL;
     if (d->act_dtype != FW_F32 && d->act_dtype != FW_BF16) return FW_EINVAL;
     if (d->router_dtype != FW_F32 && d->router_dtype != FW_BF16) return FW_EINVAL;
-    if (d->expert_q < FW_Q8_0 || d->expert_q > FW_Q6_K) return FW_EINVAL;
-    if (d->shared_q < FW_Q8_0 || d->shared_q > FW_Q6_K) return FW_EINVAL;
+    if (d->expert_q < FW_Q8_0 || d->expert_q > FW_MXFP4) return FW_EINVAL;
+    if (d->shared_q < FW_Q8_0 || d->shared_q > FW_MXFP4) return FW_EINVAL;
     if (d->score != FW_SOFTMAX_RENORM && d->score != FW_SIGMOID_RENORM) return FW_EINVAL;
     if (d->path < FW_PATH_AUTO || d->path > FW_PATH_GEMM) return FW_EINVAL;
     if (d->router_dtype != d->act_dtype) return FW_EUNSUPPORTED;

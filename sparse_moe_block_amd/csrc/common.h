@@ -112,6 +112,15 @@ template <> struct QT<FW_Q6_K> {
     static constexpr int kUnitBytes = 210, kUnitX4 = 14;
     static constexpr size_t row_bytes(int K) { return (size_t)(K / 256) * kUnitBytes; }
 };
+// MXFP4 (MLX packing, group 32): a matrix of R rows is R x K/2 bytes of E2M1
+// codes (element j in nibble j % 2 of byte j / 2) followed by R x K/32 E8M0
+// scale bytes.  Rows here are code rows (row_bytes); a row's scales sit at
+// the matrix base + R K/2 + row K/32.  A unit is the 128 code bytes of 256
+// elements plus the 16-byte aligned piece holding its 8 scales (kUnitX4 = 9).
+template <> struct QT<FW_MXFP4> {
+    static constexpr int kUnitBytes = 128, kUnitX4 = 9;
+    static constexpr size_t row_bytes(int K) { return (size_t)K / 2; }
+};
 
 
 // Uniform read of data no kernel writes while the reader runs (schedules,

@@ -67,6 +67,11 @@ struct Tile {
     // region its piece covers (unit 0) and the piece's offset in that region;
     // per column group, the offset of the lane's own row
     uint32_t q6s[2][kQ6PX], q6e[2][kQ6PX], q6p[kQ6PX], q6r[2];
+    // MXFP4: 16-byte aligned bases of the two matrices' scales (their own
+    // offset mod 16 is in the offsets) and, per column group, the offset of
+    // the lane's own row's scales
+    const uint8_t *sbase[2];
+    uint32_t mxs[2];
     _Float16 *hout;
     float *yout;
     const int32_t *s_ex;     // LDS: each tile row's exponent
@@ -83,6 +88,9 @@ struct Tile {
 // Q6_K's half is four separate regions at a 2-byte aligned row offset: its
 // 64 ql bytes (5 pieces), 32 qh bytes (3), and from its 8 scales to the
 // unit's end (2): kQ6PX pieces, a region's spare pieces repeating its last.
+// MXFP4's half is its 64 code bytes (4 pieces) plus the aligned piece
+// holding its scales; a buffer keeps all rows' code pieces first and the
+// scale pieces after them, so that every DMA instruction reads one kind.
 template <int Q> constexpr int half_pieces() {
     return Q == FW_Q8_0 ? 9 : Q == FW_Q6_K ? kQ6PX : 5;
 }
@@ -188,8 +196,20 @@ __device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 
         if (i < PX) {
             const int h = st & 1;
             const uint8_t *base = GU && (NW * i + wave >= NW * PX / 2) ? c.bbase[1] : c.bbase[0];
-            uint32_t off;
-            if constexpr (Q == FW_Q6_K) {
+            uint32_t off = 0;
+            if constexpr (Q == FW_MXFP4) {
+                // code pieces: rows' 64 code bytes of the half; scale
+                // pieces: the aligned piece holding the unit's 8 scales
+                const int j = NW * i + wave;
+                const uint32_t u = (uint32_t)(st >> 1);
+                if (j < 4 * NW) {
+                    base = GU && j >= 2 * NW ? c.bbase[1] : c.bbase[0];
+                    off = c.woff[i] + 128u * u + 64u * (uint32_t)h;
+                } else {
+                    base = GU && 2 * j >= 9 * NW ? c.sbase[1] : c.sbase[0];
+                    off = (c.woff[i] + 8u * u) & ~15u;
+                }
+            } else if constexpr (Q == FW_Q6_K) {
                 // the piece's aligned address, clamped to its region's last
                 // piece: every piece holds a byte of its region
                 const uint32_t uo = (uint32_t)(st >> 1) * UB;
@@ -211,7 +231,20 @@ __device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 
     // the windows of step st (half st % 2) from buffer buf
     auto read_w = [&](const uint4 *buf, int st) {
         const int h = st & 1;
-        if constexpr (Q == FW_Q6_K) {
+        if constexpr (Q == FW_MXFP4) {
+            // codes of LDS row Rl at 64 Rl, its scale piece at 16 (256 NW + Rl)
+#pragma unroll
+            for (int cg = 0; cg < 2; ++cg) {
+                const int Rl = lds_wrow<GU, NW>(wave, cg, n);
+                const uint4 *cd = (const uint4 *)((const uint8_t *)buf + 64 * Rl + 32 * g);
+                const uint4 q0 = cd[0], q1 = cd[1];
+                wh[cg][0] = q0.x; wh[cg][1] = q0.y; wh[cg][2] = q0.z; wh[cg][3] = q0.w;
+                wh[cg][4] = q1.x; wh[cg][5] = q1.y; wh[cg][6] = q1.z; wh[cg][7] = q1.w;
+                const uint32_t sub = (c.mxs[cg] + 8u * (uint32_t)(st >> 1)) & 15u;
+                wh[cg][8] = *(const uint32_t *)((const uint8_t *)buf + 16 * (256 * NW + Rl) +
+                                                sub + 4 * h) >> (16 * g);
+            }
+        } else if constexpr (Q == FW_Q6_K) {
             const uint32_t uo = (uint32_t)(st >> 1) * UB;
             lds_window<Q>((const uint8_t *)buf + wr0, h, g, wh[0], (c.q6r[0] + uo) & 15u);
             lds_window<Q>((const uint8_t *)buf + wr1, h, g, wh[1], (c.q6r[1] + uo) & 15u);
@@ -248,6 +281,9 @@ __device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 
                 q6k_consts(wh[cg], kq[cg]);
                 wmax = fmaxf(wmax, q6k_bound(kq[cg]));
             }
+        } else if constexpr (Q == FW_MXFP4) {
+#pragma unroll
+            for (int cg = 0; cg < 2; ++cg) wmax = fmaxf(wmax, mx_consts(wh[cg], kq[cg]));
         } else {
 #pragma unroll
             for (int cg = 0; cg < 2; ++cg) dmax = max(dmax, d_bits<Q>(wh[cg]));
@@ -330,7 +366,7 @@ __device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 
     // ---- epilogue: acc[mi][cg][v] is tile row 32 mi + 8 (v / 4) + 4 g + v % 4,
     // weight row (column group cg) n ----
     const int rows = c.rows, rb = c.rb, N = c.N;
-    bool range = (Q == FW_Q4_K || Q == FW_Q6_K)
+    bool range = (Q == FW_Q4_K || Q == FW_Q6_K || Q == FW_MXFP4)
                      ? !(wmax <= 65504.0f)
                      : dmax > (Q == FW_Q4_0 ? kQ4DMaxBits : kQ8DMaxBits);
     if constexpr (GU) {
@@ -388,7 +424,9 @@ __device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 
 // column counts eight waves do not divide and Q8_0, whose wider windows and
 // 272-byte units need the registers and the LDS.
 template <int Q, int NW> constexpr int waves_per_simd() { return NW == 8 ? 2 : 1; }
-template <int Q> constexpr bool eight_waves() { return Q == FW_Q4_0 || Q == FW_Q4_K; }
+template <int Q> constexpr bool eight_waves() {
+    return Q == FW_Q4_0 || Q == FW_Q4_K || Q == FW_MXFP4;
+}
 
 template <int Q, bool GU, int NW>
 __global__ __launch_bounds__(64 * NW, (waves_per_simd<Q, NW>() * 4 / NW)) void gemm_kernel(
@@ -397,7 +435,7 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<Q, NW>() * 4 / NW)) void g
     const int32_t *__restrict__ sorted, const _Float16 *__restrict__ ain,
     _Float16 *__restrict__ hout, float *__restrict__ yout, int K, int N, int k, int P,
     int col_tiles, int n_row_tiles_max, int shared, int shared_rows,
-    const int32_t *__restrict__ iexp, int32_t *__restrict__ oexp) {
+    const int32_t *__restrict__ iexp, int32_t *__restrict__ oexp, size_t sreg) {
     constexpr int PX = half_pieces<Q>();
     __shared__ uint4 A0[kChunks];
     __shared__ uint4 A1[kChunks];
@@ -472,7 +510,44 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<Q, NW>() * 4 / NW)) void g
     // weight piece of DMA instruction i: LDS piece p = i kThreads + tid is
     // piece p % PX of LDS row p / PX (gate/up: rows from 32 NW on are the up
     // matrix's, read from bbase[1])
-    if constexpr (Q == FW_Q6_K) {
+    if constexpr (Q == FW_MXFP4) {
+        // codes: the expert's matrix rows of K / 2 bytes; scales: rows of
+        // K / 32 bytes from sreg bytes into each matrix
+        c.bbase[0] = ba;
+        c.bbase[1] = bb;
+        const uint8_t *sa0 = wa + sreg + (size_t)expert * N * (K / 32);
+        const uint8_t *sb0 = (GU ? wb : wa) + sreg + (size_t)expert * N * (K / 32);
+        const uint32_t smis[2] = {(uint32_t)(uintptr_t)sa0 & 15u, (uint32_t)(uintptr_t)sb0 & 15u};
+        c.sbase[0] = sa0 - smis[0];
+        c.sbase[1] = sb0 - smis[1];
+#pragma unroll
+        for (int i = 0; i < PX; ++i) {
+            const int p = i * kThreads + tid;
+            int Rl, m = 0;
+            uint32_t piece = 0;
+            const bool code = p < 256 * NW;
+            if (code) {
+                Rl = p / 4;
+                piece = p % 4;
+            } else {
+                Rl = p - 256 * NW;
+            }
+            if (GU && Rl >= 32 * NW) {
+                Rl -= 32 * NW;
+                m = 1;
+            }
+            const int row = GU ? ct * (32 * NW) + Rl : ct * (64 * NW) + Rl;
+            c.woff[i] = code ? (uint32_t)row * (uint32_t)(K / 2) + 16u * piece
+                             : smis[m] + (uint32_t)row * (uint32_t)(K / 32);
+        }
+        const int n = c.lane & 31;
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg) {
+            const int row = GU ? ct * (32 * NW) + 32 * c.wave + n
+                               : ct * (64 * NW) + 64 * c.wave + 32 * cg + n;
+            c.mxs[cg] = smis[GU ? cg : 0] + (uint32_t)row * (uint32_t)(K / 32);
+        }
+    } else if constexpr (Q == FW_Q6_K) {
         // 16-byte aligned bases; offsets carry the matrices' own misalignment
         const uint32_t mis[2] = {(uint32_t)(uintptr_t)ba & 15u, (uint32_t)(uintptr_t)bb & 15u};
         c.bbase[0] = ba - mis[0];
@@ -552,7 +627,8 @@ void launch_nw(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Fl
     const int nblk = (row_tiles + 7) / 8 * 8 * col_tiles;   // eight XCDs x whole row tiles
     gemm_kernel<Q, GU, NW><<<nblk, 64 * NW, 0, s>>>(
         wa, wb, (const int4 *)(a.ws + a.L.tiles), (WsHeader *)a.ws, a.sorted, ain, hout, yout,
-        K, N, a.d.top_k, a.P, col_tiles, row_tiles, shared, shared ? a.T : 0, iexp, oexp);
+        K, N, a.d.top_k, a.P, col_tiles, row_tiles, shared, shared ? a.T : 0, iexp, oexp,
+        (size_t)(shared ? 1 : a.d.n_experts) * N * (size_t)(K / 2));
 }
 
 // Eight-wave workgroups wherever the format allows and the columns divide
@@ -580,6 +656,8 @@ void launch_q(int q, const FwdArgs &a, const uint8_t *wa, const uint8_t *wb,
         launch<FW_Q4_K, GU>(a, wa, wb, ain, hout, yout, K, N, shared, iexp, oexp, s);
     else if (q == FW_Q6_K)
         launch<FW_Q6_K, GU>(a, wa, wb, ain, hout, yout, K, N, shared, iexp, oexp, s);
+    else if (q == FW_MXFP4)
+        launch<FW_MXFP4, GU>(a, wa, wb, ain, hout, yout, K, N, shared, iexp, oexp, s);
     else
         launch<FW_Q8_0, GU>(a, wa, wb, ain, hout, yout, K, N, shared, iexp, oexp, s);
 }

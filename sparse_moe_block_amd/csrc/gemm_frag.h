@@ -15,8 +15,10 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 // Q6_K: 8 ql dwords (the lane group's 32 bytes of the half's low bits), 8
 // qh dwords (the half's top bits, shifted right by 2g), the half's 8 scales
 // (2 dwords, shifted right by 16g) and d.
+// MXFP4: 8 code dwords (blocks 2g, 2g + 1 of the half) and the half's four
+// scale bytes, shifted right by 16g.
 template <int Q> constexpr int win_dwords() {
-    return Q == FW_Q4_0 ? 9 : Q == FW_Q4_K ? 12 : Q == FW_Q6_K ? 19 : 17;
+    return Q == FW_Q4_0 ? 9 : Q == FW_Q4_K ? 12 : Q == FW_Q6_K ? 19 : Q == FW_MXFP4 ? 9 : 17;
 }
 
 // Per-step constants of a Q4_K window (sub-blocks A = 2g, B = 2g + 1 of the
@@ -193,13 +195,65 @@ __device__ __forceinline__ h8 frag_b_q6k(const uint32_t *w, const uint32_t *k) {
     return f;
 }
 
-// B fragment of slice I of any format (kq: the Q4_K / Q6_K per-step constants).
+// Per-step constants of an MXFP4 window: for the lane group's blocks
+// b = 0, 1, k[2b] = 2^(scale_b - 127) and k[2b + 1] = 16 times that, each as
+// an fp16 pair (exact: a normal or subnormal power of two while scale_b is
+// 103 .. 142).  Returns the bound 96 * 2^(scale - 127) on the magnitude of
+// the window's fp16 weights.
+__device__ __forceinline__ float mx_consts(const uint32_t *w, uint32_t *k) {
+    float b = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int e = (int)__builtin_amdgcn_ubfe(w[8], 8 * i, 8) - 127;
+        const uint32_t c = __builtin_bit_cast(uint16_t, (_Float16)__builtin_amdgcn_ldexpf(1.0f, e));
+        const uint32_t c16 =
+            __builtin_bit_cast(uint16_t, (_Float16)__builtin_amdgcn_ldexpf(1.0f, e + 4));
+        k[2 * i] = c | c << 16;
+        k[2 * i + 1] = c16 | c16 << 16;
+        b = fmaxf(b, __builtin_amdgcn_ldexpf(96.0f, e));
+    }
+    return b;
+}
+
+// B fragment of slice I from an MXFP4 window: block I / 4 of the lane's two,
+// pairs 4 (I % 4) .. + 3.  Each pair's two nibbles (bytes 2m, 2m + 1 of the
+// block's first or second 16 bytes, low nibbles for pairs j = 0, 1) become
+// fp16 E2M1 / 2^14 (magnitude bits at 11..9, sign at 15), times 2^14 (the
+// exact E2M1 value) and the block's power of two (x 16 for j = 1, 3): exact
+// while the result stays within fp16.
+template <int I>
+__device__ __forceinline__ h8 frag_b_mxfp4(const uint32_t *w, const uint32_t *k) {
+    constexpr int B = I / 4, m = I % 4;
+    constexpr uint32_t sel = (m & 1) ? 0x0C030C02u : 0x0C010C00u;
+    const uint32_t g0 = __builtin_amdgcn_perm(0u, w[4 * B + m / 2], sel);
+    const uint32_t g1 = __builtin_amdgcn_perm(0u, w[4 * B + 2 + m / 2], sel);
+    const h2 k14 = {(_Float16)16384.0f, (_Float16)16384.0f};
+    const h2 c = as_h2(k[2 * B]), c16 = as_h2(k[2 * B + 1]);
+    const h2 p0 = as_h2(((g0 << 9) & 0x0E000E00u) | ((g0 << 12) & 0x80008000u)) * k14 * c;
+    const h2 p1 = as_h2(((g1 << 9) & 0x0E000E00u) | ((g1 << 12) & 0x80008000u)) * k14 * c16;
+    const h2 p2 = as_h2(((g0 << 5) & 0x0E000E00u) | ((g0 << 8) & 0x80008000u)) * k14 * c;
+    const h2 p3 = as_h2(((g1 << 5) & 0x0E000E00u) | ((g1 << 8) & 0x80008000u)) * k14 * c16;
+    h8 f;
+    f[0] = p0[0];
+    f[1] = p0[1];
+    f[2] = p1[0];
+    f[3] = p1[1];
+    f[4] = p2[0];
+    f[5] = p2[1];
+    f[6] = p3[0];
+    f[7] = p3[1];
+    return f;
+}
+
+// B fragment of slice I of any format (kq: the Q4_K / Q6_K / MXFP4 per-step constants).
 template <int Q, int I>
 __device__ __forceinline__ h8 frag_any(const uint32_t *w, const uint32_t *kq) {
     if constexpr (Q == FW_Q4_K)
         return frag_b_q4k<I>(w, kq);
     else if constexpr (Q == FW_Q6_K)
         return frag_b_q6k<I>(w, kq);
+    else if constexpr (Q == FW_MXFP4)
+        return frag_b_mxfp4<I>(w, kq);
     else
         return frag_b<Q, I>(w);
 }

@@ -49,8 +49,23 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 // c = 64 i + lane, chunk c being piece c % X4 of row c / X4.
 template <int Q>
 __device__ __forceinline__ void stage_unit(uint4 *buf, const uint8_t *tile, uint32_t rowbytes,
-                                           int u, int lane) {
+                                           int u, int lane, const uint8_t *stile = nullptr) {
     constexpr int X4 = QT<Q>::kUnitX4;
+    if constexpr (Q == FW_MXFP4) {
+        // pieces 0..7: the row's 128 code bytes of unit u; piece 8: the
+        // 16-byte aligned piece holding its 8 scales (stile: the tile's first
+        // scale row, 8-byte aligned; rows of rowbytes / 16 scale bytes)
+#pragma unroll
+        for (int i = 0; i < X4; ++i) {
+            const uint32_t c = i * kWave + lane, row = c / X4, piece = c % X4;
+            const uint8_t *src =
+                piece < 8 ? tile + (row * rowbytes + (uint32_t)u * 128u + piece * 16)
+                          : (const uint8_t *)((uintptr_t)(stile + row * (rowbytes / 16) + 8u * u) &
+                                              ~(uintptr_t)15);
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + i * kWave), 16, 0, 0);
+        }
+        return;
+    }
     if constexpr (Q == FW_Q6_K) {
         // 2-byte aligned units: row r's unit starts at byte o_r = mis + r *
         // rowbytes + 210 u of the 16-byte aligned base below the tile; its 14
@@ -340,6 +355,69 @@ __device__ __forceinline__ void dot_unit_q6k(const uint32_t *w, int u, cu32 *con
 #undef FW_Q6B
 }
 
+// MXFP4 unit: w[0..31] the 128 code bytes (block B in w[4B .. 4B + 3],
+// element j of a block in nibble j % 2 of byte j / 2), the unit's 8 scales
+// in w[so], w[so + 1].  Pair 4m + j takes bytes 2m, 2m + 1 of the block's
+// first (j = 0, 2) or second (j = 1, 3) 16 bytes, low nibbles for j < 2.  A
+// nibble becomes the fp16 whose bits 11..9 are the code's magnitude bits and
+// bit 15 its sign: exactly E2M1(code) * 2^-14 (the two smallest magnitudes
+// land on fp16 subnormals, 0 and 2^-15).  The exact products meet the
+// activations in fp32 dot sums, and the block's 2^(scale - 127) (x 2^14, and
+// x 16 for pairs j = 1, 3) applies once, exactly, by ldexp.
+__device__ __forceinline__ uint32_t e2m1_pair_lo(uint32_t g) {   // nibbles at bits 0, 16
+    return and_or(g << 9, 0x0E000E00u, (g << 12) & 0x80008000u);
+}
+__device__ __forceinline__ uint32_t e2m1_pair_hi(uint32_t g) {   // nibbles at bits 4, 20
+    return and_or(g << 5, 0x0E000E00u, (g << 8) & 0x80008000u);
+}
+
+template <int NTK>
+__device__ __forceinline__ void dot_unit_mxfp4(const uint32_t *w, int u, cu32 *const *in,
+                                               float *acc, int so) {
+    const uint32_t sc0 = so ? w[34] : w[32], sc1 = so ? w[35] : w[33];
+    constexpr int NB = x_sets<NTK>();
+    uint32_t xs[NB][NTK][16];
+#pragma unroll
+    for (int j = 0; j < NB - 1; ++j) load_x<NTK>(xs[j], in, u, j);
+#define FW_MXB(B)                                                                        \
+    {                                                                                    \
+        if (B + NB - 1 < 8) load_x<NTK>(xs[(B + NB - 1) % NB], in, u, B + NB - 1);       \
+        const uint32_t(*X)[16] = xs[B % NB];                                             \
+        h2 p[16];                                                                        \
+        _Pragma("unroll") for (int m = 0; m < 4; ++m) {                                  \
+            /* bytes 2m, 2m + 1 of the block's halves moved to bytes 0 and 2 */          \
+            const uint32_t sel = (m & 1) ? 0x0C030C02u : 0x0C010C00u;                    \
+            const uint32_t g0 = __builtin_amdgcn_perm(0u, w[4 * (B) + m / 2], sel);      \
+            const uint32_t g1 = __builtin_amdgcn_perm(0u, w[4 * (B) + 2 + m / 2], sel);  \
+            p[4 * m + 0] = as_h2(e2m1_pair_lo(g0));                                      \
+            p[4 * m + 1] = as_h2(e2m1_pair_lo(g1));                                      \
+            p[4 * m + 2] = as_h2(e2m1_pair_hi(g0));                                      \
+            p[4 * m + 3] = as_h2(e2m1_pair_hi(g1));                                      \
+        }                                                                                \
+        const int ex = (int)__builtin_amdgcn_ubfe((B) < 4 ? sc0 : sc1, 8 * ((B) & 3), 8) - 113; \
+        _Pragma("unroll") for (int n = 0; n < NTK; ++n) {                                \
+            float lo = 0.f, hi = 0.f;                                                    \
+            _Pragma("unroll") for (int m = 0; m < 4; ++m) {                              \
+                lo = __builtin_amdgcn_fdot2(p[4 * m + 0], as_h2(X[n][4 * m + 0]), lo, false); \
+                lo = __builtin_amdgcn_fdot2(p[4 * m + 2], as_h2(X[n][4 * m + 2]), lo, false); \
+                hi = __builtin_amdgcn_fdot2(p[4 * m + 1], as_h2(X[n][4 * m + 1]), hi, false); \
+                hi = __builtin_amdgcn_fdot2(p[4 * m + 3], as_h2(X[n][4 * m + 3]), hi, false); \
+            }                                                                            \
+            acc[n] += __builtin_amdgcn_ldexpf(lo, ex) + __builtin_amdgcn_ldexpf(hi, ex + 4); \
+        }                                                                                \
+    }                                                                                    \
+    __builtin_amdgcn_sched_barrier(0);
+    FW_MXB(0)
+    FW_MXB(1)
+    FW_MXB(2)
+    FW_MXB(3)
+    FW_MXB(4)
+    FW_MXB(5)
+    FW_MXB(6)
+    FW_MXB(7)
+#undef FW_MXB
+}
+
 template <int Q, int NTK>
 __device__ __forceinline__ void dot_unit(const uint32_t *w, int u, cu32 *const *in,
                                          cu32 *const *sum, float *acc) {
@@ -447,7 +525,7 @@ __global__ __launch_bounds__(kWave *S) void gemv_kernel(
     _Float16 *__restrict__ hout, float *__restrict__ yout, int K, int N, int k, int P,
     int tpg, int max_chunks, int shared, int shared_rows, int ks, int *__restrict__ split_cnt,
     float *__restrict__ split_part, const float *__restrict__ isum, float *__restrict__ osum,
-    const int32_t *__restrict__ iexp, int32_t *__restrict__ oexp) {
+    const int32_t *__restrict__ iexp, int32_t *__restrict__ oexp, size_t sreg) {
     constexpr int X4 = QT<Q>::kUnitX4;
     constexpr int NV = GU ? 2 : 1;
     constexpr int NT = kGemvTokens;
@@ -470,6 +548,11 @@ __global__ __launch_bounds__(kWave *S) void gemv_kernel(
     const int nb = NV * (us / S);           // batches per wavefront per item
     const int total = my_items * nb;
     const uint32_t rb32 = (uint32_t)rowbytes;
+    // MXFP4: a tile's first scale row, from its first code row (row bytes K/2
+    // of codes, K/32 of scales; the scales of a matrix start sreg bytes in)
+    auto scale_tile = [&](const uint8_t *mat, const uint8_t *tile) {
+        return Q == FW_MXFP4 ? mat + sreg + (size_t)(tile - mat) / 16 : nullptr;
+    };
     // staging cursor: batch js overall, bs within its item (D ahead of use);
     // only the item's two weight tiles are needed to stage
     int js = 0, is_ = 0, bs = 0;
@@ -483,7 +566,8 @@ __global__ __launch_bounds__(kWave *S) void gemv_kernel(
             tile_bases((g0 + is_ * G) / ks, wa, wbb, tiles, rowbytes, esz, tpg, shared, sa, sb); \
         }                                                                                   \
         stage_unit<Q>(stage[wave][js % D], (NV == 2 && (bs & 1)) ? sb : sa, rb32,           \
-                      ((g0 + is_ * G) % ks) * us + wave + (bs / NV) * S, lane);             \
+                      ((g0 + is_ * G) % ks) * us + wave + (bs / NV) * S, lane,              \
+                      (NV == 2 && (bs & 1)) ? scale_tile(wbb, sb) : scale_tile(wa, sa));    \
         ++bs;                                                                               \
         ++js;                                                                               \
     } while (0)
@@ -503,6 +587,12 @@ __global__ __launch_bounds__(kWave *S) void gemv_kernel(
         for (int b = 0; b < nb; ++b, ++j) {
             uint32_t w[4 * X4];
             const int u = slice * us + wave + (b / NV) * S;
+            int so = 0;   // MXFP4: the dword of the scale piece holding the unit's scales
+            if constexpr (Q == FW_MXFP4) {
+                const uint8_t *st = (NV == 2 && (b & 1)) ? scale_tile(wbb, it.tb)
+                                                         : scale_tile(wa, it.ta);
+                so = (int)(((uintptr_t)st + (uint32_t)lane * (rb32 / 16) + 8u * (uint32_t)u) >> 2) & 2;
+            }
             if constexpr (Q == FW_Q6_K) {
                 const uint8_t *tl = (NV == 2 && (b & 1)) ? it.tb : it.ta;
                 const uint32_t sub =
@@ -513,8 +603,13 @@ __global__ __launch_bounds__(kWave *S) void gemv_kernel(
             }
             if (js < total) FW_STAGE_NEXT();
             float *a = acc[NV == 2 ? (b & 1) : 0];
-            if (it.nt == 1) dot_unit<Q, 1>(w, u, it.in, it.sum, a);
-            else dot_unit<Q, 2>(w, u, it.in, it.sum, a);
+            if constexpr (Q == FW_MXFP4) {
+                if (it.nt == 1) dot_unit_mxfp4<1>(w, u, it.in, a, so);
+                else dot_unit_mxfp4<2>(w, u, it.in, a, so);
+            } else {
+                if (it.nt == 1) dot_unit<Q, 1>(w, u, it.in, it.sum, a);
+                else dot_unit<Q, 2>(w, u, it.in, it.sum, a);
+            }
         }
         // partial sums of waves 1..S-1 meet wave 0's in LDS, added in wave order
         if (S > 1) {
@@ -667,7 +762,8 @@ void launch_sd(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Fl
         wa, wb, (const int4 *)(a.ws + a.L.tiles), (WsHeader *)a.ws, a.sorted, xin, hout, yout,
         K, N, a.d.top_k, a.P, tpg, max_chunks, shared, shared ? a.T : 0, ks,
         (int *)(a.ws + a.L.split_cnt),
-        (float *)(a.ws + a.L.split_part), isum, osum, iexp, oexp);
+        (float *)(a.ws + a.L.split_part), isum, osum, iexp, oexp,
+        (size_t)(shared ? 1 : a.d.n_experts) * N * (size_t)(K / 2));
 }
 
 // LDS is the in-flight buffer: about 144 KB of DMA batches per CU keeps HBM
@@ -744,9 +840,12 @@ void launch_q(int q, const FwdArgs &a, const uint8_t *wa, const uint8_t *wb,
     else if (q == FW_Q4_K)
         launch<FW_Q4_K, GU>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, isum, osum,
                             iexp, oexp, s);
-    else
+    else if (q == FW_Q6_K)
         launch<FW_Q6_K, GU>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, nullptr,
                             nullptr, iexp, oexp, s);
+    else
+        launch<FW_MXFP4, GU>(a, wa, wb, xin, hout, yout, K, N, max_chunks, shared, nullptr,
+                             nullptr, iexp, oexp, s);
 }
 
 // Block sums: x rows (prepare), then h rows of the routed pairs [P][F/32]

@@ -15,14 +15,15 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfwmoe.so
 FW_OK, FW_EINVAL, FW_EUNSUPPORTED, FW_EWORKSPACE, FW_EALIGN, FW_EHIP = 0, -1, -2, -3, -4, -5
 FW_STATUS_BAD_EXPERT_ID, FW_STATUS_BAD_OFFSETS, FW_STATUS_BAD_PAIR, FW_STATUS_RANGE = 1, 2, 4, 8
 FW_F32, FW_BF16 = 0, 1
-FW_Q8_0, FW_Q4_0, FW_Q4_K, FW_Q6_K = 0, 1, 2, 3
+FW_Q8_0, FW_Q4_0, FW_Q4_K, FW_Q6_K, FW_MXFP4 = 0, 1, 2, 3, 4
 FW_SOFTMAX_RENORM, FW_SIGMOID_RENORM = 0, 1
 FW_PATH_AUTO, FW_PATH_GEMV, FW_PATH_GEMM = 0, 1, 2
 FW_N_STAGE_EVENTS = 5
 FW_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 DTYPES = {"f32": FW_F32, "bf16": FW_BF16}
-QTYPES = {"q8_0": FW_Q8_0, "q4_0": FW_Q4_0, "q4_k": FW_Q4_K, "q6_k": FW_Q6_K}
+QTYPES = {"q8_0": FW_Q8_0, "q4_0": FW_Q4_0, "q4_k": FW_Q4_K, "q6_k": FW_Q6_K,
+          "mxfp4": FW_MXFP4}
 SCORES = {"softmax": FW_SOFTMAX_RENORM, "sigmoid": FW_SIGMOID_RENORM}
 PATHS = {"auto": FW_PATH_AUTO, "gemv": FW_PATH_GEMV, "gemm": FW_PATH_GEMM}
 

@@ -38,7 +38,7 @@ def good_desc(**kw):
 @pytest.mark.parametrize("field,value", [
     ("hidden", 300), ("hidden", 0), ("hidden", 16640), ("n_experts", 0), ("n_experts", 513),
     ("top_k", 0), ("top_k", 17), ("ffn", 100), ("ffn", 0), ("act_dtype", 7), ("expert_q", 5),
-    ("expert_q", 4), ("expert_q", -1), ("shared_q", 4), ("score", 3)])
+    ("expert_q", 5), ("expert_q", -1), ("shared_q", 5), ("score", 3)])
 def test_invalid_descriptors(field, value):
     d = good_desc()
     setattr(d, field, value)
@@ -57,7 +57,9 @@ def test_top_k_above_experts_and_mixed_dtypes():
                                         shared_q="q4_k")) == fw.FW_OK
     assert fw.fw_moe_validate(good_desc(expert_q="q6_k", shared_ffn=2048,
                                         shared_q="q6_k")) == fw.FW_OK
-    assert fw.fw_moe_validate(good_desc(expert_q=4)) == fw.FW_EINVAL
+    assert fw.fw_moe_validate(good_desc(expert_q="mxfp4", shared_ffn=2048,
+                                        shared_q="mxfp4")) == fw.FW_OK
+    assert fw.fw_moe_validate(good_desc(expert_q=5)) == fw.FW_EINVAL
 
 
 def test_workspace_size_grows_with_T():

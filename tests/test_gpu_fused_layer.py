@@ -36,6 +36,8 @@ CASES = [
     (C.QWEN3_PREFILL.with_(expert_q=C.Q4_K), 2048, "auto"),
     (C.QWEN3_DECODE.with_(expert_q=C.Q6_K), 16, "auto"),
     (C.QWEN3_PREFILL.with_(expert_q=C.Q6_K), 2048, "auto"),
+    (C.QWEN3_DECODE.with_(expert_q=C.MXFP4), 16, "auto"),
+    (C.QWEN3_PREFILL.with_(expert_q=C.MXFP4), 2048, "auto"),
 ]
 IDS = [f"c{c.cid}-{c.expert_q}-T{T}-{p}" for c, T, p in CASES]
 

@@ -6,7 +6,7 @@ taken back out exactly), so rows of any finite magnitude keep the accuracy of a
 unit-scale row; what fp16 still cannot hold sets FW_STATUS_RANGE.  Checked
 here against the CPU oracle on the same bytes:
   - token rows whose magnitudes span 1e-6 .. 1e5, through both families and
-    all four expert formats: each row within the layer's relative accuracy;
+    all five expert formats: each row within the layer's relative accuracy;
   - the edge blocks of the pinned block-decode fixtures (subnormal and
     negative scales, the extreme codes -128 / 0 / 15) placed in routed expert
     weights: in range, so within the layer tolerance and no status bit;
@@ -72,7 +72,7 @@ def _x_rows(cfg, scales, seed=11):
 
 
 @pytest.mark.parametrize("path", ["gemv", "gemm"])
-@pytest.mark.parametrize("qtype", ["q4_0", "q8_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0", "q4_k", "q6_k", "mxfp4"])
 def test_rows_of_any_scale(ref, qtype, path):
     """Each row within relative L2 1e-3 and a max error of 4e-3 of its own
     largest output; the unit-scale rows also within the absolute tolerance."""
@@ -147,7 +147,7 @@ def test_edge_blocks_in_range(ref, qtype, path):
 
 
 @pytest.mark.parametrize("path", ["gemv", "gemm"])
-@pytest.mark.parametrize("qtype", ["q4_0", "q8_0", "q6_k"])
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0", "q6_k", "mxfp4"])
 def test_out_of_range_is_flagged(ref, qtype, path):
     print(f"out of range {qtype} {path}", flush=True)
     cfg = BASE
@@ -157,8 +157,15 @@ def test_out_of_range_is_flagged(ref, qtype, path):
     # a block scale of 65504 in gate row 0 of every expert (Q6_K: the first
     # super-block's d, its last two bytes)
     L = _host_layer(cfg, qtype)
-    at = slice(208, 210) if qtype == "q6_k" else slice(0, 2)
-    L["w_gate"][:, 0, at] = np.frombuffer(np.uint16(0x7BFF).tobytes(), np.uint8)
+    if qtype == "mxfp4":
+        # MXFP4: the first group's scale byte of gate row 0 (2^73 times the
+        # codes); the scales follow all E x F x H/2 code bytes
+        E, F, H = cfg.n_experts, cfg.ffn, cfg.hidden
+        for e in range(E):
+            L["w_gate"][E * F * H // 2 + e * F * H // 32] = 200
+    else:
+        at = slice(208, 210) if qtype == "q6_k" else slice(0, 2)
+        L["w_gate"][:, 0, at] = np.frombuffer(np.uint16(0x7BFF).tobytes(), np.uint8)
     status, _, _ = _run(cfg, qtype, path, L, xh, ids, w, ref)
     assert status & fw.FW_STATUS_RANGE, status
     # a non-finite activation, ordinary weights
