@@ -37,6 +37,7 @@ TRAFFIC_SOURCES = {"gemv_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip"
                    "gemm_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "gemm_frag.h",
                                             "gemm.hip"]}
 
+N_STAGES = fw.FW_N_STAGE_EVENTS - 1   # front/staging, gate/up routed, shared, down, combine
 HEADLINE = "deepseek4096"   # the largest configuration, MFMA-bound (grouped GEMM)
 DECODE_EXTRA = "decode16"   # the metric's HBM-bound decode point, carried as "decode"
 
@@ -226,10 +227,11 @@ def measure(a, workload, steps, warmup, setup_only=False):
     torch.cuda.synchronize()
     direct_ms = t0.elapsed_time(t1) / steps
     if timed:
-        stage_ms = np.array([[e[s].elapsed_time(e[s + 1]) for s in range(4)] for e in evs])
+        stage_ms = np.array([[e[s].elapsed_time(e[s + 1]) for s in range(N_STAGES)]
+                             for e in evs])
         stage_avg = stage_ms.mean(axis=0)
     else:
-        stage_avg = np.full(4, np.nan)
+        stage_avg = np.full(N_STAGES, np.nan)
 
     # the same K steps as HIP-graph replays (one captured step per weight copy;
     # decode runtimes replay the layer as a graph).  Every ABI call is
@@ -267,23 +269,21 @@ def measure(a, workload, steps, warmup, setup_only=False):
     status = fw.fw_moe_read_status(ws)
     assert status == 0, f"device status {status}"
 
-    # dominant kernel: the gate/up projection (2/3 of the expert bytes and flops)
+    # dominant kernel: the routed experts' gate/up launch (2/3 of the routed
+    # expert bytes and flops); the shared expert's launch is timed apart
     path = fw.fw_moe_forward_path(desc, T)
     gu_ms = float(stage_avg[1])
     if path == fw.FW_PATH_GEMV:
-        # bytes: the active experts' gate and up rows, x in (bf16), a out
+        # bytes: the active experts' gate and up rows, x in (fp16), a out
         gu_alg = (n_active * 2 * cfg.ffn * moegen.row_bytes(cfg.expert_q, H) + T * H * 2 +
                   P * cfg.ffn * 2)
-        if cfg.shared_ffn:
-            gu_alg += 2 * cfg.shared_ffn * moegen.row_bytes(cfg.shared_q, H)
-            gu_alg += T * cfg.shared_ffn * 2
         achieved = gu_alg / (gu_ms * 1e-3) / 1e9
         roof = {"kernel": "gemv_kernel<gate/up>", "bound": "hbm", "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                 "traffic": None, "algorithmic_bytes": gu_alg}
     else:
-        # flops: 2 projections x 2 flops x P x H x F (+ the shared expert on T rows)
-        gu_alg = 4 * P * H * cfg.ffn + 4 * T * H * cfg.shared_ffn
+        # flops: 2 projections x 2 flops x P x H x F
+        gu_alg = 4 * P * H * cfg.ffn
         achieved = gu_alg / (gu_ms * 1e-3) / 1e12
         roof = {"kernel": "gemm_kernel<gate/up>", "bound": "mfma", "achieved": achieved,
                 "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -320,7 +320,8 @@ def measure(a, workload, steps, warmup, setup_only=False):
         "layer_GBps": layer_bytes / (ms * 1e-3) / 1e9,
         "layer_TFLOPs": layer_flops / (ms * 1e-3) / 1e12,
         "stage_us": {n: round(float(v) * 1e3, 2) for n, v in
-                     zip([stage0, "gate_up", "down", "combine"], stage_avg)},
+                     zip([stage0, "gate_up", "gate_up_shared", "down", "combine"], stage_avg)
+                     if cfg.shared_ffn or n != "gate_up_shared"},
         "roofline": roof,
     }
     return line, ctx
@@ -539,10 +540,13 @@ def traffic(workload, roof):
 
 
 def reduce_counters(a):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the dominant gate/up
-    kernel, averaged over its dispatches, each scaled by what the counter read
-    for the --copy-mib negation kernel (which reads and writes exactly that
-    many bytes)."""
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the dominant kernel (the
+    routed experts' gate/up launch), averaged over its dispatches, each scaled
+    by what the counter read for the --copy-mib negation kernel (which reads
+    and writes exactly that many bytes).  Where the shared expert's gate/up
+    launch is the same kernel (same weight format), every step dispatches the
+    routed launch first and the shared one right after it, so the routed ones
+    are every other dispatch in dispatch order."""
     import csv
     import glob
     cfg, T, _ = WORKLOADS[a.workload]
@@ -553,18 +557,22 @@ def reduce_counters(a):
     kernel = "gemv_kernel<gate/up>" if path_gemv else "gemm_kernel<gate/up>"
     frag = KERNELS[kernel][1] + {"q8_0": "0", "q4_0": "1", "q4_k": "2", "q6_k": "3", "mxfp4": "4"}[cfg.expert_q] + "ELb1E"
 
-    def per_dispatch(d, counter, sub):
+    both = cfg.shared_ffn > 0 and cfg.shared_q == cfg.expert_q
+
+    def per_dispatch(d, counter, sub, routed_only=False):
         vals = {}
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(f) as fh:
                 for r in csv.DictReader(fh):
                     if r["Counter_Name"] == counter and sub in r["Kernel_Name"]:
-                        key = (f, r["Dispatch_Id"])
+                        key = (f, int(r["Dispatch_Id"]))
                         vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
-        return list(vals.values())
+        v = [vals[k] for k in sorted(vals)]
+        return v[0::2] if routed_only and both else v
 
     fd, wd = a.reduce_counters
-    kf, kw = per_dispatch(fd, "FETCH_SIZE", frag), per_dispatch(wd, "WRITE_SIZE", frag)
+    kf = per_dispatch(fd, "FETCH_SIZE", frag, routed_only=True)
+    kw = per_dispatch(wd, "WRITE_SIZE", frag, routed_only=True)
     cf, cw = per_dispatch(fd, "FETCH_SIZE", "neg_kernel"), per_dispatch(wd, "WRITE_SIZE", "neg_kernel")
     if not (kf and kw and cf and cw):
         sys.exit("counter files lack the kernel or the calibration copy")

@@ -271,13 +271,14 @@ const char *fw_moe_status_string(int status);
  * as fw_moe_layer, plus HIP events recorded on `stream` around the forward's
  * stages: stage_events[0] before its first kernel and stage_events[s+1]
  * after stage s, s in {0: the fused front end (GEMV batches) or the
- * activation staging, 1: gate/up projection, 2: down projection, 3:
- * combine}; the logits, top-k and permutation launches that precede stage 0
- * fall outside.  stage_events: FW_N_STAGE_EVENTS caller-created hipEvent_t
+ * activation staging, 1: the routed experts' gate/up projection (one
+ * launch), 2: the shared expert's gate/up projection (nothing when
+ * shared_ffn is 0), 3: down projections, 4: combine}; the logits, top-k and
+ * permutation launches that precede stage 0 fall outside.  stage_events: FW_N_STAGE_EVENTS caller-created hipEvent_t
  * handles (required; FW_EINVAL if any is NULL).  For benchmarks and
  * profilers: it keeps no state between calls, so concurrent callers with
  * their own events and workspaces do not interfere. */
-enum { FW_N_STAGE_EVENTS = 5 };
+enum { FW_N_STAGE_EVENTS = 6 };
 int fw_moe_layer_timed(const fw_moe_desc *desc, int32_t T, const void *x,
                        const void *router_w, const float *logit_bias, const void *w_gate,
                        const void *w_up, const void *w_down, const void *ws_gate,

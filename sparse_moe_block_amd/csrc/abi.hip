@@ -149,7 +149,8 @@ struct FrontArgs {
 
 // The forward's launches: staging (or, with `front`, the fused top-k +
 // permutation + staging kernel), gate/up, down, combine; with `ev`
-// (FW_N_STAGE_EVENTS events) an event before the first and after each.
+// (FW_N_STAGE_EVENTS events) an event before the first and after each, the
+// routed experts' gate/up launch timed apart from the shared expert's.
 int enqueue_forward(const FwdArgs &a, const FrontArgs *front, const hipEvent_t *ev,
                     hipStream_t s) {
     int rc;
@@ -160,14 +161,16 @@ int enqueue_forward(const FwdArgs &a, const FrontArgs *front, const hipEvent_t *
     if (rc != FW_OK) return rc;
     if (ev) (void)hipEventRecord(ev[1], s);
     const bool gemm = a.path == FW_PATH_GEMM;
-    rc = hip_status(gemm ? launch_gemm_gate_up(a, s) : launch_gemv_gate_up(a, s));
-    if (rc != FW_OK) return rc;
-    if (ev) (void)hipEventRecord(ev[2], s);
-    rc = hip_status(gemm ? launch_gemm_down(a, s) : launch_gemv_down(a, s));
+    const hipEvent_t routed_done = ev ? ev[2] : nullptr;
+    rc = hip_status(gemm ? launch_gemm_gate_up(a, routed_done, s)
+                         : launch_gemv_gate_up(a, routed_done, s));
     if (rc != FW_OK) return rc;
     if (ev) (void)hipEventRecord(ev[3], s);
-    if ((rc = hip_status(launch_combine(a, s))) != FW_OK) return rc;
+    rc = hip_status(gemm ? launch_gemm_down(a, s) : launch_gemv_down(a, s));
+    if (rc != FW_OK) return rc;
     if (ev) (void)hipEventRecord(ev[4], s);
+    if ((rc = hip_status(launch_combine(a, s))) != FW_OK) return rc;
+    if (ev) (void)hipEventRecord(ev[5], s);
     return FW_OK;
 }
 

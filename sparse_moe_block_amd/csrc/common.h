@@ -336,9 +336,11 @@ struct FwdArgs {
     WsLayout L;
 };
 hipError_t launch_prepare(const FwdArgs &a, hipStream_t s);
-hipError_t launch_gemv_gate_up(const FwdArgs &a, hipStream_t s);
+// gate/up launchers: routed_done (may be null) is recorded between the
+// routed experts' launch and the shared expert's
+hipError_t launch_gemv_gate_up(const FwdArgs &a, hipEvent_t routed_done, hipStream_t s);
 hipError_t launch_gemv_down(const FwdArgs &a, hipStream_t s);
-hipError_t launch_gemm_gate_up(const FwdArgs &a, hipStream_t s);
+hipError_t launch_gemm_gate_up(const FwdArgs &a, hipEvent_t routed_done, hipStream_t s);
 hipError_t launch_gemm_down(const FwdArgs &a, hipStream_t s);
 hipError_t launch_combine(const FwdArgs &a, hipStream_t s);
 // fw_moe_layer's fused decode front end (top-k + permutation + staging in one

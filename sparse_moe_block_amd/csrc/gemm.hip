@@ -664,13 +664,14 @@ void launch_q(int q, const FwdArgs &a, const uint8_t *wa, const uint8_t *wb,
 
 }  // namespace
 
-hipError_t launch_gemm_gate_up(const FwdArgs &a, hipStream_t s) {
+hipError_t launch_gemm_gate_up(const FwdArgs &a, hipEvent_t routed_done, hipStream_t s) {
     const fw_moe_desc &d = a.d;
     const _Float16 *x = (const _Float16 *)(a.ws + a.L.x16);
     _Float16 *h = (_Float16 *)(a.ws + a.L.h);
     const int32_t *xe = (const int32_t *)(a.ws + a.L.xe);
     int32_t *he = (int32_t *)(a.ws + a.L.he);
     launch_q<true>(d.expert_q, a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, 0, xe, he, s);
+    if (routed_done) (void)hipEventRecord(routed_done, s);
     if (d.shared_ffn > 0)
         launch_q<true>(d.shared_q, a, a.sg, a.su, x, h + (size_t)a.P * d.ffn, nullptr, d.hidden,
                         d.shared_ffn, 1, xe, he + a.P, s);

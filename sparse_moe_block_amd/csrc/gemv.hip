@@ -850,7 +850,7 @@ void launch_q(int q, const FwdArgs &a, const uint8_t *wa, const uint8_t *wb,
 
 // Block sums: x rows (prepare), then h rows of the routed pairs [P][F/32]
 // followed by the shared expert's [T][Fs/32].
-hipError_t launch_gemv_gate_up(const FwdArgs &a, hipStream_t s) {
+hipError_t launch_gemv_gate_up(const FwdArgs &a, hipEvent_t routed_done, hipStream_t s) {
     const fw_moe_desc &d = a.d;
     const _Float16 *x = (const _Float16 *)(a.ws + a.L.x16);
     _Float16 *h = (_Float16 *)(a.ws + a.L.h);
@@ -861,6 +861,7 @@ hipError_t launch_gemv_gate_up(const FwdArgs &a, hipStream_t s) {
     const int mc = max_routed_chunks(a);
     launch_q<true>(d.expert_q, a, a.wg, a.wu, x, h, nullptr, d.hidden, d.ffn, mc, 0, xs, hs, xe,
                    he, s);
+    if (routed_done) (void)hipEventRecord(routed_done, s);
     if (d.shared_ffn > 0) {
         _Float16 *hsh = h + (size_t)a.P * d.ffn;
         float *hssh = hs + (size_t)a.P * (d.ffn / 32);

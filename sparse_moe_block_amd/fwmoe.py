@@ -18,7 +18,7 @@ FW_F32, FW_BF16 = 0, 1
 FW_Q8_0, FW_Q4_0, FW_Q4_K, FW_Q6_K, FW_MXFP4 = 0, 1, 2, 3, 4
 FW_SOFTMAX_RENORM, FW_SIGMOID_RENORM = 0, 1
 FW_PATH_AUTO, FW_PATH_GEMV, FW_PATH_GEMM = 0, 1, 2
-FW_N_STAGE_EVENTS = 5
+FW_N_STAGE_EVENTS = 6
 FW_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 DTYPES = {"f32": FW_F32, "bf16": FW_BF16}

@@ -38,7 +38,7 @@ def good_desc(**kw):
 @pytest.mark.parametrize("field,value", [
     ("hidden", 300), ("hidden", 0), ("hidden", 16640), ("n_experts", 0), ("n_experts", 513),
     ("top_k", 0), ("top_k", 17), ("ffn", 100), ("ffn", 0), ("act_dtype", 7), ("expert_q", 5),
-    ("expert_q", 5), ("expert_q", -1), ("shared_q", 5), ("score", 3)])
+    ("expert_q", 99), ("expert_q", -1), ("shared_q", 5), ("score", 3)])
 def test_invalid_descriptors(field, value):
     d = good_desc()
     setattr(d, field, value)
