@@ -43,6 +43,18 @@
  *    scales, R x K/32 bytes; value = E2M1(code) * 2^(scale - 127), exact in
  *    fp32 below 2^128 (from scale 253 on the larger values are infinite);
  *    scale 255 is NaN.  PARITY UNPINNED against an outside encoder;
+ *  - MXFP8 expert activations beside MXFP4 experts (vOOM, the lossy artifact
+ *    notes: the MXFP8 control and MX formats with group size 32; an option,
+ *    fwref_forward_mx8).  OCP MX quantisation of a 32-element block V:
+ *    shared scale X = 2^(floor(log2(max |V_i|)) - 8), 8 being E4M3's largest
+ *    exponent, stored as the E8M0 byte floor(log2 amax) - 8 + 127 clamped to
+ *    0..254 (an all-zero block: byte 0, codes 0); elements E4M3 (OCP E4M3FN:
+ *    bias 7, 3 mantissa bits, largest 448) of V_i / X, nearest with ties to
+ *    the even code, magnitudes above 448 clamped to 448.  The quantiser's
+ *    input is the fp32 value (x as handed in; the SwiGLU output rounded to
+ *    fp32), so that both sides of a comparison take each code decision on
+ *    the same number.  PARITY UNPINNED against an outside encoder; pinned by
+ *    hand-decoded blocks and a brute-force nearest-code search;
  *  - SwiGLU expert FFNs (vOOM, module layout: layer_runner's block math);
  *  - top-k routing with k a tunable (vOOM notes: the request-local top-2
  *    expert schedule) and DeepSeek-shaped sigmoid routing with an always-on
@@ -343,6 +355,78 @@ int fwref_permute(int T, int E, int k, const int32_t *ids, int32_t *offsets,
     return 0;
 }
 
+/* E4M3 (OCP E4M3FN) value of a code: sign bit 7, exponent bits 6..3 (bias
+ * 7), mantissa bits 2..0; exponent 0 is subnormal (m / 8 * 2^-6); 0x7F and
+ * 0xFF are NaN. */
+double fwref_e4m3_value(int code)
+{
+    int sgn = code & 0x80, e = (code >> 3) & 15, m = code & 7;
+    if ((code & 0x7F) == 0x7F)
+        return NAN;
+    double v = e == 0 ? ldexp(m, -9) : ldexp(8 + m, e - 10);
+    return sgn ? -v : v;
+}
+
+/* E4M3 code of the nearest value to y (|y| <= 448 after the clamp), ties to
+ * the even code: the step at |y|'s binade (2^(E - 3), E = max(floor(log2 |y|),
+ * -6)) divides |y| exactly, rint rounds half to even, and the multiple of the
+ * step that results is an E4M3 value (possibly the next binade's first). */
+static int e4m3_code(float y)
+{
+    int sgn = signbit(y) ? 0x80 : 0;
+    double a = fabs((double)y);
+    if (a >= 448.0)
+        return sgn | 0x7E;
+    if (a == 0.0)
+        return sgn;
+    int E = ilogb(a);
+    if (E < -6)
+        E = -6;
+    double q = rint(ldexp(a, 3 - E));       /* units of the step 2^(E - 3) */
+    if (q == 16.0) {                        /* rounded up into the next binade */
+        E += 1;
+        q = 8.0;
+    }
+    if (q < 8.0)                            /* subnormal (E = -6) */
+        return sgn | (int)q;
+    return sgn | ((E + 7) << 3) | ((int)q - 8);
+}
+
+/* OCP MX quantisation of n (a multiple of 32) fp32 values to MXFP8: E4M3
+ * codes[n] and one E8M0 scale per 32-element block, scales[n / 32]. */
+void fwref_mxfp8_quantize(const float *v, int n, uint8_t *codes, uint8_t *scales)
+{
+    for (int b = 0; b < n / 32; ++b) {
+        float amax = 0.0f;
+        for (int i = 0; i < 32; ++i)
+            if (fabsf(v[32 * b + i]) > amax)
+                amax = fabsf(v[32 * b + i]);
+        if (amax == 0.0f) {
+            scales[b] = 0;
+            for (int i = 0; i < 32; ++i)
+                codes[32 * b + i] = signbit(v[32 * b + i]) ? 0x80 : 0;
+            continue;
+        }
+        int e = ilogbf(amax) - 8;
+        if (e < -127)
+            e = -127;
+        if (e > 127)
+            e = 127;
+        scales[b] = (uint8_t)(e + 127);
+        for (int i = 0; i < 32; ++i)
+            codes[32 * b + i] = (uint8_t)e4m3_code(ldexpf(v[32 * b + i], -e));
+    }
+}
+
+/* The values an MXFP8 round trip gives: out = E4M3(code) * 2^(scale - 127). */
+static void mxfp8_round_trip(const float *v, int n, float *out, uint8_t *codes,
+                             uint8_t *scales)
+{
+    fwref_mxfp8_quantize(v, n, codes, scales);
+    for (int i = 0; i < n; ++i)
+        out[i] = (float)ldexp(fwref_e4m3_value(codes[i]), scales[i / 32] - 127);
+}
+
 /* One SwiGLU expert on one token:
  *   g_f = sum_h Wg[f][h] x_h,  u_f = sum_h Wu[f][h] x_h
  *   a_f = g_f * sigmoid(g_f) * u_f          (SiLU(gate) * up)
@@ -352,7 +436,8 @@ int fwref_permute(int T, int E, int k, const int32_t *ids, int32_t *offsets,
  * along the row (the reduction dimension). */
 static void expert_ffn(int qtype, int F, int H, const uint8_t *wg, const uint8_t *wu,
                        const uint8_t *wd, size_t Rgu, size_t Rd, size_t r0gu, size_t r0d,
-                       const float *x, double *y, float *row, double *a)
+                       const float *x, double *y, float *row, double *a, int mx8,
+                       float *hq, uint8_t *qc, uint8_t *qs)
 {
     for (int f = 0; f < F; ++f) {
         double g = 0.0, u = 0.0;
@@ -363,6 +448,13 @@ static void expert_ffn(int qtype, int F, int H, const uint8_t *wg, const uint8_t
         for (int h = 0; h < H; ++h)
             u += (double)row[h] * (double)x[h];
         a[f] = g / (1.0 + exp(-g)) * u;
+    }
+    if (mx8) {   /* MXFP8 mode: the down projection's input is MXFP8(fp32(a)) */
+        for (int f = 0; f < F; ++f)
+            hq[f] = (float)a[f];
+        mxfp8_round_trip(hq, F, hq, qc, qs);
+        for (int f = 0; f < F; ++f)
+            a[f] = hq[f];
     }
     for (int o = 0; o < H; ++o) {
         double acc = 0.0;
@@ -380,11 +472,11 @@ static void expert_ffn(int qtype, int F, int H, const uint8_t *wg, const uint8_t
  * e * H .. (down: E * H rows of F elements) of the routed matrices.  Tokens are independent, so they are spread over
  * n_threads OpenMP threads (0: the runtime's default).
  * Returns 0, or -1 on a bad argument or id. */
-int fwref_forward(int T, int H, int E, int k, int F, int qtype, int Fs, int qtype_s,
-                  int act_dtype, const void *x, const uint8_t *wg, const uint8_t *wu,
-                  const uint8_t *wd, const uint8_t *sg, const uint8_t *su,
-                  const uint8_t *sd, const int32_t *ids, const float *w, float *out,
-                  int n_threads)
+static int forward_impl(int T, int H, int E, int k, int F, int qtype, int Fs, int qtype_s,
+                        int act_dtype, const void *x, const uint8_t *wg, const uint8_t *wu,
+                        const uint8_t *wd, const uint8_t *sg, const uint8_t *su,
+                        const uint8_t *sd, const int32_t *ids, const float *w, float *out,
+                        int n_threads, int mx8)
 {
     if (T < 0 || H <= 0 || H % 32 || F <= 0 || F % 32 || k < 1 || k > E || Fs < 0 ||
         Fs % 32)
@@ -411,6 +503,9 @@ int fwref_forward(int T, int H, int E, int k, int F, int qtype, int Fs, int qtyp
         double *a = malloc(sizeof(double) * (size_t)maxf);
         double *y = malloc(sizeof(double) * (size_t)H);
         double *acc = malloc(sizeof(double) * (size_t)H);
+        float *hq = malloc(sizeof(float) * (size_t)maxr);
+        uint8_t *qc = malloc((size_t)maxr);
+        uint8_t *qs = malloc((size_t)maxr / 32 + 1);
 #ifdef _OPENMP
 #pragma omp for schedule(dynamic, 1)
 #endif
@@ -419,16 +514,18 @@ int fwref_forward(int T, int H, int E, int k, int F, int qtype, int Fs, int qtyp
                 xf[h] = act_value(act_dtype, x, (size_t)t * H + h);
                 acc[h] = 0.0;
             }
+            if (mx8)   /* MXFP8 mode: the experts' input is MXFP8(x) */
+                mxfp8_round_trip(xf, H, xf, qc, qs);
             for (int j = 0; j < k; ++j) {
                 int e = ids[(size_t)t * k + j];
                 expert_ffn(qtype, F, H, wg, wu, wd, (size_t)E * F, (size_t)E * H,
-                           (size_t)e * F, (size_t)e * H, xf, y, row, a);
+                           (size_t)e * F, (size_t)e * H, xf, y, row, a, mx8, hq, qc, qs);
                 for (int h = 0; h < H; ++h)
                     acc[h] += (double)w[(size_t)t * k + j] * y[h];
             }
             if (Fs > 0) {
                 expert_ffn(qtype_s, Fs, H, sg, su, sd, (size_t)Fs, (size_t)H, 0, 0, xf, y,
-                           row, a);
+                           row, a, mx8, hq, qc, qs);
                 for (int h = 0; h < H; ++h)
                     acc[h] += y[h];
             }
@@ -440,8 +537,38 @@ int fwref_forward(int T, int H, int E, int k, int F, int qtype, int Fs, int qtyp
         free(a);
         free(y);
         free(acc);
+        free(hq);
+        free(qc);
+        free(qs);
     }
     return 0;
+}
+
+int fwref_forward(int T, int H, int E, int k, int F, int qtype, int Fs, int qtype_s,
+                  int act_dtype, const void *x, const uint8_t *wg, const uint8_t *wu,
+                  const uint8_t *wd, const uint8_t *sg, const uint8_t *su,
+                  const uint8_t *sd, const int32_t *ids, const float *w, float *out,
+                  int n_threads)
+{
+    return forward_impl(T, H, E, k, F, qtype, Fs, qtype_s, act_dtype, x, wg, wu, wd, sg, su,
+                        sd, ids, w, out, n_threads, 0);
+}
+
+/* fwref_forward with MXFP8 expert activations: each expert's input is the
+ * MXFP8 round trip of the token's fp32 x (blocks of 32 along H) and its down
+ * projection's input the MXFP8 round trip of the SwiGLU output rounded to
+ * fp32 (blocks of 32 along F); routing and everything else as in
+ * fwref_forward.  Only for MXFP4 experts (and an MXFP4 shared expert). */
+int fwref_forward_mx8(int T, int H, int E, int k, int F, int qtype, int Fs, int qtype_s,
+                      int act_dtype, const void *x, const uint8_t *wg, const uint8_t *wu,
+                      const uint8_t *wd, const uint8_t *sg, const uint8_t *su,
+                      const uint8_t *sd, const int32_t *ids, const float *w, float *out,
+                      int n_threads)
+{
+    if (qtype != REF_MXFP4 || (Fs > 0 && qtype_s != REF_MXFP4))
+        return -1;
+    return forward_impl(T, H, E, k, F, qtype, Fs, qtype_s, act_dtype, x, wg, wu, wd, sg, su,
+                        sd, ids, w, out, n_threads, 1);
 }
 
 /* Threads an OpenMP region would use with n_threads (0: default). */

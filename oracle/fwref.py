@@ -52,6 +52,12 @@ def lib():
         L.fwref_permute.restype = I
         L.fwref_forward.argtypes = [I] * 9 + [P] * 10 + [I]
         L.fwref_forward.restype = I
+        L.fwref_forward_mx8.argtypes = [I] * 9 + [P] * 10 + [I]
+        L.fwref_forward_mx8.restype = I
+        L.fwref_mxfp8_quantize.argtypes = [P, I, P, P]
+        L.fwref_mxfp8_quantize.restype = None
+        L.fwref_e4m3_value.argtypes = [I]
+        L.fwref_e4m3_value.restype = ctypes.c_double
         L.fwref_threads.argtypes = [I]
         L.fwref_threads.restype = I
         _lib = L
@@ -113,15 +119,32 @@ def permute(ids, n_experts):
     return offsets, sorted_pairs, inv_pos
 
 
+def e4m3_value(code: int) -> float:
+    return lib().fwref_e4m3_value(code)
+
+
+def mxfp8_quantize(v: np.ndarray):
+    """fp32 [n] (n a multiple of 32) -> (E4M3 codes uint8 [n], E8M0 scales uint8 [n/32])."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    assert v.ndim == 1 and v.size % 32 == 0
+    codes = np.empty(v.size, dtype=np.uint8)
+    scales = np.empty(v.size // 32, dtype=np.uint8)
+    lib().fwref_mxfp8_quantize(_p(v), v.size, _p(codes), _p(scales))
+    return codes, scales
+
+
 def forward(x, w_gate, w_up, w_down, ids, w, *, n_experts, ffn, qtype, act_dtype,
             s_gate=None, s_up=None, s_down=None, shared_ffn=0, shared_q="q8_0",
-            n_threads=0):
-    """Layer output [T][H] f32 for tokens x with routing (ids, w)."""
+            n_threads=0, act_quant="none"):
+    """Layer output [T][H] f32 for tokens x with routing (ids, w).  act_quant
+    "mxfp8": the experts' inputs (x, and the SwiGLU output before the down
+    projection) are MXFP8 round trips (MXFP4 experts only)."""
     T, H = x.shape
     k = ids.shape[1]
     out = np.empty((T, H), dtype=np.float32)
     c = np.ascontiguousarray
-    rc = lib().fwref_forward(
+    fn = {"none": lib().fwref_forward, "mxfp8": lib().fwref_forward_mx8}[act_quant]
+    rc = fn(
         T, H, n_experts, k, ffn, QTYPE[qtype], shared_ffn, QTYPE[shared_q],
         DTYPE[act_dtype], _p(c(x)), _p(c(w_gate)), _p(c(w_up)), _p(c(w_down)),
         _p(None if s_gate is None else c(s_gate)), _p(None if s_up is None else c(s_up)),

@@ -88,3 +88,54 @@ def act(a):
 
 def silu(z):
     return z / (1.0 + np.exp(-z))
+
+
+def e4m3_table():
+    """Values of all 256 OCP E4M3FN codes (NaN for 0x7F / 0xFF), float64,
+    decoded from the bit fields: sign 7, exponent 6..3 (bias 7), mantissa
+    2..0; exponent 0 is subnormal."""
+    c = np.arange(256)
+    e, m = (c >> 3) & 15, c & 7
+    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    v = np.where(c & 0x80, -v, v)
+    return np.where((c & 0x7F) == 0x7F, np.nan, v)
+
+
+def mxfp8_brute(v):
+    """MXFP8 quantisation by exhaustive search: per 32-element block the E8M0
+    scale floor(log2 amax) - 8 (from frexp; clamped to -127..127; all-zero
+    block: -127 and byte 0), then each element's code is the finite E4M3 value
+    nearest to fp32(v) / 2^e (magnitudes above 448 clamped to 448), ties to
+    the even code.  Returns (codes uint8 [n], scale bytes uint8 [n/32])."""
+    v = np.asarray(v, dtype=np.float32).reshape(-1)
+    tab = e4m3_table()
+    finite = np.where(~np.isnan(tab))[0]
+    codes = np.zeros(v.size, np.uint8)
+    scales = np.zeros(v.size // 32, np.uint8)
+    for b in range(v.size // 32):
+        blk = v[32 * b:32 * b + 32]
+        amax = float(np.max(np.abs(blk)))
+        if amax == 0.0:
+            codes[32 * b:32 * b + 32] = np.where(np.signbit(blk), 0x80, 0)
+            continue
+        e = int(np.frexp(amax)[1]) - 1 - 8
+        e = min(max(e, -127), 127)
+        scales[b] = e + 127
+        for i, x in enumerate(blk):
+            y = float(np.ldexp(np.float32(x), -e))
+            y = min(max(y, -448.0), 448.0)
+            d = np.abs(tab[finite] - y)
+            best = finite[d == d.min()]
+            if best.size > 1:   # a tie: the code with the even mantissa
+                best = best[(best & 1) == 0]
+            c = int(best[0])
+            if y == 0.0 or (c & 0x7F) == 0:   # zero keeps the input's sign
+                c = 0x80 if np.signbit(np.float32(x)) else 0
+            codes[32 * b + i] = c
+    return codes, scales
+
+
+def mxfp8_round_trip(v):
+    """fp32 values -> float64 values after an MXFP8 round trip (mxfp8_brute)."""
+    c, s = mxfp8_brute(v)
+    return e4m3_table()[c] * np.repeat(np.exp2(s.astype(np.float64) - 127.0), 32)
