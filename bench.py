@@ -29,11 +29,14 @@ from sparse_moe_block_amd import fwmoe as fw  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MFMA_FP16_PEAK_TFLOPS = 2500.0
+MFMA_FP8_PEAK_TFLOPS = 5000.0    # dense fp8 (E4M3 x E2M1 runs at the fp8 rate)
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)"
 CSRC = os.path.join(ROOT, "sparse_moe_block_amd", "csrc")
 # sources that decide each dominant kernel's memory traffic (a change to any
 # voids its counter figures)
 TRAFFIC_SOURCES = {"gemv_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "gemv.hip"],
+                   "gemm_mx_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "stages.h",
+                                               "gemm_mx.hip"],
                    "gemm_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "gemm_frag.h",
                                             "gemm.hip"]}
 
@@ -59,6 +62,11 @@ WORKLOADS = {
     # and on MXFP4 experts (MLX packing, group 32)
     "decode16_mxfp4": (moegen.QWEN3_DECODE.with_(expert_q=moegen.MXFP4), 16, 16),
     "prefill2048_mxfp4": (moegen.QWEN3_PREFILL.with_(expert_q=moegen.MXFP4), 2048, 4),
+    # MXFP4 experts with MXFP8 activations on the block-scaled MFMA
+    "prefill2048_mx8": (moegen.QWEN3_PREFILL.with_(expert_q=moegen.MXFP4, act_quant="mxfp8"),
+                        2048, 4),
+    "deepseek4096_mx8": (moegen.DEEPSEEK.with_(expert_q=moegen.MXFP4, shared_q=moegen.MXFP4,
+                                               act_quant="mxfp8"), 4096, 1),
     # and on Q8_0 experts (the sweep's other format)
     "decode16_q8": (moegen.QWEN3_DECODE.with_(expert_q=moegen.Q8_0), 16, 8),
     "prefill2048_q8": (moegen.QWEN3_PREFILL.with_(expert_q=moegen.Q8_0), 2048, 2),
@@ -166,7 +174,7 @@ def measure(a, workload, steps, warmup, setup_only=False):
     ctx["layers"] = layers
     desc = fw.make_desc(cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn, cfg.shared_ffn,
                         cfg.act_dtype, cfg.router_dtype, cfg.expert_q, cfg.shared_q,
-                        cfg.score, a.path)
+                        cfg.score, a.path, cfg.act_quant)
     E, k, H = cfg.n_experts, cfg.top_k, cfg.hidden
     P = T * k
     logits = torch.empty(T, E, device=dev)
@@ -285,9 +293,11 @@ def measure(a, workload, steps, warmup, setup_only=False):
         # flops: 2 projections x 2 flops x P x H x F
         gu_alg = 4 * P * H * cfg.ffn
         achieved = gu_alg / (gu_ms * 1e-3) / 1e12
-        roof = {"kernel": "gemm_kernel<gate/up>", "bound": "mfma", "achieved": achieved,
-                "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_FP16_PEAK_TFLOPS, "traffic": None,
+        mx8 = cfg.act_quant == "mxfp8"
+        peak = MFMA_FP8_PEAK_TFLOPS if mx8 else MFMA_FP16_PEAK_TFLOPS
+        roof = {"kernel": "gemm_mx_kernel<gate/up>" if mx8 else "gemm_kernel<gate/up>",
+                "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None,
                 "algorithmic_flops": gu_alg}
     roof["duration_us"] = gu_ms * 1e3
     layer_bytes = (n_active * cfg.expert_bytes + cfg.shared_bytes + cfg.router_bytes +
@@ -308,10 +318,11 @@ def measure(a, workload, steps, warmup, setup_only=False):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "e4m3 x e2m1" if cfg.act_quant == "mxfp8" else "f16",
         "data": "synthetic (seeded N(0,0.02) weights quantized to GGUF blocks, N(0,1) bf16 tokens)",
         "config": {"workload": f"{cfg.name}, T={T}", "hidden": H, "experts": E, "top_k": k,
                    "ffn": cfg.ffn, "expert_format": cfg.expert_q, "shared_ffn": cfg.shared_ffn,
+                   "activations": "mxfp8" if cfg.act_quant == "mxfp8" else "fp16",
                    "tokens": T, "active_experts": n_active, "weight_copies": copies,
                    "path": "gemv" if path == fw.FW_PATH_GEMV else "gemm"},
         "timing": "hip-graph replay per step" if graph_ms is not None else "direct launches",
@@ -517,6 +528,7 @@ def source_hash(kernel):
 
 # dominant kernel: label in the JSON line, mangled-name fragment in counter files
 KERNELS = {"gemv_kernel<gate/up>": ("gemv_gate_up", "gemv_kernelILi"),
+           "gemm_mx_kernel<gate/up>": ("gemm_mx_gate_up", "gemm_mx_kernelILb1E"),
            "gemm_kernel<gate/up>": ("gemm_gate_up", "gemm_kernelILi")}
 
 
@@ -552,10 +564,13 @@ def reduce_counters(a):
     cfg, T, _ = WORKLOADS[a.workload]
     desc = fw.make_desc(cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn, cfg.shared_ffn,
                         cfg.act_dtype, cfg.router_dtype, cfg.expert_q, cfg.shared_q,
-                        cfg.score, a.path)
+                        cfg.score, a.path, cfg.act_quant)
     path_gemv = fw.fw_moe_forward_path(desc, T) == fw.FW_PATH_GEMV
     kernel = "gemv_kernel<gate/up>" if path_gemv else "gemm_kernel<gate/up>"
     frag = KERNELS[kernel][1] + {"q8_0": "0", "q4_0": "1", "q4_k": "2", "q6_k": "3", "mxfp4": "4"}[cfg.expert_q] + "ELb1E"
+    if cfg.act_quant == "mxfp8":
+        kernel = "gemm_mx_kernel<gate/up>"
+        frag = KERNELS[kernel][1]
 
     both = cfg.shared_ffn > 0 and cfg.shared_q == cfg.expert_q
 
@@ -621,7 +636,7 @@ def cpu_baseline(cfg, L, x, T, seconds):
         fwref.forward(xs, wg, wu, wd, ids, w, n_experts=cfg.n_experts, ffn=cfg.ffn,
                       qtype=cfg.expert_q, act_dtype=cfg.act_dtype, s_gate=sg, s_up=su,
                       s_down=sd, shared_ffn=cfg.shared_ffn, shared_q=cfg.shared_q,
-                      n_threads=threads)
+                      n_threads=threads, act_quant=cfg.act_quant)
 
     threads = fwref.threads(0)
     chunk = min(T, 16)

@@ -92,6 +92,17 @@ enum { FW_F32 = 0, FW_BF16 = 1 };                 /* activation / router dtype *
 enum { FW_Q8_0 = 0, FW_Q4_0 = 1, FW_Q4_K = 2, FW_Q6_K = 3, FW_MXFP4 = 4 };  /* weight format */
 enum { FW_SOFTMAX_RENORM = 0, FW_SIGMOID_RENORM = 1 };
 enum { FW_PATH_AUTO = 0, FW_PATH_GEMV = 1, FW_PATH_GEMM = 2 };
+/* Expert activations: as handed in (fp16 staging, exact for bf16 inputs in
+ * range), or MXFP8 -- the MX alternative beside MXFP4 experts (vOOM, the lossy
+ * artifact notes: MX formats of group size 32, MXFP8 as the control).  With
+ * FW_ACT_MXFP8 each expert's input (x, and the SwiGLU output before the down
+ * projection) is quantised per 32 consecutive values by the OCP MX rule
+ * (scale 2^(floor(log2 amax) - 8), E4M3 elements nearest-even, clamped at
+ * 448) and the expert GEMMs run on the block-scaled MFMA (E4M3 x E2M1, no
+ * weight dequantisation).  Requires MXFP4 experts (and an MXFP4 shared expert
+ * if any) and the grouped-GEMM family: FW_PATH_GEMV is FW_EUNSUPPORTED and
+ * AUTO takes FW_PATH_GEMM for every T.  Routing uses x as handed in. */
+enum { FW_ACT_NONE = 0, FW_ACT_MXFP8 = 1 };
 
 /* Shape and formats of one MoE layer.  All fields are int32. */
 typedef struct {
@@ -106,6 +117,7 @@ typedef struct {
     int32_t shared_q;     /* same choices: shared expert (ignored if Fs = 0)      */
     int32_t score;        /* FW_SOFTMAX_RENORM | FW_SIGMOID_RENORM                 */
     int32_t path;         /* FW_PATH_*: forward kernel family (AUTO picks by T)    */
+    int32_t act_quant;    /* FW_ACT_NONE | FW_ACT_MXFP8: expert activations         */
 } fw_moe_desc;
 
 /* Library version string. */
@@ -263,6 +275,15 @@ int fw_moe_clear_status(void *workspace, void *stream);
 /* Blocking: wait for the device and copy the status word to *host_status.
  * For tests and harnesses, not for the hot path. */
 int fw_moe_read_status(const void *workspace, int32_t *host_status);
+
+/* Where a forward call on T tokens keeps its staged expert inputs inside the
+ * workspace: byte offsets of the activation staging area (with
+ * FW_ACT_MXFP8: x as E4M3 codes [T][H], then the E8M0 scales [T][H/32]) and
+ * of the SwiGLU output area (with FW_ACT_MXFP8: codes [T*k][F] then [T][Fs],
+ * then the scales of those rows, one per 32).  Host-only; for tests that
+ * read those areas back.  FW_OK, or an error for an invalid descriptor / T. */
+int fw_moe_workspace_offsets(const fw_moe_desc *desc, int32_t T, size_t *x_stage,
+                             size_t *h_stage);
 
 /* Human-readable text of a return code. */
 const char *fw_moe_status_string(int status);

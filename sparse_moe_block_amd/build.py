@@ -14,7 +14,8 @@ LIB = os.path.join(PKG, "libfwmoe.so")
 # the peak microbenchmarks (fp16 MFMA, HBM streaming): a library of their own
 PEAK_SOURCE = "peak.hip"
 PEAK_LIB = os.path.join(PKG, "libfwpeak.so")
-SOURCES = ["abi.hip", "route.hip", "permute.hip", "forward.hip", "gemv.hip", "gemm.hip", "layer.hip"]
+SOURCES = ["abi.hip", "route.hip", "permute.hip", "forward.hip", "gemv.hip", "gemm.hip",
+           "gemm_mx.hip", "layer.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall",

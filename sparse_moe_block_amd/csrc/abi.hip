@@ -71,7 +71,12 @@ int check_desc(const fw_moe_desc *d) {
     if (d->shared_q < FW_Q8_0 || d->shared_q > FW_MXFP4) return FW_EINVAL;
     if (d->score != FW_SOFTMAX_RENORM && d->score != FW_SIGMOID_RENORM) return FW_EINVAL;
     if (d->path < FW_PATH_AUTO || d->path > FW_PATH_GEMM) return FW_EINVAL;
+    if (d->act_quant != FW_ACT_NONE && d->act_quant != FW_ACT_MXFP8) return FW_EINVAL;
     if (d->router_dtype != d->act_dtype) return FW_EUNSUPPORTED;
+    if (d->act_quant == FW_ACT_MXFP8 &&
+        (d->expert_q != FW_MXFP4 || (d->shared_ffn > 0 && d->shared_q != FW_MXFP4) ||
+         d->path == FW_PATH_GEMV))
+        return FW_EUNSUPPORTED;
     return FW_OK;
 }
 
@@ -91,6 +96,7 @@ int check_forward_T(const fw_moe_desc *d, int32_t T) {
 
 int resolve_path(const fw_moe_desc *d, int32_t T) {
     if (d->path != FW_PATH_AUTO) return d->path;
+    if (d->act_quant == FW_ACT_MXFP8) return FW_PATH_GEMM;   // block-scaled MFMA only
     const int64_t pairs = (int64_t)T * d->top_k;
     return pairs <= (int64_t)kGemvMaxRowsPerExpert * d->n_experts ? FW_PATH_GEMV : FW_PATH_GEMM;
 }
@@ -259,6 +265,18 @@ int fw_moe_forward_path(const fw_moe_desc *desc, int32_t T) {
     if ((rc = check_T(desc, T)) != FW_OK) return rc;
     if ((rc = check_forward_T(desc, T)) != FW_OK) return rc;
     return resolve_path(desc, T);
+}
+
+int fw_moe_workspace_offsets(const fw_moe_desc *desc, int32_t T, size_t *x_stage,
+                             size_t *h_stage) {
+    int rc = check_desc(desc);
+    if (rc != FW_OK) return rc;
+    if ((rc = check_T(desc, T)) != FW_OK) return rc;
+    if (!x_stage || !h_stage) return FW_EINVAL;
+    const WsLayout L = ws_layout(*desc, T);
+    *x_stage = L.x16;
+    *h_stage = L.h;
+    return FW_OK;
 }
 
 int fw_moe_route(const fw_moe_desc *desc, int32_t T, const void *x, const void *router_w,

@@ -343,6 +343,11 @@ hipError_t launch_gemv_down(const FwdArgs &a, hipStream_t s);
 hipError_t launch_gemm_gate_up(const FwdArgs &a, hipEvent_t routed_done, hipStream_t s);
 hipError_t launch_gemm_down(const FwdArgs &a, hipStream_t s);
 hipError_t launch_combine(const FwdArgs &a, hipStream_t s);
+// MXFP8 expert activations (FW_ACT_MXFP8): the staging and the block-scaled
+// grouped GEMMs (gemm_mx.hip); the launchers above hand over to these.
+hipError_t launch_prepare_mx8(const FwdArgs &a, hipStream_t s);
+hipError_t launch_gemm_mx_gate_up(const FwdArgs &a, hipEvent_t routed_done, hipStream_t s);
+hipError_t launch_gemm_mx_down(const FwdArgs &a, hipStream_t s);
 // fw_moe_layer's fused decode front end (top-k + permutation + staging in one
 // launch): taken when the forward runs the GEMV family and the pairs fit the
 // one-workgroup permutation.

@@ -26,6 +26,8 @@ QTYPES = {"q8_0": FW_Q8_0, "q4_0": FW_Q4_0, "q4_k": FW_Q4_K, "q6_k": FW_Q6_K,
           "mxfp4": FW_MXFP4}
 SCORES = {"softmax": FW_SOFTMAX_RENORM, "sigmoid": FW_SIGMOID_RENORM}
 PATHS = {"auto": FW_PATH_AUTO, "gemv": FW_PATH_GEMV, "gemm": FW_PATH_GEMM}
+FW_ACT_NONE, FW_ACT_MXFP8 = 0, 1
+ACT_QUANTS = {"none": FW_ACT_NONE, "mxfp8": FW_ACT_MXFP8}
 
 
 class FwMoeError(RuntimeError):
@@ -37,19 +39,19 @@ class FwMoeError(RuntimeError):
 class fw_moe_desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "hidden", "n_experts", "top_k", "ffn", "shared_ffn", "act_dtype", "router_dtype",
-        "expert_q", "shared_q", "score", "path")]
+        "expert_q", "shared_q", "score", "path", "act_quant")]
 
 
 def make_desc(hidden, n_experts, top_k, ffn, shared_ffn=0, act_dtype="bf16",
               router_dtype=None, expert_q="q4_0", shared_q="q8_0", score="softmax",
-              path="auto"):
+              path="auto", act_quant="none"):
     """A descriptor from readable names (dtype / format / score / path strings
     or the FW_* integers)."""
     enum = lambda table, v: table[v] if isinstance(v, str) else int(v)
     return fw_moe_desc(hidden, n_experts, top_k, ffn, shared_ffn,
                        enum(DTYPES, act_dtype), enum(DTYPES, router_dtype or act_dtype),
                        enum(QTYPES, expert_q), enum(QTYPES, shared_q),
-                       enum(SCORES, score), enum(PATHS, path))
+                       enum(SCORES, score), enum(PATHS, path), enum(ACT_QUANTS, act_quant))
 
 
 _lib = None
@@ -67,6 +69,8 @@ def lib():
             "fw_moe_validate": ([D], ctypes.c_int),
             "fw_moe_workspace_size": ([D, I], ctypes.c_size_t),
             "fw_moe_forward_path": ([D, I], ctypes.c_int),
+            "fw_moe_workspace_offsets": ([D, I, ctypes.POINTER(ctypes.c_size_t),
+                                          ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
             "fw_moe_route": ([D, I] + [P] * 8, ctypes.c_int),
             "fw_moe_permute": ([D, I, P, P, P, P, P, ctypes.c_size_t, P], ctypes.c_int),
             "fw_moe_forward": ([D, I] + [P] * 13 + [ctypes.c_size_t, P], ctypes.c_int),
@@ -120,6 +124,14 @@ def fw_moe_workspace_size(desc, max_T):
 
 def fw_moe_forward_path(desc, T):
     return lib().fw_moe_forward_path(ctypes.byref(desc), T)
+
+
+def fw_moe_workspace_offsets(desc, T):
+    """(x staging, h staging) byte offsets inside a workspace for T tokens."""
+    xo, ho = ctypes.c_size_t(), ctypes.c_size_t()
+    _check("fw_moe_workspace_offsets", lib().fw_moe_workspace_offsets(
+        ctypes.byref(desc), T, ctypes.byref(xo), ctypes.byref(ho)))
+    return xo.value, ho.value
 
 
 def fw_moe_route(desc, T, x, router_w, logit_bias, logits_in, logits, topk_ids, topk_w,

@@ -22,7 +22,7 @@ GAP = 1e-3             # below this k-th/(k+1)-th logit gap the oracle's logits 
 def desc_of(cfg, path="auto", qtype=None):
     return fw.make_desc(cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn, cfg.shared_ffn,
                         cfg.act_dtype, cfg.router_dtype, qtype or cfg.expert_q, cfg.shared_q,
-                        cfg.score, path)
+                        cfg.score, path, cfg.act_quant)
 
 
 class DevLayer:
@@ -97,7 +97,8 @@ def oracle_forward(ref, cfg, dl, x_host, ids, w):
     return ref.forward(x_host, hh["w_gate"], hh["w_up"], hh["w_down"], ids, w,
                        n_experts=cfg.n_experts, ffn=cfg.ffn, qtype=dl.qtype,
                        act_dtype=cfg.act_dtype, s_gate=hh["s_gate"], s_up=hh["s_up"],
-                       s_down=hh["s_down"], shared_ffn=cfg.shared_ffn, shared_q=cfg.shared_q)
+                       s_down=hh["s_down"], shared_ffn=cfg.shared_ffn, shared_q=cfg.shared_q,
+                       act_quant=cfg.act_quant)
 
 
 def small_gaps(logits, k):

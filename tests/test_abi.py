@@ -208,3 +208,21 @@ def test_layer_timed_validation():
     assert call(ev, router=None) == fw.FW_EINVAL
     assert call(ev, ws=128) == fw.FW_EALIGN
     assert call(ev, T=-1) == fw.FW_EINVAL
+
+
+def test_mx8_mode_refusals():
+    """MXFP8 activations need MXFP4 experts (and an MXFP4 shared expert) and
+    the grouped-GEMM family; AUTO takes the GEMM at every T."""
+    def d(**kw):
+        base = dict(hidden=2048, n_experts=128, top_k=8, ffn=768, expert_q="mxfp4",
+                    act_quant="mxfp8")
+        base.update(kw)
+        return fw.make_desc(**base)
+    assert fw.fw_moe_validate(d()) == fw.FW_OK
+    assert fw.fw_moe_validate(d(expert_q="q4_0")) == fw.FW_EUNSUPPORTED
+    assert fw.fw_moe_validate(d(shared_ffn=256, shared_q="q8_0")) == fw.FW_EUNSUPPORTED
+    assert fw.fw_moe_validate(d(shared_ffn=256, shared_q="mxfp4")) == fw.FW_OK
+    assert fw.fw_moe_validate(d(path="gemv")) == fw.FW_EUNSUPPORTED
+    assert fw.fw_moe_validate(d(act_quant=2)) == fw.FW_EINVAL
+    assert fw.fw_moe_forward_path(d(), 1) == fw.FW_PATH_GEMM
+    assert fw.fw_moe_forward_path(d(), 4096) == fw.FW_PATH_GEMM
