@@ -567,10 +567,13 @@ def reduce_counters(a):
                         cfg.score, a.path, cfg.act_quant)
     path_gemv = fw.fw_moe_forward_path(desc, T) == fw.FW_PATH_GEMV
     kernel = "gemv_kernel<gate/up>" if path_gemv else "gemm_kernel<gate/up>"
-    frag = KERNELS[kernel][1] + {"q8_0": "0", "q4_0": "1", "q4_k": "2", "q6_k": "3", "mxfp4": "4"}[cfg.expert_q] + "ELb1E"
+    qi = {"q8_0": "0", "q4_0": "1", "q4_k": "2", "q6_k": "3", "mxfp4": "4"}[cfg.expert_q]
+    # the profiler writes kernel names mangled or demangled: match either
+    frags = (KERNELS[kernel][1] + qi + "ELb1E",
+             KERNELS[kernel][1].replace("ILi", "<") + qi + ", true")
     if cfg.act_quant == "mxfp8":
         kernel = "gemm_mx_kernel<gate/up>"
-        frag = KERNELS[kernel][1]
+        frags = (KERNELS[kernel][1], "gemm_mx_kernel<true>")
 
     both = cfg.shared_ffn > 0 and cfg.shared_q == cfg.expert_q
 
@@ -579,16 +582,17 @@ def reduce_counters(a):
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(f) as fh:
                 for r in csv.DictReader(fh):
-                    if r["Counter_Name"] == counter and sub in r["Kernel_Name"]:
+                    if r["Counter_Name"] == counter and any(f in r["Kernel_Name"] for f in sub):
                         key = (f, int(r["Dispatch_Id"]))
                         vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
         v = [vals[k] for k in sorted(vals)]
         return v[0::2] if routed_only and both else v
 
     fd, wd = a.reduce_counters
-    kf = per_dispatch(fd, "FETCH_SIZE", frag, routed_only=True)
-    kw = per_dispatch(wd, "WRITE_SIZE", frag, routed_only=True)
-    cf, cw = per_dispatch(fd, "FETCH_SIZE", "neg_kernel"), per_dispatch(wd, "WRITE_SIZE", "neg_kernel")
+    kf = per_dispatch(fd, "FETCH_SIZE", frags, routed_only=True)
+    kw = per_dispatch(wd, "WRITE_SIZE", frags, routed_only=True)
+    cf = per_dispatch(fd, "FETCH_SIZE", ("neg_kernel",))
+    cw = per_dispatch(wd, "WRITE_SIZE", ("neg_kernel",))
     if not (kf and kw and cf and cw):
         sys.exit("counter files lack the kernel or the calibration copy")
     copy_bytes = a.copy_mib << 20
