@@ -220,6 +220,13 @@ int fw_moe_permute(const fw_moe_desc *desc, int32_t T, const int32_t *topk_ids,
  * MXFP4 scale above 136 (96 x 2^(scale - 127) beyond fp16; scale 255, NaN
  * by the format, included).  The GEMV family has no weight limit (codes stay
  * exact, scales apply in fp32).
+ * With act_quant = FW_ACT_MXFP8 the experts' inputs are MXFP8 (see
+ * FW_ACT_MXFP8) and the contraction is the block-scaled MFMA's (E4M3 x E2M1
+ * products exact; each 64-product slice summed in the instruction's own
+ * accumulation, within ~1e-4 of the slice's sum of |products|); the output
+ * then follows an fp64 evaluation of the same MXFP8 layer within 1e-3
+ * relative L2, a SwiGLU value on an E4M3 rounding boundary possibly taking
+ * the neighbouring code.  FW_STATUS_RANGE is set for non-finite x or h.
  * Q4_K and Q6_K (GGUF K-quants, 144- and 210-byte super-blocks of 256
  * elements) need H, F and Fs to be multiples of 256, which every descriptor
  * already is.  MXFP4 requires the routed and shared matrices to be stored
