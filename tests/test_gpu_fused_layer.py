@@ -38,8 +38,13 @@ CASES = [
     (C.QWEN3_PREFILL.with_(expert_q=C.Q6_K), 2048, "auto"),
     (C.QWEN3_DECODE.with_(expert_q=C.MXFP4), 16, "auto"),
     (C.QWEN3_PREFILL.with_(expert_q=C.MXFP4), 2048, "auto"),
+    # MXFP8 activations on the block-scaled MFMA (the GEMM family at every T)
+    (C.QWEN3_DECODE.with_(expert_q=C.MXFP4, act_quant="mxfp8"), 1, "auto"),
+    (C.QWEN3_PREFILL.with_(expert_q=C.MXFP4, act_quant="mxfp8"), 2048, "auto"),
+    (C.DEEPSEEK.with_(expert_q=C.MXFP4, shared_q=C.MXFP4, act_quant="mxfp8"), 64, "auto"),
 ]
-IDS = [f"c{c.cid}-{c.expert_q}-T{T}-{p}" for c, T, p in CASES]
+IDS = [f"c{c.cid}-{c.expert_q}{'-mx8' if c.act_quant == 'mxfp8' else ''}-T{T}-{p}"
+       for c, T, p in CASES]
 
 
 def _three_calls(desc, cfg, dl, x):
@@ -90,4 +95,8 @@ def test_layer_matches_three_calls_and_oracle(ref, cfg, T, path):
     tok = np.intersect1d(G.compare_tokens(T, rids, cfg.n_experts), np.nonzero(ok)[0])
     assert tok.size > 0
     want = G.oracle_forward(ref, cfg, dl, np.ascontiguousarray(xh[tok]), rids[tok], rw[tok])
-    G.check_out(out[tok], want)
+    if cfg.act_quant == "mxfp8":
+        from tests.test_gpu_mx8 import check_mx8
+        check_mx8(out[tok], want)
+    else:
+        G.check_out(out[tok], want)
