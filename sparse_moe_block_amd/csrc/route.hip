@@ -201,6 +201,12 @@ hipError_t launch_logits(const fw_moe_desc &d, int T, const void *x, const void 
     } else if (T <= kLogitsTileMaxT) {
         dim3 grid((T + 15) / 16, (E + 15) / 16);
         logits_bf16_kernel<1, 1, 16, 4><<<grid, 16 * kWave, 0, s>>>(xb, wb, bias, logits, T, H, E);
+    } else if (E >= 64 && (long long)((T + 63) / 64) * ((E + 63) / 64) >= 256) {
+        // enough 64 x 64 tiles for every CU: each x row is read by E/64
+        // workgroups and each router row by T/64 (32 x 64 tiles: twice as
+        // many router reads and two rounds of workgroups)
+        dim3 grid((T + 63) / 64, (E + 63) / 64);
+        logits_bf16_kernel<4, 4, 4, 2><<<grid, 4 * kWave, 0, s>>>(xb, wb, bias, logits, T, H, E);
     } else if (E >= 64 && (long long)((T + 31) / 32) * ((E + 63) / 64) >= 512) {
         dim3 grid((T + 31) / 32, (E + 63) / 64);
         logits_bf16_kernel<2, 4, 4, 2><<<grid, 4 * kWave, 0, s>>>(xb, wb, bias, logits, T, H, E);
