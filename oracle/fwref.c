@@ -55,6 +55,20 @@
  *    fp32), so that both sides of a comparison take each code decision on
  *    the same number.  PARITY UNPINNED against an outside encoder; pinned by
  *    hand-decoded blocks and a brute-force nearest-code search;
+ *  - int8 expert activations beside Q8_0 / Q4_0 experts, the pages' MMQ
+ *    path: prompt processing's routed experts on block-table MMQ kernels
+ *    (Flyweight 0.2.0, "Runtime controls", --routed-moe), activations
+ *    quantised to int8 for them (Flyweight 0.2.0, "Image generation", the
+ *    `fast` precision) and Q8 activations in the dp4a kernels (Flyweight
+ *    0.2.0, "Quantization"); an option, fwref_forward_q8a.  The pages print
+ *    no activation format; the reading taken is GGUF's Q8_1-style block of
+ *    32: d = max |V_i| / 127 (fp32 division), codes round(V_i / d) (fp32
+ *    division, ties away from zero, at most 127 in magnitude), d kept in
+ *    fp32 (an all-zero block: d = 0, codes 0).  The value a code stands for
+ *    is d * code, exact in fp64.  As for MXFP8 the quantiser's input is the
+ *    fp32 value (x as handed in; the SwiGLU output rounded to fp32).  PARITY
+ *    UNPINNED against an outside encoder; pinned by hand-computed blocks and
+ *    the round-trip bound;
  *  - SwiGLU expert FFNs (vOOM, module layout: layer_runner's block math);
  *  - top-k routing with k a tunable (vOOM notes: the request-local top-2
  *    expert schedule) and DeepSeek-shaped sigmoid routing with an always-on
@@ -427,6 +441,38 @@ static void mxfp8_round_trip(const float *v, int n, float *out, uint8_t *codes,
         out[i] = (float)ldexp(fwref_e4m3_value(codes[i]), scales[i / 32] - 127);
 }
 
+/* int8 (Q8_1-style) quantisation of n (a multiple of 32) fp32 values:
+ * codes[n] and one fp32 scale per 32-element block, scales[n / 32]. */
+void fwref_q8a_quantize(const float *v, int n, int8_t *codes, float *scales)
+{
+    for (int b = 0; b < n / 32; ++b) {
+        float amax = 0.0f;
+        for (int i = 0; i < 32; ++i)
+            if (fabsf(v[32 * b + i]) > amax)
+                amax = fabsf(v[32 * b + i]);
+        float d = amax / 127.0f;
+        scales[b] = d;
+        for (int i = 0; i < 32; ++i) {
+            float q = d == 0.0f ? 0.0f : roundf(v[32 * b + i] / d);
+            if (q > 127.0f)
+                q = 127.0f;
+            if (q < -127.0f)
+                q = -127.0f;
+            codes[32 * b + i] = (int8_t)q;
+        }
+    }
+}
+
+/* The values an int8 round trip stands for, in fp64: out = d * code. */
+static void q8a_round_trip(const float *v, int n, double *out, int8_t *codes, float *scales)
+{
+    fwref_q8a_quantize(v, n, codes, scales);
+    for (int i = 0; i < n; ++i)
+        out[i] = (double)scales[i / 32] * (double)codes[i];
+}
+
+enum { AQ_NONE = 0, AQ_MXFP8 = 1, AQ_Q8A = 2 };
+
 /* One SwiGLU expert on one token:
  *   g_f = sum_h Wg[f][h] x_h,  u_f = sum_h Wu[f][h] x_h
  *   a_f = g_f * sigmoid(g_f) * u_f          (SiLU(gate) * up)
@@ -436,8 +482,8 @@ static void mxfp8_round_trip(const float *v, int n, float *out, uint8_t *codes,
  * along the row (the reduction dimension). */
 static void expert_ffn(int qtype, int F, int H, const uint8_t *wg, const uint8_t *wu,
                        const uint8_t *wd, size_t Rgu, size_t Rd, size_t r0gu, size_t r0d,
-                       const float *x, double *y, float *row, double *a, int mx8,
-                       float *hq, uint8_t *qc, uint8_t *qs)
+                       const double *x, double *y, float *row, double *a, int aq,
+                       float *hq, uint8_t *qc, uint8_t *qs, float *qd)
 {
     for (int f = 0; f < F; ++f) {
         double g = 0.0, u = 0.0;
@@ -449,12 +495,16 @@ static void expert_ffn(int qtype, int F, int H, const uint8_t *wg, const uint8_t
             u += (double)row[h] * (double)x[h];
         a[f] = g / (1.0 + exp(-g)) * u;
     }
-    if (mx8) {   /* MXFP8 mode: the down projection's input is MXFP8(fp32(a)) */
+    if (aq == AQ_MXFP8) {   /* the down projection's input is MXFP8(fp32(a)) */
         for (int f = 0; f < F; ++f)
             hq[f] = (float)a[f];
         mxfp8_round_trip(hq, F, hq, qc, qs);
         for (int f = 0; f < F; ++f)
             a[f] = hq[f];
+    } else if (aq == AQ_Q8A) {   /* ... or the int8 round trip of fp32(a) */
+        for (int f = 0; f < F; ++f)
+            hq[f] = (float)a[f];
+        q8a_round_trip(hq, F, a, (int8_t *)qc, qd);
     }
     for (int o = 0; o < H; ++o) {
         double acc = 0.0;
@@ -476,7 +526,7 @@ static int forward_impl(int T, int H, int E, int k, int F, int qtype, int Fs, in
                         int act_dtype, const void *x, const uint8_t *wg, const uint8_t *wu,
                         const uint8_t *wd, const uint8_t *sg, const uint8_t *su,
                         const uint8_t *sd, const int32_t *ids, const float *w, float *out,
-                        int n_threads, int mx8)
+                        int n_threads, int aq)
 {
     if (T < 0 || H <= 0 || H % 32 || F <= 0 || F % 32 || k < 1 || k > E || Fs < 0 ||
         Fs % 32)
@@ -499,6 +549,8 @@ static int forward_impl(int T, int H, int E, int k, int F, int qtype, int Fs, in
 #endif
     {
         float *xf = malloc(sizeof(float) * (size_t)H);
+        double *xd = malloc(sizeof(double) * (size_t)H);
+        float *qd = malloc(sizeof(float) * ((size_t)maxr / 32 + 1));
         float *row = malloc(sizeof(float) * (size_t)maxr);
         double *a = malloc(sizeof(double) * (size_t)maxf);
         double *y = malloc(sizeof(double) * (size_t)H);
@@ -514,18 +566,25 @@ static int forward_impl(int T, int H, int E, int k, int F, int qtype, int Fs, in
                 xf[h] = act_value(act_dtype, x, (size_t)t * H + h);
                 acc[h] = 0.0;
             }
-            if (mx8)   /* MXFP8 mode: the experts' input is MXFP8(x) */
+            /* the experts' input: x, or its MXFP8 or int8 round trip */
+            if (aq == AQ_MXFP8)
                 mxfp8_round_trip(xf, H, xf, qc, qs);
+            if (aq == AQ_Q8A) {
+                q8a_round_trip(xf, H, xd, (int8_t *)qc, qd);
+            } else {
+                for (int h = 0; h < H; ++h)
+                    xd[h] = xf[h];
+            }
             for (int j = 0; j < k; ++j) {
                 int e = ids[(size_t)t * k + j];
                 expert_ffn(qtype, F, H, wg, wu, wd, (size_t)E * F, (size_t)E * H,
-                           (size_t)e * F, (size_t)e * H, xf, y, row, a, mx8, hq, qc, qs);
+                           (size_t)e * F, (size_t)e * H, xd, y, row, a, aq, hq, qc, qs, qd);
                 for (int h = 0; h < H; ++h)
                     acc[h] += (double)w[(size_t)t * k + j] * y[h];
             }
             if (Fs > 0) {
-                expert_ffn(qtype_s, Fs, H, sg, su, sd, (size_t)Fs, (size_t)H, 0, 0, xf, y,
-                           row, a, mx8, hq, qc, qs);
+                expert_ffn(qtype_s, Fs, H, sg, su, sd, (size_t)Fs, (size_t)H, 0, 0, xd, y,
+                           row, a, aq, hq, qc, qs, qd);
                 for (int h = 0; h < H; ++h)
                     acc[h] += y[h];
             }
@@ -533,6 +592,8 @@ static int forward_impl(int T, int H, int E, int k, int F, int qtype, int Fs, in
                 out[(size_t)t * H + h] = (float)acc[h];
         }
         free(xf);
+        free(xd);
+        free(qd);
         free(row);
         free(a);
         free(y);
@@ -551,7 +612,7 @@ int fwref_forward(int T, int H, int E, int k, int F, int qtype, int Fs, int qtyp
                   int n_threads)
 {
     return forward_impl(T, H, E, k, F, qtype, Fs, qtype_s, act_dtype, x, wg, wu, wd, sg, su,
-                        sd, ids, w, out, n_threads, 0);
+                        sd, ids, w, out, n_threads, AQ_NONE);
 }
 
 /* fwref_forward with MXFP8 expert activations: each expert's input is the
@@ -568,7 +629,24 @@ int fwref_forward_mx8(int T, int H, int E, int k, int F, int qtype, int Fs, int 
     if (qtype != REF_MXFP4 || (Fs > 0 && qtype_s != REF_MXFP4))
         return -1;
     return forward_impl(T, H, E, k, F, qtype, Fs, qtype_s, act_dtype, x, wg, wu, wd, sg, su,
-                        sd, ids, w, out, n_threads, 1);
+                        sd, ids, w, out, n_threads, AQ_MXFP8);
+}
+
+/* fwref_forward with int8 expert activations: each expert's input is the
+ * int8 round trip of the token's fp32 x (blocks of 32 along H) and its down
+ * projection's input the int8 round trip of the SwiGLU output rounded to fp32
+ * (blocks of 32 along F); routing and everything else as in fwref_forward.
+ * Only for Q8_0 / Q4_0 experts (and a Q8_0 / Q4_0 shared expert). */
+int fwref_forward_q8a(int T, int H, int E, int k, int F, int qtype, int Fs, int qtype_s,
+                      int act_dtype, const void *x, const uint8_t *wg, const uint8_t *wu,
+                      const uint8_t *wd, const uint8_t *sg, const uint8_t *su,
+                      const uint8_t *sd, const int32_t *ids, const float *w, float *out,
+                      int n_threads)
+{
+    if (qtype > REF_Q4_0 || (Fs > 0 && qtype_s > REF_Q4_0))
+        return -1;
+    return forward_impl(T, H, E, k, F, qtype, Fs, qtype_s, act_dtype, x, wg, wu, wd, sg, su,
+                        sd, ids, w, out, n_threads, AQ_Q8A);
 }
 
 /* Threads an OpenMP region would use with n_threads (0: default). */

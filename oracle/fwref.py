@@ -54,6 +54,10 @@ def lib():
         L.fwref_forward.restype = I
         L.fwref_forward_mx8.argtypes = [I] * 9 + [P] * 10 + [I]
         L.fwref_forward_mx8.restype = I
+        L.fwref_forward_q8a.argtypes = [I] * 9 + [P] * 10 + [I]
+        L.fwref_forward_q8a.restype = I
+        L.fwref_q8a_quantize.argtypes = [P, I, P, P]
+        L.fwref_q8a_quantize.restype = None
         L.fwref_mxfp8_quantize.argtypes = [P, I, P, P]
         L.fwref_mxfp8_quantize.restype = None
         L.fwref_e4m3_value.argtypes = [I]
@@ -133,17 +137,29 @@ def mxfp8_quantize(v: np.ndarray):
     return codes, scales
 
 
+def q8a_quantize(v: np.ndarray):
+    """fp32 [n] (n a multiple of 32) -> (int8 codes [n], fp32 scales [n/32])."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    assert v.ndim == 1 and v.size % 32 == 0
+    codes = np.empty(v.size, dtype=np.int8)
+    scales = np.empty(v.size // 32, dtype=np.float32)
+    lib().fwref_q8a_quantize(_p(v), v.size, _p(codes), _p(scales))
+    return codes, scales
+
+
 def forward(x, w_gate, w_up, w_down, ids, w, *, n_experts, ffn, qtype, act_dtype,
             s_gate=None, s_up=None, s_down=None, shared_ffn=0, shared_q="q8_0",
             n_threads=0, act_quant="none"):
     """Layer output [T][H] f32 for tokens x with routing (ids, w).  act_quant
     "mxfp8": the experts' inputs (x, and the SwiGLU output before the down
-    projection) are MXFP8 round trips (MXFP4 experts only)."""
+    projection) are MXFP8 round trips (MXFP4 experts only); "q8a": they are
+    int8 round trips, d = amax / 127 per 32 (Q8_0 / Q4_0 experts only)."""
     T, H = x.shape
     k = ids.shape[1]
     out = np.empty((T, H), dtype=np.float32)
     c = np.ascontiguousarray
-    fn = {"none": lib().fwref_forward, "mxfp8": lib().fwref_forward_mx8}[act_quant]
+    fn = {"none": lib().fwref_forward, "mxfp8": lib().fwref_forward_mx8,
+          "q8a": lib().fwref_forward_q8a}[act_quant]
     rc = fn(
         T, H, n_experts, k, ffn, QTYPE[qtype], shared_ffn, QTYPE[shared_q],
         DTYPE[act_dtype], _p(c(x)), _p(c(w_gate)), _p(c(w_up)), _p(c(w_down)),

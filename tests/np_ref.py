@@ -139,3 +139,46 @@ def mxfp8_round_trip(v):
     """fp32 values -> float64 values after an MXFP8 round trip (mxfp8_brute)."""
     c, s = mxfp8_brute(v)
     return e4m3_table()[c] * np.repeat(np.exp2(s.astype(np.float64) - 127.0), 32)
+
+
+def q8a_brute(v):
+    """int8 (Q8_1-style) quantisation by search: per 32-element block the fp32
+    scale d = fp32(amax / 127); each element's code is the integer q in
+    -127..127 whose d q is nearest to v, compared exactly (d q is exact in
+    float64), ties to the larger magnitude; d = 0 gives codes 0.  The oracle
+    divides in fp32 and rounds the quotient, so the two may differ by one
+    where the exact quotient lies within fp32 rounding of a half-integer.
+    Returns (codes int8 [n], scales float32 [n/32])."""
+    v = np.asarray(v, dtype=np.float32).reshape(-1)
+    codes = np.zeros(v.size, np.int8)
+    scales = np.zeros(v.size // 32, np.float32)
+    q = np.arange(-127, 128, dtype=np.float64)
+    for b in range(v.size // 32):
+        blk = v[32 * b:32 * b + 32].astype(np.float64)
+        d = np.float32(np.max(np.abs(v[32 * b:32 * b + 32]))) / np.float32(127)
+        scales[b] = d
+        if d == 0:
+            continue
+        for i, x in enumerate(blk):
+            err = np.abs(x - float(d) * q)
+            best = q[err == err.min()]
+            codes[32 * b + i] = int(best[np.argmax(np.abs(best))])
+    return codes, scales
+
+
+def q8a_quantize(v):
+    """The int8 quantiser's definition in numpy: d = fp32(amax / 127), codes
+    round(fp32(v / d)) with ties away from zero, clamped to -127..127."""
+    v = np.asarray(v, dtype=np.float32).reshape(-1, 32)
+    d = (np.max(np.abs(v), axis=1) / np.float32(127)).astype(np.float32)
+    safe = np.where(d == 0, np.float32(1), d).astype(np.float32)
+    t = (v / safe[:, None]).astype(np.float32).astype(np.float64)
+    c = np.clip(np.sign(t) * np.floor(np.abs(t) + 0.5), -127, 127)
+    c = np.where(d[:, None] == 0, 0, c)
+    return c.astype(np.int8).reshape(-1), d
+
+
+def q8a_round_trip(v):
+    """fp32 values -> float64 d * code after the int8 round trip."""
+    c, d = q8a_quantize(v)
+    return c.astype(np.float64) * np.repeat(d.astype(np.float64), 32)
