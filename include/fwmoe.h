@@ -101,8 +101,17 @@ enum { FW_PATH_AUTO = 0, FW_PATH_GEMV = 1, FW_PATH_GEMM = 2 };
  * 448) and the expert GEMMs run on the block-scaled MFMA (E4M3 x E2M1, no
  * weight dequantisation).  Requires MXFP4 experts (and an MXFP4 shared expert
  * if any) and the grouped-GEMM family: FW_PATH_GEMV is FW_EUNSUPPORTED and
- * AUTO takes FW_PATH_GEMM for every T.  Routing uses x as handed in. */
-enum { FW_ACT_NONE = 0, FW_ACT_MXFP8 = 1 };
+ * AUTO takes FW_PATH_GEMM for every T.  Routing uses x as handed in.
+ * FW_ACT_INT8 is the int8-activation path of the pages' MMQ kernels (Flyweight
+ * 0.2.0 wheel METADATA: "Runtime controls", prompt processing's routed experts
+ * on block-table MMQ kernels; "Image generation", activations quantised to
+ * int8 for them): each expert's input is quantised per 32 consecutive values
+ * as GGUF's Q8_1-style block (d = fp32(amax / 127), codes round(fp32(v / d))
+ * with halves away from zero, d kept in fp32) and the expert GEMMs run on the
+ * int8 MFMA, one 32-element weight block per instruction, the scales d_x d_w
+ * applied to its int32 sums in fp32.  Requires Q8_0 or Q4_0 experts (and
+ * shared expert, if any) and the grouped-GEMM family, as FW_ACT_MXFP8 does. */
+enum { FW_ACT_NONE = 0, FW_ACT_MXFP8 = 1, FW_ACT_INT8 = 2 };
 
 /* Shape and formats of one MoE layer.  All fields are int32. */
 typedef struct {
@@ -117,7 +126,7 @@ typedef struct {
     int32_t shared_q;     /* same choices: shared expert (ignored if Fs = 0)      */
     int32_t score;        /* FW_SOFTMAX_RENORM | FW_SIGMOID_RENORM                 */
     int32_t path;         /* FW_PATH_*: forward kernel family (AUTO picks by T)    */
-    int32_t act_quant;    /* FW_ACT_NONE | FW_ACT_MXFP8: expert activations         */
+    int32_t act_quant;    /* FW_ACT_NONE | FW_ACT_MXFP8 | FW_ACT_INT8: expert inputs */
 } fw_moe_desc;
 
 /* Library version string. */
@@ -227,6 +236,12 @@ int fw_moe_permute(const fw_moe_desc *desc, int32_t T, const int32_t *topk_ids,
  * then follows an fp64 evaluation of the same MXFP8 layer within 1e-3
  * relative L2, a SwiGLU value on an E4M3 rounding boundary possibly taking
  * the neighbouring code.  FW_STATUS_RANGE is set for non-finite x or h.
+ * With act_quant = FW_ACT_INT8 the experts' inputs are int8 blocks (see
+ * FW_ACT_INT8): the int32 block sums are exact and each adds (d_x d_w) S in
+ * fp32, so the output follows an fp64 evaluation of the same int8 layer
+ * within the layer's tolerances, a SwiGLU value within rounding of a code
+ * boundary possibly taking the neighbouring code; no fp16 range limits
+ * apply.  FW_STATUS_RANGE is set for non-finite x or h.
  * Q4_K and Q6_K (GGUF K-quants, 144- and 210-byte super-blocks of 256
  * elements) need H, F and Fs to be multiples of 256, which every descriptor
  * already is.  MXFP4 requires the routed and shared matrices to be stored
@@ -285,9 +300,10 @@ int fw_moe_read_status(const void *workspace, int32_t *host_status);
 
 /* Where a forward call on T tokens keeps its staged expert inputs inside the
  * workspace: byte offsets of the activation staging area (with
- * FW_ACT_MXFP8: x as E4M3 codes [T][H], then the E8M0 scales [T][H/32]) and
- * of the SwiGLU output area (with FW_ACT_MXFP8: codes [T*k][F] then [T][Fs],
- * then the scales of those rows, one per 32).  Host-only; for tests that
+ * FW_ACT_MXFP8: x as E4M3 codes [T][H], then the E8M0 scales [T][H/32];
+ * with FW_ACT_INT8: int8 codes [T][H], then fp32 scales [T][H/32]) and of the
+ * SwiGLU output area (codes [T*k][F] then [T][Fs], then the scales of those
+ * rows, one per 32: E8M0 bytes for FW_ACT_MXFP8, fp32 for FW_ACT_INT8).  Host-only; for tests that
  * read those areas back.  FW_OK, or an error for an invalid descriptor / T. */
 int fw_moe_workspace_offsets(const fw_moe_desc *desc, int32_t T, size_t *x_stage,
                              size_t *h_stage);

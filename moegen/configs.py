@@ -58,7 +58,8 @@ class LayerConfig:
     shared_q: str = Q8_0
     zipf: Optional[float] = None # per-expert logit bias b_e = -s*ln(e+1)
     tokens: Tuple[int, ...] = field(default=(1,))
-    act_quant: str = "none"      # "mxfp8": MXFP8 expert activations (MXFP4 experts)
+    act_quant: str = "none"      # "mxfp8": MXFP8 expert activations (MXFP4 experts);
+                                 # "int8": int8 expert activations (Q8_0 / Q4_0 experts)
 
     def with_(self, **kw):
         return replace(self, **kw)

@@ -152,14 +152,14 @@ def forward(x, w_gate, w_up, w_down, ids, w, *, n_experts, ffn, qtype, act_dtype
             n_threads=0, act_quant="none"):
     """Layer output [T][H] f32 for tokens x with routing (ids, w).  act_quant
     "mxfp8": the experts' inputs (x, and the SwiGLU output before the down
-    projection) are MXFP8 round trips (MXFP4 experts only); "q8a": they are
+    projection) are MXFP8 round trips (MXFP4 experts only); "int8": they are
     int8 round trips, d = amax / 127 per 32 (Q8_0 / Q4_0 experts only)."""
     T, H = x.shape
     k = ids.shape[1]
     out = np.empty((T, H), dtype=np.float32)
     c = np.ascontiguousarray
     fn = {"none": lib().fwref_forward, "mxfp8": lib().fwref_forward_mx8,
-          "q8a": lib().fwref_forward_q8a}[act_quant]
+          "int8": lib().fwref_forward_q8a}[act_quant]
     rc = fn(
         T, H, n_experts, k, ffn, QTYPE[qtype], shared_ffn, QTYPE[shared_q],
         DTYPE[act_dtype], _p(c(x)), _p(c(w_gate)), _p(c(w_up)), _p(c(w_down)),

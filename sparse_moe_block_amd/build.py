@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libfwmoe.so")
 PEAK_SOURCE = "peak.hip"
 PEAK_LIB = os.path.join(PKG, "libfwpeak.so")
 SOURCES = ["abi.hip", "route.hip", "permute.hip", "forward.hip", "gemv.hip", "gemm.hip",
-           "gemm_mx.hip", "layer.hip"]
+           "gemm_mx.hip", "gemm_i8.hip", "layer.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall",

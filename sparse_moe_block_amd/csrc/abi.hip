@@ -71,10 +71,15 @@ int check_desc(const fw_moe_desc *d) {
     if (d->shared_q < FW_Q8_0 || d->shared_q > FW_MXFP4) return FW_EINVAL;
     if (d->score != FW_SOFTMAX_RENORM && d->score != FW_SIGMOID_RENORM) return FW_EINVAL;
     if (d->path < FW_PATH_AUTO || d->path > FW_PATH_GEMM) return FW_EINVAL;
-    if (d->act_quant != FW_ACT_NONE && d->act_quant != FW_ACT_MXFP8) return FW_EINVAL;
+    if (d->act_quant < FW_ACT_NONE || d->act_quant > FW_ACT_INT8) return FW_EINVAL;
     if (d->router_dtype != d->act_dtype) return FW_EUNSUPPORTED;
     if (d->act_quant == FW_ACT_MXFP8 &&
         (d->expert_q != FW_MXFP4 || (d->shared_ffn > 0 && d->shared_q != FW_MXFP4) ||
+         d->path == FW_PATH_GEMV))
+        return FW_EUNSUPPORTED;
+    auto mmq = [](int q) { return q == FW_Q8_0 || q == FW_Q4_0; };
+    if (d->act_quant == FW_ACT_INT8 &&
+        (!mmq(d->expert_q) || (d->shared_ffn > 0 && !mmq(d->shared_q)) ||
          d->path == FW_PATH_GEMV))
         return FW_EUNSUPPORTED;
     return FW_OK;
@@ -96,7 +101,8 @@ int check_forward_T(const fw_moe_desc *d, int32_t T) {
 
 int resolve_path(const fw_moe_desc *d, int32_t T) {
     if (d->path != FW_PATH_AUTO) return d->path;
-    if (d->act_quant == FW_ACT_MXFP8) return FW_PATH_GEMM;   // block-scaled MFMA only
+    // block-scaled MFMA / int8 MFMA: the grouped GEMM family only
+    if (d->act_quant != FW_ACT_NONE) return FW_PATH_GEMM;
     const int64_t pairs = (int64_t)T * d->top_k;
     return pairs <= (int64_t)kGemvMaxRowsPerExpert * d->n_experts ? FW_PATH_GEMV : FW_PATH_GEMM;
 }

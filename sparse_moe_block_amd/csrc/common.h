@@ -348,6 +348,11 @@ hipError_t launch_combine(const FwdArgs &a, hipStream_t s);
 hipError_t launch_prepare_mx8(const FwdArgs &a, hipStream_t s);
 hipError_t launch_gemm_mx_gate_up(const FwdArgs &a, hipEvent_t routed_done, hipStream_t s);
 hipError_t launch_gemm_mx_down(const FwdArgs &a, hipStream_t s);
+// int8 expert activations (FW_ACT_INT8): the staging and the int8-MFMA
+// grouped GEMMs (gemm_i8.hip); the launchers above hand over to these.
+hipError_t launch_prepare_i8(const FwdArgs &a, hipStream_t s);
+hipError_t launch_gemm_i8_gate_up(const FwdArgs &a, hipEvent_t routed_done, hipStream_t s);
+hipError_t launch_gemm_i8_down(const FwdArgs &a, hipStream_t s);
 // fw_moe_layer's fused decode front end (top-k + permutation + staging in one
 // launch): taken when the forward runs the GEMV family and the pairs fit the
 // one-workgroup permutation.

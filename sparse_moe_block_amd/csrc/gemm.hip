@@ -666,6 +666,7 @@ void launch_q(int q, const FwdArgs &a, const uint8_t *wa, const uint8_t *wb,
 
 hipError_t launch_gemm_gate_up(const FwdArgs &a, hipEvent_t routed_done, hipStream_t s) {
     if (a.d.act_quant == FW_ACT_MXFP8) return launch_gemm_mx_gate_up(a, routed_done, s);
+    if (a.d.act_quant == FW_ACT_INT8) return launch_gemm_i8_gate_up(a, routed_done, s);
     const fw_moe_desc &d = a.d;
     const _Float16 *x = (const _Float16 *)(a.ws + a.L.x16);
     _Float16 *h = (_Float16 *)(a.ws + a.L.h);
@@ -681,6 +682,7 @@ hipError_t launch_gemm_gate_up(const FwdArgs &a, hipEvent_t routed_done, hipStre
 
 hipError_t launch_gemm_down(const FwdArgs &a, hipStream_t s) {
     if (a.d.act_quant == FW_ACT_MXFP8) return launch_gemm_mx_down(a, s);
+    if (a.d.act_quant == FW_ACT_INT8) return launch_gemm_i8_down(a, s);
     const fw_moe_desc &d = a.d;
     const _Float16 *h = (const _Float16 *)(a.ws + a.L.h);
     float *y = (float *)(a.ws + a.L.y);

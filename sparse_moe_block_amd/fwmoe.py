@@ -26,8 +26,8 @@ QTYPES = {"q8_0": FW_Q8_0, "q4_0": FW_Q4_0, "q4_k": FW_Q4_K, "q6_k": FW_Q6_K,
           "mxfp4": FW_MXFP4}
 SCORES = {"softmax": FW_SOFTMAX_RENORM, "sigmoid": FW_SIGMOID_RENORM}
 PATHS = {"auto": FW_PATH_AUTO, "gemv": FW_PATH_GEMV, "gemm": FW_PATH_GEMM}
-FW_ACT_NONE, FW_ACT_MXFP8 = 0, 1
-ACT_QUANTS = {"none": FW_ACT_NONE, "mxfp8": FW_ACT_MXFP8}
+FW_ACT_NONE, FW_ACT_MXFP8, FW_ACT_INT8 = 0, 1, 2
+ACT_QUANTS = {"none": FW_ACT_NONE, "mxfp8": FW_ACT_MXFP8, "int8": FW_ACT_INT8}
 
 
 class FwMoeError(RuntimeError):

@@ -223,6 +223,27 @@ def test_mx8_mode_refusals():
     assert fw.fw_moe_validate(d(shared_ffn=256, shared_q="q8_0")) == fw.FW_EUNSUPPORTED
     assert fw.fw_moe_validate(d(shared_ffn=256, shared_q="mxfp4")) == fw.FW_OK
     assert fw.fw_moe_validate(d(path="gemv")) == fw.FW_EUNSUPPORTED
-    assert fw.fw_moe_validate(d(act_quant=2)) == fw.FW_EINVAL
+    assert fw.fw_moe_validate(d(act_quant=3)) == fw.FW_EINVAL
+    assert fw.fw_moe_validate(d(act_quant=-1)) == fw.FW_EINVAL
+    assert fw.fw_moe_forward_path(d(), 1) == fw.FW_PATH_GEMM
+    assert fw.fw_moe_forward_path(d(), 4096) == fw.FW_PATH_GEMM
+
+
+def test_int8_mode_refusals():
+    """int8 activations need Q8_0 or Q4_0 experts (and shared expert) and the
+    grouped-GEMM family; AUTO takes the GEMM at every T."""
+    def d(**kw):
+        base = dict(hidden=2048, n_experts=128, top_k=8, ffn=768, expert_q="q4_0",
+                    act_quant="int8")
+        base.update(kw)
+        return fw.make_desc(**base)
+    assert fw.fw_moe_validate(d()) == fw.FW_OK
+    assert fw.fw_moe_validate(d(expert_q="q8_0")) == fw.FW_OK
+    for q in ("q4_k", "q6_k", "mxfp4"):
+        assert fw.fw_moe_validate(d(expert_q=q)) == fw.FW_EUNSUPPORTED
+        assert fw.fw_moe_validate(d(shared_ffn=256, shared_q=q)) == fw.FW_EUNSUPPORTED
+    assert fw.fw_moe_validate(d(shared_ffn=256, shared_q="q8_0")) == fw.FW_OK
+    assert fw.fw_moe_validate(d(path="gemv")) == fw.FW_EUNSUPPORTED
+    assert fw.fw_moe_validate(d(path="gemm")) == fw.FW_OK
     assert fw.fw_moe_forward_path(d(), 1) == fw.FW_PATH_GEMM
     assert fw.fw_moe_forward_path(d(), 4096) == fw.FW_PATH_GEMM

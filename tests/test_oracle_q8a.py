@@ -108,7 +108,7 @@ def test_q8a_layer_float64(ref, qtype, shared):
         kw.update(s_gate=L.s_gate.numpy(), s_up=L.s_up.numpy(), s_down=L.s_down.numpy(),
                   shared_ffn=shared, shared_q="q8_0")
     out = ref.forward(x, L.w_gate.numpy(), L.w_up.numpy(), L.w_down.numpy(), ids, w,
-                      act_quant="q8a", **kw)
+                      act_quant="int8", **kw)
     H, F, E = cfg.hidden, cfg.ffn, cfg.n_experts
     dq = lambda buf, R, n, qt=qtype: np_ref.dequant_matrix(qt, buf, R, n)
     Wg = dq(L.w_gate.numpy(), E * F, H).reshape(E, F, H)
@@ -149,4 +149,4 @@ def test_q8a_needs_q8_0_or_q4_0(ref):
     with pytest.raises(ValueError):
         ref.forward(x, L.w_gate.numpy(), L.w_up.numpy(), L.w_down.numpy(), ids, w,
                     n_experts=cfg.n_experts, ffn=cfg.ffn, qtype="mxfp4", act_dtype="f32",
-                    act_quant="q8a")
+                    act_quant="int8")
