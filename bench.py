@@ -30,6 +30,7 @@ from sparse_moe_block_amd import fwmoe as fw  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 MFMA_FP16_PEAK_TFLOPS = 2500.0
 MFMA_FP8_PEAK_TFLOPS = 5000.0    # dense fp8 (E4M3 x E2M1 runs at the fp8 rate)
+MFMA_INT8_PEAK_TOPS = 5000.0     # dense int8
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)"
 CSRC = os.path.join(ROOT, "sparse_moe_block_amd", "csrc")
 # sources that decide each dominant kernel's memory traffic (a change to any
@@ -38,7 +39,9 @@ TRAFFIC_SOURCES = {"gemv_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip"
                    "gemm_mx_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "stages.h",
                                                "gemm_mx.hip"],
                    "gemm_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "gemm_frag.h",
-                                            "gemm.hip"]}
+                                            "gemm.hip"],
+                   "gemm_i8_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "stages.h",
+                                               "gemm_i8.hip"]}
 
 N_STAGES = fw.FW_N_STAGE_EVENTS - 1   # front/staging, gate/up routed, shared, down, combine
 HEADLINE = "deepseek4096"   # the largest configuration, MFMA-bound (grouped GEMM)
@@ -67,6 +70,9 @@ WORKLOADS = {
                         2048, 4),
     "deepseek4096_mx8": (moegen.DEEPSEEK.with_(expert_q=moegen.MXFP4, shared_q=moegen.MXFP4,
                                                act_quant="mxfp8"), 4096, 1),
+    # int8 activations (Q8_1-style blocks) on the int8 MFMA
+    "prefill2048_int8": (moegen.QWEN3_PREFILL.with_(act_quant="int8"), 2048, 4),
+    "deepseek4096_int8": (moegen.DEEPSEEK.with_(act_quant="int8"), 4096, 1),
     # and on Q8_0 experts (the sweep's other format)
     "decode16_q8": (moegen.QWEN3_DECODE.with_(expert_q=moegen.Q8_0), 16, 8),
     "prefill2048_q8": (moegen.QWEN3_PREFILL.with_(expert_q=moegen.Q8_0), 2048, 2),
@@ -293,11 +299,12 @@ def measure(a, workload, steps, warmup, setup_only=False):
         # flops: 2 projections x 2 flops x P x H x F
         gu_alg = 4 * P * H * cfg.ffn
         achieved = gu_alg / (gu_ms * 1e-3) / 1e12
-        mx8 = cfg.act_quant == "mxfp8"
-        peak = MFMA_FP8_PEAK_TFLOPS if mx8 else MFMA_FP16_PEAK_TFLOPS
-        roof = {"kernel": "gemm_mx_kernel<gate/up>" if mx8 else "gemm_kernel<gate/up>",
-                "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": None,
+        kernel, peak, unit = {
+            "none": ("gemm_kernel<gate/up>", MFMA_FP16_PEAK_TFLOPS, "TFLOP/s"),
+            "mxfp8": ("gemm_mx_kernel<gate/up>", MFMA_FP8_PEAK_TFLOPS, "TFLOP/s"),
+            "int8": ("gemm_i8_kernel<gate/up>", MFMA_INT8_PEAK_TOPS, "TOP/s")}[cfg.act_quant]
+        roof = {"kernel": kernel, "bound": "mfma", "achieved": achieved, "peak": peak,
+                "unit": unit, "frac": achieved / peak, "traffic": None,
                 "algorithmic_flops": gu_alg}
     roof["duration_us"] = gu_ms * 1e3
     layer_bytes = (n_active * cfg.expert_bytes + cfg.shared_bytes + cfg.router_bytes +
@@ -318,11 +325,11 @@ def measure(a, workload, steps, warmup, setup_only=False):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 x e2m1" if cfg.act_quant == "mxfp8" else "f16",
+        "dtype": {"none": "f16", "mxfp8": "e4m3 x e2m1", "int8": "i8"}[cfg.act_quant],
         "data": "synthetic (seeded N(0,0.02) weights quantized to GGUF blocks, N(0,1) bf16 tokens)",
         "config": {"workload": f"{cfg.name}, T={T}", "hidden": H, "experts": E, "top_k": k,
                    "ffn": cfg.ffn, "expert_format": cfg.expert_q, "shared_ffn": cfg.shared_ffn,
-                   "activations": "mxfp8" if cfg.act_quant == "mxfp8" else "fp16",
+                   "activations": {"none": "fp16"}.get(cfg.act_quant, cfg.act_quant),
                    "tokens": T, "active_experts": n_active, "weight_copies": copies,
                    "path": "gemv" if path == fw.FW_PATH_GEMV else "gemm"},
         "timing": "hip-graph replay per step" if graph_ms is not None else "direct launches",
@@ -529,7 +536,8 @@ def source_hash(kernel):
 # dominant kernel: label in the JSON line, mangled-name fragment in counter files
 KERNELS = {"gemv_kernel<gate/up>": ("gemv_gate_up", "gemv_kernelILi"),
            "gemm_mx_kernel<gate/up>": ("gemm_mx_gate_up", "gemm_mx_kernelILb1E"),
-           "gemm_kernel<gate/up>": ("gemm_gate_up", "gemm_kernelILi")}
+           "gemm_kernel<gate/up>": ("gemm_gate_up", "gemm_kernelILi"),
+           "gemm_i8_kernel<gate/up>": ("gemm_i8_gate_up", "gemm_i8_kernelILi")}
 
 
 def traffic_path(workload, kernel):
@@ -574,6 +582,9 @@ def reduce_counters(a):
     if cfg.act_quant == "mxfp8":
         kernel = "gemm_mx_kernel<gate/up>"
         frags = (KERNELS[kernel][1], "gemm_mx_kernel<true>")
+    if cfg.act_quant == "int8":
+        kernel = "gemm_i8_kernel<gate/up>"
+        frags = (KERNELS[kernel][1] + qi + "ELb1E", "gemm_i8_kernel<" + qi + ", true")
 
     both = cfg.shared_ffn > 0 and cfg.shared_q == cfg.expert_q
 
