@@ -42,9 +42,13 @@ CASES = [
     (C.QWEN3_DECODE.with_(expert_q=C.MXFP4, act_quant="mxfp8"), 1, "auto"),
     (C.QWEN3_PREFILL.with_(expert_q=C.MXFP4, act_quant="mxfp8"), 2048, "auto"),
     (C.DEEPSEEK.with_(expert_q=C.MXFP4, shared_q=C.MXFP4, act_quant="mxfp8"), 64, "auto"),
+    # int8 activations on the int8 MFMA (the GEMM family at every T)
+    (C.QWEN3_DECODE.with_(act_quant="int8"), 4, "auto"),
+    (C.QWEN3_PREFILL.with_(act_quant="int8"), 2048, "auto"),
+    (C.DEEPSEEK.with_(act_quant="int8"), 64, "auto"),
 ]
-IDS = [f"c{c.cid}-{c.expert_q}{'-mx8' if c.act_quant == 'mxfp8' else ''}-T{T}-{p}"
-       for c, T, p in CASES]
+AQ = {"none": "", "mxfp8": "-mx8", "int8": "-int8"}
+IDS = [f"c{c.cid}-{c.expert_q}{AQ[c.act_quant]}-T{T}-{p}" for c, T, p in CASES]
 
 
 def _three_calls(desc, cfg, dl, x):
@@ -70,7 +74,7 @@ def _one_call(desc, cfg, dl, x):
     fw.fw_moe_layer(desc, T, x, L.router, L.bias, L.w_gate, L.w_up, L.w_down, L.s_gate,
                     L.s_up, L.s_down, logits, ids, w, off, sp, inv, out, ws)
     assert fw.fw_moe_read_status(ws) == 0
-    return logits, ids, w, off, sp, inv, out
+    return logits, ids, w, off, sp, inv, out, ws
 
 
 @pytest.mark.parametrize("cfg,T,path", CASES, ids=IDS)
@@ -86,7 +90,7 @@ def test_layer_matches_three_calls_and_oracle(ref, cfg, T, path):
         assert torch.equal(a, b), f"{name} differs from the three calls"
     # against the oracle: tokens without a near tie were routed as the oracle
     # routes them, and their outputs agree within the layer tolerance
-    logits, ids, w, _, _, _, out = (t.cpu().numpy() for t in one)
+    logits, ids, w, _, _, _, out = (t.cpu().numpy() for t in one[:7])
     rl, rids, rw = G.oracle_route(ref, cfg, dl, xh)
     assert np.abs(logits - rl).max() <= G.LOGIT_MAX_ABS
     ok = ~G.small_gaps(rl, cfg.top_k)
@@ -98,5 +102,8 @@ def test_layer_matches_three_calls_and_oracle(ref, cfg, T, path):
     if cfg.act_quant == "mxfp8":
         from tests.test_gpu_mx8 import check_mx8
         check_mx8(out[tok], want)
+    elif cfg.act_quant == "int8":
+        from tests.test_gpu_int8 import check_int8, down_max_abs, h_step_max
+        check_int8(out[tok], want, h_step_max(desc, cfg, one[7], T) * down_max_abs(cfg, dl))
     else:
         G.check_out(out[tok], want)

@@ -18,12 +18,15 @@ C = moegen
 MX8 = dict(expert_q=C.MXFP4, act_quant="mxfp8")
 CASES = [(C.QWEN3_DECODE, 16, "auto"), (C.DEEPSEEK, 1, "auto"), (C.DEEPSEEK, 32, "auto"),
          (C.QWEN3_PREFILL, 256, "gemm"), (C.QWEN3_DECODE.with_(**MX8), 16, "auto"),
-         (C.DEEPSEEK.with_(shared_q=C.MXFP4, **MX8), 32, "auto")]
+         (C.DEEPSEEK.with_(shared_q=C.MXFP4, **MX8), 32, "auto"),
+         (C.QWEN3_DECODE.with_(act_quant="int8"), 16, "auto"),
+         (C.DEEPSEEK.with_(act_quant="int8"), 32, "auto")]
 
 
 @pytest.mark.parametrize("one_call", [False, True], ids=["three-calls", "fw_moe_layer"])
 @pytest.mark.parametrize("cfg,T,path", CASES, ids=["c1-T16", "c3-T1", "c3-T32", "c2-T256-gemm",
-                                                  "c1-mx8-T16", "c3-mx8-T32"])
+                                                  "c1-mx8-T16", "c3-mx8-T32", "c1-int8-T16",
+                                                  "c3-int8-T32"])
 def test_graph_replays_equal_eager(cfg, T, path, one_call):
     print(f"graph {cfg.name} T={T} {path} one_call={one_call}", flush=True)
     dl = G.layer(cfg)

@@ -152,3 +152,32 @@ def test_mx8_bad_offsets_and_pairs_flagged_and_contained(ref):
     assert intact
     status, intact, _ = _run_forward(desc, cfg, dl, x, d(w), d(roff), d(rsp), d(rinv))
     assert status == 0 and intact
+
+
+I8 = C.QWEN3_DECODE.with_(act_quant="int8")
+
+
+def test_int8_bad_offsets_and_pairs_flagged_and_contained(ref):
+    """The int8 kernels share the grouped GEMM's tile list and its clamps:
+    corrupt offsets and pair ids are flagged and contained."""
+    cfg, T = I8, 16
+    print(f"bad offsets and pairs, int8 mode, T={T}", flush=True)
+    dl = G.layer(cfg)
+    desc = G.desc_of(cfg)
+    x = moegen.make_x(cfg, T, device=G.DEV)
+    ids, w = _routing(cfg, T, seed=5)
+    P = T * cfg.top_k
+    roff, rsp, rinv = ref.permute(ids, cfg.n_experts)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(G.DEV)
+    off = np.array([0 if e % 2 == 0 else 1 for e in range(cfg.n_experts + 1)], np.int32)
+    status, intact, _ = _run_forward(desc, cfg, dl, x, d(w), d(off), d(rsp), d(rinv))
+    assert status & fw.FW_STATUS_BAD_OFFSETS
+    assert intact, "bytes outside the workspace were written"
+    sp = rsp.copy()
+    sp[3], sp[P - 1] = -3, P + 5
+    status, intact, _ = _run_forward(desc, cfg, dl, x, d(w), d(roff), d(sp), d(rinv))
+    assert status & fw.FW_STATUS_BAD_PAIR
+    assert (status & fw.FW_STATUS_BAD_OFFSETS) == 0
+    assert intact
+    status, intact, _ = _run_forward(desc, cfg, dl, x, d(w), d(roff), d(rsp), d(rinv))
+    assert status == 0 and intact

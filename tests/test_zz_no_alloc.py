@@ -55,13 +55,15 @@ def _no_alloc(desc, cfg, L, x):
 # (config, first T, second T): decode batches of the DeepSeek-shaped layer
 # (GEMV family, fused front end, shared expert, split-K at T = 1), a
 # Qwen3-shaped batch on the grouped GEMM followed by a decode batch, and the
-# MXFP8-activation mode (block-scaled GEMMs at every T)
+# MXFP8-activation mode (block-scaled GEMMs at every T), and the int8 one
 MX8 = C.QWEN3_DECODE.with_(expert_q=C.MXFP4, act_quant="mxfp8")
+I8 = C.QWEN3_DECODE.with_(act_quant="int8")
 
 
 @pytest.mark.parametrize("cfg,T1,T2", [(C.DEEPSEEK, 32, 1), (C.QWEN3_DECODE, 256, 16),
-                                       (MX8, 64, 4)],
-                         ids=["deepseek-32-then-1", "qwen3-256-then-16", "qwen3-mx8-64-then-4"])
+                                       (MX8, 64, 4), (I8, 64, 4)],
+                         ids=["deepseek-32-then-1", "qwen3-256-then-16", "qwen3-mx8-64-then-4",
+                              "qwen3-int8-64-then-4"])
 def test_noalloc_matches_workspace_call(cfg, T1, T2):
     print(f"no-alloc {cfg.name} T={T1} then T={T2}", flush=True)
     dl = G.layer(cfg)
