@@ -462,8 +462,9 @@ def peaks(a):
     """The two ceilings, measured on this GPU with libfwpeak.so: dense fp16
     MFMA throughput (16x16x32 and 32x32x16, every SIMD busy, eight independent
     accumulators per wavefront) and HBM streaming bandwidth (a 4 GiB read with
-    16-byte loads; a 2 GiB copy).  One JSON line per figure, each the best of
-    five timed launches after a warm-up."""
+    16-byte loads; a 2 GiB copy); and the price of a grid-wide rendezvous
+    inside one kernel.  One JSON line per figure, each the best of five timed
+    launches after a warm-up."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "sparse_moe_block_amd", "libfwpeak.so"))
     lib.fw_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -523,6 +524,31 @@ def peaks(a):
         print(json.dumps({"peak": "hbm copy (read + write)", "bytes_moved": 2 * half,
                           "workgroups": blocks, "seconds": t,
                           "GB/s": 2 * half / t / 1e9}), flush=True)
+    del src, dst
+    # one grid-wide rendezvous inside a kernel: (101 rounds - 1 round) / 100
+    lib.fw_peak_grid_barrier.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 4
+    for blocks in (cus // 2, cus, 2 * cus):
+        for fence in (0, 1):
+            per = {}
+            for rounds in (1, 101):
+                flags = torch.zeros(blocks * 16, dtype=torch.int32, device=dev)
+                data = torch.zeros(blocks * 256, dtype=torch.float32, device=dev)
+                err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+                def launch():
+                    flags.zero_()
+                    err.zero_()
+                    lib.fw_peak_grid_barrier(blocks, rounds, 200000, fence,
+                                             ctypes.c_void_p(flags.data_ptr()),
+                                             ctypes.c_void_p(data.data_ptr()),
+                                             ctypes.c_void_p(err.data_ptr()),
+                                             ctypes.c_void_p(stream.cuda_stream))
+                per[rounds] = best(launch)
+                if int(err.item()):
+                    sys.exit("grid barrier: a poll gave up (grid not co-resident)")
+            print(json.dumps({"peak": "grid-wide rendezvous in one kernel", "workgroups": blocks,
+                              "device_fence": bool(fence),
+                              "us_per_round": (per[101] - per[1]) / 100 * 1e6}), flush=True)
 
 
 def source_hash(kernel):

@@ -10,6 +10,14 @@
 //  - fw_peak_read: a grid-stride read of a buffer with 16-byte loads, four in
 //    flight per lane, folded into one XOR per thread that is written out.
 //  - fw_peak_copy: the same stride, reading and writing (a copy).
+//  - fw_peak_grid_barrier: the price of one grid-wide rendezvous inside a
+//    kernel, what a single persistent kernel pays between dependent phases
+//    (router logits -> routing, gate/up -> down, down -> combine): every
+//    workgroup writes a payload, releases it (optionally behind a full
+//    device-scope fence), publishes a per-workgroup flag, polls every flag
+//    with relaxed loads and acquires once.  Polls are bounded (they give up
+//    after `limit` tries and set *err), so a grid that is not co-resident
+//    ends instead of hanging.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -96,6 +104,36 @@ __global__ __launch_bounds__(256) void copy_kernel(const uint4 *__restrict__ src
         dst[i] = src[i];
 }
 
+// flags: gridDim.x flags 64 bytes apart, zero before the launch
+__global__ __launch_bounds__(256) void grid_barrier_kernel(int *flags, float *data, int rounds,
+                                                           int limit, int fence,
+                                                           int *err) {
+    const int G = gridDim.x, wg = blockIdx.x, t = threadIdx.x;
+    for (int r = 1; r <= rounds; ++r) {
+        data[(size_t)wg * 256 + t] = (float)(r + t);
+        if (fence) __threadfence();
+        __syncthreads();
+        if (t == 0)
+            __hip_atomic_store(&flags[wg * 16], r, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        bool ok = true;
+        for (int f = t; f < G; f += 256) {
+            int n = 0;
+            while (__hip_atomic_load(&flags[f * 16], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT) < r) {
+                if (++n > limit) {
+                    ok = false;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        if (!ok) atomicOr(err, 1);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __syncthreads();
+        if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,6 +169,21 @@ int fw_peak_copy(const void *src, void *dst, size_t bytes, int blocks, void *str
     if (!src || !dst || bytes % 16 || blocks < 1) return hipErrorInvalidValue;
     copy_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>((const uint4 *)src, (uint4 *)dst,
                                                          bytes / 16);
+    return hipGetLastError();
+}
+
+/* `rounds` grid-wide rendezvous of `blocks` workgroups of 256 threads (see
+ * grid_barrier_kernel; fence: a device-scope fence after each round's
+ * payload).  flags: blocks * 16 ints, data: blocks * 256 floats, err: one
+ * int, all zeroed by the caller; *err != 0 afterwards means a poll gave up
+ * (the grid was not co-resident).  blocks must not exceed what the device
+ * holds at once. */
+int fw_peak_grid_barrier(int blocks, int rounds, int limit, int fence, int *flags, float *data,
+                         int *err, void *stream) {
+    if (blocks < 1 || rounds < 1 || limit < 1 || !flags || !data || !err)
+        return hipErrorInvalidValue;
+    grid_barrier_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>(flags, data, rounds, limit,
+                                                                 fence, err);
     return hipGetLastError();
 }
 
