@@ -195,3 +195,29 @@ def test_h_codes_valid(ref, cfg, T):
     print(f"  h codes differing at a rounding boundary: {n_diff} of {P * F}; "
           f"blocks whose scale differs in its last bits: {n_scale} of {P * F // 32}", flush=True)
     assert n_diff <= P * F // 100
+
+
+# Descriptor extremes (the edge-shape configs): the smallest hidden and ffn
+# with 512 experts and top-16, the largest hidden with top-1 sigmoid routing,
+# uneven step counts with k = E and a Q4_0 shared expert, one expert with
+# fp32 activations.
+def _edge_cases():
+    from tests.test_gpu_edge_shapes import EDGE_MIN, EDGE_ONE, EDGE_RAGGED, EDGE_WIDE
+    return [(c.with_(**I8), T) for c, Ts in [(EDGE_MIN, (1, 33)), (EDGE_WIDE, (1, 40)),
+                                             (EDGE_RAGGED, (9, 70)), (EDGE_ONE, (3, 100))]
+            for T in Ts]
+
+
+EDGE = _edge_cases()
+
+
+@pytest.mark.parametrize("cfg,T", EDGE, ids=[f"c{c.cid}-T{T}" for c, T in EDGE])
+def test_edge_shapes_int8(ref, cfg, T):
+    print(f"edge int8 {cfg.name} T={T}", flush=True)
+    dl, desc, x, xh, rids, rw, ws, out, _ = run(ref, cfg, T)
+    assert fw.fw_moe_read_status(ws) == 0
+    want = G.oracle_forward(ref, cfg, dl, xh, rids, rw)
+    step = h_step_max(desc, cfg, ws, T) * down_max_abs(cfg, dl)
+    err, rel, n_big = check_int8(out, want, step)
+    print(f"  max-abs {err:.2e} rel-L2 {rel:.2e}; elements above {G.OUT_MAX_ABS}: {n_big}",
+          flush=True)
