@@ -135,7 +135,7 @@ static size_t row_bytes(int qtype, int n)
 static double e2m1_value(int code)
 {
     int ex = (code >> 1) & 3, m = code & 1;
-    double v = ex == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, ex - 1);
+    double v = ex == 0 ? 0.5 * m : (1.0 + 0.5 * m) * (double)(1 << (ex - 1));
     return code & 8 ? -v : v;
 }
 
@@ -144,10 +144,13 @@ static void mxfp4_row(const uint8_t *base, size_t R, size_t r, int n, float *out
 {
     const uint8_t *codes = base + r * (size_t)(n / 2);
     const uint8_t *scales = base + R * (size_t)(n / 2) + r * (size_t)(n / 32);
-    for (int j = 0; j < n; ++j) {
-        int code = j % 2 ? codes[j / 2] >> 4 : codes[j / 2] & 15;
-        int s = scales[j / 32];
-        out[j] = s == 255 ? NAN : (float)ldexp(e2m1_value(code), s - 127);
+    for (int b = 0; b < n / 32; ++b) {
+        int s = scales[b];
+        double x = ldexp(1.0, s - 127);   /* the block's scale 2^(s - 127), exact */
+        for (int j = 32 * b; j < 32 * b + 32; ++j) {
+            int code = j % 2 ? codes[j / 2] >> 4 : codes[j / 2] & 15;
+            out[j] = s == 255 ? NAN : (float)(e2m1_value(code) * x);
+        }
     }
 }
 

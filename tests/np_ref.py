@@ -182,3 +182,15 @@ def q8a_round_trip(v):
     """fp32 values -> float64 d * code after the int8 round trip."""
     c, d = q8a_quantize(v)
     return c.astype(np.float64) * np.repeat(d.astype(np.float64), 32)
+
+
+def matrix_rows(qtype, buf, R, n, r0, r1):
+    """Rows r0 .. r1 - 1 of an R x n matrix of any format -> float64 [r1 - r0, n]
+    (decoding only those rows)."""
+    buf = np.asarray(buf, dtype=np.uint8).reshape(-1)
+    if qtype == "mxfp4":
+        codes = buf[:R * n // 2].reshape(R, n // 2)[r0:r1]
+        sc = buf[R * n // 2:R * n // 2 + R * n // 32].reshape(R, n // 32)[r0:r1]
+        return mxfp4_matrix(np.concatenate([codes.reshape(-1), sc.reshape(-1)]), r1 - r0, n)
+    rb = buf.size // R
+    return dequant(qtype, buf.reshape(R, rb)[r0:r1], n)

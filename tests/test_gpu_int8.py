@@ -149,8 +149,13 @@ def test_h_codes_valid(ref, cfg, T):
     so = ho + P * F + T * cfg.shared_ffn
     hs = raw[so:so + P * F // 8].view(np.float32).reshape(P, F // 32)
     hh = dl.host
-    Wg = np_ref.dequant_matrix(cfg.expert_q, hh["w_gate"], E * F, H).reshape(E, F, H)
-    Wu = np_ref.dequant_matrix(cfg.expert_q, hh["w_up"], E * F, H).reshape(E, F, H)
+    cache = {}
+
+    def gate_up(e):   # expert e's gate and up rows, decoded once
+        if e not in cache:
+            cache[e] = tuple(np_ref.matrix_rows(cfg.expert_q, hh[m], E * F, H, e * F, (e + 1) * F)
+                             for m in ("w_gate", "w_up"))
+        return cache[e]
     xf = np_ref.act(xh).astype(np.float32)
     n_diff = n_scale = 0
     for row in range(P):
@@ -158,9 +163,10 @@ def test_h_codes_valid(ref, cfg, T):
         t, e = q // k, int(rids.reshape(-1)[q])
         xc, xs = ref.q8a_quantize(xf[t])
         xq = xc.astype(np.float64) * np.repeat(xs.astype(np.float64), 32)
-        g, u = Wg[e] @ xq, Wu[e] @ xq
-        dg = ACC_REL * (np.abs(Wg[e]) @ np.abs(xq))
-        du = ACC_REL * (np.abs(Wu[e]) @ np.abs(xq))
+        Wge, Wue = gate_up(e)
+        g, u = Wge @ xq, Wue @ xq
+        dg = ACC_REL * (np.abs(Wge) @ np.abs(xq))
+        du = ACC_REL * (np.abs(Wue) @ np.abs(xq))
         sg = 1.0 / (1.0 + np.exp(-g))
         a64 = g * sg * u
         da = np.abs((sg + g * sg * (1 - sg)) * u) * dg + np.abs(g * sg) * du + dg * du
