@@ -12,6 +12,11 @@ here against the CPU oracle on the same bytes:
     weights: in range, so within the layer tolerance and no status bit;
   - a block scale of 65504 (fp16's largest) and a non-finite activation: the
     status bit is set.
+The int8-activation mode (Q8_0 / Q4_0 experts) holds activations and the
+SwiGLU output as int8 blocks with fp32 scales and applies the weights' fp16
+scales in fp32, so it has no such limits: the same rows of any scale, the
+edge blocks and a block scale of 65504 all match the oracle's int8 mode, with
+no status bit; a non-finite activation still sets it.
 """
 
 import numpy as np
@@ -53,7 +58,8 @@ def _run(cfg, qtype, path, L, xh, ids, w, ref):
     torch.cuda.synchronize()
     status = fw.fw_moe_read_status(ws)
     want = ref.forward(xh, L["w_gate"], L["w_up"], L["w_down"], ids, w,
-                       n_experts=cfg.n_experts, ffn=cfg.ffn, qtype=qtype, act_dtype="bf16")
+                       n_experts=cfg.n_experts, ffn=cfg.ffn, qtype=qtype, act_dtype="bf16",
+                       act_quant=cfg.act_quant)
     return status, out.cpu().numpy(), want
 
 
@@ -173,4 +179,55 @@ def test_out_of_range_is_flagged(ref, qtype, path):
     xb = xh.copy()
     xb[3, 17] = 0x7F80                                         # bf16 +inf
     status, _, _ = _run(cfg, qtype, path, L, xb, ids, w, ref)
+    assert status & fw.FW_STATUS_RANGE, status
+
+
+I8 = BASE.with_(act_quant="int8")
+
+
+def _check_rows(got, want, scales):
+    worst = [0.0, 0.0]
+    for t, sc in enumerate(scales):
+        d, r = got[t] - want[t], want[t]
+        rel = np.linalg.norm(d) / np.linalg.norm(r)
+        mx = np.abs(d).max() / np.abs(r).max()
+        worst = [max(worst[0], rel), max(worst[1], mx)]
+        assert rel <= G.OUT_REL_L2 and mx <= 4e-3, (t, sc, rel, mx)
+    return worst
+
+
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+def test_int8_rows_of_any_scale(ref, qtype):
+    """int8 mode: each row within relative L2 1e-3 and a max error of 4e-3 of
+    its own largest output, against the oracle's int8 mode."""
+    print(f"row scales int8 {qtype}", flush=True)
+    L = _host_layer(I8, qtype)
+    xh = _x_rows(I8, SCALES)
+    ids, w = _routing(I8, len(SCALES))
+    status, got, want = _run(I8, qtype, "auto", L, xh, ids, w, ref)
+    assert status == 0, status
+    assert np.all(np.isfinite(got))
+    worst = _check_rows(got, want, SCALES)
+    print(f"  worst row: rel-L2 {worst[0]:.2e}, max error / row max {worst[1]:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("qtype", ["q4_0", "q8_0"])
+def test_int8_edge_blocks_and_largest_scale(ref, qtype):
+    """int8 mode: the edge blocks (subnormal and negative scales, extreme
+    codes) and a block scale of 65504 in gate row 0 of every expert stay in
+    range: no status bit, rows within the relative criteria; a non-finite
+    activation sets FW_STATUS_RANGE."""
+    print(f"edge blocks and largest scale int8 {qtype}", flush=True)
+    T = 24
+    xh = moegen.as_numpy_bits(moegen.make_x(I8, T))
+    ids, w = _routing(I8, T, seed=7)
+    L = _edge_weights(I8, qtype)
+    L["w_gate"][:, 0, 0:2] = np.frombuffer(np.uint16(0x7BFF).tobytes(), np.uint8)
+    status, got, want = _run(I8, qtype, "auto", L, xh, ids, w, ref)
+    assert status == 0, status
+    assert np.all(np.isfinite(got))
+    _check_rows(got, want, range(T))
+    xb = xh.copy()
+    xb[3, 17] = 0x7F80                                         # bf16 +inf
+    status, _, _ = _run(I8, qtype, "auto", _host_layer(I8, qtype), xb, ids, w, ref)
     assert status & fw.FW_STATUS_RANGE, status
