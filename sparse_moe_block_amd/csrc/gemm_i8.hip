@@ -10,11 +10,14 @@
 // The contraction.  GGUF scales are per 32-element block of both operands, so
 // one v_mfma_i32_32x32x32_i8 covers exactly one block: its K of 32 is the
 // block.  Its exact int32 dot products S then take the block's two scales:
-// y += (d_x d_w) S.  The products d_x d_w of a 32 x 32 tile are an outer
-// product, formed on the matrix cores as well (v_mfma_f32_32x32x2_f32 with the
-// second k term zero: each lane supplies one d_x and one d_w), so the VALU
-// work is a conversion and an fma per output and block -- the part that
-// bounds this kernel (32 VALU instructions per 32-cycle int8 MFMA).
+// y += (d_x d_w) S, a conversion, a product and an fma per output and block
+// on the VALU -- the part that bounds this kernel (48 VALU instructions per
+// 32-cycle int8 MFMA).  A lane's 16 outputs share its weight row (one d_w)
+// and span 16 token rows, whose d_x it reads from LDS as four 16-byte runs
+// (the step's activation scales sit there block-major).  Forming the d_x d_w
+// tile on the matrix cores instead (an fp32 outer-product MFMA) saves the
+// products but makes every tile's scaling wait for a second MFMA; Q8_0 does
+// that all the same, its register budget having no room for the d_x runs.
 //
 // Weights reach the MFMA as stored: Q8_0 codes are int8 already; Q4_0 codes q
 // become the int8 16 (q - 8) = (q << 4) ^ 0x80 (low nibble) or (q & 0xF0) ^
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(IThreads, 1) void gemm_i8_kernel(
     // two buffer sets, each its own array (the compiler tells a pending DMA
     // into one from reads of the other only when they are distinct objects)
     __shared__ uint4 A0[kIAChunks], A1[kIAChunks];
-    __shared__ float AS0[IBM * 4], AS1[IBM * 4];   // per row, the step's four block scales
+    __shared__ float AS0[4 * IBM], AS1[4 * IBM];   // the step's block scales, [block][row]
     static_assert(WD <= kIMaxWDma, "weight pieces");
     __shared__ uint4 B0[WD * IThreads], B1[WD * IThreads];
     auto Abuf = [&](int buf) { return buf ? A1 : A0; };
@@ -221,8 +224,9 @@ __global__ __launch_bounds__(IThreads, 1) void gemm_i8_kernel(
         const int s = i * IThreads + tid, r = s / 8, c = (s % 8) ^ (r % 8);
         aoff[i] = (uint32_t)src_row(r) * (uint32_t)K + 16u * c;
     }
-    // activation scales: slot tid is scale tid % 4 of the step, row tid / 4
-    const uint32_t asoff = ((uint32_t)src_row(tid / 4) * (uint32_t)(K / 32) + (tid % 4)) * 4u;
+    // activation scales: slot tid is block tid / 128 of the step, tile row
+    // tid % 128
+    const uint32_t asoff = ((uint32_t)src_row(tid % IBM) * (uint32_t)(K / 32) + tid / IBM) * 4u;
     // weight rows: LDS row Rl is matrix row wrow(Rl) of the expert (gate/up:
     // rows 128 .. 255 are the up matrix's)
     const size_t rowbytes = (size_t)(K / 32) * BB;
@@ -283,6 +287,8 @@ __global__ __launch_bounds__(IThreads, 1) void gemm_i8_kernel(
                         0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const int steps = K / IKS;
     const int Rw = 32 * wave + n;   // the lane's LDS weight row
+    // how a block tile's scales d_x d_w are formed (see FW_I8_BLOCK)
+    constexpr bool kVecScale = Q == FW_Q4_0;
 
     // one step from buffer set BUF (first piece byte 8 BUF); pf(b) issues the
     // next step's DMA after block b's MFMAs
@@ -292,42 +298,70 @@ __global__ __launch_bounds__(IThreads, 1) void gemm_i8_kernel(
         const uint4 *abuf = Abuf(BUF);
         const float *as = ASbuf(BUF);
         v4i a[2][MI], w[2];
-        float dx[2][MI], dw[2];
+        float dw[2];
+        float dxl[2][MI], dwl[2];   // Q8_0: the outer-product MFMA's operands
         auto load = [&](auto xc, auto bc) {
             constexpr int X = decltype(xc)::value, b = decltype(bc)::value;
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
                 const int r = 32 * mi + n;
                 a[X][mi] = __builtin_bit_cast(v4i, abuf[8 * r + ((2 * b + g) ^ (r % 8))]);
-                const float d = as[4 * r + b];
-                dx[X][mi] = g ? 0.0f : d;
+                if constexpr (!kVecScale) {
+                    const float d = as[IBM * b + r];
+                    dxl[X][mi] = g ? 0.0f : d;
+                }
             }
-            float d;
-            weight_frag<Q, 8 * BUF, b>(wrow, g, w[X], d);
-            dw[X] = g ? 0.0f : d;
+            weight_frag<Q, 8 * BUF, b>(wrow, g, w[X], dw[X]);
+            if constexpr (!kVecScale) dwl[X] = g ? 0.0f : dw[X];
+        };
+        // d_x of the lane's 16 output rows of group mi, block b: rows
+        // 32 mi + 8 j + 4 g + i (output element 4 j + i), four runs of 4
+        auto scales_x = [&](int b, int mi, float4 *dx) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                dx[j] = *(const float4 *)&as[IBM * b + 32 * mi + 8 * j + 4 * g];
         };
         load(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
     // Block B: the next block's operands are read first; then row group mi's
-    // two MFMAs are issued ahead of the scaling of group mi - 1's sums, so at
-    // most two groups' sums and scale tiles are live.
+    // MFMAs (and d_x reads) are issued ahead of the scaling of group mi - 1's
+    // sums, so at most two groups' sums and scales are live.
+    //  - Q4_0: d_x d_w on the VALU, d_x read a group ahead;
+    //  - Q8_0: its wider weight reads leave too few registers for that (the
+    //    VALU form spilled), so the d_x d_w tile comes from an fp32
+    //    outer-product MFMA (v_mfma_f32_32x32x2_f32, the second k term zero:
+    //    each lane supplies its row's d_x and its weight row's d_w).
 #define FW_I8_BLOCK(B)                                                                        \
     {                                                                                         \
         constexpr int X = (B) & 1;                                                            \
         if constexpr ((B) < 3)                                                                \
             load(std::integral_constant<int, X ^ 1>{}, std::integral_constant<int, (B) + 1>{}); \
         v16i s[2];                                                                            \
+        float4 dx[2][4];                                                                      \
         f16v c[2];                                                                            \
         _Pragma("unroll") for (int mi = 0; mi <= MI; ++mi) {                                  \
             if (mi < MI) {                                                                    \
                 s[mi & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[X][mi], w[X], izero, 0,   \
                                                                   0, 0);                      \
-                c[mi & 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(dx[X][mi], dw[X], fzero, 0,  \
-                                                                 0, 0);                       \
+                if constexpr (kVecScale) {                                                    \
+                    scales_x((B), mi, dx[mi & 1]);                                            \
+                } else {                                                                      \
+                    c[mi & 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(dxl[X][mi], dwl[X], fzero, \
+                                                                     0, 0, 0);                \
+                }                                                                             \
             }                                                                                 \
             if (mi > 0) {                                                                     \
                 const int p = (mi - 1) & 1;                                                   \
-                _Pragma("unroll") for (int v = 0; v < 16; ++v)                                \
-                    acc[mi - 1][v] = __builtin_fmaf((float)s[p][v], c[p][v], acc[mi - 1][v]); \
+                _Pragma("unroll") for (int v = 0; v < 16; ++v) {                              \
+                    float sc;                                                                 \
+                    if constexpr (kVecScale) {                                                \
+                        const float4 q = dx[p][v >> 2];                                       \
+                        sc = ((v & 3) == 0 ? q.x : (v & 3) == 1 ? q.y                         \
+                                                 : (v & 3) == 2 ? q.z : q.w) * dw[X];         \
+                    } else {                                                                  \
+                        sc = c[p][v];                                                         \
+                    }                                                                         \
+                    acc[mi - 1][v] = __builtin_fmaf((float)s[p][v], sc, acc[mi - 1][v]);      \
+                }                                                                             \
             }                                                                                 \
             __builtin_amdgcn_sched_barrier(0);                                                \
         }                                                                                     \
