@@ -9,11 +9,14 @@
 //
 // The weights reach the matrix cores as stored: no dequantisation at all.
 // Per workgroup a tile of up to 128 rows of one expert's pairs times 256
-// weight rows; four wavefronts (one per SIMD), each 128 rows x 64 weight rows
-// (four 32-row groups x two 32-column groups, 8 MFMAs per 64-k slice).  K
-// advances 256 per step (four slices); a step's activation codes (128 x 256
-// bytes) and scales, and its weight codes (256 x 128 bytes) and scales move
-// HBM/L2 -> LDS by DMA into one of two buffer sets while the other is used.
+// weight rows; eight wavefronts (two per SIMD), wavefront w taking row half
+// w / 4 (rows 64 (w / 4) ..) and weight quarter w % 4: 64 rows x 64 weight
+// rows, two 32-row groups x two 32-column groups, 4 MFMAs per 64-k slice.
+// (Four wavefronts of 128 rows each left one wavefront per SIMD, nothing to
+// run while it waited at the step's rendezvous.)  K advances 256 per step
+// (four slices); a step's activation codes (128 x 256 bytes) and scales, and
+// its weight codes (256 x 128 bytes) and scales move HBM/L2 -> LDS by DMA
+// into one of two buffer sets while the other is used.
 //
 // Operand layout of the MFMA (per lane l, i = l % 32, h = l / 32; within a
 // 64-k slice): the E4M3 operand's 32 bytes are k 16h .. 16h + 15 then
@@ -33,7 +36,7 @@ namespace {
 constexpr int MBM = kGemmBM;     // token rows per tile
 constexpr int MBN = 256;         // weight rows per tile
 constexpr int MKS = 256;         // k per step
-constexpr int MNW = 4;           // wavefronts per workgroup (one per SIMD)
+constexpr int MNW = 8;           // wavefronts per workgroup (two per SIMD)
 constexpr int MThreads = 64 * MNW;
 constexpr int kAChunks = MBM * MKS / 16;   // 16-byte chunks of a step's activation codes: 2048
 constexpr int kBChunks = MBN * MKS / 32;   // of its weight codes: 2048
@@ -109,13 +112,13 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_mx8_kernel(
 // ---- the block-scaled grouped GEMM -----------------------------------------
 // LDS weight row Rl of the tile:
 //   gate/up: Rl < 128: gate feature 128 ct + Rl, else up feature 128 ct +
-//            Rl - 128; wavefront w reads rows 32 w + n (gate, column group 0)
-//            and 128 + 32 w + n (up, column group 1), so a lane holds gate and
-//            up of the same features, and the wavefront's 32 features are one
-//            32-element block of h;
-//   down:    output row 256 ct + Rl; wavefront w reads 64 w + 32 cg + n.
-template <bool GU> __device__ __forceinline__ int mx_wrow(int wave, int cg, int n) {
-    return GU ? 128 * cg + 32 * wave + n : 64 * wave + 32 * cg + n;
+//            Rl - 128; weight quarter q reads rows 32 q + n (gate, column
+//            group 0) and 128 + 32 q + n (up, column group 1), so a lane holds
+//            gate and up of the same features, and the quarter's 32 features
+//            are one 32-element block of h;
+//   down:    output row 256 ct + Rl; weight quarter q reads 64 q + 32 cg + n.
+template <bool GU> __device__ __forceinline__ int mx_wrow(int q, int cg, int n) {
+    return GU ? 128 * cg + 32 * q + n : 64 * q + 32 * cg + n;
 }
 
 // The four scale bytes a lane of half h uses in one step: blocks h, 2 + h,
@@ -141,7 +144,9 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
     // into one from reads of the other only when they are distinct objects
     __shared__ uint4 A0[kAChunks], A1[kAChunks];
     __shared__ uint4 B0[kBChunks], B1[kBChunks];
-    __shared__ uint32_t AS0[MBM * 2], AS1[MBM * 2];   // 8 scale bytes per row and step
+    // 8 scale bytes per row and step (the second half: padding the scale DMA
+    // of wavefronts 4..7 writes, so that every thread issues it)
+    __shared__ uint32_t AS0[MBM * 4], AS1[MBM * 4];
     __shared__ uint32_t BS0[MBN * 2], BS1[MBN * 2];
     auto Abuf = [&](int buf) { return buf ? A1 : A0; };
     auto Bbuf = [&](int buf) { return buf ? B1 : B0; };
@@ -169,6 +174,7 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
     }
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int n = lane & 31, g = lane >> 5;
+    const int rh = wave / 4, wq = wave % 4;   // the wavefront's row half and weight quarter
     // the activation row (token row, or h row) of tile row r
     auto src_row = [&](int r) {
         r = min(r, rows - 1);
@@ -180,18 +186,20 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
     };
     if (GU && !shared && tid < rows && (unsigned)sorted[rb + tid] >= (unsigned)P)
         atomicOr(&hdr->status, FW_STATUS_BAD_PAIR);
-    // DMA slots: instruction i of thread tid fills LDS slot i * 256 + tid.
+    // DMA slots: instruction i of thread tid fills LDS slot i * 512 + tid.
     // activation codes: slot s is position s % 16 of tile row s / 16 and holds
     // its chunk (s % 16) ^ (row % 16) (so that the 32 lanes reading one chunk
-    // of 32 rows hit distinct banks)
-    uint32_t aoff[8];
+    // of 32 rows hit distinct banks); instruction i covers row group i
+    uint32_t aoff[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
         const int s = i * MThreads + tid, r = s / 16, c = (s % 16) ^ (r % 16);
         aoff[i] = (uint32_t)src_row(r) * (uint32_t)K + 16u * c;
     }
-    // activation scales: slot tid is dword tid % 2 of row tid / 2's 8 bytes
-    const uint32_t asoff = (uint32_t)src_row(tid / 2) * (uint32_t)(K / 32) + 4u * (tid % 2);
+    // activation scales: slot tid (< 256) is dword tid % 2 of row tid / 2's 8
+    // bytes; threads 256.. repeat those of threads 0.. into the padding
+    const uint32_t asoff = (uint32_t)src_row((tid % 256) / 2) * (uint32_t)(K / 32) +
+                           4u * (tid % 2);
     // weight rows: LDS row Rl is matrix row wrow(Rl) of the expert
     auto wrow = [&](int Rl) {
         if (GU) return ct * 128 + (Rl & 127);   // the gate or the up matrix's row
@@ -203,31 +211,28 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
     const uint8_t *usc = (GU ? wb : wa) + sreg + (size_t)expert * N * (K / 32);
     // weight codes: slot s is position s % 8 of LDS row s / 8 and holds its
     // chunk (s % 8) ^ (row / 2 % 8); rows 128 .. 255 of a gate/up tile are the
-    // up matrix's (instructions 4 .. 7)
-    uint32_t boff[8];
+    // up matrix's (instructions 2 and 3)
+    uint32_t boff[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
         const int s = i * MThreads + tid, Rl = s / 8, c = (s % 8) ^ ((Rl / 2) % 8);
         boff[i] = (uint32_t)wrow(Rl) * (uint32_t)(K / 2) + 16u * c;
     }
-    // weight scales: slot s (instructions 0, 1) is dword s % 2 of row s / 2
-    uint32_t bsoff[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int s = i * MThreads + tid;
-        bsoff[i] = (uint32_t)wrow(s / 2) * (uint32_t)(K / 32) + 4u * (s % 2);
-    }
-    // The main loop for MI 32-row groups (the groups that hold rows of the
-    // tile: their DMA, fragments and MFMAs only).  MI is a template parameter
-    // so that the loop body has no branch: the compiler would otherwise sink
-    // a step's MFMAs past the DMA wait at its end.
-    auto run = [&]<int MI>() {
+    // weight scales: slot tid is dword tid % 2 of row tid / 2 (rows 128 ..
+    // 255 of a gate/up tile: the up matrix's, threads 256 ..)
+    const uint32_t bsoff = (uint32_t)wrow(tid / 2) * (uint32_t)(K / 32) + 4u * (tid % 2);
+    // The main loop for a tile of MI 32-row groups (the groups that hold rows:
+    // their DMA only) of which this wavefront's row half holds MW (0 .. 2:
+    // its fragments and MFMAs).  Both are template parameters so that the
+    // loop body has no branch: the compiler would otherwise sink a step's
+    // MFMAs past the DMA wait at its end.
+    auto run = [&]<int MI, int MW>() __attribute__((always_inline)) {
     auto dma = [&](int buf, int st, int part) {
         const uint32_t ka = (uint32_t)st * MKS, kb = (uint32_t)st * (MKS / 2),
                        ks = (uint32_t)st * (MKS / 32);
         if (part == 0) {
 #pragma unroll
-            for (int i = 0; i < 2 * MI; ++i)   // rows 16 i .. 16 i + 15
+            for (int i = 0; i < MI; ++i)   // rows 32 i .. 32 i + 31
                 __builtin_amdgcn_global_load_lds(
                     a8 + (aoff[i] + ka), (lds_void *)(&Abuf(buf)[i * MThreads + 64 * wave]), 16, 0,
                     0);
@@ -235,15 +240,12 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
                                              (lds_void *)(&ASbuf(buf)[64 * wave]), 4, 0, 0);
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                __builtin_amdgcn_global_load_lds((GU && i >= 4 ? ubase : gbase) + (boff[i] + kb),
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_global_load_lds((GU && i >= 2 ? ubase : gbase) + (boff[i] + kb),
                                                  (lds_void *)(&Bbuf(buf)[i * MThreads + 64 * wave]),
                                                  16, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                __builtin_amdgcn_global_load_lds((GU && i >= 1 ? usc : gsc) + (bsoff[i] + ks),
-                                                 (lds_void *)(&BSbuf(buf)[i * MThreads + 64 * wave]),
-                                                 4, 0, 0);
+            __builtin_amdgcn_global_load_lds((GU && wave >= 4 ? usc : gsc) + (bsoff + ks),
+                                             (lds_void *)(&BSbuf(buf)[64 * wave]), 4, 0, 0);
         }
     };
     // everything issued so far has landed and every wavefront is here
@@ -253,46 +255,50 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    f16v acc[MI][2];
+    constexpr int MA = MW > 0 ? MW : 1;   // array extent (a row half may hold no rows)
+    f16v acc[MA][2];
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MA; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     const int steps = K / MKS;
-    const int wr[2] = {mx_wrow<GU>(wave, 0, n), mx_wrow<GU>(wave, 1, n)};
+    const int wr[2] = {mx_wrow<GU>(wq, 0, n), mx_wrow<GU>(wq, 1, n)};
+    const int r0 = 64 * rh + n;   // the lane's first tile row
 
     // one step from buffer set `buf`; pf(S) issues the next step's DMA after
     // slice S's MFMAs
     auto step = [&](int buf, auto &&pf) {
-        uint32_t sa[MI], sb[2];
+        uint32_t sa[MA], sb[2];
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-            const int r = 32 * mi + n;
+        for (int mi = 0; mi < MW; ++mi) {
+            const int r = r0 + 32 * mi;
             sa[mi] = mx_scale_word(*(const uint2 *)&ASbuf(buf)[2 * r], g);
         }
 #pragma unroll
         for (int cg = 0; cg < 2; ++cg)
             sb[cg] = mx_scale_word(*(const uint2 *)&BSbuf(buf)[2 * wr[cg]], g);
-        v8i a[2][MI], b[2][2];
-        // slice S's fragments: row 32 mi + n, chunks 4 S + g and 4 S + 2 + g;
+        v8i a[2][MA], b[2][2];
+        // slice S's fragments: row r0 + 32 mi, chunks 4 S + g and 4 S + 2 + g;
         // weight row wr[cg], chunk 2 S + g
         auto load = [&](int X, int S) {
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi) {
-                const int r = 32 * mi + n, x = r % 16;
+            for (int mi = 0; mi < MW; ++mi) {
+                const int r = r0 + 32 * mi, x = r % 16;
                 const uint4 lo = Abuf(buf)[16 * r + ((4 * S + g) ^ x)];
                 const uint4 hi = Abuf(buf)[16 * r + ((4 * S + 2 + g) ^ x)];
                 a[X][mi] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                                (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
             }
+            if constexpr (MW > 0) {
 #pragma unroll
-            for (int cg = 0; cg < 2; ++cg) {
-                const int Rl = wr[cg];
-                const uint4 q = Bbuf(buf)[8 * Rl + ((2 * S + g) ^ ((Rl / 2) % 8))];
-                b[X][cg] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+                for (int cg = 0; cg < 2; ++cg) {
+                    const int Rl = wr[cg];
+                    const uint4 q = Bbuf(buf)[8 * Rl + ((2 * S + g) ^ ((Rl / 2) % 8))];
+                    b[X][cg] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+                }
             }
         };
         load(0, 0);
@@ -301,7 +307,7 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
         constexpr int X = (S) & 1;                                                           \
         if constexpr ((S) < 3) load(X ^ 1, (S) + 1);                                         \
         _Pragma("unroll") for (int cg = 0; cg < 2; ++cg)                                     \
-            _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                                \
+            _Pragma("unroll") for (int mi = 0; mi < MW; ++mi)                                \
                 acc[mi][cg] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
                     a[X][mi], b[X][cg], acc[mi][cg], 0, 4, (S), (int)sa[mi], (S),            \
                     (int)sb[cg]);                                                            \
@@ -333,18 +339,18 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
     }
     if (st < steps) step(0, [](int) {});
 
-    // ---- epilogue: acc[mi][cg][v] is tile row 32 mi + 8 (v / 4) + 4 g + v % 4,
-    // LDS weight row wr[cg] ----
+    // ---- epilogue: acc[mi][cg][v] is tile row 64 rh + 32 mi + 8 (v / 4) +
+    // 4 g + v % 4, LDS weight row wr[cg] ----
     bool range = false;
     if constexpr (GU) {
-        // features 128 ct + 32 wave + n: one 32-element block of h per row,
+        // features 128 ct + 32 wq + n: one 32-element block of h per row,
         // spread over the 32 lanes of a half-wavefront
-        const int f0 = 128 * ct + 32 * wave;
+        const int f0 = 128 * ct + 32 * wq;
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
+        for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int row = 32 * mi + 8 * (v >> 2) + 4 * g + (v & 3);
+                const int row = 64 * rh + 32 * mi + 8 * (v >> 2) + 4 * g + (v & 3);
                 const float gv = acc[mi][0][v], up = acc[mi][1][v];
                 const float av = gv / (1.0f + __expf(-gv)) * up;
                 uint32_t m = __float_as_uint(av) & 0x7FFFFFFFu;
@@ -359,12 +365,12 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
                 }
             }
     } else {
-        float *yrow = yout + (size_t)ct * 256 + 64 * wave + n;
+        float *yrow = yout + (size_t)ct * 256 + 64 * wq + n;
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
+        for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int row = 32 * mi + 8 * (v >> 2) + 4 * g + (v & 3);
+                const int row = 64 * rh + 32 * mi + 8 * (v >> 2) + 4 * g + (v & 3);
                 if (row < rows) {
 #pragma unroll
                     for (int cg = 0; cg < 2; ++cg)
@@ -374,11 +380,16 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
     }
     if (range) atomicOr(&hdr->status, FW_STATUS_RANGE);
     };
+    // the tile's row groups, and the share of this wavefront's row half
+    auto go = [&]<int MI>() __attribute__((always_inline)) {
+        if (rh == 0) run.template operator()<MI, (MI < 2 ? MI : 2)>();
+        else run.template operator()<MI, (MI > 2 ? MI - 2 : 0)>();
+    };
     const int mi = (rows + 31) / 32;
-    if (mi > 3) run.template operator()<4>();
-    else if (mi > 2) run.template operator()<3>();
-    else if (mi > 1) run.template operator()<2>();
-    else run.template operator()<1>();
+    if (mi > 3) go.template operator()<4>();
+    else if (mi > 2) go.template operator()<3>();
+    else if (mi > 1) go.template operator()<2>();
+    else go.template operator()<1>();
 }
 
 // The MXFP8 areas inside the fp16 staging areas of the workspace: x8 [T][H]
