@@ -90,7 +90,8 @@ def parse():
                          "'decode' (the metric's HBM-bound point)")
     ap.add_argument("--peaks", action="store_true",
                     help="instead of the layer: measure the fp16 MFMA and streaming-read "
-                         "peaks of this GPU with the microbenchmarks of libfwpeak.so")
+                         "peaks of this GPU and the price of a grid-wide rendezvous inside "
+                         "one kernel, with the microbenchmarks of libfwpeak.so")
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
     ap.add_argument("--three-calls", action="store_true",
                     help="time the layer as fw_moe_route + fw_moe_permute + fw_moe_forward "
