@@ -30,8 +30,8 @@ WsLayout ws_layout(const fw_moe_desc &d, int T) {
         off = align256(off + bytes);
         return at;
     };
-    // row tiles of either family: GEMM tiles of kGemmBM rows, GEMV chunks of
-    // kGemvTokens rows (the larger count)
+    // row tiles of either family: GEMM tiles of 128 or 160 rows, GEMV chunks
+    // of kGemvTokens rows (the larger count)
     L.max_tiles = (int)((P + kGemvTokens - 1) / kGemvTokens + E);
     L.active = take((E + 1) * sizeof(int4));
     L.tiles = take((size_t)L.max_tiles * sizeof(int4));

@@ -16,8 +16,21 @@ constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 16;
 constexpr int kUnit = 256;        // elements per 16-byte-aligned run of 8 blocks
 constexpr int kGemvTokens = 2;    // token rows a GEMV work item carries
-constexpr int kGemm2BM = 64;      // token rows per tile of the 16x16x32 grouped GEMM
-constexpr int kGemmBM = 128;      // token rows per tile of the 32x32x16 grouped GEMM
+constexpr int kGemmBM = 128;      // token rows per tile of the block-scaled and int8 GEMMs
+// Token rows per tile of the fp16 grouped GEMM: five 32-row groups for Q4_0
+// experts, four for the other formats (whose fragments need more registers).
+// An expert whose segment has at most this many rows is one tile.
+constexpr int gemm_tile_rows(int q) { return q == FW_Q4_0 ? 160 : 128; }
+// Bound on the row tiles of a routed GEMM (at most one partial tile per
+// expert), and the row tiles each XCD's share of the launch has room for:
+// a launch holds 8 * xcd_tile_cap rows of column tiles of workgroups.
+__host__ __device__ constexpr int gemm_row_tiles(int P, int E, int tile_rows, int max_tiles) {
+    return (P + tile_rows - 1) / tile_rows + E < max_tiles ? (P + tile_rows - 1) / tile_rows + E
+                                                           : max_tiles;
+}
+__host__ __device__ constexpr int xcd_tile_cap(int P, int E, int tile_rows, int max_tiles) {
+    return (gemm_row_tiles(P, E, tile_rows, max_tiles) + 7) / 8;
+}
 // AUTO: the GEMV family while the routed pairs average at most this many rows
 // per expert (T * k <= 2 E), the grouped GEMM above.  Measured crossovers, in
 // rows per expert: the hidden-4096 / 64-expert top-4 layer between 2 and 3
@@ -52,7 +65,9 @@ struct WsHeader {
     int32_t status;     // sticky FW_STATUS_* bits
     int32_t n_active;   // experts with at least one routed pair
     int32_t n_tiles;    // row tiles of the routed experts (GEMM tiles or GEMV chunks)
-    int32_t reserved[61];
+    // GEMM tiles: XCD x runs row tiles [xcd_first[x], xcd_first[x + 1])
+    int32_t xcd_first[9];
+    int32_t reserved[52];
 };
 static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 

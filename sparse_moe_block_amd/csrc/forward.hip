@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
 hipError_t launch_prepare(const FwdArgs &a, hipStream_t s) {
     if (a.d.act_quant == FW_ACT_MXFP8) return launch_prepare_mx8(a, s);
     if (a.d.act_quant == FW_ACT_INT8) return launch_prepare_i8(a, s);
-    const int tile_rows = a.path == FW_PATH_GEMM ? kGemmBM : kGemvTokens;
+    const int tile_rows = a.path == FW_PATH_GEMM ? gemm_tile_rows(a.d.expert_q) : kGemvTokens;
     // the Q4_K GEMV needs the activation rows' block sums
     const bool sums = a.path == FW_PATH_GEMV &&
                       (a.d.expert_q == FW_Q4_K || (a.d.shared_ffn > 0 && a.d.shared_q == FW_Q4_K));

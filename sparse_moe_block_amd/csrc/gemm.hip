@@ -5,14 +5,17 @@
 // What bounds it.  Every dequantised weight fragment costs about 14 VALU
 // instructions (code bits into fp16 pairs, exact, then times the block's
 // fp16 scale), so the VALU work per MFMA is 14 divided by the number of
-// token-row groups the fragment feeds.  Each wavefront here owns all 128
-// token rows of its tile (four 32-row groups) and 64 weight rows (two 32-row
-// groups), so a fragment feeds four 32x32x16 MFMAs (32768 flops each); the
-// accumulators take 128 VGPRs.
+// token-row groups the fragment feeds.  Each wavefront here owns all token
+// rows of its tile (four 32-row groups; five for Q4_0) and 64 weight rows
+// (two 32-row groups), so a fragment feeds four or five 32x32x16 MFMAs
+// (32768 flops each); the accumulators take 128 or 160 VGPRs.
 //
-//  - a workgroup tile is up to 128 rows of one expert's segment of the sorted
-//    pair list (tokens gathered through sorted_pairs) times 256 weight rows;
-//    a tile with fewer rows runs only the 32-row groups that hold rows;
+//  - a workgroup tile is up to 128 rows (Q4_0: 160) of one expert's segment
+//    of the sorted pair list (tokens gathered through sorted_pairs) times 256
+//    weight rows; a tile with fewer rows runs only the 32-row groups that
+//    hold rows.  An expert's rows take as few tiles as the size allows, and
+//    every tile re-streams and re-dequantises the expert's weights, so the
+//    fifth group saves a whole tile wherever an expert has 129-160 rows;
 //  - K advances 128 elements (half a 256-element unit, four GGUF blocks) per
 //    step, eight 16-wide MFMA slices.  Lane group g = lane / 32 covers blocks
 //    2g and 2g + 1 of the half unit, slice s block 2g + s / 4, fp16 pairs
@@ -32,9 +35,12 @@
 //    forms SiLU(g)*u in registers; the 32 features of a wavefront are one
 //    32-element block of h, stored in pair order straight from the registers;
 //    the down projection's fp32 rows go straight from the accumulators too;
-//  - each XCD takes a contiguous eighth of the row-tile list (the tiles of one
-//    expert share its L2, so the expert's weights are fetched about once);
-//    consecutive workgroups of one XCD take the column tiles of one row tile.
+//  - each XCD takes a contiguous range of the row-tile list (the tiles of one
+//    expert share its L2, so the expert's weights are fetched about once),
+//    the ranges of about equal work (the schedule weighs each tile by its
+//    row groups): under skewed routing the hottest experts' full tiles no
+//    longer pile onto one XCD; consecutive workgroups of one XCD take the
+//    column tiles of one row tile.
 #include <math.h>
 
 #include "common.h"
@@ -43,13 +49,15 @@
 namespace fw {
 namespace {
 
-constexpr int BM = kGemmBM;   // token rows per tile
 constexpr int BK = 128;       // k per step
-constexpr int kChunks = BM * BK / 8;   // 16-byte chunks of a step's activations: 2048
-constexpr int kMaxDma = kChunks / 256;  // DMA instructions per thread (4-wave workgroups)
+// token rows per tile (four or five 32-row MFMA groups) and the 16-byte
+// chunks of a step's activations (2048 or 2560)
+template <int Q> constexpr int tile_bm() { return gemm_tile_rows(Q); }
+template <int Q> constexpr int a_chunks() { return tile_bm<Q>() * BK / 8; }
+constexpr int kMaxDma = 160 * BK / 8 / 256;  // DMA instructions per thread, at most
 constexpr int kMaxPX = 9;               // 16-byte weight pieces per row and half unit (Q8_0)
 constexpr int kQ6PX = 10;               // Q6_K: pieces per row and half (ql 5, qh 3, tail 2)
-static_assert(BM == 128, "tile shape");
+static_assert(tile_bm<FW_Q4_0>() == 160 && tile_bm<FW_Q8_0>() == 128, "tile shapes");
 
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -74,7 +82,7 @@ struct Tile {
     uint32_t mxs[2];
     _Float16 *hout;
     float *yout;
-    const int32_t *s_ex;     // LDS: each tile row's exponent
+    int ex;                  // thread tid < rows: the exponent of tile row tid
     WsHeader *hdr;
     int lane, wave, steps, rows, rb, ct, N;
 };
@@ -167,6 +175,7 @@ __device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 
     constexpr int kDma = (32 * MI + 4 * NW - 1) / (4 * NW);
     constexpr int WD = win_dwords<Q>();
     constexpr int UB = QT<Q>::kUnitBytes, PX = half_pieces<Q>();
+    constexpr bool kRollA = MI > 4;
     const int lane = c.lane, steps = c.steps;
     const int g = lane >> 5, n = lane & 31, wave = c.wave;
 
@@ -293,17 +302,31 @@ __device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 
         for (int mi = 0; mi < MI; ++mi) a[0][mi] = __builtin_bit_cast(h8, buf[apos(0) + mi * 512]);
         b[0][0] = frag_any<Q, 0>(wh[0], kq[0]);
         b[0][1] = frag_any<Q, 0>(wh[1], kq[1]);
+        // Five row groups (160 accumulators) leave no registers for a second
+        // set of A fragments: there each group's next-slice fragment is read
+        // into its own registers right after the group's two MFMAs, and is
+        // waited on a slice later, behind the other groups' MFMAs.
 #define FW_SLICE(S)                                                                          \
     {                                                                                        \
         constexpr int X = (S) & 1, Y = X ^ 1;                                                \
-        if constexpr ((S) < 7) {                                                             \
-            _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                                \
-                a[Y][mi] = __builtin_bit_cast(h8, buf[apos((S) + 1) + mi * 512]);            \
+        if constexpr (kRollA) {                                                              \
+            _Pragma("unroll") for (int mi = 0; mi < MI; ++mi) {                              \
+                _Pragma("unroll") for (int cg = 0; cg < 2; ++cg)                             \
+                    acc[mi][cg] = __builtin_amdgcn_mfma_f32_32x32x16_f16(                    \
+                        a[0][mi], b[X][cg], acc[mi][cg], 0, 0, 0);                           \
+                if constexpr ((S) < 7)                                                       \
+                    a[0][mi] = __builtin_bit_cast(h8, buf[apos((S) + 1) + mi * 512]);        \
+            }                                                                                \
+        } else {                                                                             \
+            if constexpr ((S) < 7) {                                                         \
+                _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                            \
+                    a[Y][mi] = __builtin_bit_cast(h8, buf[apos((S) + 1) + mi * 512]);        \
+            }                                                                                \
+            _Pragma("unroll") for (int cg = 0; cg < 2; ++cg)                                 \
+                _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                            \
+                    acc[mi][cg] = __builtin_amdgcn_mfma_f32_32x32x16_f16(                    \
+                        a[X][mi], b[X][cg], acc[mi][cg], 0, 0, 0);                           \
         }                                                                                    \
-        _Pragma("unroll") for (int cg = 0; cg < 2; ++cg)                                     \
-            _Pragma("unroll") for (int mi = 0; mi < MI; ++mi)                                \
-                acc[mi][cg] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[X][mi], b[X][cg],     \
-                                                                     acc[mi][cg], 0, 0, 0);  \
         if constexpr ((S) < 7) {                                                             \
             b[Y][0] = frag_any<Q, ((S) + 1) & 7>(wh[0], kq[0]);                              \
             b[Y][1] = frag_any<Q, ((S) + 1) & 7>(wh[1], kq[1]);                              \
@@ -366,6 +389,11 @@ __device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 
     // ---- epilogue: acc[mi][cg][v] is tile row 32 mi + 8 (v / 4) + 4 g + v % 4,
     // weight row (column group cg) n ----
     const int rows = c.rows, rb = c.rb, N = c.N;
+    // each tile row's exponent, through LDS: the activation buffers are free
+    // once the last step's sync has passed
+    int32_t *s_ex = (int32_t *)A1;
+    if ((int)threadIdx.x < rows) s_ex[threadIdx.x] = c.ex;
+    __syncthreads();
     bool range = (Q == FW_Q4_K || Q == FW_Q6_K || Q == FW_MXFP4)
                      ? !(wmax <= 65504.0f)
                      : dmax > (Q == FW_Q4_0 ? kQ4DMaxBits : kQ8DMaxBits);
@@ -380,7 +408,7 @@ __device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 
             for (int v = 0; v < 16; ++v) {
                 const int row = 32 * mi + 8 * (v >> 2) + 4 * g + (v & 3);
                 if (row < rows) {
-                    const int e = c.s_ex[row];
+                    const int e = s_ex[row];
                     const float gv = __builtin_amdgcn_ldexpf(acc[mi][0][v], -e);
                     const float up = __builtin_amdgcn_ldexpf(acc[mi][1][v], -e);
                     const float a = gv / (1.0f + __expf(-gv)) * up;
@@ -399,7 +427,7 @@ __device__ __forceinline__ void tile_run(uint4 *A0, uint4 *A1, uint4 *B0, uint4 
             for (int v = 0; v < 16; ++v) {
                 const int row = 32 * mi + 8 * (v >> 2) + 4 * g + (v & 3);
                 if (row < rows) {
-                    const int e = c.s_ex[row];
+                    const int e = s_ex[row];
 #pragma unroll
                     for (int cg = 0; cg < 2; ++cg)
                         yrow[(size_t)(rb + row) * N + 32 * cg] =
@@ -437,22 +465,27 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<Q, NW>() * 4 / NW)) void g
     int col_tiles, int n_row_tiles_max, int shared, int shared_rows,
     const int32_t *__restrict__ iexp, int32_t *__restrict__ oexp, size_t sreg) {
     constexpr int PX = half_pieces<Q>();
-    __shared__ uint4 A0[kChunks];
-    __shared__ uint4 A1[kChunks];
+    constexpr int BM = tile_bm<Q>();
+    __shared__ uint4 A0[a_chunks<Q>()];
+    __shared__ uint4 A1[a_chunks<Q>()];
     __shared__ uint4 B0[64 * NW * PX];   // half units of the workgroup's weight rows
     __shared__ uint4 B1[64 * NW * PX];
-    __shared__ int s_ex[BM];
     // XCD-aware order: workgroup b runs on XCD b % 8.  Each XCD takes a
-    // contiguous eighth of the row tiles (the tiles of one expert are
-    // consecutive), column tiles fastest.
+    // contiguous range of the row tiles (the tiles of one expert are
+    // consecutive), column tiles fastest: for the routed experts the ranges
+    // the schedule balanced by work, for the shared expert eighths.
     const int xcd = blockIdx.x % 8, bi = blockIdx.x / 8;
-    const int n_rt = shared ? (shared_rows + BM - 1) / BM
-                            : min(ld_const(&hdr->n_tiles), n_row_tiles_max);
-    const int per = (n_rt + 7) / 8;
     const int rl = bi / col_tiles, ct = bi % col_tiles;
-    if (rl >= per) return;
-    const int rt = xcd * per + rl;
-    if (rt >= n_rt) return;
+    int rt;
+    if (shared) {
+        const int n_rt = (shared_rows + BM - 1) / BM, per = (n_rt + 7) / 8;
+        rt = xcd * per + rl;
+        if (rl >= per || rt >= n_rt) return;
+    } else {
+        const int n_rt = min(ld_const(&hdr->n_tiles), n_row_tiles_max);
+        rt = ld_const(&hdr->xcd_first[xcd]) + rl;
+        if (rt >= min(ld_const(&hdr->xcd_first[xcd + 1]), n_rt)) return;
+    }
     int expert = 0, rb = 0, rows = 0;
     if (shared) {
         rb = rt * BM;
@@ -477,24 +510,22 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<Q, NW>() * 4 / NW)) void g
         }
         return rb + r;
     };
+    // the exponent of tile row tid: its token's x exponent (gate/up) or the
+    // h row's (down)
+    int ex = 0;
     if (tid < rows) {
-        const int src = src_row(tid);
-        if (GU) {
-            const int e = iexp[src];   // the token's x exponent
-            s_ex[tid] = e;
-            if (ct == 0) oexp[rb + tid] = 2 * e;
-        } else {
-            s_ex[tid] = iexp[rb + tid];   // the h row's exponent
-        }
+        ex = iexp[src_row(tid)];
+        if (GU && ct == 0) oexp[rb + tid] = 2 * ex;
     }
     Tile c;
+    c.ex = ex;
     c.lane = tid % kWave;
     c.wave = wave_id();
     // DMA rows 4 NW i + tid / 16 (past the tile's end: its last row), chunk
     // (tid % 16) ^ (tid / 16 % 16), as byte offsets into ain
     const int chunk = (tid & 15) ^ ((tid >> 4) & 15);
 #pragma unroll
-    for (int i = 0; i < kChunks / kThreads; ++i) {
+    for (int i = 0; i < a_chunks<Q>() / kThreads; ++i) {
         const int r = min(4 * NW * i + (tid >> 4), rows - 1);
         int s = rb + r;
         if (GU && !shared) {
@@ -600,17 +631,16 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<Q, NW>() * 4 / NW)) void g
     }
     c.hout = hout;
     c.yout = yout;
-    c.s_ex = s_ex;
     c.hdr = hdr;
     c.steps = K / BK;
     c.rows = rows;
     c.rb = rb;
     c.ct = ct;
     c.N = N;
-    __syncthreads();   // s_ex
     // only the 32-row groups that hold rows of this tile run
     const int mi = (rows + 31) / 32;
-    if (mi > 3) tile_run<Q, GU, NW, 4>(A0, A1, B0, B1, c);
+    if (BM > 128 && mi > 4) tile_run<Q, GU, NW, BM / 32>(A0, A1, B0, B1, c);
+    else if (mi > 3) tile_run<Q, GU, NW, 4>(A0, A1, B0, B1, c);
     else if (mi > 2) tile_run<Q, GU, NW, 3>(A0, A1, B0, B1, c);
     else if (mi > 1) tile_run<Q, GU, NW, 2>(A0, A1, B0, B1, c);
     else tile_run<Q, GU, NW, 1>(A0, A1, B0, B1, c);
@@ -622,8 +652,9 @@ void launch_nw(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const _Fl
                 int32_t *oexp, hipStream_t s) {
     const int col_tiles = GU ? N / (32 * NW) : N / (64 * NW);
     // routed: at most one partial tile per expert
+    constexpr int BM = tile_bm<Q>();
     const int row_tiles = shared ? (a.T + BM - 1) / BM
-                                 : std::min(a.L.max_tiles, (a.P + BM - 1) / BM + a.d.n_experts);
+                                 : gemm_row_tiles(a.P, a.d.n_experts, BM, a.L.max_tiles);
     const int nblk = (row_tiles + 7) / 8 * 8 * col_tiles;   // eight XCDs x whole row tiles
     gemm_kernel<Q, GU, NW><<<nblk, 64 * NW, 0, s>>>(
         wa, wb, (const int4 *)(a.ws + a.L.tiles), (WsHeader *)a.ws, a.sorted, ain, hout, yout,

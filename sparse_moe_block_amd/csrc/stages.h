@@ -212,23 +212,34 @@ __device__ __forceinline__ void permute_block(const int32_t *ids, int P, int E,
 }
 
 
+// Work estimate of a GEMM row tile of r rows, used to split the tile list
+// among the XCDs: streaming and dequantising the weights cost each tile about
+// one and a half times what one 32-row MFMA group adds.
+__device__ __forceinline__ int gemm_tile_work(int r) { return 3 + 2 * ((r + 31) / 32); }
+
 // Block-0 part of the forward's staging: the active-expert list and the row
 // tiles from expert_offsets, and the GEMV split-K arrival counters cleared.
 // Thread tid owns experts 2*tid and 2*tid+1, so a block of 256 to 1024
 // threads covers E <= 512; every thread of the block must call it.
+// GEMM tiles (tile_rows >= 32) are also split among the 8 XCDs: contiguous
+// ranges of about equal work (gemm_tile_work), each at most xcd_tile_cap
+// tiles, in hdr->xcd_first.  Tiles are in expert order, so the tiles of an
+// expert share an XCD's L2 unless a boundary falls inside them.
 __device__ __forceinline__ void build_schedule(const int32_t *offsets, int E, int P,
                                                int tile_rows, int max_tiles,
                                                int4 *__restrict__ active, int4 *__restrict__ tiles,
                                                int *__restrict__ split_cnt,
                                                WsHeader *__restrict__ hdr) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const bool balance = tile_rows >= 32;
     // the GEMV's split-K arrival counters start every call at zero
     for (int i = tid; i < kSplitTiles; i += blockDim.x) split_cnt[i] = 0;
     // one entry per wave of a block of up to 1024 threads: threads from 256
     // on own experts >= 512 >= E, so they contribute zeros
-    __shared__ int wsum_a[1024 / kWave], wsum_t[1024 / kWave];
+    __shared__ int wsum_a[1024 / kWave], wsum_t[1024 / kWave], wsum_w[1024 / kWave];
+    __shared__ int s_first[8];   // raw XCD boundaries: the tile holding 1/8 .. 7/8 of the work
     // each thread owns experts 2*tid and 2*tid+1
-    int beg[2], cnt[2], na = 0, nt = 0;
+    int beg[2], cnt[2], na = 0, nt = 0, nw = 0;
     bool bad = false;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -244,41 +255,85 @@ __device__ __forceinline__ void build_schedule(const int32_t *offsets, int E, in
             cnt[i] = n - b;
             na += cnt[i] > 0;
             nt += (cnt[i] + tile_rows - 1) / tile_rows;
+            if (balance) {
+                const int rem = cnt[i] % tile_rows;
+                nw += cnt[i] / tile_rows * gemm_tile_work(tile_rows) +
+                      (rem ? gemm_tile_work(rem) : 0);
+            }
         }
     }
     if (bad) atomicOr(&hdr->status, FW_STATUS_BAD_OFFSETS);
-    int ia = na, it = nt;   // inclusive scans
+    if (tid < 8) s_first[tid] = 0x7FFFFFFF;
+    int ia = na, it = nt, iw = nw;   // inclusive scans
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
-        const int oa = __shfl_up(ia, off), ot = __shfl_up(it, off);
+        const int oa = __shfl_up(ia, off), ot = __shfl_up(it, off), ow = __shfl_up(iw, off);
         if (lane >= off) {
             ia += oa;
             it += ot;
+            iw += ow;
         }
     }
     if (lane == kWave - 1) {
         wsum_a[wave] = ia;
         wsum_t[wave] = it;
+        wsum_w[wave] = iw;
     }
     __syncthreads();
-    int ba = 0, bt = 0;
-    for (int w = 0; w < wave; ++w) {
-        ba += wsum_a[w];
-        bt += wsum_t[w];
+    int ba = 0, bt = 0, bw = 0, total_t = 0, total_w = 0;
+    for (int w = 0; w < (int)blockDim.x / kWave; ++w) {
+        if (w < wave) {
+            ba += wsum_a[w];
+            bt += wsum_t[w];
+            bw += wsum_w[w];
+        }
+        total_t += wsum_t[w];
+        total_w += wsum_w[w];
     }
-    int pa = ba + ia - na, pt = bt + it - nt;   // exclusive positions
+    int pa = ba + ia - na, pt = bt + it - nt, pw = bw + iw - nw;   // exclusive positions
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         if (cnt[i] > 0) {
             active[pa++] = int4{2 * tid + i, beg[i], cnt[i], 0};
             // bounded: overlapping (invalid) offsets can claim more
-            for (int m = 0; m < cnt[i] && pt < max_tiles; m += tile_rows)
-                tiles[pt++] = int4{2 * tid + i, beg[i] + m, min(tile_rows, cnt[i] - m), 0};
+            for (int m = 0; m < cnt[i] && pt < max_tiles; m += tile_rows) {
+                const int r = min(tile_rows, cnt[i] - m);
+                tiles[pt] = int4{2 * tid + i, beg[i] + m, r, 0};
+                if (balance) {
+                    // the tile holding the point x/8 of the work starts XCD
+                    // x's range if less than half of it lies before the point
+                    const int w = gemm_tile_work(r);
+                    for (int x = 1; x < 8; ++x) {
+                        const int64_t at = (int64_t)x * total_w - 8 * (int64_t)pw;
+                        if (at >= 0 && at < 8 * (int64_t)w) s_first[x] = at < 4 * w ? pt : pt + 1;
+                    }
+                    pw += w;
+                }
+                ++pt;
+            }
         }
     }
+    const int n_tiles = min(total_t, max_tiles);
     if (tid == kPrepThreads - 1) {
         hdr->n_active = ba + ia;
-        hdr->n_tiles = min(bt + it, max_tiles);
+        hdr->n_tiles = n_tiles;
+    }
+    if (balance) {
+        __syncthreads();
+        if (tid == 0) {
+            // capped ranges: none longer than cap, and each leaves the XCDs
+            // after it no more than they have room for
+            const int cap = xcd_tile_cap(P, E, tile_rows, max_tiles);
+            const int n = min(n_tiles, 8 * cap);
+            int f = 0;
+            hdr->xcd_first[0] = 0;
+            for (int x = 1; x < 8; ++x) {
+                const int lo = max(f, n - (8 - x) * cap), hi = min(f + cap, n);
+                f = min(max(s_first[x], lo), hi);
+                hdr->xcd_first[x] = f;
+            }
+            hdr->xcd_first[8] = n;
+        }
     }
 }
 

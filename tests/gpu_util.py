@@ -118,7 +118,7 @@ def compare_tokens(T, ids, n_experts, n_random=48, seed=0):
     up to FULL_COMPARE_MAX_T; above that, both ends, n_random tokens drawn at
     random, and, for every expert, the token of its last routed row in the
     expert-sorted pair order -- a row of the expert's last (usually partial)
-    64-row GEMM tile and of its last GEMV row chunk.  Relative L2 is then
+    row tile of the grouped GEMM and of its last GEMV row chunk.  Relative L2 is then
     computed over the rows of this sample."""
     if T <= FULL_COMPARE_MAX_T:
         return np.arange(T)
