@@ -35,11 +35,12 @@ METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefil
 CSRC = os.path.join(ROOT, "sparse_moe_block_amd", "csrc")
 # sources that decide each dominant kernel's memory traffic (a change to any
 # voids its counter figures)
-TRAFFIC_SOURCES = {"gemv_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "gemv.hip"],
+TRAFFIC_SOURCES = {"gemv_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "stages.h",
+                                            "gemv.hip"],
                    "gemm_mx_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "stages.h",
                                                "gemm_mx.hip"],
-                   "gemm_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "gemm_frag.h",
-                                            "gemm.hip"],
+                   "gemm_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "stages.h",
+                                            "gemm_frag.h", "gemm.hip"],
                    "gemm_i8_kernel<gate/up>": ["common.h", "abi.hip", "forward.hip", "stages.h",
                                                "gemm_i8.hip"]}
 

@@ -31,6 +31,24 @@ __host__ __device__ constexpr int gemm_row_tiles(int P, int E, int tile_rows, in
 __host__ __device__ constexpr int xcd_tile_cap(int P, int E, int tile_rows, int max_tiles) {
     return (gemm_row_tiles(P, E, tile_rows, max_tiles) + 7) / 8;
 }
+// Work estimate of a grouped-GEMM row tile by kernel, for splitting the tile
+// list among the XCDs: a fixed part for an expert's first tile and for each
+// later tile of the expert, and a part per 32-row MFMA group.  Measured on
+// Zipf-routed prefill: the eight-wave fp16 and the int8 kernels run faster
+// with ranges of equal estimated work (a one-group tile costing about half a
+// four-group one, as timed on the DeepSeek-shaped layer); the four-wave fp16 and the block-scaled kernels
+// with ranges of equal tile counts -- by work their gate/up launches were
+// 4-8 % slower, and slower still when an expert's later tiles counted less.
+struct TileCost {
+    int first, rep, group;
+};
+constexpr TileCost kCostF16{3, 3, 2};    // fp16, eight-wave workgroups (Q4_0, Q4_K, MXFP4)
+constexpr TileCost kCostF16W4{1, 1, 0};  // fp16, four-wave workgroups (Q8_0, Q6_K): counts
+constexpr TileCost kCostMx8{1, 1, 0};    // block-scaled MFMA (MXFP8 activations): counts
+constexpr TileCost kCostI8{3, 3, 2};     // int8 MFMA
+constexpr TileCost gemm_tile_cost(int q) {
+    return q == FW_Q8_0 || q == FW_Q6_K ? kCostF16W4 : kCostF16;
+}
 // AUTO: the GEMV family while the routed pairs average at most this many rows
 // per expert (T * k <= 2 E), the grouped GEMM above.  Measured crossovers, in
 // rows per expert: the hidden-4096 / 64-expert top-4 layer between 2 and 3
@@ -147,6 +165,27 @@ __device__ __forceinline__ int ld_const(const int *p) {
 __device__ __forceinline__ int4 ld_const(const int4 *p) {
     const int *q = (const int *)p;
     return int4{ld_const(q), ld_const(q + 1), ld_const(q + 2), ld_const(q + 3)};
+}
+
+// The row tile a grouped-GEMM workgroup runs (-1: none) and, in ct, its
+// column tile.  Workgroup b runs on XCD b % 8; each XCD takes a contiguous
+// range of row tiles, column tiles fastest: for the routed experts the
+// schedule's ranges of about equal work (hdr->xcd_first, at most
+// n_row_tiles_max / 8 rounded up tiles each, which the launch has room
+// for), for the shared expert's n_shared tiles eighths.
+__device__ __forceinline__ int xcd_row_tile(const WsHeader *hdr, int col_tiles,
+                                            int n_row_tiles_max, int shared, int n_shared,
+                                            int &ct) {
+    const int xcd = blockIdx.x % 8, bi = blockIdx.x / 8;
+    const int rl = bi / col_tiles;
+    ct = bi % col_tiles;
+    if (shared) {
+        const int per = (n_shared + 7) / 8, rt = xcd * per + rl;
+        return rl < per && rt < n_shared ? rt : -1;
+    }
+    const int n_rt = min(ld_const(&hdr->n_tiles), n_row_tiles_max);
+    const int rt = ld_const(&hdr->xcd_first[xcd]) + rl;
+    return rt < min(ld_const(&hdr->xcd_first[xcd + 1]), n_rt) ? rt : -1;
 }
 
 // The wavefront index inside the workgroup, as a value the compiler knows to

@@ -17,9 +17,10 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_kernel(
     const int32_t *__restrict__ offsets, int E, int P, const void *__restrict__ x, int act_bf16,
     int H, int T, int tile_rows, int max_tiles, int4 *__restrict__ active, int4 *__restrict__ tiles,
     _Float16 *__restrict__ x16, float *__restrict__ xsum, int32_t *__restrict__ xe,
-    int *__restrict__ split_cnt, WsHeader *__restrict__ hdr) {
+    int *__restrict__ split_cnt, WsHeader *__restrict__ hdr, TileCost cost) {
     if (blockIdx.x == 0) {
-        build_schedule(offsets, E, P, tile_rows, max_tiles, active, tiles, split_cnt, hdr);
+        build_schedule(offsets, E, P, tile_rows, max_tiles, active, tiles, split_cnt, hdr,
+                       cost);
         return;
     }
     const int t = (blockIdx.x - 1) * (kPrepThreads / kWave) + wave_id();
@@ -75,7 +76,8 @@ hipError_t launch_prepare(const FwdArgs &a, hipStream_t s) {
         a.offsets, a.d.n_experts, a.P, a.x, a.d.act_dtype == FW_BF16, a.d.hidden, a.T, tile_rows,
         a.L.max_tiles, (int4 *)(a.ws + a.L.active), (int4 *)(a.ws + a.L.tiles),
         (_Float16 *)(a.ws + a.L.x16), sums ? (float *)(a.ws + a.L.xsum) : nullptr,
-        (int32_t *)(a.ws + a.L.xe), (int *)(a.ws + a.L.split_cnt), (WsHeader *)a.ws);
+        (int32_t *)(a.ws + a.L.xe), (int *)(a.ws + a.L.split_cnt), (WsHeader *)a.ws,
+        gemm_tile_cost(a.d.expert_q));
     return hipGetLastError();
 }
 

@@ -470,22 +470,11 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<Q, NW>() * 4 / NW)) void g
     __shared__ uint4 A1[a_chunks<Q>()];
     __shared__ uint4 B0[64 * NW * PX];   // half units of the workgroup's weight rows
     __shared__ uint4 B1[64 * NW * PX];
-    // XCD-aware order: workgroup b runs on XCD b % 8.  Each XCD takes a
-    // contiguous range of the row tiles (the tiles of one expert are
-    // consecutive), column tiles fastest: for the routed experts the ranges
-    // the schedule balanced by work, for the shared expert eighths.
-    const int xcd = blockIdx.x % 8, bi = blockIdx.x / 8;
-    const int rl = bi / col_tiles, ct = bi % col_tiles;
-    int rt;
-    if (shared) {
-        const int n_rt = (shared_rows + BM - 1) / BM, per = (n_rt + 7) / 8;
-        rt = xcd * per + rl;
-        if (rl >= per || rt >= n_rt) return;
-    } else {
-        const int n_rt = min(ld_const(&hdr->n_tiles), n_row_tiles_max);
-        rt = ld_const(&hdr->xcd_first[xcd]) + rl;
-        if (rt >= min(ld_const(&hdr->xcd_first[xcd + 1]), n_rt)) return;
-    }
+    // XCD-aware order (the tiles of one expert are consecutive)
+    int ct;
+    const int rt = xcd_row_tile(hdr, col_tiles, n_row_tiles_max, shared,
+                                (shared_rows + BM - 1) / BM, ct);
+    if (rt < 0) return;
     int expert = 0, rb = 0, rows = 0;
     if (shared) {
         rb = rt * BM;

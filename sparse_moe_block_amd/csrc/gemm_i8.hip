@@ -115,7 +115,8 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_i8_kernel(
     int8_t *__restrict__ x8, float *__restrict__ xs, int *__restrict__ split_cnt,
     WsHeader *__restrict__ hdr) {
     if (blockIdx.x == 0) {
-        build_schedule(offsets, E, P, IBM, max_tiles, active, tiles, split_cnt, hdr);
+        build_schedule(offsets, E, P, IBM, max_tiles, active, tiles, split_cnt, hdr,
+                       kCostI8);
         return;
     }
     const int t = (blockIdx.x - 1) * (kPrepThreads / kWave) + wave_id();
@@ -181,16 +182,11 @@ __global__ __launch_bounds__(IThreads, 1) void gemm_i8_kernel(
     auto Abuf = [&](int buf) { return buf ? A1 : A0; };
     auto ASbuf = [&](int buf) { return buf ? AS1 : AS0; };
     auto Bbuf = [&](int buf) { return buf ? B1 : B0; };
-    // XCD-aware order (workgroup b runs on XCD b % 8): each XCD takes a
-    // contiguous eighth of the row tiles, column tiles fastest
-    const int xcd = blockIdx.x % 8, bi = blockIdx.x / 8;
-    const int n_rt = shared ? (shared_rows + IBM - 1) / IBM
-                            : min(ld_const(&hdr->n_tiles), n_row_tiles_max);
-    const int per = (n_rt + 7) / 8;
-    const int rl = bi / col_tiles, ct = bi % col_tiles;
-    if (rl >= per) return;
-    const int rt = xcd * per + rl;
-    if (rt >= n_rt) return;
+    // XCD-aware order (the tiles of one expert are consecutive)
+    int ct;
+    const int rt = xcd_row_tile(hdr, col_tiles, n_row_tiles_max, shared,
+                                (shared_rows + IBM - 1) / IBM, ct);
+    if (rt < 0) return;
     int expert = 0, rb = 0, rows = 0;
     if (shared) {
         rb = rt * IBM;
@@ -470,7 +466,7 @@ void launch_i8(const FwdArgs &a, int q, const uint8_t *wa, const uint8_t *wb, co
                hipStream_t s) {
     const int col_tiles = GU ? N / 128 : N / 256;
     const int row_tiles = shared ? (a.T + IBM - 1) / IBM
-                                 : std::min(a.L.max_tiles, (a.P + IBM - 1) / IBM + a.d.n_experts);
+                                 : gemm_row_tiles(a.P, a.d.n_experts, IBM, a.L.max_tiles);
     const int nblk = (row_tiles + 7) / 8 * 8 * col_tiles;   // eight XCDs x whole row tiles
     if (q == FW_Q4_0)
         gemm_i8_kernel<FW_Q4_0, GU><<<nblk, IThreads, 0, s>>>(

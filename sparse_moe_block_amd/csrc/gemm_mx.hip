@@ -101,7 +101,8 @@ __global__ __launch_bounds__(kPrepThreads) void prepare_mx8_kernel(
     uint8_t *__restrict__ x8, uint8_t *__restrict__ xs, int *__restrict__ split_cnt,
     WsHeader *__restrict__ hdr) {
     if (blockIdx.x == 0) {
-        build_schedule(offsets, E, P, MBM, max_tiles, active, tiles, split_cnt, hdr);
+        build_schedule(offsets, E, P, MBM, max_tiles, active, tiles, split_cnt, hdr,
+                       kCostMx8);
         return;
     }
     const int t = (blockIdx.x - 1) * (kPrepThreads / kWave) + wave_id();
@@ -152,16 +153,11 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
     auto Bbuf = [&](int buf) { return buf ? B1 : B0; };
     auto ASbuf = [&](int buf) { return buf ? AS1 : AS0; };
     auto BSbuf = [&](int buf) { return buf ? BS1 : BS0; };
-    // XCD-aware order (workgroup b runs on XCD b % 8): each XCD takes a
-    // contiguous eighth of the row tiles, column tiles fastest
-    const int xcd = blockIdx.x % 8, bi = blockIdx.x / 8;
-    const int n_rt = shared ? (shared_rows + MBM - 1) / MBM
-                            : min(ld_const(&hdr->n_tiles), n_row_tiles_max);
-    const int per = (n_rt + 7) / 8;
-    const int rl = bi / col_tiles, ct = bi % col_tiles;
-    if (rl >= per) return;
-    const int rt = xcd * per + rl;
-    if (rt >= n_rt) return;
+    // XCD-aware order (the tiles of one expert are consecutive)
+    int ct;
+    const int rt = xcd_row_tile(hdr, col_tiles, n_row_tiles_max, shared,
+                                (shared_rows + MBM - 1) / MBM, ct);
+    if (rt < 0) return;
     int expert = 0, rb = 0, rows = 0;
     if (shared) {
         rb = rt * MBM;
@@ -414,7 +410,7 @@ void launch_mx(const FwdArgs &a, const uint8_t *wa, const uint8_t *wb, const uin
                int shared, hipStream_t s) {
     const int col_tiles = GU ? N / 128 : N / 256;
     const int row_tiles = shared ? (a.T + MBM - 1) / MBM
-                                 : std::min(a.L.max_tiles, (a.P + MBM - 1) / MBM + a.d.n_experts);
+                                 : gemm_row_tiles(a.P, a.d.n_experts, MBM, a.L.max_tiles);
     const int nblk = (row_tiles + 7) / 8 * 8 * col_tiles;   // eight XCDs x whole row tiles
     gemm_mx_kernel<GU><<<nblk, MThreads, 0, s>>>(
         wa, wb, (const int4 *)(a.ws + a.L.tiles), (WsHeader *)a.ws, a.sorted, a8, asc, h8, hsc,

@@ -213,9 +213,11 @@ __device__ __forceinline__ void permute_block(const int32_t *ids, int P, int E,
 
 
 // Work estimate of a GEMM row tile of r rows, used to split the tile list
-// among the XCDs: streaming and dequantising the weights cost each tile about
-// one and a half times what one 32-row MFMA group adds.
-__device__ __forceinline__ int gemm_tile_work(int r) { return 3 + 2 * ((r + 31) / 32); }
+// among the XCDs (TileCost: a fixed part for an expert's first tile and for
+// each later one, and a part per 32-row MFMA group).
+__device__ __forceinline__ int gemm_tile_work(int r, bool first, TileCost c) {
+    return (first ? c.first : c.rep) + c.group * ((r + 31) / 32);
+}
 
 // Block-0 part of the forward's staging: the active-expert list and the row
 // tiles from expert_offsets, and the GEMV split-K arrival counters cleared.
@@ -229,7 +231,8 @@ __device__ __forceinline__ void build_schedule(const int32_t *offsets, int E, in
                                                int tile_rows, int max_tiles,
                                                int4 *__restrict__ active, int4 *__restrict__ tiles,
                                                int *__restrict__ split_cnt,
-                                               WsHeader *__restrict__ hdr) {
+                                               WsHeader *__restrict__ hdr,
+                                               TileCost cost = TileCost{1, 1, 0}) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const bool balance = tile_rows >= 32;
     // the GEMV's split-K arrival counters start every call at zero
@@ -256,9 +259,10 @@ __device__ __forceinline__ void build_schedule(const int32_t *offsets, int E, in
             na += cnt[i] > 0;
             nt += (cnt[i] + tile_rows - 1) / tile_rows;
             if (balance) {
-                const int rem = cnt[i] % tile_rows;
-                nw += cnt[i] / tile_rows * gemm_tile_work(tile_rows) +
-                      (rem ? gemm_tile_work(rem) : 0);
+                const int full = cnt[i] / tile_rows, rem = cnt[i] % tile_rows;
+                if (full) nw += gemm_tile_work(tile_rows, true, cost) +
+                                (full - 1) * gemm_tile_work(tile_rows, false, cost);
+                if (rem) nw += gemm_tile_work(rem, full == 0, cost);
             }
         }
     }
@@ -302,7 +306,7 @@ __device__ __forceinline__ void build_schedule(const int32_t *offsets, int E, in
                 if (balance) {
                     // the tile holding the point x/8 of the work starts XCD
                     // x's range if less than half of it lies before the point
-                    const int w = gemm_tile_work(r);
+                    const int w = gemm_tile_work(r, m == 0, cost);
                     for (int x = 1; x < 8; ++x) {
                         const int64_t at = (int64_t)x * total_w - 8 * (int64_t)pw;
                         if (at >= 0 && at < 8 * (int64_t)w) s_first[x] = at < 4 * w ? pt : pt + 1;
