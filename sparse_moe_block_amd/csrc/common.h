@@ -16,7 +16,7 @@ constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 16;
 constexpr int kUnit = 256;        // elements per 16-byte-aligned run of 8 blocks
 constexpr int kGemvTokens = 2;    // token rows a GEMV work item carries
-constexpr int kGemmBM = 128;      // token rows per tile of the block-scaled and int8 GEMMs
+constexpr int kGemmBM = 128;      // token rows per tile of the int8 GEMM
 // Token rows per tile of the fp16 grouped GEMM: five 32-row groups for Q4_0
 // experts, four for the other formats (whose fragments need more registers).
 // An expert whose segment has at most this many rows is one tile.

@@ -8,13 +8,17 @@
 // clamped at 448.
 //
 // The weights reach the matrix cores as stored: no dequantisation at all.
-// Per workgroup a tile of up to 128 rows of one expert's pairs times 256
-// weight rows; eight wavefronts (two per SIMD), wavefront w taking row half
-// w / 4 (rows 64 (w / 4) ..) and weight quarter w % 4: 64 rows x 64 weight
-// rows, two 32-row groups x two 32-column groups, 4 MFMAs per 64-k slice.
-// (Four wavefronts of 128 rows each left one wavefront per SIMD, nothing to
-// run while it waited at the step's rendezvous.)  K advances 256 per step
-// (four slices); a step's activation codes (128 x 256 bytes) and scales, and
+// Per workgroup a tile of up to 160 rows (five 32-row groups) of one
+// expert's pairs times 256 weight rows; eight wavefronts (two per SIMD),
+// wavefront w taking row half w / 4 and weight quarter w % 4: of a tile's
+// MI row groups the first half takes two (three when MI = 5), the second the
+// rest, each against 64 weight rows (two 32-column groups), so each SIMD runs
+// 2 MI MFMAs per 64-k slice.  (Four wavefronts of 128 rows each left one
+// wavefront per SIMD, nothing to run while it waited at the step's
+// rendezvous.)  Each tile streams its expert's weights, so an expert of
+// 129-160 rows is one tile rather than a full one plus a one-group one.  K
+// advances 256 per step (four slices); a step's activation codes (160 x 256
+// bytes) and scales, and
 // its weight codes (256 x 128 bytes) and scales move HBM/L2 -> LDS by DMA
 // into one of two buffer sets while the other is used.
 //
@@ -33,14 +37,14 @@
 namespace fw {
 namespace {
 
-constexpr int MBM = kGemmBM;     // token rows per tile
+constexpr int MBM = 160;         // token rows per tile
 constexpr int MBN = 256;         // weight rows per tile
 constexpr int MKS = 256;         // k per step
 constexpr int MNW = 8;           // wavefronts per workgroup (two per SIMD)
 constexpr int MThreads = 64 * MNW;
-constexpr int kAChunks = MBM * MKS / 16;   // 16-byte chunks of a step's activation codes: 2048
+constexpr int kAChunks = MBM * MKS / 16;   // 16-byte chunks of a step's activation codes: 2560
 constexpr int kBChunks = MBN * MKS / 32;   // of its weight codes: 2048
-static_assert(MBM == 128, "tile shape");
+static_assert(MBM == 160 && 2 * MBM <= MThreads, "tile shape");
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
@@ -93,7 +97,7 @@ __device__ __forceinline__ void stage_x_row_mx8(const void *__restrict__ x, int 
     if (bad) atomicOr(&hdr->status, FW_STATUS_RANGE);
 }
 
-// Block 0: the schedule (active experts, 128-row tiles); the other blocks:
+// Block 0: the schedule (active experts, 160-row tiles); the other blocks:
 // one wavefront per token row, staged as MXFP8.
 __global__ __launch_bounds__(kPrepThreads) void prepare_mx8_kernel(
     const int32_t *__restrict__ offsets, int E, int P, const void *__restrict__ x, int act_bf16,
@@ -145,9 +149,9 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
     // into one from reads of the other only when they are distinct objects
     __shared__ uint4 A0[kAChunks], A1[kAChunks];
     __shared__ uint4 B0[kBChunks], B1[kBChunks];
-    // 8 scale bytes per row and step (the second half: padding the scale DMA
-    // of wavefronts 4..7 writes, so that every thread issues it)
-    __shared__ uint32_t AS0[MBM * 4], AS1[MBM * 4];
+    // 8 scale bytes per row and step (dwords past 2 MBM: padding that the
+    // scale DMA of the remaining threads writes, so that every thread issues it)
+    __shared__ uint32_t AS0[MThreads], AS1[MThreads];
     __shared__ uint32_t BS0[MBN * 2], BS1[MBN * 2];
     auto Abuf = [&](int buf) { return buf ? A1 : A0; };
     auto Bbuf = [&](int buf) { return buf ? B1 : B0; };
@@ -186,15 +190,15 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
     // activation codes: slot s is position s % 16 of tile row s / 16 and holds
     // its chunk (s % 16) ^ (row % 16) (so that the 32 lanes reading one chunk
     // of 32 rows hit distinct banks); instruction i covers row group i
-    uint32_t aoff[4];
+    uint32_t aoff[MBM / 32];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MBM / 32; ++i) {
         const int s = i * MThreads + tid, r = s / 16, c = (s % 16) ^ (r % 16);
         aoff[i] = (uint32_t)src_row(r) * (uint32_t)K + 16u * c;
     }
-    // activation scales: slot tid (< 256) is dword tid % 2 of row tid / 2's 8
-    // bytes; threads 256.. repeat those of threads 0.. into the padding
-    const uint32_t asoff = (uint32_t)src_row((tid % 256) / 2) * (uint32_t)(K / 32) +
+    // activation scales: slot tid (< 2 MBM) is dword tid % 2 of row tid / 2's
+    // 8 bytes; threads 2 MBM.. repeat those of threads 0.. into the padding
+    const uint32_t asoff = (uint32_t)src_row((tid % (2 * MBM)) / 2) * (uint32_t)(K / 32) +
                            4u * (tid % 2);
     // weight rows: LDS row Rl is matrix row wrow(Rl) of the expert
     auto wrow = [&](int Rl) {
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
     // 255 of a gate/up tile: the up matrix's, threads 256 ..)
     const uint32_t bsoff = (uint32_t)wrow(tid / 2) * (uint32_t)(K / 32) + 4u * (tid % 2);
     // The main loop for a tile of MI 32-row groups (the groups that hold rows:
-    // their DMA only) of which this wavefront's row half holds MW (0 .. 2:
+    // their DMA only) of which this wavefront's row half holds MW (0 .. 3:
     // its fragments and MFMAs).  Both are template parameters so that the
     // loop body has no branch: the compiler would otherwise sink a step's
     // MFMAs past the DMA wait at its end.
@@ -262,7 +266,8 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
 
     const int steps = K / MKS;
     const int wr[2] = {mx_wrow<GU>(wq, 0, n), mx_wrow<GU>(wq, 1, n)};
-    const int r0 = 64 * rh + n;   // the lane's first tile row
+    constexpr int kHalf0 = MI > 4 ? 3 : 2;   // row groups of the first row half
+    const int r0 = 32 * kHalf0 * rh + n;   // the lane's first tile row
 
     // one step from buffer set `buf`; pf(S) issues the next step's DMA after
     // slice S's MFMAs
@@ -335,7 +340,7 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
     }
     if (st < steps) step(0, [](int) {});
 
-    // ---- epilogue: acc[mi][cg][v] is tile row 64 rh + 32 mi + 8 (v / 4) +
+    // ---- epilogue: acc[mi][cg][v] is tile row r0 - n + 32 mi + 8 (v / 4) +
     // 4 g + v % 4, LDS weight row wr[cg] ----
     bool range = false;
     if constexpr (GU) {
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
         for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int row = 64 * rh + 32 * mi + 8 * (v >> 2) + 4 * g + (v & 3);
+                const int row = r0 - n + 32 * mi + 8 * (v >> 2) + 4 * g + (v & 3);
                 const float gv = acc[mi][0][v], up = acc[mi][1][v];
                 const float av = gv / (1.0f + __expf(-gv)) * up;
                 uint32_t m = __float_as_uint(av) & 0x7FFFFFFFu;
@@ -366,7 +371,7 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
         for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int row = 64 * rh + 32 * mi + 8 * (v >> 2) + 4 * g + (v & 3);
+                const int row = r0 - n + 32 * mi + 8 * (v >> 2) + 4 * g + (v & 3);
                 if (row < rows) {
 #pragma unroll
                     for (int cg = 0; cg < 2; ++cg)
@@ -378,11 +383,13 @@ __global__ __launch_bounds__(MThreads, 1) void gemm_mx_kernel(
     };
     // the tile's row groups, and the share of this wavefront's row half
     auto go = [&]<int MI>() __attribute__((always_inline)) {
-        if (rh == 0) run.template operator()<MI, (MI < 2 ? MI : 2)>();
-        else run.template operator()<MI, (MI > 2 ? MI - 2 : 0)>();
+        constexpr int H0 = MI > 4 ? 3 : 2;
+        if (rh == 0) run.template operator()<MI, (MI < H0 ? MI : H0)>();
+        else run.template operator()<MI, (MI > H0 ? MI - H0 : 0)>();
     };
     const int mi = (rows + 31) / 32;
-    if (mi > 3) go.template operator()<4>();
+    if (mi > 4) go.template operator()<5>();
+    else if (mi > 3) go.template operator()<4>();
     else if (mi > 2) go.template operator()<3>();
     else if (mi > 1) go.template operator()<2>();
     else go.template operator()<1>();

@@ -2,9 +2,13 @@
 output row.  Top-1 routing written on the host sets each expert's row count
 directly: counts at and around the 32-row MFMA groups and the 128-row (Q8_0)
 and 160-row (Q4_0) tiles, experts with no rows, and one expert with several
-tiles.  The shared expert (Q4_0) runs all 1891 rows as 160-row tiles with a
-131-row last tile.  The schedule's XCD ranges split this list by work, so
-range boundaries fall inside the larger experts' tiles."""
+tiles.  The shared expert runs all 1891 rows as 160-row (Q4_0, fp16
+activations; MXFP4, MXFP8 activations) or 128-row tiles, the last one partial.
+The same row counts go through the two activation-quantising modes: the
+block-scaled GEMM (160-row tiles, five groups split three and two over the
+row halves) and the int8 GEMM (128-row tiles).  The schedule's XCD ranges
+split the tile list by work or by count, so range boundaries fall inside the
+larger experts' tiles."""
 
 import numpy as np
 import pytest
@@ -14,6 +18,8 @@ import moegen
 from moegen.configs import LayerConfig
 from sparse_moe_block_amd import fwmoe as fw
 from tests import gpu_util as G
+from tests.test_gpu_int8 import check_int8, h_step_max
+from tests.test_gpu_mx8 import check_mx8
 
 pytestmark = pytest.mark.gpu
 
@@ -23,18 +29,21 @@ TILES = LayerConfig(9, "tiles: H=512 F=512 E=16 k=1 shared q4_0", 512, len(COUNT
                     C.Q4_0, C.BF16, C.BF16, C.SOFTMAX, 0.02, shared_ffn=256, shared_q=C.Q4_0)
 
 
+MODES = {"mxfp8": TILES.with_(expert_q=C.MXFP4, shared_q=C.MXFP4, act_quant="mxfp8"),
+         "int8": TILES.with_(act_quant="int8")}
+
+
 def _ids():
     ids = np.concatenate([np.full(n, e, np.int32) for e, n in enumerate(COUNTS)])
     np.random.default_rng(9).shuffle(ids)   # an expert's rows gather scattered tokens
     return ids[:, None]
 
 
-@pytest.mark.parametrize("qtype", [C.Q4_0, C.Q8_0, C.Q4_K])
-def test_tile_boundaries(ref, qtype):
-    cfg = TILES
+def _run(ref, cfg, qtype=None):
     ids = _ids()
     T = ids.shape[0]
-    print(f"tile rows {qtype} T={T} counts={COUNTS}", flush=True)
+    print(f"tile rows {qtype or cfg.expert_q} act_quant={cfg.act_quant} T={T} "
+          f"counts={COUNTS}", flush=True)
     dl = G.layer(cfg, qtype=qtype)
     desc = G.desc_of(cfg, path="gemm", qtype=qtype)
     x = moegen.make_x(cfg, T, device=G.DEV)
@@ -46,4 +55,20 @@ def test_tile_boundaries(ref, qtype):
     assert fw.fw_moe_read_status(ws) == 0
     assert np.array_equal(np.diff(off.cpu().numpy()), COUNTS)
     want = G.oracle_forward(ref, cfg, dl, moegen.as_numpy_bits(x), ids, w)
-    G.check_out(out.cpu().numpy(), want)
+    return out.cpu().numpy(), want, desc, ws, T
+
+
+@pytest.mark.parametrize("qtype", [C.Q4_0, C.Q8_0, C.Q4_K])
+def test_tile_boundaries(ref, qtype):
+    got, want, _, _, _ = _run(ref, TILES, qtype)
+    G.check_out(got, want)
+
+
+@pytest.mark.parametrize("mode", sorted(MODES))
+def test_tile_boundaries_quantised_activations(ref, mode):
+    cfg = MODES[mode]
+    got, want, desc, ws, T = _run(ref, cfg)
+    if mode == "mxfp8":
+        check_mx8(got, want)
+    else:
+        check_int8(got, want, h_step_max(desc, cfg, ws, T))
