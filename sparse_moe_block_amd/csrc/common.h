@@ -36,18 +36,24 @@ __host__ __device__ constexpr int xcd_tile_cap(int P, int E, int tile_rows, int 
 // later tile of the expert, and a part per 32-row MFMA group.  Measured on
 // Zipf-routed prefill: the eight-wave fp16 and the int8 kernels run faster
 // with ranges of equal estimated work (a one-group tile costing about half a
-// four-group one, as timed on the DeepSeek-shaped layer); the four-wave fp16 and the block-scaled kernels
-// with ranges of equal tile counts -- by work their gate/up launches were
-// 4-8 % slower, and slower still when an expert's later tiles counted less.
+// four-group one, as timed on the DeepSeek-shaped layer; for Q4_0's 160-row
+// tiles a larger fixed part, (12, 12, 2) against (3, 3, 2): gate/up 170 ->
+// 160 us, while Q4_K and MXFP4 were 4-5 % slower with it); the four-wave
+// fp16 and the block-scaled kernels with ranges of equal tile counts -- by
+// work their gate/up launches were 4-8 % slower, and slower still when an
+// expert's later tiles counted less.
 struct TileCost {
     int first, rep, group;
 };
-constexpr TileCost kCostF16{3, 3, 2};    // fp16, eight-wave workgroups (Q4_0, Q4_K, MXFP4)
-constexpr TileCost kCostF16W4{1, 1, 0};  // fp16, four-wave workgroups (Q8_0, Q6_K): counts
-constexpr TileCost kCostMx8{1, 1, 0};    // block-scaled MFMA (MXFP8 activations): counts
-constexpr TileCost kCostI8{3, 3, 2};     // int8 MFMA
+constexpr TileCost kCostF16Q4{12, 12, 2};  // fp16, Q4_0 (160-row tiles)
+constexpr TileCost kCostF16{3, 3, 2};      // fp16, eight-wave workgroups (Q4_K, MXFP4)
+constexpr TileCost kCostF16W4{1, 1, 0};    // fp16, four-wave workgroups (Q8_0, Q6_K): counts
+constexpr TileCost kCostMx8{1, 1, 0};      // block-scaled MFMA (MXFP8 activations): counts
+constexpr TileCost kCostI8{3, 3, 2};       // int8 MFMA
 constexpr TileCost gemm_tile_cost(int q) {
-    return q == FW_Q8_0 || q == FW_Q6_K ? kCostF16W4 : kCostF16;
+    return q == FW_Q4_0                   ? kCostF16Q4
+           : q == FW_Q8_0 || q == FW_Q6_K ? kCostF16W4
+                                          : kCostF16;
 }
 // AUTO: the GEMV family while the routed pairs average at most this many rows
 // per expert (T * k <= 2 E), the grouped GEMM above.  Measured crossovers, in
